@@ -1,0 +1,371 @@
+"""Plain float64 NumPy oracle for fused RoPE + SDPA.  TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check and the bench's CPU-baseline leg may call this module.
+It shares nothing with the HIP path.  Every step is the definition written out; the
+only structure added is that query rows are processed in chunks (each chunk takes
+an exact softmax over all keys of its rows, so chunking changes nothing but memory)
+and that (batch, head) pairs may be mapped over a thread pool.
+
+Citations name the page and section the step follows:
+  [FR]  "Metal Flash Attention" (SimpleTuner docs), section "Fused RoPE + SDPA"
+  [EN]  same page, section "Enable In SimpleTuner"
+  [RQ]  same page, section "Requirements"
+  [PR]  SimpleTuner pull request "metal-flash-attention: causal training ungated;
+        fused RoPE + Attention for Flux1/Flux2, Z-Image and Krea"
+Where the pages are silent the reading taken is stated at the function.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+
+def _np64(x) -> np.ndarray:
+    """Exact float64 upcast of a torch tensor or array (bf16/fp16/fp32 values are exact in float64)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        import torch
+
+        x = x.detach().to("cpu")
+        if x.dtype == torch.bool:
+            return x.numpy()
+        return x.to(torch.float64).numpy()
+    x = np.asarray(x)
+    return x if x.dtype == np.bool_ else x.astype(np.float64)
+
+
+def _tables4(t: np.ndarray) -> np.ndarray:
+    """Cos/sin table as [Bt, 1, S, D] (Bt = 1 or B): shapes [S,D], [1,S,D], [B,S,D] are accepted [FR]."""
+    t = np.asarray(t, dtype=np.float64)
+    if t.ndim == 2:
+        t = t[None]
+    assert t.ndim == 3, "rope tables are [S,D], [1,S,D] or [B,S,D]"
+    return t[:, None, :, :]
+
+
+# --------------------------------------------------------------------------------------
+# Rotation  [FR]: interleaved-pair rotary embedding applied to Q and K (not V); the
+# complex-multiply formulation (x_2i + i x_2i+1) * (cos + i sin) is the same rotation.
+# --------------------------------------------------------------------------------------
+def _pair_swap(x: np.ndarray) -> np.ndarray:
+    """J(x): J(x)[2i] = -x[2i+1], J(x)[2i+1] = x[2i]  (multiplication by i on each pair)."""
+    out = np.empty_like(x)
+    out[..., 0::2] = -x[..., 1::2]
+    out[..., 1::2] = x[..., 0::2]
+    return out
+
+
+def rope_rotate(x, cos, sin) -> np.ndarray:
+    """R(x) = x * cos + J(x) * sin on [B, H, S, D] with per-position tables [FR].
+
+    With pair-duplicated tables this is x'_2i = x_2i c - x_2i+1 s, x'_2i+1 = x_2i s + x_2i+1 c.
+    """
+    x = _np64(x)
+    c, s = _tables4(_np64(cos)), _tables4(_np64(sin))
+    return x * c + _pair_swap(x) * s
+
+
+def rope_rotate_vjp(g, cos, sin) -> np.ndarray:
+    """Exact vector-Jacobian product of rope_rotate w.r.t. x (the gradient of the unrotated input).
+
+    gx_2i   =  g_2i c_2i   + g_2i+1 s_2i+1
+    gx_2i+1 = -g_2i s_2i   + g_2i+1 c_2i+1
+    For pair-duplicated tables this is the same pairwise rotation with sin negated,
+    which is how [FR] states the backward of the fused path.
+    """
+    g = _np64(g)
+    c, s = _tables4(_np64(cos)), _tables4(_np64(sin))
+    gc = g * c
+    gs = g * s
+    out = np.empty_like(g)
+    out[..., 0::2] = gc[..., 0::2] + gs[..., 1::2]
+    out[..., 1::2] = -gs[..., 0::2] + gc[..., 1::2]
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# Masks  [EN]: bool masks mean True = attend; additive float masks are added to the
+# scores; batched [B,H,Sq,Skv] and broadcast shapes such as [B,1,1,Skv] (up to 4-D).
+# Reading: the additive mask is added after scaling and is not itself scaled (the page
+# mirrors the PyTorch SDPA signature, whose convention this is).
+# --------------------------------------------------------------------------------------
+def mask_to_additive(mask, kind: str):
+    """Return a float64 array broadcastable to [B,H,Sq,Skv] (4-D), or None."""
+    if kind in (None, "none") or mask is None:
+        return None
+    m = _np64(mask)
+    while m.ndim < 4:
+        m = m[None]
+    if kind == "bool":
+        return np.where(m.astype(bool), 0.0, -np.inf)
+    if kind == "additive":
+        return m.astype(np.float64)
+    raise ValueError(f"unknown mask kind {kind!r}")
+
+
+def _mask_slice(madd, b: int, h: int):
+    if madd is None:
+        return None
+    return madd[b if madd.shape[0] > 1 else 0, h if madd.shape[1] > 1 else 0]
+
+
+def _scores(qr_rows, kr, scale, mrows, causal, rows):
+    """s_ij = scale <q'_i, k'_j> + m_ij, with -inf above the diagonal when causal (top-left aligned)."""
+    s = scale * (qr_rows @ kr.T)
+    if mrows is not None:
+        s = s + mrows
+    if causal:
+        s = np.where(np.arange(kr.shape[0])[None, :] > rows[:, None], -np.inf, s)
+    return s
+
+
+def _softmax_rows(s):
+    """Exact row softmax.  A row whose every score is -inf has no key to attend: P = 0, LSE = -inf."""
+    m = s.max(axis=1)
+    ok = np.isfinite(m)
+    m0 = np.where(ok, m, 0.0)
+    e = np.exp(s - m0[:, None])
+    l = e.sum(axis=1)
+    p = np.where(ok[:, None], e / np.where(ok, l, 1.0)[:, None], 0.0)
+    lse = np.where(ok, m0 + np.log(np.where(ok, l, 1.0)), -np.inf)
+    return p, lse
+
+
+def _mask_rows(mhead, rows):
+    if mhead is None:
+        return None
+    return mhead[rows] if mhead.shape[0] > 1 else mhead[0][None, :]
+
+
+def _map_heads(fn, pairs, workers):
+    if workers <= 1 or len(pairs) <= 1:
+        return [fn(p) for p in pairs]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, pairs))
+
+
+def _blas_single_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+
+        return threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover - threadpoolctl is present in this image
+        import contextlib
+
+        return contextlib.nullcontext()
+
+
+def attention_forward(qr, kr, v, scale, madd=None, causal=False, rows=None, pairs=None,
+                      chunk=512, workers=1):
+    """O = softmax(scale * Q' K'^T + M) V and LSE per row, on already-rotated Q', K'.
+
+    qr, kr, v: float64 [B, H, S, D].  rows: optional query indices to evaluate (all by
+    default).  pairs: optional list of (b, h) to evaluate (all by default).
+    Returns (O [len(pairs), len(rows), D], LSE [len(pairs), len(rows)]) when pairs is
+    given, else ([B, H, rows, D], [B, H, rows]).
+    """
+    B, H, Sq, D = qr.shape
+    idx = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    plist = [(b, h) for b in range(B) for h in range(H)] if pairs is None else list(pairs)
+
+    def one(bh):
+        b, h = bh
+        mh = _mask_slice(madd, b, h)
+        O = np.empty((len(idx), v.shape[-1]))
+        L = np.empty(len(idx))
+        for c0 in range(0, len(idx), chunk):
+            r = idx[c0:c0 + chunk]
+            s = _scores(qr[b, h, r], kr[b, h], scale, _mask_rows(mh, r), causal, r)
+            p, lse = _softmax_rows(s)
+            O[c0:c0 + len(r)] = p @ v[b, h]
+            L[c0:c0 + len(r)] = lse
+        return O, L
+
+    with _blas_single_thread() if workers > 1 else _null():
+        res = _map_heads(one, plist, workers)
+    O = np.stack([r[0] for r in res])
+    L = np.stack([r[1] for r in res])
+    if pairs is None:
+        O = O.reshape(B, H, len(idx), -1)
+        L = L.reshape(B, H, len(idx))
+    return O, L
+
+
+def attention_backward(qr, kr, v, do, scale, madd=None, causal=False, pairs=None, chunk=512, workers=1):
+    """Gradients of sum(O * dO) w.r.t. Q', K', V (rotated frame), textbook softmax backward.
+
+    dV = P^T dO;  dP = dO V^T;  delta_i = sum_j P_ij dP_ij;  dS = P o (dP - delta);
+    dQ' = scale dS K';  dK' = scale dS^T Q'.
+    Returns (dqr, dkr, dv), each [B,H,S,D] (or [len(pairs),S,D] when pairs is given).
+    """
+    B, H, Sq, D = qr.shape
+    Skv = kr.shape[2]
+    plist = [(b, h) for b in range(B) for h in range(H)] if pairs is None else list(pairs)
+
+    def one(bh):
+        b, h = bh
+        mh = _mask_slice(madd, b, h)
+        dq = np.zeros((Sq, D))
+        dk = np.zeros((Skv, D))
+        dv = np.zeros((Skv, v.shape[-1]))
+        for c0 in range(0, Sq, chunk):
+            r = np.arange(c0, min(Sq, c0 + chunk))
+            s = _scores(qr[b, h, r], kr[b, h], scale, _mask_rows(mh, r), causal, r)
+            p, _ = _softmax_rows(s)
+            dov = do[b, h, r]
+            dv += p.T @ dov
+            dp = dov @ v[b, h].T
+            delta = (p * dp).sum(axis=1)
+            ds = p * (dp - delta[:, None])
+            dq[r] = scale * (ds @ kr[b, h])
+            dk += scale * (ds.T @ qr[b, h, r])
+        return dq, dk, dv
+
+    with _blas_single_thread() if workers > 1 else _null():
+        res = _map_heads(one, plist, workers)
+    out = [np.stack([r[i] for r in res]) for i in range(3)]
+    if pairs is None:
+        out = [o.reshape(B, H, *o.shape[1:]) for o in out]
+    return tuple(out)
+
+
+def _null():
+    import contextlib
+
+    return contextlib.nullcontext()
+
+
+def _resolve_scale(scale, D):
+    """[FR]: scale=None means 1/sqrt(D), taken here as the float64 nearest to the exact value
+    (1/math.sqrt(D) can be one ulp off, e.g. at D = 128)."""
+    if scale is not None:
+        return float(scale)
+    from decimal import Decimal, localcontext
+
+    with localcontext() as ctx:
+        ctx.prec = 60
+        return float(Decimal(1) / Decimal(int(D)).sqrt())
+
+
+def rope_sdpa_forward(q, k, v, cos, sin, mask=None, mask_kind="none", causal=False, scale=None,
+                      rows=None, pairs=None, workers=1):
+    """Fused RoPE + SDPA forward [FR]: rotate Q and K, then exact attention.  Returns (O, LSE)."""
+    q64, k64, v64 = _np64(q), _np64(k), _np64(v)
+    qr = rope_rotate(q64, cos, sin)
+    kr = rope_rotate(k64, cos, sin)
+    madd = mask_to_additive(mask, mask_kind)
+    return attention_forward(qr, kr, v64, _resolve_scale(scale, q64.shape[-1]), madd, causal,
+                             rows=rows, pairs=pairs, workers=workers)
+
+
+def rope_sdpa_backward(q, k, v, cos, sin, do, mask=None, mask_kind="none", causal=False, scale=None,
+                       pairs=None, workers=1):
+    """Gradients w.r.t. the unrotated Q, K and V [FR]: attention backward in the rotated frame,
+    then the exact VJP of the rotation on dQ' and dK'.  The mask and tables get no gradient.
+    Returns (dQ, dK, dV).
+    """
+    q64, k64, v64, do64 = _np64(q), _np64(k), _np64(v), _np64(do)
+    qr = rope_rotate(q64, cos, sin)
+    kr = rope_rotate(k64, cos, sin)
+    madd = mask_to_additive(mask, mask_kind)
+    dqr, dkr, dv = attention_backward(qr, kr, v64, do64, _resolve_scale(scale, q64.shape[-1]), madd,
+                                      causal, pairs=pairs, workers=workers)
+    if pairs is None:
+        return rope_rotate_vjp(dqr, cos, sin), rope_rotate_vjp(dkr, cos, sin), dv
+    # per-pair tables: index the batch of each (b, h)
+    c, s = _np64(cos), _np64(sin)
+    if c.ndim == 2:
+        c, s = c[None], s[None]
+    dq = np.stack([rope_rotate_vjp(dqr[i][None, None], c[b if c.shape[0] > 1 else 0][None],
+                                   s[b if s.shape[0] > 1 else 0][None])[0, 0]
+                   for i, (b, _) in enumerate(pairs)])
+    dk = np.stack([rope_rotate_vjp(dkr[i][None, None], c[b if c.shape[0] > 1 else 0][None],
+                                   s[b if s.shape[0] > 1 else 0][None])[0, 0]
+                   for i, (b, _) in enumerate(pairs)])
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------------------------------
+# Blockwise int8 variant.  The pages name an int8 mode with blockwise quantization
+# ([EN] quantized aliases; [RQ] QUANT_INT8 / QUANT_BLOCK_WISE) but do not say what is
+# quantized.  Reading taken: the rotated Q and K are quantized symmetrically to
+# [-127, 127] with one fp32 scale per (batch, head, 64-token block) spanning all of D;
+# V stays in the input precision.  Because the quantizer turns floating point into
+# integers, it takes its decisions in fp32, the precision of the kernel that must
+# reproduce them: the rotation is two fp32 products each rounded, then an fp32
+# sum/difference rounded (no fused multiply-add); scale = fp32(amax / 127); code =
+# round-half-even(fp32(x / scale)) clipped to [-127, 127]; an all-zero block gets code 0.
+# --------------------------------------------------------------------------------------
+def rope_rotate_f32(x, cos, sin) -> np.ndarray:
+    """Rotation evaluated in fp32 with every product and sum rounded to fp32 (no FMA)."""
+    import torch
+
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").to(torch.float32).numpy()
+    x = np.asarray(x, dtype=np.float32)
+    c = _tables4(_np64(cos)).astype(np.float32)
+    s = _tables4(_np64(sin)).astype(np.float32)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = (x0 * c[..., 0::2]) - (x1 * s[..., 0::2])
+    out[..., 1::2] = (x0 * s[..., 1::2]) + (x1 * c[..., 1::2])
+    return out
+
+
+def quantize_blockwise_int8(xr32: np.ndarray, block: int = 64):
+    """Symmetric int8 codes and fp32 scales per (b, h, block of `block` tokens).
+
+    Returns (codes int8 [B,H,S,D], scales float32 [B,H,ceil(S/block)]).  A final
+    partial block uses only its valid rows.
+    """
+    xr32 = np.asarray(xr32, dtype=np.float32)
+    B, H, S, D = xr32.shape
+    nb = (S + block - 1) // block
+    codes = np.zeros((B, H, S, D), dtype=np.int8)
+    scales = np.zeros((B, H, nb), dtype=np.float32)
+    for t in range(nb):
+        blk = xr32[:, :, t * block:(t + 1) * block, :]
+        amax = np.abs(blk).max(axis=(2, 3)).astype(np.float32)  # [B,H]
+        sc = (amax / np.float32(127.0)).astype(np.float32)
+        safe = np.where(amax > 0, sc, np.float32(1.0)).astype(np.float32)
+        qv = np.rint(blk / safe[:, :, None, None])  # fp32 division, round half to even
+        qv = np.clip(qv, -127, 127)
+        qv = np.where((amax > 0)[:, :, None, None], qv, 0)
+        codes[:, :, t * block:(t + 1) * block, :] = qv.astype(np.int8)
+        scales[:, :, t] = np.where(amax > 0, sc, np.float32(0.0))
+    return codes, scales
+
+
+def dequantize_blockwise(codes: np.ndarray, scales: np.ndarray, block: int = 64) -> np.ndarray:
+    """x_hat = scale_t * code, in float64."""
+    S = codes.shape[2]
+    sc = np.repeat(scales.astype(np.float64), block, axis=2)[:, :, :S]
+    return codes.astype(np.float64) * sc[..., None]
+
+
+def rope_sdpa_forward_int8(q, k, v, cos, sin, scale=None, rows=None, pairs=None, block=64, workers=1,
+                           codes=None):
+    """int8 variant: rotate in fp32, quantize Q' and K' blockwise, attend on the dequantized values.
+
+    `codes` may carry externally supplied ((q_codes, q_scales), (k_codes, k_scales)) so the
+    attention part can be checked on exactly those quantized values.
+    Returns (O, LSE).
+    """
+    if codes is None:
+        qc, qs = quantize_blockwise_int8(rope_rotate_f32(q, cos, sin), block)
+        kc, ks = quantize_blockwise_int8(rope_rotate_f32(k, cos, sin), block)
+    else:
+        (qc, qs), (kc, ks) = codes
+    qh = dequantize_blockwise(qc, qs, block)
+    kh = dequantize_blockwise(kc, ks, block)
+    v64 = _np64(v)
+    return attention_forward(qh, kh, v64, _resolve_scale(scale, qh.shape[-1]), None, False,
+                             rows=rows, pairs=pairs, workers=workers)
+
+
+def default_workers() -> int:
+    return len(os.sched_getaffinity(0))
