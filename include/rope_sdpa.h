@@ -1,0 +1,154 @@
+/*
+ * rope_sdpa.h - C ABI of the MI355X (gfx950) fused rotary-embedding + scaled dot-product
+ * attention library.
+ *
+ * What it computes (page "Metal Flash Attention", SimpleTuner docs, section "Fused RoPE + SDPA"):
+ *
+ *     Q' = R(Q),  K' = R(K)       interleaved-pair rotation with caller-built cos/sin tables:
+ *                                 x'_2i = x_2i c_i - x_2i+1 s_i,  x'_2i+1 = x_2i s_i + x_2i+1 c_i
+ *     O  = softmax(scale * Q' K'^T + M) V      (softmax accumulated in fp32)
+ *
+ * with M from a bool mask (True = attend) or an additive float mask, broadcast over up to
+ * four dimensions (same page, section "Enable In SimpleTuner"), or a causal (top-left,
+ * key j > query i excluded) pattern.  The rotation happens inside the attention kernels:
+ * no rotated copy of Q or K is ever written to memory.  The backward returns gradients
+ * with respect to the unrotated Q and K (the inverse rotation, i.e. the same rotation with
+ * sin negated, applied to dQ' and dK'), and V.
+ *
+ * Conventions for every entry point
+ *  - All tensors are described by rs_tensor: a DEVICE pointer, a dtype and four sizes and
+ *    strides counted in ELEMENTS (not bytes).  Q, K, V, O, dO, dQ, dK, dV are [B, H, S, D]
+ *    ("BHSD"); any strides are accepted (e.g. a transpose(1,2) view of a BSHD projection or
+ *    an unbind view of a fused QKV tensor) provided stride[3] == 1, the base pointer is
+ *    16-byte aligned and strides 0..2 are multiples of 16 bytes.
+ *  - Ownership: the caller owns every buffer (inputs, outputs, LSE, workspace).  The library
+ *    allocates no device memory in these calls and keeps no pointer after a call returns.
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the
+ *    call returns without waiting.  Inputs must stay valid and unmodified, and outputs and
+ *    workspace untouched by others, until the stream reaches this work.
+ *  - Errors: every argument is validated on the host BEFORE anything is enqueued; on any
+ *    error nothing is launched, outputs are untouched and a negative rs_status is returned.
+ *    Faults during execution surface at the caller's next synchronisation, as in HIP.
+ *  - Thread safety: all entry points are re-entrant; there is no global mode.
+ */
+#ifndef ROPE_SDPA_H
+#define ROPE_SDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROPE_SDPA_ABI_VERSION 1
+
+typedef enum {
+  RS_OK = 0,
+  RS_ERR_NULL = -1,        /* a required pointer is NULL */
+  RS_ERR_DTYPE = -2,       /* dtype not accepted, or Q/K/V/O dtypes differ */
+  RS_ERR_SHAPE = -3,       /* sizes inconsistent or not supported (e.g. D not 64/128) */
+  RS_ERR_STRIDE = -4,      /* stride[3] != 1 or a stride not a multiple of 16 bytes */
+  RS_ERR_ALIGN = -5,       /* base pointer not 16-byte aligned (workspace: 256-byte) */
+  RS_ERR_UNSUPPORTED = -6, /* valid request this build does not implement */
+  RS_ERR_WORKSPACE = -7,   /* workspace NULL or smaller than rope_sdpa_workspace_size() */
+  RS_ERR_INVALID = -8,     /* bad flag, mask kind, scale, or causal together with a mask */
+  RS_ERR_NO_DEVICE = -9,   /* no usable gfx950 device is current */
+  RS_ERR_LAUNCH = -10      /* the HIP launch itself failed */
+} rs_status;
+
+typedef enum { RS_F32 = 0, RS_F16 = 1, RS_BF16 = 2, RS_BOOL = 3 } rs_dtype;
+
+/* How args->mask is read (section "Enable In SimpleTuner"): a bool mask keeps the score where
+ * True and excludes it where False; an additive mask is added to the scaled scores (it is not
+ * itself scaled).  A row with every key excluded yields O = 0 and LSE = -inf (never NaN). */
+typedef enum { RS_MASK_NONE = 0, RS_MASK_BOOL = 1, RS_MASK_ADDITIVE = 2 } rs_mask_kind;
+
+enum {
+  RS_FLAG_CAUSAL = 1u << 0,       /* exclude key j > query i; cannot be combined with a mask */
+  RS_FLAG_QUANT_INT8_QK = 1u << 1 /* forward only: blockwise int8 Q'/K' (see rope_sdpa_fwd) */
+};
+
+typedef struct {
+  void* data;        /* device pointer (never dereferenced on the host) */
+  int32_t dtype;     /* rs_dtype */
+  int32_t reserved;  /* must be 0 */
+  int64_t size[4];   /* elements */
+  int64_t stride[4]; /* elements; a dimension of size 1 may have any stride */
+} rs_tensor;
+
+typedef struct {
+  const rs_tensor* q;    /* [B, H, S, D]  f32 | f16 | bf16 */
+  const rs_tensor* k;    /* [B, H, S, D]  same dtype as q */
+  const rs_tensor* v;    /* [B, H, S, D]  same dtype as q */
+  /* Pair-duplicated rotation tables (cos[2i] == cos[2i+1]), fp32, sizes [Bt, 1, S, D] with
+   * Bt == 1 (shared) or Bt == B (per sample), stride[3] == 1.  Only the even entries are
+   * read; duplication is the caller's precondition (section "Fused RoPE + SDPA"). */
+  const rs_tensor* cos;
+  const rs_tensor* sin;
+  /* Optional mask, sizes [Bm, Hm, Sqm, Skm] with each dimension 1 (broadcast) or full
+   * (B, H, S, S).  RS_MASK_BOOL: dtype RS_BOOL (one byte, nonzero = attend).
+   * RS_MASK_ADDITIVE: dtype RS_F32 or the dtype of q.  Must be NULL for RS_MASK_NONE. */
+  const rs_tensor* mask;
+  int32_t mask_kind;     /* rs_mask_kind */
+  uint32_t flags;        /* RS_FLAG_* */
+  float scale;           /* softmax scale; 0 means 1/sqrt(D); otherwise finite and > 0 */
+} rs_args;
+
+/* Bytes of device workspace a call needs (0 is never returned: the rotation tables are
+ * repacked into it).  `backward` = 0 for rope_sdpa_fwd, 1 for rope_sdpa_bwd. */
+rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* bytes);
+
+/*
+ * Forward.  Writes o (same dtype, sizes as q; any valid strides) and, when lse is not NULL,
+ * the natural-log row normaliser lse[b][h][i] = log(sum_j exp(scale q'_i.k'_j + m_ij)) into a
+ * contiguous fp32 [B, H, S] buffer (-inf for a row with no valid key); lse is what
+ * rope_sdpa_bwd needs.  An all-true bool mask is detected on the device and then costs no
+ * per-element mask reads.
+ * RS_FLAG_QUANT_INT8_QK (bf16/f16 inputs, no mask, no causal, lse may be NULL): after the
+ * fp32 rotation, Q' and K' are quantized per (b, h, 64-token block) to int8 codes
+ * round-half-even(x * fp32(127/amax)) with scale amax/127, QK^T runs on int8 MFMA with exact
+ * int32 accumulation, and P.V stays in the input precision (pages: "Requirements" and
+ * "Enable In SimpleTuner" name an int8 blockwise mode; what is quantized is this library's
+ * reading).
+ */
+rs_status rope_sdpa_fwd(const rs_args* args, const rs_tensor* o, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of rope_sdpa_fwd (section "Fused RoPE + SDPA": gradients with respect to the
+ * pre-rotation Q and K).  Inputs: the same args as the forward, its o and lse, and the
+ * upstream gradient dout (sizes and dtype of o).  Writes dq, dk, dv (dtype of q, sizes of q).
+ * The mask (if any) is a constant: no mask gradient.  Not available with RS_FLAG_QUANT_INT8_QK.
+ */
+rs_status rope_sdpa_bwd(const rs_args* args, const rs_tensor* o, const float* lse,
+                        const rs_tensor* dout, const rs_tensor* dq, const rs_tensor* dk,
+                        const rs_tensor* dv, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* rope_sdpa_status_string(rs_status status);
+
+/* Dispatch counters since load or the last reset (section "Enable In SimpleTuner" describes
+ * counters of this kind).  Host counters count successfully enqueued calls; the all-true
+ * count is kept on the device and reading it synchronises the current device. */
+typedef struct {
+  uint64_t fwd_instream;       /* forward calls without LSE (no-grad) */
+  uint64_t fwd_autograd;       /* forward calls writing LSE (for a later backward) */
+  uint64_t bwd_calls;
+  uint64_t masked_bool;        /* calls (fwd or bwd) with a bool mask */
+  uint64_t masked_additive;
+  uint64_t causal;
+  uint64_t quant_int8;
+  uint64_t mask_all_true_skipped; /* bool masks found all-true on the device */
+  uint64_t errors;             /* calls rejected with a negative status */
+} rs_stats;
+
+void rope_sdpa_get_stats(rs_stats* out);
+void rope_sdpa_reset_stats(void);
+int rope_sdpa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ROPE_SDPA_H */

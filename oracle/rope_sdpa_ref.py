@@ -297,8 +297,9 @@ def rope_sdpa_backward(q, k, v, cos, sin, do, mask=None, mask_kind="none", causa
 # V stays in the input precision.  Because the quantizer turns floating point into
 # integers, it takes its decisions in fp32, the precision of the kernel that must
 # reproduce them: the rotation is two fp32 products each rounded, then an fp32
-# sum/difference rounded (no fused multiply-add); scale = fp32(amax / 127); code =
-# round-half-even(fp32(x / scale)) clipped to [-127, 127]; an all-zero block gets code 0.
+# sum/difference rounded (no fused multiply-add); inv = fp32(127 / amax); code =
+# round-half-even(fp32(x * inv)) clipped to [-127, 127]; the dequantization scale is
+# fp32(amax / 127); an all-zero block gets code 0 and scale 0.
 # --------------------------------------------------------------------------------------
 def rope_rotate_f32(x, cos, sin) -> np.ndarray:
     """Rotation evaluated in fp32 with every product and sum rounded to fp32 (no FMA)."""
@@ -331,8 +332,8 @@ def quantize_blockwise_int8(xr32: np.ndarray, block: int = 64):
         blk = xr32[:, :, t * block:(t + 1) * block, :]
         amax = np.abs(blk).max(axis=(2, 3)).astype(np.float32)  # [B,H]
         sc = (amax / np.float32(127.0)).astype(np.float32)
-        safe = np.where(amax > 0, sc, np.float32(1.0)).astype(np.float32)
-        qv = np.rint(blk / safe[:, :, None, None])  # fp32 division, round half to even
+        inv = (np.float32(127.0) / np.where(amax > 0, amax, np.float32(1.0))).astype(np.float32)
+        qv = np.rint(blk * inv[:, :, None, None])  # fp32 product, round half to even
         qv = np.clip(qv, -127, 127)
         qv = np.where((amax > 0)[:, :, None, None], qv, 0)
         codes[:, :, t * block:(t + 1) * block, :] = qv.astype(np.int8)

@@ -41,12 +41,14 @@ def test_brute_force_nearest_code_with_ties_to_even():
     x = rs.standard_normal((1, 1, 64, 8)).astype(np.float32)
     x[0, 0, 0, 0] = 4.0  # amax -> scale = 4/127
     sc = np.float32(4.0) / np.float32(127.0)
-    x[0, 0, 1, 1] = np.float32(2.5) * sc  # lands (near) a tie
+    inv = np.float32(127.0) / np.float32(4.0)
+    x[0, 0, 1, 1] = np.float32(2.5) / inv  # lands (near) a tie
+    x[0, 0, 2, 2] = np.float32(0.5) * np.float32(4.0) / np.float32(127.0)
     codes, scales = quantize_blockwise_int8(x)
     assert scales[0, 0, 0] == sc
     cands = np.arange(-127, 128)
     for idx in np.ndindex(x.shape):
-        t = np.float32(x[idx]) / sc  # the fp32 quotient the quantizer decides on
+        t = np.float32(x[idx]) * inv  # the fp32 product the quantizer decides on
         d = np.abs(cands - np.float64(t))
         best = cands[d == d.min()]
         want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
