@@ -1,0 +1,223 @@
+"""Throughput of fused RoPE + SDPA on one MI355X.
+
+Workload (N=1): FLUX joint text+image attention, B=1, H=24, S=512+4096=4608, D=128, bf16,
+3-axis RoPE (16,56,56) theta=10000, no mask, forward without gradient.  One step is one
+forward call (table packing + attention kernel) over the whole batch.  The same run also
+times the training step at the FLUX training shape (B=2, forward with LSE + backward).
+
+TFLOP/s use the dense attention count 4*B*H*Sq*Skv*D for the forward (halved for causal)
+and 2.5x that for the backward.  Inputs are generated once on the host and are resident
+in HBM before timing starts.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "fused RoPE+attention TFLOP/s (fwd, fwd+bwd) & % MFMA peak, FLUX S=4608"
+
+
+def flops_fwd(B, H, S, D, causal=False):
+    f = 4.0 * B * H * S * S * D
+    return f / 2 if causal else f
+
+
+def _events_time(fn, steps, warmup, stream):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per step
+
+
+def _source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rope_flash_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        e = d.get(kernel_key)
+        if e and e.get("source_hash") == _source_hash():
+            return e.get("bytes_per_launch")
+    except Exception:
+        return None
+    return None
+
+
+def cpu_baseline(budget_s=20.0):
+    """The CPU float64 oracle on the host cores: the same FLUX forward, whole heads, as many as
+    fit in roughly `budget_s` seconds (at least one)."""
+    import synthetic as syn
+    from oracle import rope_sdpa_forward
+    from oracle.rope_sdpa_ref import default_workers
+
+    cores = default_workers()
+    w = syn.flux(batch=1, heads=24, grid=64, dtype="bf16", seed=2000)
+    B, H, S, D = w.q.shape
+    # probe one head per worker to size the sample
+    n_probe = min(H, cores)
+    t0 = time.perf_counter()
+    rope_sdpa_forward(w.q, w.k, w.v, w.cos, w.sin, pairs=[(0, h) for h in range(n_probe)], workers=cores)
+    t_probe = time.perf_counter() - t0
+    per_round = max(t_probe, 1e-3)
+    rounds = max(1, min(int(budget_s / per_round), -(-H // n_probe)))
+    heads = min(H, rounds * n_probe)
+    t0 = time.perf_counter()
+    rope_sdpa_forward(w.q, w.k, w.v, w.cos, w.sin, pairs=[(0, h) for h in range(heads)], workers=cores)
+    dt = time.perf_counter() - t0
+    fl = flops_fwd(1, heads, S, S, D)
+    return {
+        "value": round(fl / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"float64 oracle forward of {heads} of 24 heads of B=1,S=4608,D=128 ({dt:.2f} s wall, "
+                  f"{platform.processor() or platform.machine()})",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train", action="store_true", help="skip the training-step timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    base = None if args.no_cpu_baseline else cpu_baseline()
+
+    import torch
+
+    import synthetic as syn
+    import rope_flash_attention_amd as rfa
+    from oracle import rope_sdpa_forward
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- forward, FLUX B=1 ------------------------------------------------------------------
+    w = syn.flux(batch=1, heads=24, grid=64, dtype="bf16", seed=2000)
+    B, H, S, D = w.q.shape
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    cos, sin = w.cos.to(dev), w.sin.to(dev)
+    out = {}
+
+    def fwd():
+        out["o"] = rfa.rope_scaled_dot_product_attention(q, k, v, cos, sin)
+
+    with torch.no_grad():
+        ms = _events_time(fwd, args.steps, args.warmup, stream)
+    fl = flops_fwd(B, H, S, D)
+    tflops = fl / (ms * 1e-3) / 1e12
+
+    # proof that the timed kernel computed the right thing: sampled rows vs the oracle
+    rows = np.array([0, 511, 512, 2000, S - 1])
+    O_ref, _ = rope_sdpa_forward(w.q, w.k, w.v, w.cos, w.sin, rows=rows, pairs=[(0, 0), (0, 23)])
+    got = out["o"].float().cpu().numpy()
+    got = np.stack([got[0, 0][rows], got[0, 23][rows]])
+    err = float(np.abs(got - O_ref).max() / np.abs(O_ref).max())
+    if not err <= 2e-2:
+        print(json.dumps({"error": f"parity failed in bench: rel err {err}"}))
+        sys.exit(1)
+
+    # ---- training step, FLUX B=2 ------------------------------------------------------------
+    train = None
+    if not args.no_train:
+        wt = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=4100, with_grad=True)
+        tq, tk, tv, tdo = (t.to(dev) for t in (wt.q, wt.k, wt.v, wt.do))
+        tc, ts = wt.cos.to(dev), wt.sin.to(dev)
+        res = {}
+
+        def fwd_lse():
+            res["o"], res["lse"] = rfa.rope_sdpa_fwd_with_lse(tq, tk, tv, tc, ts)
+
+        def bwd():
+            rfa.rope_sdpa_bwd_explicit(tq, tk, tv, tc, ts, res["o"], res["lse"], tdo)
+
+        def step():
+            fwd_lse()
+            bwd()
+
+        fwd_lse()
+        ms_bwd = _events_time(bwd, max(5, args.steps // 2), 2, stream)
+        ms_train = _events_time(step, max(5, args.steps // 2), 2, stream)
+        fl_f = flops_fwd(2, 24, S, D)
+        train = {
+            "config": "B=2,H=24,S=4608,D=128,bf16",
+            "ms_fwd_bwd": round(ms_train, 4),
+            "ms_bwd": round(ms_bwd, 4),
+            "tflops_fwd_bwd": round(3.5 * fl_f / (ms_train * 1e-3) / 1e12, 2),
+            "tflops_bwd": round(2.5 * fl_f / (ms_bwd * 1e-3) / 1e12, 2),
+        }
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "FLUX joint attention forward, B=1 H=24 S=4608 (512 text + 64x64 image) D=128, "
+                               "3-axis RoPE (16,56,56), no mask", "B": B, "H": H, "S": S, "D": D,
+                   "parallelism": "none"},
+        "pct_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": _traffic("fwd_bf16_d128_flux_b1"),
+            "kernel": "fwd_kernel<bf16,128,nomask> (+ table pack kernel inside the timed call)",
+        },
+        "train": train,
+        "parity_rel_err": err,
+        "cpu_baseline": base,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -93,18 +93,51 @@ def rope_rotate_vjp(g, cos, sin) -> np.ndarray:
 # Reading: the additive mask is added after scaling and is not itself scaled (the page
 # mirrors the PyTorch SDPA signature, whose convention this is).
 # --------------------------------------------------------------------------------------
-def mask_to_additive(mask, kind: str):
-    """Return a float64 array broadcastable to [B,H,Sq,Skv] (4-D), or None."""
-    if kind in (None, "none") or mask is None:
-        return None
-    m = _np64(mask)
-    while m.ndim < 4:
-        m = m[None]
+def _additive(m, kind):
+    """bool -> 0 where True, -inf where False; additive -> the values, as float64."""
+    m = _np64(m)
     if kind == "bool":
         return np.where(m.astype(bool), 0.0, -np.inf)
-    if kind == "additive":
-        return m.astype(np.float64)
-    raise ValueError(f"unknown mask kind {kind!r}")
+    return m.astype(np.float64)
+
+
+class _LazyMask:
+    """A 4-D mask kept in its own dtype; (b, h, rows) slices are converted on demand so that
+    full-size [B, H, S, S] masks never need a float64 copy."""
+
+    def __init__(self, mask, kind):
+        while mask.dim() < 4 if hasattr(mask, "dim") else np.ndim(mask) < 4:
+            mask = mask[None]
+        self.m, self.kind = mask, kind
+        self.shape = tuple(mask.shape)
+
+    def __getitem__(self, bh):
+        b, h = bh
+        return _LazyHead(self.m[b, h], self.kind)
+
+
+class _LazyHead:
+    def __init__(self, m2, kind):
+        self.m2, self.kind = m2, kind
+        self.shape = tuple(m2.shape)
+
+    def __getitem__(self, rows):
+        return _additive(self.m2[rows], self.kind)
+
+
+def mask_to_additive(mask, kind: str):
+    """The mask as additive float64 values broadcastable to [B,H,Sq,Skv], or None.  Large
+    masks stay lazy: indexing [b, h] and then rows converts only that slice."""
+    if kind in (None, "none") or mask is None:
+        return None
+    if kind not in ("bool", "additive"):
+        raise ValueError(f"unknown mask kind {kind!r}")
+    if (mask.numel() if hasattr(mask, "numel") else np.size(mask)) <= (1 << 22):
+        m = _additive(mask, kind)
+        while m.ndim < 4:
+            m = m[None]
+        return m
+    return _LazyMask(mask, kind)
 
 
 def _mask_slice(madd, b: int, h: int):
@@ -138,7 +171,7 @@ def _softmax_rows(s):
 def _mask_rows(mhead, rows):
     if mhead is None:
         return None
-    return mhead[rows] if mhead.shape[0] > 1 else mhead[0][None, :]
+    return mhead[rows] if mhead.shape[0] > 1 else mhead[0:1]
 
 
 def _map_heads(fn, pairs, workers):

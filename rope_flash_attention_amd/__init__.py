@@ -1,0 +1,259 @@
+"""Fused rotary position embedding + scaled dot-product attention on AMD MI355X (gfx950).
+
+Python binding over the C ABI in include/rope_sdpa.h.  This module only marshals
+arguments: every step of the computation runs in the library's HIP kernels, on the
+caller's current HIP stream; PyTorch provides device memory and streams.  There is no
+fallback implementation: if the library is missing or rejects a call, an error is raised.
+
+Entry point (page "Metal Flash Attention", SimpleTuner docs, section "Fused RoPE + SDPA"):
+
+    rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin,
+                                      attn_mask=None, is_causal=False, scale=None)
+
+query/key/value are BHSD (strided views accepted), rope_cos/rope_sin are pair-duplicated
+tables of shape [S, D], [1, S, D] or [B, S, D] in any float dtype (normalised to fp32),
+masks are bool (True = attend) or additive float, broadcastable, up to 4-D.  Gradients
+flow to query, key (pre-rotation) and value.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+from ._abi import (RS_BF16, RS_BOOL, RS_F16, RS_F32, RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT8_QK,
+                   RS_MASK_ADDITIVE, RS_MASK_BOOL, RS_MASK_NONE, RsArgs, RsStats, make_tensor)
+
+__all__ = [
+    "rope_scaled_dot_product_attention", "rope_sdpa_fwd", "rope_sdpa_bwd", "rope_sdpa_workspace_size",
+    "rope_sdpa_get_stats", "rope_sdpa_reset_stats", "rope_sdpa_abi_version", "rope_sdpa_status_string",
+    "get_dispatch_stats", "RopeSdpaError", "library_path",
+]
+
+_DT = {torch.float32: RS_F32, torch.float16: RS_F16, torch.bfloat16: RS_BF16, torch.bool: RS_BOOL}
+
+
+class RopeSdpaError(RuntimeError):
+    def __init__(self, code: int):
+        self.code = code
+        super().__init__(_abi.status_string(code))
+
+
+def library_path() -> str:
+    return _abi.LIB_PATH
+
+
+def _check(code: int):
+    if code != 0:
+        raise RopeSdpaError(code)
+
+
+def _desc(t: torch.Tensor) -> _abi.RsTensor:
+    if t.dim() != 4:
+        raise ValueError("expected a 4-D tensor")
+    return make_tensor(t.data_ptr(), _DT[t.dtype], t.shape, t.stride())
+
+
+def _tables4(t: torch.Tensor, device) -> torch.Tensor:
+    """[S,D] | [1,S,D] | [B,S,D] in any float dtype -> fp32 [Bt, 1, S, D] view on `device`."""
+    if t.dim() == 2:
+        t = t.unsqueeze(0)
+    if t.dim() != 3:
+        raise ValueError("rope tables must be [S, D], [1, S, D] or [B, S, D]")
+    t = t.to(device=device, dtype=torch.float32)
+    if t.stride(-1) != 1:
+        t = t.contiguous()
+    return t.unsqueeze(1)
+
+
+def _mask4(mask: torch.Tensor | None, qdtype):
+    if mask is None:
+        return None, RS_MASK_NONE
+    while mask.dim() < 4:
+        mask = mask.unsqueeze(0)
+    if mask.dim() != 4:
+        raise ValueError("attn_mask must have at most 4 dimensions")
+    if mask.dtype == torch.bool:
+        kind = RS_MASK_BOOL
+    else:
+        kind = RS_MASK_ADDITIVE
+        if mask.dtype not in (torch.float32, qdtype):
+            mask = mask.to(torch.float32)
+    if mask.shape[-1] > 1:
+        es = mask.element_size()
+        ok = mask.stride(-1) == 1 and mask.data_ptr() % 16 == 0 and all(
+            (st * es) % 16 == 0 for st, n in zip(mask.stride()[:3], mask.shape[:3]) if n > 1)
+        if not ok:
+            # rows of the mask must start on 16-byte boundaries: copy into a padded buffer
+            n = mask.shape[-1]
+            pad = -(-n * es // 16) * 16 // es
+            buf = torch.empty((*mask.shape[:3], pad), dtype=mask.dtype, device=mask.device)
+            buf[..., :n].copy_(mask)
+            mask = buf[..., :n]
+    return mask, kind
+
+
+class _Call:
+    """Holds the ctypes descriptors of one call (kept alive for the duration of the call)."""
+
+    def __init__(self, q, k, v, cos4, sin4, mask, mask_kind, causal, scale, int8=False):
+        self.tq, self.tk, self.tv = _desc(q), _desc(k), _desc(v)
+        self.tc, self.ts = _desc(cos4), _desc(sin4)
+        self.tm = _desc(mask) if mask is not None else None
+        a = RsArgs()
+        a.q, a.k, a.v = ctypes.pointer(self.tq), ctypes.pointer(self.tk), ctypes.pointer(self.tv)
+        a.cos, a.sin = ctypes.pointer(self.tc), ctypes.pointer(self.ts)
+        a.mask = ctypes.pointer(self.tm) if self.tm is not None else None
+        a.mask_kind = mask_kind
+        a.flags = (RS_FLAG_CAUSAL if causal else 0) | (RS_FLAG_QUANT_INT8_QK if int8 else 0)
+        a.scale = 0.0 if scale is None else float(scale)
+        self.args = a
+
+    def workspace(self, backward: bool, device) -> torch.Tensor:
+        n = ctypes.c_size_t(0)
+        _check(_abi.load().rope_sdpa_workspace_size(ctypes.byref(self.args), int(backward), ctypes.byref(n)))
+        return torch.empty(int(n.value), dtype=torch.uint8, device=device)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _forward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, need_lse, int8=False):
+    lib = _abi.load()
+    call = _Call(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, int8)
+    B, H, S, D = q.shape
+    o = torch.empty((B, H, S, D), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if need_lse else None
+    ws = call.workspace(False, q.device)
+    to = _desc(o)
+    _check(lib.rope_sdpa_fwd(ctypes.byref(call.args), ctypes.byref(to),
+                             lse.data_ptr() if lse is not None else None,
+                             ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return o, lse
+
+
+def _backward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, o, lse, do):
+    lib = _abi.load()
+    call = _Call(q, k, v, cos4, sin4, mask, mask_kind, causal, scale)
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    dk = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    dv = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    ws = call.workspace(True, q.device)
+    tdo, tdq, tdk, tdv, to = _desc(do), _desc(dq), _desc(dk), _desc(dv), _desc(o)
+    _check(lib.rope_sdpa_bwd(ctypes.byref(call.args), ctypes.byref(to), lse.data_ptr(), ctypes.byref(tdo),
+                             ctypes.byref(tdq), ctypes.byref(tdk), ctypes.byref(tdv),
+                             ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return dq, dk, dv
+
+
+class _RopeSdpaFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cos4, sin4, mask, mask_kind, causal, scale):
+        o, lse = _forward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, need_lse=True)
+        ctx.save_for_backward(q, k, v, cos4, sin4, o, lse, mask if mask is not None else torch.empty(0))
+        ctx.has_mask = mask is not None
+        ctx.mask_kind, ctx.causal, ctx.scale = mask_kind, causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, cos4, sin4, o, lse, mask = ctx.saved_tensors
+        if do.stride(-1) != 1 or do.data_ptr() % 16 != 0 or any(
+                (s * do.element_size()) % 16 for s, n in zip(do.stride()[:3], do.shape[:3]) if n > 1):
+            do = do.contiguous()
+        dq, dk, dv = _backward(q, k, v, cos4, sin4, mask if ctx.has_mask else None, ctx.mask_kind, ctx.causal,
+                               ctx.scale, o, lse, do)
+        return dq, dk, dv, None, None, None, None, None, None
+
+
+def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, attn_mask=None, is_causal=False,
+                                      scale=None, quantization=None):
+    """softmax(scale * R(Q) R(K)^T + mask) V with R the interleaved-pair rotation of the tables.
+
+    quantization: None, or "int8" for the blockwise int8 Q'/K' forward (no gradient).
+    """
+    if not (query.is_cuda and key.is_cuda and value.is_cuda):
+        raise ValueError("query, key and value must be device tensors")
+    if query.dtype != key.dtype or query.dtype != value.dtype:
+        raise RopeSdpaError(-2)
+    cos4 = _tables4(rope_cos, query.device)
+    sin4 = _tables4(rope_sin, query.device)
+    mask, kind = _mask4(attn_mask, query.dtype)
+    if quantization not in (None, "int8"):
+        raise ValueError("quantization must be None or 'int8'")
+    needs_grad = torch.is_grad_enabled() and (query.requires_grad or key.requires_grad or value.requires_grad)
+    if quantization == "int8":
+        if needs_grad:
+            raise RopeSdpaError(-6)
+        return _forward(query, key, value, cos4, sin4, mask, kind, is_causal, scale, False, int8=True)[0]
+    if needs_grad:
+        return _RopeSdpaFn.apply(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale)
+    return _forward(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale, need_lse=False)[0]
+
+
+def rope_sdpa_fwd_with_lse(query, key, value, rope_cos, rope_sin, attn_mask=None, is_causal=False, scale=None):
+    """Forward returning (O, LSE) without autograd (LSE is fp32 [B, H, S], natural log)."""
+    mask, kind = _mask4(attn_mask, query.dtype)
+    return _forward(query, key, value, _tables4(rope_cos, query.device), _tables4(rope_sin, query.device),
+                    mask, kind, bool(is_causal), scale, need_lse=True)
+
+
+def rope_sdpa_bwd_explicit(query, key, value, rope_cos, rope_sin, out, lse, dout, attn_mask=None,
+                           is_causal=False, scale=None):
+    """Backward as a plain call: returns (dQ, dK, dV) w.r.t. the unrotated inputs."""
+    mask, kind = _mask4(attn_mask, query.dtype)
+    return _backward(query, key, value, _tables4(rope_cos, query.device), _tables4(rope_sin, query.device),
+                     mask, kind, bool(is_causal), scale, out, lse, dout)
+
+
+# ---- C-ABI names, re-exported -------------------------------------------------------------
+def rope_sdpa_fwd(args, o, lse_ptr, ws_ptr, ws_bytes, stream) -> int:
+    return _abi.load().rope_sdpa_fwd(args, o, lse_ptr, ws_ptr, ws_bytes, stream)
+
+
+def rope_sdpa_bwd(args, o, lse_ptr, dout, dq, dk, dv, ws_ptr, ws_bytes, stream) -> int:
+    return _abi.load().rope_sdpa_bwd(args, o, lse_ptr, dout, dq, dk, dv, ws_ptr, ws_bytes, stream)
+
+
+def rope_sdpa_workspace_size(args, backward: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_abi.load().rope_sdpa_workspace_size(args, int(backward), ctypes.byref(n)))
+    return int(n.value)
+
+
+def rope_sdpa_status_string(code: int) -> str:
+    return _abi.status_string(code)
+
+
+def rope_sdpa_get_stats() -> dict:
+    s = RsStats()
+    _abi.load().rope_sdpa_get_stats(ctypes.byref(s))
+    return {name: int(getattr(s, name)) for name, _ in RsStats._fields_}
+
+
+def rope_sdpa_reset_stats() -> None:
+    _abi.load().rope_sdpa_reset_stats()
+
+
+def rope_sdpa_abi_version() -> int:
+    return int(_abi.load().rope_sdpa_abi_version())
+
+
+def get_dispatch_stats() -> dict:
+    """Dispatch counters under the names the page uses: rope_instream counts no-grad calls,
+    rope_autograd counts gradient calls, mask_all_true_skipped counts all-true bool masks."""
+    s = rope_sdpa_get_stats()
+    return {
+        "rope_instream": s["fwd_instream"],
+        "rope_autograd": s["fwd_autograd"],
+        "backward": s["bwd_calls"],
+        "masked_bool": s["masked_bool"],
+        "masked_additive": s["masked_additive"],
+        "causal": s["causal"],
+        "quantized_int8": s["quant_int8"],
+        "mask_all_true_skipped": s["mask_all_true_skipped"],
+        "errors": s["errors"],
+        "pytorch_fallback": 0,
+    }

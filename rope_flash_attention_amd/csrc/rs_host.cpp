@@ -1,0 +1,445 @@
+// Host side of the C ABI declared in include/rope_sdpa.h: argument validation (pure host
+// code that never dereferences a device pointer), workspace layout, device checks,
+// dispatch counters and kernel launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/rope_sdpa.h"
+#include "rs_internal.h"
+
+namespace {
+
+using namespace rs;
+
+struct Counters {
+  std::atomic<uint64_t> fwd_instream{0}, fwd_autograd{0}, bwd_calls{0}, masked_bool{0},
+      masked_additive{0}, causal{0}, quant_int8{0}, errors{0};
+};
+Counters g_ctr;
+
+rs_status fail(rs_status s) {
+  g_ctr.errors.fetch_add(1, std::memory_order_relaxed);
+  return s;
+}
+
+size_t elem_size(int dt) {
+  switch (dt) {
+    case RS_F32: return 4;
+    case RS_F16: return 2;
+    case RS_BF16: return 2;
+    case RS_BOOL: return 1;
+    default: return 0;
+  }
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Checks a [B,H,S,D]-like operand: pointer, dtype, exact sizes, contiguous last dim,
+// 16-byte base alignment and 16-byte multiples for the strides of non-trivial dims.
+rs_status check_bhsd(const rs_tensor* t, int dtype, const int64_t* size) {
+  if (!t || !t->data) return RS_ERR_NULL;
+  if (t->dtype != dtype) return RS_ERR_DTYPE;
+  if (t->reserved != 0) return RS_ERR_INVALID;
+  for (int i = 0; i < 4; ++i)
+    if (t->size[i] != size[i]) return RS_ERR_SHAPE;
+  if (t->stride[3] != 1) return RS_ERR_STRIDE;
+  const int64_t es = (int64_t)elem_size(dtype);
+  for (int i = 0; i < 3; ++i) {
+    if (t->size[i] <= 1) continue;
+    if (t->stride[i] < 0 || (t->stride[i] * es) % 16 != 0) return RS_ERR_STRIDE;
+  }
+  if (((uintptr_t)t->data) % 16 != 0) return RS_ERR_ALIGN;
+  return RS_OK;
+}
+
+constexpr bool kInt8Available = false;
+
+struct Shape {
+  int64_t B, H, S, D;
+  int dtype;
+  float scale;
+  int64_t Bt;
+  int64_t mB, mH, mQ, mK;  // mask extents (0 when there is no mask)
+};
+
+rs_status check_table(const rs_tensor* t, const Shape& s, int64_t* bt) {
+  if (!t || !t->data) return RS_ERR_NULL;
+  if (t->dtype != RS_F32) return RS_ERR_DTYPE;
+  if (t->reserved != 0) return RS_ERR_INVALID;
+  if (!(t->size[0] == 1 || t->size[0] == s.B) || t->size[1] != 1 || t->size[2] != s.S || t->size[3] != s.D)
+    return RS_ERR_SHAPE;
+  if (t->stride[3] != 1) return RS_ERR_STRIDE;
+  if (t->stride[0] < 0 || t->stride[2] < 0) return RS_ERR_STRIDE;
+  if (((uintptr_t)t->data) % 4 != 0) return RS_ERR_ALIGN;
+  *bt = t->size[0];
+  return RS_OK;
+}
+
+// Validates everything both directions share: Q/K/V, tables, mask, flags and scale.
+rs_status validate_args(const rs_args* a, Shape* out) {
+  if (!a || !a->q || !a->k || !a->v || !a->cos || !a->sin) return RS_ERR_NULL;
+  const rs_tensor* q = a->q;
+  if (!q->data) return RS_ERR_NULL;
+  const int dt = q->dtype;
+  if (dt != RS_F32 && dt != RS_F16 && dt != RS_BF16) return RS_ERR_DTYPE;
+  Shape s{};
+  s.B = q->size[0];
+  s.H = q->size[1];
+  s.S = q->size[2];
+  s.D = q->size[3];
+  s.dtype = dt;
+  if (s.B < 1 || s.H < 1 || s.S < 1) return RS_ERR_SHAPE;
+  if (s.D != 64 && s.D != 128) return RS_ERR_SHAPE;
+  if (s.S > (int64_t)1 << 24) return RS_ERR_SHAPE;
+  const int64_t nqt = (s.S + 127) / 128;
+  if (s.B * s.H * nqt >= ((int64_t)1 << 31) || s.B * s.H * s.S >= ((int64_t)1 << 31)) return RS_ERR_SHAPE;
+  const int64_t sz[4] = {s.B, s.H, s.S, s.D};
+  rs_status st;
+  if ((st = check_bhsd(q, dt, sz)) != RS_OK) return st;
+  // K and V: same dtype as Q (mixed dtypes, e.g. fp32 Q/K with bf16 V, are rejected)
+  if (a->k->dtype != dt || a->v->dtype != dt) return RS_ERR_DTYPE;
+  if ((st = check_bhsd(a->k, dt, sz)) != RS_OK) return st;
+  if ((st = check_bhsd(a->v, dt, sz)) != RS_OK) return st;
+  int64_t bt_c = 0, bt_s = 0;
+  if ((st = check_table(a->cos, s, &bt_c)) != RS_OK) return st;
+  if ((st = check_table(a->sin, s, &bt_s)) != RS_OK) return st;
+  if (bt_c != bt_s) return RS_ERR_SHAPE;
+  s.Bt = bt_c;
+
+  if (a->flags & ~(uint32_t)(RS_FLAG_CAUSAL | RS_FLAG_QUANT_INT8_QK)) return RS_ERR_INVALID;
+  const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
+  if (!(std::isfinite(a->scale)) || a->scale < 0.f) return RS_ERR_INVALID;
+  s.scale = a->scale == 0.f ? (float)(1.0 / std::sqrt((double)s.D)) : a->scale;
+
+  if (a->mask_kind == RS_MASK_NONE) {
+    if (a->mask) return RS_ERR_INVALID;
+  } else if (a->mask_kind == RS_MASK_BOOL || a->mask_kind == RS_MASK_ADDITIVE) {
+    const rs_tensor* m = a->mask;
+    if (!m || !m->data) return RS_ERR_NULL;
+    if (causal) return RS_ERR_INVALID;
+    if (m->reserved != 0) return RS_ERR_INVALID;
+    if (a->mask_kind == RS_MASK_BOOL) {
+      if (m->dtype != RS_BOOL) return RS_ERR_DTYPE;
+    } else if (m->dtype != RS_F32 && m->dtype != dt) {
+      return RS_ERR_DTYPE;
+    }
+    const int64_t full[4] = {s.B, s.H, s.S, s.S};
+    for (int i = 0; i < 4; ++i)
+      if (m->size[i] != 1 && m->size[i] != full[i]) return RS_ERR_SHAPE;
+    const int64_t es = (int64_t)elem_size(m->dtype);
+    if (m->size[3] > 1 && m->stride[3] != 1) return RS_ERR_STRIDE;
+    for (int i = 0; i < 3; ++i) {
+      if (m->size[i] <= 1) continue;
+      if (m->stride[i] < 0) return RS_ERR_STRIDE;
+      if (m->size[3] > 1 && (m->stride[i] * es) % 16 != 0) return RS_ERR_STRIDE;
+    }
+    if (m->size[3] > 1 && ((uintptr_t)m->data) % 16 != 0) return RS_ERR_ALIGN;
+    if (((uintptr_t)m->data) % es != 0) return RS_ERR_ALIGN;
+    s.mB = m->size[0];
+    s.mH = m->size[1];
+    s.mQ = m->size[2];
+    s.mK = m->size[3];
+  } else {
+    return RS_ERR_INVALID;
+  }
+  if (a->flags & RS_FLAG_QUANT_INT8_QK) {
+    if (!kInt8Available || dt == RS_F32) return RS_ERR_UNSUPPORTED;
+    if (a->mask_kind != RS_MASK_NONE || causal) return RS_ERR_UNSUPPORTED;
+  }
+  if (a->mask_kind == RS_MASK_BOOL) {
+    // grid limits of the tile classifier (y: query tiles, z: mask batch x heads)
+    if ((s.mQ + kMaskTile - 1) / kMaskTile > 65535 || s.mB * s.mH > 65535) return RS_ERR_SHAPE;
+  }
+  *out = s;
+  return RS_OK;
+}
+
+struct Layout {
+  size_t ctrl, table, tiles, delta, total;
+  int64_t nqt, nkt;
+};
+
+Layout layout(const Shape& s, int mask_kind, bool backward) {
+  Layout L{};
+  size_t off = 0;
+  L.ctrl = off;
+  off += 256;
+  L.table = off;
+  off += round_up((size_t)s.Bt * s.S * s.D * sizeof(float), 256);  // D/2 float2 per row
+  L.tiles = off;
+  if (mask_kind == RS_MASK_BOOL) {
+    L.nqt = (s.mQ + kMaskTile - 1) / kMaskTile;
+    L.nkt = (s.mK + kMaskTile - 1) / kMaskTile;
+    off += round_up((size_t)(s.mB * s.mH * L.nqt * L.nkt), 256);
+  }
+  L.delta = off;
+  if (backward) off += round_up((size_t)(s.B * s.H * s.S) * sizeof(float), 256);
+  L.total = off;
+  return L;
+}
+
+// One check per device: the library is built for gfx950 only.
+std::mutex g_dev_mu;
+int g_dev_ok[64] = {0};  // 0 unknown, 1 ok, -1 not usable
+
+rs_status current_device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return RS_ERR_NO_DEVICE;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      g_dev_ok[dev] = -1;
+    } else {
+      g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+  }
+  return g_dev_ok[dev] == 1 ? RS_OK : RS_ERR_NO_DEVICE;
+}
+
+MaskView mask_view(const rs_args* a, const Shape& s, const Layout& L, char* ws) {
+  MaskView mv{};
+  if (a->mask_kind == RS_MASK_NONE) return mv;
+  const rs_tensor* m = a->mask;
+  mv.ptr = m->data;
+  mv.sb = m->size[0] > 1 ? m->stride[0] : 0;
+  mv.sh = m->size[1] > 1 ? m->stride[1] : 0;
+  mv.sq = m->size[2] > 1 ? m->stride[2] : 0;
+  mv.sk = m->size[3] > 1 ? m->stride[3] : 0;
+  mv.dtype = m->dtype;
+  mv.key_bcast = m->size[3] == 1;
+  if (a->mask_kind == RS_MASK_BOOL) {
+    mv.tiles = (const uint8_t*)(ws + L.tiles);
+    mv.t_nqt = (int)L.nqt;
+    mv.t_nkt = (int)L.nkt;
+    mv.t_sh = s.mH > 1 ? L.nqt * L.nkt : 0;
+    mv.t_sb = s.mB > 1 ? s.mH * L.nqt * L.nkt : 0;
+  }
+  return mv;
+}
+
+AttnShape attn_shape(const Shape& s) {
+  AttnShape a{};
+  a.B = (int)s.B;
+  a.H = (int)s.H;
+  a.S = (int)s.S;
+  a.scale = s.scale;
+  a.scale_log2 = (float)((double)s.scale * 1.4426950408889634);
+  a.inv_scale = (float)(1.0 / (double)s.scale);
+  return a;
+}
+
+// Enqueues the preparation kernels shared by both directions.
+rs_status prepare(const rs_args* a, const Shape& s, const Layout& L, char* ws, hipStream_t stream) {
+  PackParams pp{};
+  pp.cos = (const float*)a->cos->data;
+  pp.sin = (const float*)a->sin->data;
+  pp.c_sb = a->cos->size[0] > 1 ? a->cos->stride[0] : 0;
+  pp.c_ss = a->cos->stride[2];
+  pp.s_sb = a->sin->size[0] > 1 ? a->sin->stride[0] : 0;
+  pp.s_ss = a->sin->stride[2];
+  pp.out = (float*)(ws + L.table);
+  pp.Bt = (int)s.Bt;
+  pp.S = (int)s.S;
+  pp.D = (int)s.D;
+  pp.ctrl = (unsigned*)(ws + L.ctrl);
+  if (launch_pack_tables(pp, stream) != 0) return RS_ERR_LAUNCH;
+  if (a->mask_kind == RS_MASK_BOOL) {
+    ClassifyParams cp{};
+    cp.mask = mask_view(a, s, L, ws);
+    cp.nb = (int)s.mB;
+    cp.nh = (int)s.mH;
+    cp.Sq = (int)s.mQ;
+    cp.Sk = (int)s.mK;
+    cp.tiles = (uint8_t*)(ws + L.tiles);
+    cp.ctrl = (unsigned*)(ws + L.ctrl);
+    cp.total_blocks = (int)(s.mB * s.mH * L.nqt * L.nkt);
+    if (launch_classify(cp, stream) != 0) return RS_ERR_LAUNCH;
+  }
+  return RS_OK;
+}
+
+Opnd opnd(const rs_tensor* t) {
+  Opnd o;
+  o.ptr = t->data;
+  o.sb = t->stride[0];
+  o.sh = t->stride[1];
+  o.ss = t->stride[2];
+  return o;
+}
+
+rs_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
+  if (!ws || ws_bytes < L.total) return RS_ERR_WORKSPACE;
+  if (((uintptr_t)ws) % 256 != 0) return RS_ERR_ALIGN;
+  return RS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rope_sdpa_abi_version(void) { return ROPE_SDPA_ABI_VERSION; }
+
+const char* rope_sdpa_status_string(rs_status st) {
+  switch (st) {
+    case RS_OK: return "RS_OK: success";
+    case RS_ERR_NULL: return "RS_ERR_NULL: a required pointer is NULL";
+    case RS_ERR_DTYPE: return "RS_ERR_DTYPE: unsupported dtype or Q/K/V/O dtypes differ";
+    case RS_ERR_SHAPE: return "RS_ERR_SHAPE: inconsistent or unsupported sizes (D must be 64 or 128)";
+    case RS_ERR_STRIDE: return "RS_ERR_STRIDE: last-dim stride must be 1 and other strides multiples of 16 bytes";
+    case RS_ERR_ALIGN: return "RS_ERR_ALIGN: base pointer misaligned (16 bytes; workspace 256 bytes)";
+    case RS_ERR_UNSUPPORTED: return "RS_ERR_UNSUPPORTED: combination not implemented";
+    case RS_ERR_WORKSPACE: return "RS_ERR_WORKSPACE: workspace missing or too small";
+    case RS_ERR_INVALID: return "RS_ERR_INVALID: bad flags, mask kind, scale, or causal with a mask";
+    case RS_ERR_NO_DEVICE: return "RS_ERR_NO_DEVICE: no current gfx950 device";
+    case RS_ERR_LAUNCH: return "RS_ERR_LAUNCH: kernel launch failed";
+  }
+  return "unknown rs_status";
+}
+
+rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* bytes) {
+  if (!bytes) return fail(RS_ERR_NULL);
+  Shape s;
+  rs_status st = validate_args(args, &s);
+  if (st != RS_OK) return fail(st);
+  *bytes = layout(s, args->mask_kind, backward != 0).total;
+  return RS_OK;
+}
+
+rs_status rope_sdpa_fwd(const rs_args* a, const rs_tensor* o, float* lse, void* ws, size_t ws_bytes,
+                        void* stream) {
+  Shape s;
+  rs_status st = validate_args(a, &s);
+  if (st != RS_OK) return fail(st);
+  const int64_t sz[4] = {s.B, s.H, s.S, s.D};
+  if (!o) return fail(RS_ERR_NULL);
+  if (o->data && o->dtype != s.dtype) return fail(RS_ERR_DTYPE);
+  if ((st = check_bhsd(o, s.dtype, sz)) != RS_OK) return fail(st);
+  if (lse && ((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
+  const Layout L = layout(s, a->mask_kind, false);
+  if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
+  if ((st = current_device_ok()) != RS_OK) return fail(st);
+
+  char* w = (char*)ws;
+  hipStream_t strm = (hipStream_t)stream;
+  if ((st = prepare(a, s, L, w, strm)) != RS_OK) return fail(st);
+  FwdParams p{};
+  p.q = opnd(a->q);
+  p.k = opnd(a->k);
+  p.v = opnd(a->v);
+  p.o = o->data;
+  p.o_sb = o->stride[0];
+  p.o_sh = o->stride[1];
+  p.o_ss = o->stride[2];
+  p.lse = lse;
+  p.tab.ptr = (const float*)(w + L.table);
+  p.tab.sb = s.Bt > 1 ? s.S * s.D : 0;
+  p.mask = mask_view(a, s, L, w);
+  p.shp = attn_shape(s);
+  const int bm = fwd_block_m(s.dtype);
+  p.num_qt = (int)((s.S + bm - 1) / bm);
+  const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
+  const bool int8 = (a->flags & RS_FLAG_QUANT_INT8_QK) != 0;
+  if (launch_fwd(s.dtype, (int)s.D, a->mask_kind, causal, int8, p, strm) != 0) return fail(RS_ERR_LAUNCH);
+
+  (lse ? g_ctr.fwd_autograd : g_ctr.fwd_instream).fetch_add(1, std::memory_order_relaxed);
+  if (a->mask_kind == RS_MASK_BOOL) g_ctr.masked_bool.fetch_add(1, std::memory_order_relaxed);
+  if (a->mask_kind == RS_MASK_ADDITIVE) g_ctr.masked_additive.fetch_add(1, std::memory_order_relaxed);
+  if (causal) g_ctr.causal.fetch_add(1, std::memory_order_relaxed);
+  if (int8) g_ctr.quant_int8.fetch_add(1, std::memory_order_relaxed);
+  return RS_OK;
+}
+
+rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, const rs_tensor* dout,
+                        const rs_tensor* dq, const rs_tensor* dk, const rs_tensor* dv, void* ws,
+                        size_t ws_bytes, void* stream) {
+  Shape s;
+  rs_status st = validate_args(a, &s);
+  if (st != RS_OK) return fail(st);
+  if (a->flags & RS_FLAG_QUANT_INT8_QK) return fail(RS_ERR_UNSUPPORTED);
+  const int64_t sz[4] = {s.B, s.H, s.S, s.D};
+  if (!o || !dout || !dq || !dk || !dv || !lse) return fail(RS_ERR_NULL);
+  const rs_tensor* ts[5] = {o, dout, dq, dk, dv};
+  for (const rs_tensor* t : ts) {
+    if (t->data && t->dtype != s.dtype) return fail(RS_ERR_DTYPE);
+    if ((st = check_bhsd(t, s.dtype, sz)) != RS_OK) return fail(st);
+  }
+  if (((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
+  const Layout L = layout(s, a->mask_kind, true);
+  if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
+  if ((st = current_device_ok()) != RS_OK) return fail(st);
+
+  char* w = (char*)ws;
+  hipStream_t strm = (hipStream_t)stream;
+  if ((st = prepare(a, s, L, w, strm)) != RS_OK) return fail(st);
+  BwdParams p{};
+  p.q = opnd(a->q);
+  p.k = opnd(a->k);
+  p.v = opnd(a->v);
+  p.o = opnd(o);
+  p.dout = opnd(dout);
+  p.dq = dq->data;
+  p.dq_sb = dq->stride[0];
+  p.dq_sh = dq->stride[1];
+  p.dq_ss = dq->stride[2];
+  p.dk = dk->data;
+  p.dk_sb = dk->stride[0];
+  p.dk_sh = dk->stride[1];
+  p.dk_ss = dk->stride[2];
+  p.dv = dv->data;
+  p.dv_sb = dv->stride[0];
+  p.dv_sh = dv->stride[1];
+  p.dv_ss = dv->stride[2];
+  p.lse = lse;
+  p.delta = (float*)(w + L.delta);
+  p.tab.ptr = (const float*)(w + L.table);
+  p.tab.sb = s.Bt > 1 ? s.S * s.D : 0;
+  p.mask = mask_view(a, s, L, w);
+  p.shp = attn_shape(s);
+  const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
+  if (launch_bwd(s.dtype, (int)s.D, a->mask_kind, causal, p, strm) != 0) return fail(RS_ERR_LAUNCH);
+
+  g_ctr.bwd_calls.fetch_add(1, std::memory_order_relaxed);
+  if (a->mask_kind == RS_MASK_BOOL) g_ctr.masked_bool.fetch_add(1, std::memory_order_relaxed);
+  if (a->mask_kind == RS_MASK_ADDITIVE) g_ctr.masked_additive.fetch_add(1, std::memory_order_relaxed);
+  if (causal) g_ctr.causal.fetch_add(1, std::memory_order_relaxed);
+  return RS_OK;
+}
+
+void rope_sdpa_get_stats(rs_stats* out) {
+  if (!out) return;
+  std::memset(out, 0, sizeof(*out));
+  out->fwd_instream = g_ctr.fwd_instream.load();
+  out->fwd_autograd = g_ctr.fwd_autograd.load();
+  out->bwd_calls = g_ctr.bwd_calls.load();
+  out->masked_bool = g_ctr.masked_bool.load();
+  out->masked_additive = g_ctr.masked_additive.load();
+  out->causal = g_ctr.causal.load();
+  out->quant_int8 = g_ctr.quant_int8.load();
+  out->errors = g_ctr.errors.load();
+  if (current_device_ok() == RS_OK) {
+    uint64_t v = 0;
+    if (hipDeviceSynchronize() == hipSuccess && read_all_true_counter(&v, false) == 0) out->mask_all_true_skipped = v;
+  }
+}
+
+void rope_sdpa_reset_stats(void) {
+  g_ctr.fwd_instream = 0;
+  g_ctr.fwd_autograd = 0;
+  g_ctr.bwd_calls = 0;
+  g_ctr.masked_bool = 0;
+  g_ctr.masked_additive = 0;
+  g_ctr.causal = 0;
+  g_ctr.quant_int8 = 0;
+  g_ctr.errors = 0;
+  if (current_device_ok() == RS_OK) {
+    uint64_t v = 0;
+    if (hipDeviceSynchronize() == hipSuccess) read_all_true_counter(&v, true);
+  }
+}
+
+}  // extern "C"

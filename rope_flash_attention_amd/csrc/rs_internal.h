@@ -1,0 +1,101 @@
+// Internal parameter blocks shared by the host library and the gfx950 kernels.
+// Nothing here is part of the public ABI (include/rope_sdpa.h is).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rs {
+
+enum DType : int { F32 = 0, F16 = 1, BF16 = 2, BOOL8 = 3 };
+enum MaskKind : int { MASK_NONE = 0, MASK_BOOL = 1, MASK_ADD = 2 };
+
+// Tile states of a bool mask over 64 x 64 (query x key) blocks: bit0 = some key attended,
+// bit1 = some key excluded.  OR-ing states combines blocks.
+enum : uint8_t { TILE_ALL_TRUE = 1, TILE_ALL_FALSE = 2, TILE_MIXED = 3 };
+constexpr int kMaskTile = 64;
+
+// A [B, H, S, D] operand: base pointer and element strides of dims 0..2 (dim 3 is contiguous).
+struct Opnd {
+  const void* ptr;
+  int64_t sb, sh, ss;
+};
+
+// A mask as the kernels read it.  Strides are "effective": 0 on broadcast dimensions.
+struct MaskView {
+  const void* ptr;
+  int64_t sb, sh, sq, sk;
+  int dtype;  // BOOL8, F32, F16 or BF16
+  int key_bcast;  // size[3] == 1
+  // tile states (bool masks only): [nb][nh][nqt][nkt] uint8, dims follow the mask's own extents
+  const uint8_t* tiles;
+  int64_t t_sb, t_sh;  // 0 when broadcast over b / h
+  int t_nqt, t_nkt;    // 1 when the mask is broadcast over queries / keys
+};
+
+struct AttnShape {
+  int B, H, S;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+  float inv_scale;   // 1 / scale
+};
+
+// Packed rotation table: per (sample, position) D/2 pairs of (cos, sin) as float2.
+struct Table {
+  const float* ptr;  // float2 pairs, contiguous [Bt][S][D/2]
+  int64_t sb;        // 0 when shared by every sample
+};
+
+struct FwdParams {
+  Opnd q, k, v;
+  void* o;
+  int64_t o_sb, o_sh, o_ss;
+  float* lse;  // nullable, contiguous [B, H, S]
+  Table tab;
+  MaskView mask;
+  AttnShape shp;
+  int num_qt;  // query tiles per (b, h)
+};
+
+struct BwdParams {
+  Opnd q, k, v, o, dout;
+  void* dq;
+  int64_t dq_sb, dq_sh, dq_ss;
+  void* dk;
+  int64_t dk_sb, dk_sh, dk_ss;
+  void* dv;
+  int64_t dv_sb, dv_sh, dv_ss;
+  const float* lse;  // contiguous [B, H, S]
+  float* delta;      // workspace, contiguous [B, H, S]
+  Table tab;
+  MaskView mask;
+  AttnShape shp;
+};
+
+// int8 variant: per-(b, h, 64-token block) codes are recomputed in-stream; nothing persists.
+struct PackParams {
+  const float* cos;
+  const float* sin;
+  int64_t c_sb, c_ss, s_sb, s_ss;  // element strides of the [Bt, 1, S, D] tables (dims 0 and 2)
+  float* out;                      // float2 pairs [Bt][S][D/2]
+  int Bt, S, D;
+  unsigned* ctrl;                  // control words cleared for the mask classifier
+};
+
+struct ClassifyParams {
+  MaskView mask;  // bool
+  int nb, nh, Sq, Sk;  // mask extents (1 on broadcast dimensions)
+  uint8_t* tiles;      // [nb][nh][nqt][nkt]
+  unsigned* ctrl;      // ctrl[0] = some block excluded a key, ctrl[1] = finished blocks
+  int total_blocks;
+};
+
+// Host-side launchers (defined in the .hip files).  Each returns 0 on success or a HIP error.
+int launch_pack_tables(const PackParams& p, void* stream);
+int launch_classify(const ClassifyParams& p, void* stream);
+int fwd_block_m(int dtype);  // query rows per forward workgroup
+int launch_fwd(int dtype, int D, int mask_kind, bool causal, bool int8, const FwdParams& p, void* stream);
+int launch_bwd(int dtype, int D, int mask_kind, bool causal, const BwdParams& p, void* stream);
+// Reads (and optionally clears) the device-side count of all-true bool masks.
+int read_all_true_counter(uint64_t* value, bool reset);
+
+}  // namespace rs

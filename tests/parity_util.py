@@ -1,0 +1,91 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI and compare
+with the CPU float64 oracle on identical seeded inputs.
+
+Tolerances (per tensor, in the tests):
+  fp32 outputs/LSE : max|gpu - ref| <= 1e-5 * max|ref|
+  bf16/fp16 outputs: max|gpu - ref| <= 2e-2 * max|ref|   (fp16 uses the bf16 bound)
+  bf16/fp16 grads  : max|gpu - ref| <= 5e-2 * rms(ref)
+  fp32 grads       : max|gpu - ref| <= 1e-5 * max|ref|
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import rope_flash_attention_amd as rfa
+
+OUT_TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2}
+GRAD_TOL = {"bf16": 5e-2, "f16": 5e-2}
+GRAD_TOL_F32 = 1e-5
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def dt_name(t: torch.Tensor) -> str:
+    return {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}[t.dtype]
+
+
+def gpu_forward(w, need_lse=True, q=None, k=None, v=None, mask=None):
+    d = dev()
+    q = w.q.to(d) if q is None else q
+    k = w.k.to(d) if k is None else k
+    v = w.v.to(d) if v is None else v
+    m = (w.mask.to(d) if w.mask is not None else None) if mask is None else mask
+    with torch.no_grad():
+        if need_lse:
+            o, lse = rfa.rope_sdpa_fwd_with_lse(q, k, v, w.cos.to(d), w.sin.to(d), attn_mask=m,
+                                                is_causal=w.causal, scale=w.scale)
+        else:
+            o = rfa.rope_scaled_dot_product_attention(q, k, v, w.cos.to(d), w.sin.to(d), attn_mask=m,
+                                                      is_causal=w.causal, scale=w.scale)
+            lse = None
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def to64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def rel_max_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    denom = np.abs(ref).max()
+    return np.abs(got - ref).max() / (denom if denom > 0 else 1.0)
+
+
+def rms_err(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt((ref ** 2).mean())
+    return np.abs(np.asarray(got, dtype=np.float64) - ref).max() / (rms if rms > 0 else 1.0)
+
+
+def check_out(name, got, ref, dtype):
+    e = rel_max_err(got, ref)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert e <= OUT_TOL[dtype], f"{name}: relative max error {e:.3e} > {OUT_TOL[dtype]}"
+    return e
+
+
+def check_lse(got, ref, dtype):
+    got = np.asarray(got)
+    ninf = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), ninf), "LSE: -inf rows differ"
+    if (~ninf).any():
+        e = rel_max_err(got[~ninf], ref[~ninf])
+        assert e <= OUT_TOL[dtype], f"LSE: relative max error {e:.3e}"
+        return e
+    return 0.0
+
+
+def check_grad(name, got, ref, dtype):
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    if dtype == "f32":
+        e = rel_max_err(got, ref)
+        assert e <= GRAD_TOL_F32, f"{name}: relative max error {e:.3e} > {GRAD_TOL_F32}"
+    else:
+        e = rms_err(got, ref)
+        assert e <= GRAD_TOL[dtype], f"{name}: max error {e:.3e} of the gradient RMS > {GRAD_TOL[dtype]}"
+    return e

@@ -1,0 +1,225 @@
+"""GPU parity of the forward (HIP kernels through the C ABI) against the CPU float64 oracle.
+
+Every case draws its inputs from the seeded generators in synthetic/, runs the HIP path
+and the oracle on the same values, and compares element by element (small sizes) or on
+sampled rows (full FLUX sizes), with the tolerances in tests/parity_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as syn
+import rope_flash_attention_amd as rfa
+from oracle import rope_sdpa_forward
+from parity_util import check_lse, check_out, dev, gpu_forward, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare(w, rows=None, pairs=None, need_lse=True):
+    dtype = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}[w.q.dtype]
+    o, lse = gpu_forward(w, need_lse=need_lse)
+    O_ref, L_ref = rope_sdpa_forward(w.q, w.k, w.v, w.cos, w.sin, mask=w.mask, mask_kind=w.mask_kind,
+                                     causal=w.causal, scale=w.scale, rows=rows, pairs=pairs, workers=8)
+    o64 = to64(o)
+    if rows is not None or pairs is not None:
+        r = np.arange(w.q.shape[2]) if rows is None else np.asarray(rows)
+        pl = pairs if pairs is not None else [(b, h) for b in range(w.q.shape[0]) for h in range(w.q.shape[1])]
+        o64 = np.stack([o64[b, h][r] for b, h in pl])
+        l64 = np.stack([to64(lse)[b, h][r] for b, h in pl]) if lse is not None else None
+    else:
+        l64 = to64(lse) if lse is not None else None
+    e = check_out("O", o64, O_ref, dtype)
+    if l64 is not None:
+        check_lse(l64, L_ref, dtype)
+    return e
+
+
+def test_tiny_fp32_config():
+    """B=1, H=2, S=128, D=64, fp32, 1-axis RoPE theta=10000, no mask."""
+    w = syn.tiny_fp32()
+    _compare(w)
+
+
+VARIANTS = ["none", "causal", "bool4d", "bool_bcast", "add_f32", "add_same", "key_bcast", "q_bcast"]
+
+
+def _small(dtype, D, S, variant, seed=3):
+    B, H = 2, 2
+    kw = {}
+    if variant == "causal":
+        kw = dict(causal=True)
+    elif variant == "bool4d":
+        kw = dict(mask_kind="bool", mask_shape=(B, H, S, S))
+    elif variant == "bool_bcast":
+        kw = dict(mask_kind="bool", mask_shape=(B, 1, 1, S))
+    elif variant in ("add_f32", "add_same"):
+        kw = dict(mask_kind="additive", mask_shape=(1, H, S, S))
+    elif variant == "key_bcast":
+        kw = dict(mask_kind="bool", mask_shape=(B, 1, S, 1), p_keep=0.9)
+    elif variant == "q_bcast":
+        kw = dict(mask_kind="additive", mask_shape=(B, H, 1, S))
+    w = syn.random_small(B, H, S, D, dtype, seed=seed + S + D, **kw)
+    if variant == "add_f32" and w.mask is not None:
+        w.mask = w.mask.float()
+    return w
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("S", [1, 77, 300])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_small_grid(dtype, D, S, variant):
+    _compare(_small(dtype, D, S, variant))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_no_lse_path_matches(dtype):
+    w = _small(dtype, 128, 200, "bool_bcast")
+    o1, _ = gpu_forward(w, need_lse=True)
+    o2, _ = gpu_forward(w, need_lse=False)
+    assert torch.equal(o1, o2)
+
+
+def test_strided_views_bshd_and_fused_qkv():
+    B, S, H, D = 2, 150, 3, 128
+    w = syn.random_small(B, H, S, D, "bf16", seed=21)
+    d = dev()
+    # BSHD projections viewed as BHSD
+    qb = w.q.transpose(1, 2).contiguous().to(d).transpose(1, 2)
+    kb = w.k.transpose(1, 2).contiguous().to(d).transpose(1, 2)
+    vb = w.v.transpose(1, 2).contiguous().to(d).transpose(1, 2)
+    assert not qb.is_contiguous()
+    o_view, _ = gpu_forward(w, q=qb, k=kb, v=vb)
+    o_ref, _ = gpu_forward(w)
+    assert torch.equal(o_view, o_ref)
+    # fused QKV [B, S, 3, H, D] unbound along dim 2
+    qkv = torch.stack([w.q.transpose(1, 2), w.k.transpose(1, 2), w.v.transpose(1, 2)], dim=2).contiguous().to(d)
+    q2, k2, v2 = (t.transpose(1, 2) for t in qkv.unbind(2))
+    o_qkv, _ = gpu_forward(w, q=q2, k=k2, v=v2)
+    assert torch.equal(o_qkv, o_ref)
+
+
+def test_per_sample_tables():
+    w = syn.random_small(3, 2, 130, 128, "bf16", seed=22, per_sample_tables=True)
+    assert w.cos.shape[0] == 3
+    _compare(w)
+
+
+@pytest.mark.parametrize("kind", ["bool", "additive"])
+def test_fully_masked_rows_give_zero(kind):
+    B, H, S, D = 1, 2, 96, 64
+    w = syn.random_small(B, H, S, D, "bf16", seed=23)
+    keep = torch.ones(B, H, S, S, dtype=torch.bool)
+    keep[:, :, 5] = False
+    keep[:, 1, 70:90] = False
+    if kind == "bool":
+        w.mask, w.mask_kind = keep, "bool"
+    else:
+        w.mask, w.mask_kind = torch.where(keep, 0.0, float("-inf")).to(torch.bfloat16), "additive"
+    o, lse = gpu_forward(w)
+    assert torch.all(o[:, :, 5] == 0) and torch.all(o[:, 1, 70:90] == 0)
+    assert torch.all(torch.isneginf(lse[:, :, 5]))
+    _compare(w)
+
+
+def test_all_true_mask_is_bitwise_no_mask_and_counted():
+    w = syn.random_small(2, 3, 333, 128, "bf16", seed=24)
+    o0, l0 = gpu_forward(w)
+    rfa.rope_sdpa_reset_stats()
+    for shape in [(2, 1, 1, 333), (2, 3, 333, 333), (333,)]:
+        w.mask, w.mask_kind = torch.ones(shape, dtype=torch.bool), "bool"
+        o1, l1 = gpu_forward(w)
+        assert torch.equal(o1, o0) and torch.equal(l1, l0)
+    stats = rfa.get_dispatch_stats()
+    assert stats["mask_all_true_skipped"] == 3, stats
+    # a mask with one excluded key is not counted
+    m = torch.ones(2, 1, 1, 333, dtype=torch.bool)
+    m[1, 0, 0, 7] = False
+    w.mask = m
+    gpu_forward(w)
+    assert rfa.get_dispatch_stats()["mask_all_true_skipped"] == 3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_causal_matches_explicit_tril_mask(dtype):
+    w = syn.random_small(1, 2, 260, 128, dtype, seed=25, causal=True)
+    oc, lc = gpu_forward(w)
+    w.causal = False
+    w.mask, w.mask_kind = torch.tril(torch.ones(260, 260, dtype=torch.bool)), "bool"
+    ot, lt = gpu_forward(w)
+    assert torch.allclose(oc.float(), ot.float(), atol=1e-6, rtol=0)
+
+
+def test_forward_is_deterministic():
+    w = syn.flux(batch=1, heads=4, grid=16)  # S = 512 + 256
+    o1, l1 = gpu_forward(w)
+    o2, l2 = gpu_forward(w)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_large_logits_stress():
+    w = syn.random_small(1, 2, 200, 128, "bf16", seed=26, std=4.0)
+    _compare(w)
+
+
+def test_explicit_scale():
+    w = syn.random_small(1, 2, 100, 64, "bf16", seed=27)
+    w.scale = 0.3
+    _compare(w)
+
+
+def test_dispatch_counters_split_instream_and_autograd():
+    rfa.rope_sdpa_reset_stats()
+    w = syn.random_small(1, 1, 64, 64, "bf16", seed=28)
+    gpu_forward(w, need_lse=False)
+    gpu_forward(w, need_lse=True)
+    s = rfa.get_dispatch_stats()
+    assert s["rope_instream"] == 1 and s["rope_autograd"] == 1 and s["pytorch_fallback"] == 0
+
+
+def test_rejects_mixed_dtypes_without_launching():
+    w = syn.random_small(1, 1, 64, 64, "bf16", seed=29)
+    d = dev()
+    with pytest.raises(rfa.RopeSdpaError):
+        rfa.rope_scaled_dot_product_attention(w.q.float().to(d), w.k.float().to(d), w.v.to(d),
+                                              w.cos.to(d), w.sin.to(d))
+
+
+# ---- full-size FLUX shapes: every head runs on the GPU, sampled rows are checked -----------
+
+def _sample_rows(S, n, seed):
+    rs = np.random.default_rng(seed)
+    fixed = [0, 1, 511, 512, 513, S - 1]
+    return np.unique(np.concatenate([fixed, rs.choice(S, n, replace=False)]))
+
+
+def test_flux_forward_full_size_sampled():
+    """B=1, H=24, S=512+4096, D=128, bf16, 3-axis RoPE (16,56,56), no mask."""
+    w = syn.flux(batch=1, heads=24, grid=64, dtype="bf16", seed=2000)
+    rows = _sample_rows(w.q.shape[2], 58, 1)
+    _compare(w, rows=rows, pairs=[(0, 0), (0, 11), (0, 23)])
+
+
+@pytest.mark.parametrize("variant", ["bool_padding", "additive_4d", "all_true"])
+def test_flux_masked_full_size_sampled(variant):
+    """B=2 FLUX shape with a key-padding mask on the text tokens (lengths U{64..512})."""
+    w = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=3000)
+    S = w.q.shape[2]
+    lens = syn.key_padding_lengths(3000, 2)
+    m = syn.key_padding_mask(lens, 512, S)
+    if variant == "bool_padding":
+        w.mask, w.mask_kind = m, "bool"
+    elif variant == "additive_4d":
+        w.mask, w.mask_kind = syn.expand_additive(m, 24, S, "bf16"), "additive"
+    else:
+        w.mask, w.mask_kind = torch.ones_like(m), "bool"
+    rows = _sample_rows(S, 26, 2)
+    _compare(w, rows=rows, pairs=[(0, 3), (1, 17)])
+
+
+def test_long_sequence_sampled():
+    """B=1, H=48, S=512+16384, D=128, bf16, 3-axis RoPE."""
+    w = syn.flux(batch=1, heads=48, grid=128, dtype="bf16", seed=5000)
+    rows = _sample_rows(w.q.shape[2], 26, 3)
+    _compare(w, rows=rows, pairs=[(0, 0), (0, 47)])
