@@ -75,9 +75,9 @@ def _traffic(kernel_key):
     return None
 
 
-def cpu_baseline(budget_s=20.0):
-    """The CPU float64 oracle on the host cores: the same FLUX forward, whole heads, as many as
-    fit in roughly `budget_s` seconds (at least one)."""
+def cpu_baseline(budget_s=10.0):
+    """The CPU float64 oracle on the host cores: the same FLUX forward (all heads), repeated
+    until about `budget_s` seconds of wall time are used."""
     import synthetic as syn
     from oracle import rope_sdpa_forward
     from oracle.rope_sdpa_ref import default_workers
@@ -85,26 +85,38 @@ def cpu_baseline(budget_s=20.0):
     cores = default_workers()
     w = syn.flux(batch=1, heads=24, grid=64, dtype="bf16", seed=2000)
     B, H, S, D = w.q.shape
-    # probe one head per worker to size the sample
-    n_probe = min(H, cores)
-    t0 = time.perf_counter()
-    rope_sdpa_forward(w.q, w.k, w.v, w.cos, w.sin, pairs=[(0, h) for h in range(n_probe)], workers=cores)
-    t_probe = time.perf_counter() - t0
-    per_round = max(t_probe, 1e-3)
-    rounds = max(1, min(int(budget_s / per_round), -(-H // n_probe)))
-    heads = min(H, rounds * n_probe)
-    t0 = time.perf_counter()
-    rope_sdpa_forward(w.q, w.k, w.v, w.cos, w.sin, pairs=[(0, h) for h in range(heads)], workers=cores)
-    dt = time.perf_counter() - t0
-    fl = flops_fwd(1, heads, S, S, D)
+    pairs = [(0, h) for h in range(H)]
+    reps, dt = 0, 0.0
+    while dt < budget_s:  # whole forward passes until the time budget is used
+        t0 = time.perf_counter()
+        rope_sdpa_forward(w.q, w.k, w.v, w.cos, w.sin, pairs=pairs, workers=cores)
+        dt += time.perf_counter() - t0
+        reps += 1
+    fl = reps * flops_fwd(1, H, S, D)
     return {
         "value": round(fl / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"float64 oracle forward of {heads} of 24 heads of B=1,S=4608,D=128 ({dt:.2f} s wall, "
-                  f"{platform.processor() or platform.machine()})",
+        "sample": f"{reps} x the full float64 oracle forward of B=1,H=24,S=4608,D=128 "
+                  f"({dt:.2f} s wall on {cores} threads, {platform.machine()})",
     }
+
+
+def summarize_rocpd(db_path, command):
+    """Text summary of a rocprofv3 kernel trace: per kernel and grid size, calls and durations."""
+    import sqlite3
+
+    con = sqlite3.connect(db_path)
+    rows = con.execute(
+        "select name, grid_x / workgroup_x, workgroup_x, count(*), avg(duration) / 1000.0, "
+        "min(duration) / 1000.0, max(duration) / 1000.0 from kernels group by name, grid_x "
+        "order by sum(duration) desc").fetchall()
+    out = [f"command: {command}", "",
+           f"{'kernel':70s} {'workgroups':>10s} {'threads':>7s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
+    for name, wg, th, n, avg, mn, mx in rows:
+        out.append(f"{name[:70]:70s} {int(wg):10d} {int(th):7d} {n:6d} {avg:10.2f} {mn:10.2f} {mx:10.2f}")
+    return "\n".join(out)
 
 
 def main():
@@ -114,7 +126,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train", action="store_true", help="skip the training-step timing")
+    ap.add_argument("--summarize", metavar="DB", help="print a summary of a rocprofv3 results database and exit")
+    ap.add_argument("--command", default="", help="command line recorded in the --summarize output")
     args = ap.parse_args()
+    if args.summarize:
+        print(summarize_rocpd(args.summarize, args.command))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
