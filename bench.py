@@ -126,6 +126,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train", action="store_true", help="skip the training-step timing")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--summarize", metavar="DB", help="print a summary of a rocprofv3 results database and exit")
     ap.add_argument("--command", default="", help="command line recorded in the --summarize output")
     args = ap.parse_args()
@@ -172,6 +174,14 @@ def main():
     if not err <= 2e-2:
         print(json.dumps({"error": f"parity failed in bench: rel err {err}"}))
         sys.exit(1)
+
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- training step, FLUX B=2 ------------------------------------------------------------
     train = None

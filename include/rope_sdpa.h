@@ -20,7 +20,7 @@
  *    strides counted in ELEMENTS (not bytes).  Q, K, V, O, dO, dQ, dK, dV are [B, H, S, D]
  *    ("BHSD"); any strides are accepted (e.g. a transpose(1,2) view of a BSHD projection or
  *    an unbind view of a fused QKV tensor) provided stride[3] == 1, the base pointer is
- *    16-byte aligned and strides 0..2 are multiples of 16 bytes.
+ *    16-byte aligned, strides 0..2 are multiples of 16 bytes and stride[2] < 2^23.
  *  - Ownership: the caller owns every buffer (inputs, outputs, LSE, workspace).  The library
  *    allocates no device memory in these calls and keeps no pointer after a call returns.
  *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the

@@ -9,15 +9,24 @@
 // BM = 256 for bf16/fp16, 128 for fp32):
 //  * each lane owns one query row m (lane r of wave w: m = q0 + 32w + r) and half of the
 //    contraction elements of each k-step; Q is loaded once, rotated in fp32 with the packed
-//    (cos, sin) table, rounded to the input dtype and kept in registers as MFMA B fragments;
+//    (cos, sin) table, multiplied by scale*log2(e) (scores come out in log2 units), rounded
+//    to the input dtype and kept in registers as MFMA B fragments;
 //  * K/V tiles of BN keys stream through LDS, double buffered: K is rotated in registers on
 //    its way in (never written back to memory), V is transposed into 128-byte rows with an
 //    XOR swizzle so the P.V operand is one 16-byte LDS read per lane;
-//  * S^T = K' Q'^T lands with one query per lane, so row max / row sum need one exchange
-//    between wave halves and the P^T fragments feed O^T += V^T P^T directly from registers;
+//  * S^T = K' Q'^T lands with one query per lane, so the row max needs one exchange between
+//    wave halves and the P^T fragments feed O^T += V^T P^T directly from registers;
+//  * the running row max m enters the S product through the MFMA accumulator (C = -m), so
+//    P = exp2(S) needs no per-score arithmetic; m (and with it O and the row sum) is only
+//    rescaled when a tile raises some row's max by more than 2^8 (exact: the max is only a
+//    range guard), which after the first tiles almost never happens;
+//  * row sums accumulate the rounded P pairs with dot2 instructions (the same values that
+//    multiply V);
 //  * the all-true / all-false state of each 64x64 bool-mask tile (computed beforehand on the
 //    device) lets all-false tiles be skipped and all-true tiles run without mask reads;
 //    causal tiles above the diagonal are never visited.
+#include <type_traits>
+
 #include "rs_device.hpp"
 
 namespace rs {
@@ -28,6 +37,40 @@ struct FwdCfg {
   static constexpr int BN = sizeof(T) == 4 ? 32 : 64;    // keys per LDS tile
   static constexpr int NT = 2 * BM;                      // threads: one wave per 32 rows
 };
+
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kLn2F = 0.6931471805599453f;
+constexpr float kRescaleLog2 = 8.f;  // rescale when a row max grows by more than 2^8
+
+// Row-sum of eight rounded probabilities (one fragment) into acc.
+__device__ inline float frag_sum(bf16x8 f, float acc) {
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  const v2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v2 x = {f[2 * e], f[2 * e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+  }
+  return acc;
+}
+__device__ inline float frag_sum(f16x8 f, float acc) {
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  const v2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v2 x = {f[2 * e], f[2 * e + 1]};
+    acc = __builtin_amdgcn_fdot2(x, one, acc, false);
+  }
+  return acc;
+}
+
+// Rotation of one pair with fused multiply-adds (the int8 variant uses rot_pair instead).
+__device__ inline float2 rot_pair_fma(float x0, float x1, float c, float s) {
+  float2 r;
+  r.x = fmaf(x0, c, -x1 * s);
+  r.y = fmaf(x0, s, x1 * c);
+  return r;
+}
 
 template <typename T, int D, int MASK, bool CAUSAL>
 __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
@@ -59,6 +102,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hh = lane >> 5;
   const int S = p.shp.S;
+  const float c2 = p.shp.scale_log2;
 
   // ---- work item -------------------------------------------------------------------------
   const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -75,7 +119,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   const T* vbase = (const T*)p.v.ptr + b * p.v.sb + hd * p.v.sh;
   const float* tab = p.tab.ptr + b * p.tab.sb;  // float2 pairs, row stride D/2 pairs = D floats
 
-  // ---- Q: load, rotate in fp32, round, keep as B fragments ---------------------------------
+  // ---- Q: load, rotate in fp32, scale by scale*log2(e), round, keep as B fragments --------
   frag qf[NQK];
   {
     const T* qrow = qbase + (int64_t)mc * p.q.ss;
@@ -92,9 +136,9 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         const float ss[4] = {cs0.y, cs0.w, cs1.y, cs1.w};
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-          float2 rr = rot_pair(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), cc[pp], ss[pp]);
-          qf[t][2 * pp] = from_f<T>(rr.x);
-          qf[t][2 * pp + 1] = from_f<T>(rr.y);
+          float2 rr = rot_pair_fma(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), cc[pp], ss[pp]);
+          qf[t][2 * pp] = from_f<T>(rr.x * c2);
+          qf[t][2 * pp + 1] = from_f<T>(rr.y * c2);
         }
       }
     } else {
@@ -102,8 +146,8 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
       for (int t = 0; t < NQK; ++t) {  // element d = 2t + hh of pair t
         const float2 x = *(const float2*)(qrow + 2 * t);
         const float2 cs = *(const float2*)(trow + 2 * t);
-        const float2 rr = rot_pair(x.x, x.y, cs.x, cs.y);
-        qf[t] = hh ? rr.y : rr.x;
+        const float2 rr = rot_pair_fma(x.x, x.y, cs.x, cs.y);
+        qf[t] = (hh ? rr.y : rr.x) * c2;
       }
     }
   }
@@ -149,17 +193,23 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   const int v_c = (tid & 7) + 8 * ((tid >> 4) % (NC / 8));
   const int v_g = ((tid >> 3) & 1) + 2 * ((tid >> 4) / (NC / 8));
   const bool v_act = tid < VIT;
+  // tile-relative element offsets of this thread's K chunks and V rows (the tile base is
+  // uniform and stays in scalar registers)
+  constexpr int KROWS_PER_IT = NT / CPR;  // K rows covered by one pass of all threads
+  const int k_key0 = tid / CPR, k_cc = tid % CPR;
+  const int k_off = k_key0 * (int)p.k.ss + k_cc * EPC;
+  const int t_off = k_key0 * D + k_cc * EPC;
+  const int v_off = 4 * v_g * (int)p.v.ss + v_c * EPC;
 
   auto load_tile = [&](int kt) {
     const int kv0 = kt * BN;
+    const T* kt_base = kbase + (int64_t)kv0 * p.k.ss;
+    const float* tt_base = tab + (int64_t)kv0 * D;
 #pragma unroll
     for (int it = 0; it < KCPT; ++it) {
-      const int ci = tid + NT * it;
-      const int key = ci / CPR, cc = ci % CPR;
-      const int j = kv0 + key;
-      if (j < S) {
-        kx[it] = *(const uint4*)(kbase + (int64_t)j * p.k.ss + cc * EPC);
-        const float* tr = tab + (int64_t)j * D + cc * EPC;  // EPC/2 pairs = EPC floats
+      if (kv0 + k_key0 + it * KROWS_PER_IT < S) {
+        kx[it] = *(const uint4*)(kt_base + k_off + it * KROWS_PER_IT * (int)p.k.ss);
+        const float* tr = tt_base + t_off + it * KROWS_PER_IT * D;
 #pragma unroll
         for (int u = 0; u < EPC / 4; ++u) kt4[it][u] = *(const float4*)(tr + 4 * u);
       } else {
@@ -169,21 +219,19 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
       }
     }
     if (v_act) {
+      const T* vs = vbase + (int64_t)kv0 * p.v.ss + v_off;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int j = kv0 + 4 * v_g + rr;
-        vx[rr] = j < S ? *(const uint4*)(vbase + (int64_t)j * p.v.ss + v_c * EPC) : make_uint4(0, 0, 0, 0);
+        vx[rr] = j < S ? *(const uint4*)(vs + rr * (int)p.v.ss) : make_uint4(0, 0, 0, 0);
       }
     }
   };
 
-  auto store_tile = [&](int stage) {
-    char* sK = smem + stage * STAGE;
+  auto store_tile = [&](char* sK) {
     char* sV = sK + KBYTES;
 #pragma unroll
     for (int it = 0; it < KCPT; ++it) {
-      const int ci = tid + NT * it;
-      const int key = ci / CPR, cc = ci % CPR;
       const float* tf = (const float*)&kt4[it][0];  // (c, s) per pair
       uint4 outw;
       if constexpr (ES == 2) {
@@ -192,7 +240,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         v8 y;
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-          float2 rr = rot_pair(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), tf[2 * pp], tf[2 * pp + 1]);
+          float2 rr = rot_pair_fma(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), tf[2 * pp], tf[2 * pp + 1]);
           y[2 * pp] = from_f<T>(rr.x);
           y[2 * pp + 1] = from_f<T>(rr.y);
         }
@@ -202,13 +250,13 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         float y[4];
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-          float2 rr = rot_pair(x[2 * pp], x[2 * pp + 1], tf[2 * pp], tf[2 * pp + 1]);
+          float2 rr = rot_pair_fma(x[2 * pp], x[2 * pp + 1], tf[2 * pp], tf[2 * pp + 1]);
           y[2 * pp] = rr.x;
           y[2 * pp + 1] = rr.y;
         }
         outw = *(const uint4*)y;
       }
-      *(uint4*)(sK + perm_row(key) * KP + cc * 16) = outw;
+      *(uint4*)(sK + perm_row(k_key0 + it * KROWS_PER_IT) * KP + k_cc * 16) = outw;
     }
     if (v_act) {
       const int kb0 = 4 * v_g * ES;  // byte column of the 4-key group
@@ -218,13 +266,15 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         const int d = v_c * EPC + dd;
         char* dst = sV + d * VROW + ((unit ^ swz(d)) << 4) + off;
         if constexpr (ES == 2) {
-          const uint16_t* e0 = (const uint16_t*)&vx[0];
-          const uint16_t* e1 = (const uint16_t*)&vx[1];
-          const uint16_t* e2 = (const uint16_t*)&vx[2];
-          const uint16_t* e3 = (const uint16_t*)&vx[3];
+          const uint32_t* w0 = (const uint32_t*)&vx[0];
+          const uint32_t* w1 = (const uint32_t*)&vx[1];
+          const uint32_t* w2 = (const uint32_t*)&vx[2];
+          const uint32_t* w3 = (const uint32_t*)&vx[3];
+          // element dd of four rows -> two 32-bit words (row0|row1, row2|row3)
+          const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
           uint2 w;
-          w.x = (uint32_t)e0[dd] | ((uint32_t)e1[dd] << 16);
-          w.y = (uint32_t)e2[dd] | ((uint32_t)e3[dd] << 16);
+          w.x = __builtin_amdgcn_perm(w1[dd >> 1], w0[dd >> 1], sel);
+          w.y = __builtin_amdgcn_perm(w3[dd >> 1], w2[dd >> 1], sel);
           *(uint2*)dst = w;
         } else {
           uint4 w;
@@ -242,34 +292,38 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = zero16();
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c2 = p.shp.scale_log2;
+  float m_run = -INFINITY;  // running row max, log2 units
+  float m_base = 0.f;       // value subtracted inside the S product (negm = -m_base)
+  float l_run = 0.f;        // this lane's partial row sum
+  f32x16 negm = zero16();
+
+  // per-lane constant parts of the LDS addresses
+  const int k_rd = r * KP + hh * KPL * ES;  // K' A-fragment: row r of each 32-key block
+  const int v_rd = r * VROW;                 // V^T A-fragment: row d = 32db + r
 
   int kt = next_tile(0);
   if (kt < kt_end) {
     load_tile(kt);
-    store_tile(0);
+    store_tile(smem);
   }
   __syncthreads();
-  int stage = 0;
 
-  while (kt < kt_end) {
-    const int ktn = next_tile(kt + 1);
-    if (ktn < kt_end) load_tile(ktn);
-
+  auto body = [&](auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
     const char* sK = smem + stage * STAGE;
     const char* sV = sK + KBYTES;
+    const int ktn = next_tile(kt + 1);
+    if (ktn < kt_end) load_tile(ktn);
     const int kv0 = kt * BN;
 
-    // S^T = K' Q'^T : rows = keys, columns = this wave's 32 queries
+    // S^T - m_base = K' Q'^T + C : rows = keys, columns = this wave's 32 queries
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = zero16();
 #pragma unroll
       for (int t = 0; t < NQK; ++t) {
-        const frag a = *(const frag*)(sK + (32 * kb + r) * KP + (t * KSTEP + hh * KPL) * ES);
-        sacc[kb] = M::mma(a, qf[t], sacc[kb]);
+        const frag a = *(const frag*)(sK + k_rd + (32 * kb) * KP + t * KSTEP * ES);
+        sacc[kb] = M::mma(a, qf[t], t == 0 ? negm : sacc[kb]);
       }
     }
 
@@ -289,7 +343,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
           float mv[8];
           mask_add8<T>(p.mask, mrow, kv0 + 32 * kb + 16 * c + 8 * hh, S, mv);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(mv[e], p.shp.inv_scale, sacc[kb][8 * c + e]);
+          for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(mv[e], kLog2eF, sacc[kb][8 * c + e]);
         }
     }
     if (tail || diag || (MASK == MASK_BOOL && st != TILE_ALL_TRUE)) {
@@ -317,32 +371,37 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         }
     }
 
-    // online softmax (scores in raw dot units; exp2 with scale*log2(e) folded in)
-    float mx = -INFINITY;
+    // lazy online softmax: rescale only when some row max grows by more than 2^8
+    float mx = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * c2);
-    const float msc = m_use * c2;
-    float rs = 0.f;
+      for (int i = (kb == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    mx = xhalf_max(mx);  // max of (s - m_base) over this tile's keys
+    const bool need = mx > (m_run - m_base) + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = fmaxf(m_run, mx + m_base);
+      const bool dead = m_new == -INFINITY;  // no attended key so far
+      const float alpha = dead ? 1.f : fast_exp2(m_run - m_new);
+      const float shift = dead ? 0.f : m_new - m_base;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] -= shift;
+      m_run = m_new;
+      m_base = dead ? 0.f : m_new;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negm[i] = -m_base;
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(fmaf(sacc[kb][i], c2, -msc));
-        sacc[kb][i] = pv;
-        rs += pv;
-      }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = fast_exp2(sacc[kb][i]);
 
     // O^T += V^T P^T
     if constexpr (KPL == 8) {
@@ -350,44 +409,51 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) pf[kb][c][e] = from_f<T>(sacc[kb][8 * c + e]);
+          l_run = frag_sum(pf[kb][c], l_run);
+        }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * db + r;
-        const char* vrow = sV + d * VROW;
-        const int sw = swz(d);
+        const int sw = swz(32 * db + r);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const int unit = 4 * kb + 2 * c + hh;  // keys 32kb + 16c + 8hh .. +7
-            const frag a = *(const frag*)(vrow + ((unit ^ sw) << 4));
+            const frag a = *(const frag*)(sV + v_rd + 32 * db * VROW + ((unit ^ sw) << 4));
             oacc[db] = M::mma(a, pf[kb][c], oacc[db]);
           }
       }
     } else {
 #pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) l_run += sacc[kb][i];
+#pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * db + r;
-        const char* vrow = sV + d * VROW;
-        const int sw = swz(d);
+        const int sw = swz(32 * db + r);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = 32 * kb + c_idx_sig(i, hh);
-            const float a = *(const float*)(vrow + (((key >> 2) ^ sw) << 4) + (key & 3) * 4);
+            const float a = *(const float*)(sV + v_rd + 32 * db * VROW + (((key >> 2) ^ sw) << 4) + (key & 3) * 4);
             oacc[db] = M::mma(a, sacc[kb][i], oacc[db]);
           }
       }
     }
 
-    if (ktn < kt_end) store_tile(stage ^ 1);
+    if (ktn < kt_end) store_tile(smem + (stage ^ 1) * STAGE);
     __syncthreads();
-    stage ^= 1;
     kt = ktn;
+  };
+
+  while (kt < kt_end) {
+    body(std::integral_constant<int, 0>{});
+    if (kt >= kt_end) break;
+    body(std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue ------------------------------------------------------------------------------
@@ -413,7 +479,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         }
       }
     if (p.lse && hh == 0) {
-      p.lse[((int64_t)b * p.shp.H + hd) * S + m] = l > 0.f ? m_run * p.shp.scale + logf(l) : -INFINITY;
+      p.lse[((int64_t)b * p.shp.H + hd) * S + m] = l > 0.f ? (m_run + __log2f(l)) * kLn2F : -INFINITY;
     }
   }
 }
