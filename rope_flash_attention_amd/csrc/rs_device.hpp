@@ -73,6 +73,25 @@ __device__ inline int c_idx_sig(int i, int hh) { return 16 * (i >> 3) + 8 * hh +
 // XOR swizzle of 16-byte units for transposed tiles whose rows are 128 bytes long.
 __device__ inline int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
+// XOR swizzle of the 16-byte chunks of row-major V tiles: four consecutive rows put the
+// same logical 64-byte column block on four different 64-byte bank ranges.
+template <int NCHUNK>
+__device__ inline int vsw(int row) { return ((row & 3) << 2) & (NCHUNK - 1); }
+
+// 16 bytes per lane from a buffer straight into LDS: lane i writes [lds + 16i, lds + 16i + 16).
+// Bytes outside the buffer's range read as zero.  (Kept out of line of the kernels' lambdas:
+// the host compilation pass drops template kernels that use this builtin inside a lambda.)
+__device__ inline void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Waits for this wave's outstanding memory loads (including loads that write LDS directly)
+// and then for every wave of the workgroup.
+__device__ inline void wait_vmem_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt(7), lgkmcnt(15)
+  __syncthreads();
+}
+
 // Interleaved-pair rotation with each product and sum rounded to fp32 (no fused
 // multiply-add), so that quantized codes computed from it are reproducible exactly.
 __device__ inline float2 rot_pair(float x0, float x1, float c, float s) {

@@ -85,17 +85,15 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   constexpr int EPC = 16 / ES;     // elements per 16-byte chunk
   constexpr int KP = D * ES + 16;  // K' LDS row pitch in bytes (padded)
   constexpr int KBYTES = BN * KP;
-  constexpr int VROW = BN * ES;    // V^T row: 128 bytes
-  static_assert(VROW == 128, "V^T rows are 8 swizzle units of 16 bytes");
-  constexpr int VBYTES = D * VROW;
+  constexpr int VRB = D * ES;      // V row bytes in LDS (row-major, unpadded)
+  constexpr int VBYTES = BN * VRB;
   constexpr int STAGE = KBYTES + VBYTES;
-  constexpr int CPR = D / EPC;     // 16-byte chunks per K row
+  constexpr int CPR = D / EPC;     // 16-byte chunks per K (and V) row
   constexpr int KCPT = BN * CPR / NT;
   static_assert(KCPT * NT == BN * CPR, "K tile split");
-  constexpr int NC = D / EPC;      // V items: d-chunks x 4-key groups
-  constexpr int NG = BN / 4;
-  constexpr int VIT = NC * NG;
-  static_assert(VIT <= NT && NC % 8 == 0 && NG % 2 == 0, "V tile split");
+  constexpr int NW = NT / 64;
+  constexpr int VLD = VBYTES / 1024 / NW;  // direct-to-LDS V loads per wave (1 KB each)
+  static_assert(VLD * NW * 1024 == VBYTES, "V tile split");
 
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -186,50 +184,61 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // ---- global -> register staging of one KV tile ------------------------------------------
   uint4 kx[KCPT];
   float4 kt4[KCPT][EPC / 4];
-  uint4 vx[4];
-  // V item of this thread: bits [2:0] -> d-chunk low bits, bit 3 -> key-group bit 0,
-  // remaining bits split between high d-chunk bits and high key-group bits.  Sixteen
-  // consecutive lanes then write sixteen distinct 8-byte slots of the swizzled V^T rows.
-  const int v_c = (tid & 7) + 8 * ((tid >> 4) % (NC / 8));
-  const int v_g = ((tid >> 3) & 1) + 2 * ((tid >> 4) / (NC / 8));
-  const bool v_act = tid < VIT;
-  // tile-relative element offsets of this thread's K chunks and V rows (the tile base is
-  // uniform and stays in scalar registers)
+  // tile-relative element offsets of this thread's K chunks (the tile base is uniform and
+  // stays in scalar registers)
   constexpr int KROWS_PER_IT = NT / CPR;  // K rows covered by one pass of all threads
   const int k_key0 = tid / CPR, k_cc = tid % CPR;
   const int k_off = k_key0 * (int)p.k.ss + k_cc * EPC;
   const int t_off = k_key0 * D + k_cc * EPC;
-  const int v_off = 4 * v_g * (int)p.v.ss + v_c * EPC;
+  // V goes straight from memory into a row-major LDS tile (buffer loads with an LDS
+  // destination: lane i of a load writes bytes [16i, 16i+16) of a 1 KB block).  The byte
+  // range check of the buffer turns rows at or past S into zeros.  16-byte chunks of row j
+  // sit at chunk ^ vsw(j) so that the transposed reads below touch distinct banks.
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)vbase, (short)0, (int)(((int64_t)(S - 1) * p.v.ss + D) * ES), 0x00020000);
+  uint32_t v_voff[VLD];
+#pragma unroll
+  for (int i = 0; i < VLD; ++i) {
+    const int byte = (wave * VLD + i) * 1024 + lane * 16;  // LDS byte within the V tile
+    const int row = byte / VRB, pch = (byte % VRB) / 16;
+    v_voff[i] = (uint32_t)(row * (int)p.v.ss * ES + ((pch ^ vsw<CPR>(row)) * 16));
+  }
 
-  auto load_tile = [&](int kt) {
+  auto load_tile = [&](int kt, char* sK) {
     const int kv0 = kt * BN;
     const T* kt_base = kbase + (int64_t)kv0 * p.k.ss;
     const float* tt_base = tab + (int64_t)kv0 * D;
+    if (kv0 + BN <= S) {
 #pragma unroll
-    for (int it = 0; it < KCPT; ++it) {
-      if (kv0 + k_key0 + it * KROWS_PER_IT < S) {
+      for (int it = 0; it < KCPT; ++it) {
         kx[it] = *(const uint4*)(kt_base + k_off + it * KROWS_PER_IT * (int)p.k.ss);
         const float* tr = tt_base + t_off + it * KROWS_PER_IT * D;
 #pragma unroll
         for (int u = 0; u < EPC / 4; ++u) kt4[it][u] = *(const float4*)(tr + 4 * u);
-      } else {
-        kx[it] = make_uint4(0, 0, 0, 0);
+      }
+    } else {
 #pragma unroll
-        for (int u = 0; u < EPC / 4; ++u) kt4[it][u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int it = 0; it < KCPT; ++it) {
+        if (kv0 + k_key0 + it * KROWS_PER_IT < S) {
+          kx[it] = *(const uint4*)(kt_base + k_off + it * KROWS_PER_IT * (int)p.k.ss);
+          const float* tr = tt_base + t_off + it * KROWS_PER_IT * D;
+#pragma unroll
+          for (int u = 0; u < EPC / 4; ++u) kt4[it][u] = *(const float4*)(tr + 4 * u);
+        } else {
+          kx[it] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < EPC / 4; ++u) kt4[it][u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
     }
-    if (v_act) {
-      const T* vs = vbase + (int64_t)kv0 * p.v.ss + v_off;
+    char* sV = sK + KBYTES;
+    const uint32_t soff = (uint32_t)((int64_t)kv0 * p.v.ss * ES);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int j = kv0 + 4 * v_g + rr;
-        vx[rr] = j < S ? *(const uint4*)(vs + rr * (int)p.v.ss) : make_uint4(0, 0, 0, 0);
-      }
-    }
+    for (int i = 0; i < VLD; ++i)
+      buffer_load_lds16(vrsrc, sV + (wave * VLD + i) * 1024, v_voff[i], soff);
   };
 
   auto store_tile = [&](char* sK) {
-    char* sV = sK + KBYTES;
 #pragma unroll
     for (int it = 0; it < KCPT; ++it) {
       const float* tf = (const float*)&kt4[it][0];  // (c, s) per pair
@@ -258,34 +267,6 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
       }
       *(uint4*)(sK + perm_row(k_key0 + it * KROWS_PER_IT) * KP + k_cc * 16) = outw;
     }
-    if (v_act) {
-      const int kb0 = 4 * v_g * ES;  // byte column of the 4-key group
-      const int unit = kb0 >> 4, off = kb0 & 15;
-#pragma unroll
-      for (int dd = 0; dd < EPC; ++dd) {
-        const int d = v_c * EPC + dd;
-        char* dst = sV + d * VROW + ((unit ^ swz(d)) << 4) + off;
-        if constexpr (ES == 2) {
-          const uint32_t* w0 = (const uint32_t*)&vx[0];
-          const uint32_t* w1 = (const uint32_t*)&vx[1];
-          const uint32_t* w2 = (const uint32_t*)&vx[2];
-          const uint32_t* w3 = (const uint32_t*)&vx[3];
-          // element dd of four rows -> two 32-bit words (row0|row1, row2|row3)
-          const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-          uint2 w;
-          w.x = __builtin_amdgcn_perm(w1[dd >> 1], w0[dd >> 1], sel);
-          w.y = __builtin_amdgcn_perm(w3[dd >> 1], w2[dd >> 1], sel);
-          *(uint2*)dst = w;
-        } else {
-          uint4 w;
-          w.x = ((const uint32_t*)&vx[0])[dd];
-          w.y = ((const uint32_t*)&vx[1])[dd];
-          w.z = ((const uint32_t*)&vx[2])[dd];
-          w.w = ((const uint32_t*)&vx[3])[dd];
-          *(uint4*)dst = w;
-        }
-      }
-    }
   };
 
   // ---- online softmax state ----------------------------------------------------------------
@@ -299,21 +280,33 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 
   // per-lane constant parts of the LDS addresses
   const int k_rd = r * KP + hh * KPL * ES;  // K' A-fragment: row r of each 32-key block
-  const int v_rd = r * VROW;                 // V^T A-fragment: row d = 32db + r
+  // V^T A-fragments from the row-major V tile.  bf16/fp16: a transposed 8-byte read by each
+  // 16-lane group G hands lane l the 4 keys key0..key0+3 at column 32db + (l % 32), when
+  // source lane s of the group points at row key0 + s/4, columns +4(s%4)..+3 of that
+  // column block; two reads (keys +0..3, +4..7) make one 8-key fragment.
+  const int ls = lane & 15, G = lane >> 4;
+  const int v_row_l = 8 * (G >> 1) + (ls >> 2);       // + 32kb + 16c + 4q
+  const int v_colb = 2 * (16 * (G & 1) + 4 * (ls & 3));  // byte column within a 64-byte d-block
+  int v_rd[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int chunk = (db * 64 + v_colb) / 16;
+    v_rd[db] = v_row_l * VRB + ((chunk ^ vsw<CPR>(v_row_l)) * 16) + (v_colb & 15);
+  }
 
   int kt = next_tile(0);
   if (kt < kt_end) {
-    load_tile(kt);
+    load_tile(kt, smem);
     store_tile(smem);
   }
-  __syncthreads();
+  wait_vmem_and_sync();
 
   auto body = [&](auto stage_c) {
     constexpr int stage = decltype(stage_c)::value;
     const char* sK = smem + stage * STAGE;
     const char* sV = sK + KBYTES;
     const int ktn = next_tile(kt + 1);
-    if (ktn < kt_end) load_tile(ktn);
+    if (ktn < kt_end) load_tile(ktn, smem + (stage ^ 1) * STAGE);
     const int kv0 = kt * BN;
 
     // S^T - m_base = K' Q'^T + C : rows = keys, columns = this wave's 32 queries
@@ -416,13 +409,19 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int sw = swz(32 * db + r);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            const int unit = 4 * kb + 2 * c + hh;  // keys 32kb + 16c + 8hh .. +7
-            const frag a = *(const frag*)(sV + v_rd + 32 * db * VROW + ((unit ^ sw) << 4));
+            // rows 32kb + 16c (+4 for the second half) keep (row & 3), so the swizzle term of
+            // v_rd stays valid: only whole-row offsets are added
+            typedef short s4 __attribute__((ext_vector_type(4)));
+            const char* base = sV + v_rd[db] + (32 * kb + 16 * c) * VRB;
+            const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)base);
+            const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(base + 4 * VRB));
+            frag a;
+            *(s4*)&a = lo;
+            *((s4*)&a + 1) = hi;
             oacc[db] = M::mma(a, pf[kb][c], oacc[db]);
           }
       }
@@ -433,20 +432,20 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) l_run += sacc[kb][i];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int sw = swz(32 * db + r);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = 32 * kb + c_idx_sig(i, hh);
-            const float a = *(const float*)(sV + v_rd + 32 * db * VROW + (((key >> 2) ^ sw) << 4) + (key & 3) * 4);
+            const int col = 4 * (32 * db + r);  // byte column of element d = 32db + r
+            const float a = *(const float*)(sV + key * VRB + (((col >> 4) ^ vsw<CPR>(key)) << 4) + (col & 15));
             oacc[db] = M::mma(a, sacc[kb][i], oacc[db]);
           }
       }
     }
 
     if (ktn < kt_end) store_tile(smem + (stage ^ 1) * STAGE);
-    __syncthreads();
+    wait_vmem_and_sync();
     kt = ktn;
   };
 

@@ -52,8 +52,10 @@ rs_status check_bhsd(const rs_tensor* t, int dtype, const int64_t* size) {
     if (t->size[i] <= 1) continue;
     if (t->stride[i] < 0 || (t->stride[i] * es) % 16 != 0) return RS_ERR_STRIDE;
   }
-  // row offsets inside a tile of up to 256 rows are 32-bit in the kernels
+  // row offsets inside a tile of up to 256 rows are 32-bit in the kernels, and one (b, h)
+  // slice is addressed through a buffer descriptor with a 32-bit byte range
   if (t->size[2] > 1 && t->stride[2] >= ((int64_t)1 << 23)) return RS_ERR_STRIDE;
+  if ((t->size[2] * t->stride[2] + t->size[3]) * es >= ((int64_t)1 << 31)) return RS_ERR_STRIDE;
   if (((uintptr_t)t->data) % 16 != 0) return RS_ERR_ALIGN;
   return RS_OK;
 }
