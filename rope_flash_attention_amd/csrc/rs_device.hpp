@@ -91,6 +91,14 @@ __device__ inline void wait_vmem_and_sync() {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt(7), lgkmcnt(15)
   __syncthreads();
 }
+// Same, but the N most recently issued loads may still be in flight (loads complete in
+// issue order for the counter).
+template <int N>
+__device__ inline void wait_vmem_but_and_sync() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+  __syncthreads();
+}
 
 // Interleaved-pair rotation with each product and sum rounded to fp32 (no fused
 // multiply-add), so that quantized codes computed from it are reproducible exactly.

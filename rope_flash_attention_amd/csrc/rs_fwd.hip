@@ -72,6 +72,12 @@ __device__ inline float2 rot_pair_fma(float x0, float x1, float c, float s) {
   return r;
 }
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int QK_AHEAD = 8;  // K' fragment reads kept in flight ahead of the QK^T products
+constexpr int PV_AHEAD = 3;  // V^T fragments (two reads each) in flight ahead of the P.V products
+
 template <typename T, int D, int MASK, bool CAUSAL>
 __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   using M = Mf<T>;
@@ -87,7 +93,6 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   constexpr int KBYTES = BN * KP;
   constexpr int VRB = D * ES;      // V row bytes in LDS (row-major, unpadded)
   constexpr int VBYTES = BN * VRB;
-  constexpr int STAGE = KBYTES + VBYTES;
   constexpr int CPR = D / EPC;     // 16-byte chunks per K (and V) row
   constexpr int KCPT = BN * CPR / NT;
   static_assert(KCPT * NT == BN * CPR, "K tile split");
@@ -95,7 +100,12 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   constexpr int VLD = VBYTES / 1024 / NW;  // direct-to-LDS V loads per wave (1 KB each)
   static_assert(VLD * NW * 1024 == VBYTES, "V tile split");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  // Separate LDS objects per buffer: the compiler can then tell that reads of one V buffer
+  // do not depend on the direct-to-LDS loads in flight into the other.
+  __shared__ __attribute__((aligned(16))) char sk0[KBYTES];
+  __shared__ __attribute__((aligned(16))) char sk1[KBYTES];
+  __shared__ __attribute__((aligned(16))) char sv0[VBYTES];
+  __shared__ __attribute__((aligned(16))) char sv1[VBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hh = lane >> 5;
@@ -204,7 +214,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     v_voff[i] = (uint32_t)(row * (int)p.v.ss * ES + ((pch ^ vsw<CPR>(row)) * 16));
   }
 
-  auto load_tile = [&](int kt, char* sK) {
+  auto load_tile = [&](int kt, char* sV) {
     const int kv0 = kt * BN;
     const T* kt_base = kbase + (int64_t)kv0 * p.k.ss;
     const float* tt_base = tab + (int64_t)kv0 * D;
@@ -231,7 +241,6 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         }
       }
     }
-    char* sV = sK + KBYTES;
     const uint32_t soff = (uint32_t)((int64_t)kv0 * p.v.ss * ES);
 #pragma unroll
     for (int i = 0; i < VLD; ++i)
@@ -296,28 +305,44 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 
   int kt = next_tile(0);
   if (kt < kt_end) {
-    load_tile(kt, smem);
-    store_tile(smem);
+    load_tile(kt, sv0);
+    store_tile(sk0);
   }
   wait_vmem_and_sync();
 
   auto body = [&](auto stage_c) {
     constexpr int stage = decltype(stage_c)::value;
-    const char* sK = smem + stage * STAGE;
-    const char* sV = sK + KBYTES;
+    const char* sK = stage ? sk1 : sk0;
+    const char* sV = stage ? sv1 : sv0;
+    char* sKn = stage ? sk0 : sk1;
+    char* sVn = stage ? sv0 : sv1;
     const int ktn = next_tile(kt + 1);
-    if (ktn < kt_end) load_tile(ktn, smem + (stage ^ 1) * STAGE);
+    if (ktn < kt_end) load_tile(ktn, sVn);
     const int kv0 = kt * BN;
 
     // S^T - m_base = K' Q'^T + C : rows = keys, columns = this wave's 32 queries
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      // all fragments of the 32-key block are requested before the first product, so the
+      // LDS latency is paid once per block rather than once per k-step
+      frag ka[NQK];
 #pragma unroll
-      for (int t = 0; t < NQK; ++t) {
-        const frag a = *(const frag*)(sK + k_rd + (32 * kb) * KP + t * KSTEP * ES);
-        sacc[kb] = M::mma(a, qf[t], t == 0 ? negm : sacc[kb]);
+      for (int t = 0; t < NQK; ++t) ka[t] = *(const frag*)(sK + k_rd + (32 * kb) * KP + t * KSTEP * ES);
+#pragma unroll
+      for (int t = 0; t < NQK; ++t) sacc[kb] = M::mma(ka[t], qf[t], t == 0 ? negm : sacc[kb]);
+    }
+    if constexpr (KPL == 8) {
+      // keep QK_AHEAD fragment reads in flight ahead of the products (the scheduler would
+      // otherwise pair each read with its product and wait out every LDS round trip)
+      constexpr int NR = NKB * NQK;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, QK_AHEAD, 0);
+#pragma unroll
+      for (int i = 0; i < NR - QK_AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, QK_AHEAD, 0);
     }
 
     // exclusions: sequence tail, causal diagonal, masks
@@ -425,6 +450,15 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
             oacc[db] = M::mma(a, pf[kb][c], oacc[db]);
           }
       }
+      // V^T fragments: PV_AHEAD products' worth of transposed reads in flight
+      constexpr int NP = NDB * NKB * 2;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PV_AHEAD, 1);
+#pragma unroll
+      for (int i = 0; i < NP - PV_AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, PV_AHEAD, 1);
     } else {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -444,7 +478,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
       }
     }
 
-    if (ktn < kt_end) store_tile(smem + (stage ^ 1) * STAGE);
+    if (ktn < kt_end) store_tile(sKn);
     wait_vmem_and_sync();
     kt = ktn;
   };
