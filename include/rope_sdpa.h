@@ -126,6 +126,20 @@ rs_status rope_sdpa_bwd(const rs_args* args, const rs_tensor* o, const float* ls
                         const rs_tensor* dv, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/*
+ * Test-only export of the int8 quantization that rope_sdpa_fwd performs under
+ * RS_FLAG_QUANT_INT8_QK (same reading, same kernel): writes the int8 codes of the rotated Q and
+ * K into q_codes / k_codes, contiguous [B, H, S, D] DEVICE buffers (8-byte aligned), and their
+ * fp32 scales into q_scales / k_scales, contiguous [B, H, ceil(S / 64)] DEVICE buffers.  args
+ * must carry RS_FLAG_QUANT_INT8_QK (else RS_ERR_INVALID) and pass the same validation as the
+ * forward; the workspace is the forward's (rope_sdpa_workspace_size(args, 0, ...)).  It lets a
+ * test compare the integer decisions bit for bit and run a reference from exactly these
+ * values.  Asynchronous on `stream`; nothing is launched on error.
+ */
+rs_status rope_sdpa_debug_quantize_qk(const rs_args* args, int8_t* q_codes, int8_t* k_codes,
+                                      float* q_scales, float* k_scales, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* rope_sdpa_status_string(rs_status status);
 

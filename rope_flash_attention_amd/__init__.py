@@ -28,7 +28,7 @@ from ._abi import (RS_BF16, RS_BOOL, RS_F16, RS_F32, RS_FLAG_CAUSAL, RS_FLAG_QUA
 __all__ = [
     "rope_scaled_dot_product_attention", "rope_sdpa_fwd", "rope_sdpa_bwd", "rope_sdpa_workspace_size",
     "rope_sdpa_get_stats", "rope_sdpa_reset_stats", "rope_sdpa_abi_version", "rope_sdpa_status_string",
-    "get_dispatch_stats", "RopeSdpaError", "library_path",
+    "get_dispatch_stats", "RopeSdpaError", "library_path", "rope_sdpa_debug_quantize_qk", "debug_quantize_qk",
 ]
 
 _DT = {torch.float32: RS_F32, torch.float16: RS_F16, torch.bfloat16: RS_BF16, torch.bool: RS_BOOL}
@@ -193,11 +193,32 @@ def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, att
     return _forward(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale, need_lse=False)[0]
 
 
-def rope_sdpa_fwd_with_lse(query, key, value, rope_cos, rope_sin, attn_mask=None, is_causal=False, scale=None):
+def rope_sdpa_fwd_with_lse(query, key, value, rope_cos, rope_sin, attn_mask=None, is_causal=False, scale=None,
+                           quantization=None):
     """Forward returning (O, LSE) without autograd (LSE is fp32 [B, H, S], natural log)."""
     mask, kind = _mask4(attn_mask, query.dtype)
     return _forward(query, key, value, _tables4(rope_cos, query.device), _tables4(rope_sin, query.device),
-                    mask, kind, bool(is_causal), scale, need_lse=True)
+                    mask, kind, bool(is_causal), scale, need_lse=True, int8=quantization == "int8")
+
+
+def debug_quantize_qk(query, key, rope_cos, rope_sin):
+    """The int8 codes and scales the int8 forward computes, for tests.
+
+    Returns (q_codes, q_scales, k_codes, k_scales): int8 [B, H, S, D] and fp32 [B, H, ceil(S/64)].
+    """
+    lib = _abi.load()
+    cos4, sin4 = _tables4(rope_cos, query.device), _tables4(rope_sin, query.device)
+    call = _Call(query, key, key, cos4, sin4, None, 0, False, None, int8=True)
+    B, H, S, D = query.shape
+    nb = -(-S // 64)
+    qc = torch.empty((B, H, S, D), dtype=torch.int8, device=query.device)
+    kc = torch.empty_like(qc)
+    qs = torch.empty((B, H, nb), dtype=torch.float32, device=query.device)
+    ks = torch.empty_like(qs)
+    ws = call.workspace(False, query.device)
+    _check(lib.rope_sdpa_debug_quantize_qk(ctypes.byref(call.args), qc.data_ptr(), kc.data_ptr(), qs.data_ptr(),
+                                           ks.data_ptr(), ws.data_ptr(), ws.numel(), _stream(query.device)))
+    return qc, qs, kc, ks
 
 
 def rope_sdpa_bwd_explicit(query, key, value, rope_cos, rope_sin, out, lse, dout, attn_mask=None,
@@ -215,6 +236,12 @@ def rope_sdpa_fwd(args, o, lse_ptr, ws_ptr, ws_bytes, stream) -> int:
 
 def rope_sdpa_bwd(args, o, lse_ptr, dout, dq, dk, dv, ws_ptr, ws_bytes, stream) -> int:
     return _abi.load().rope_sdpa_bwd(args, o, lse_ptr, dout, dq, dk, dv, ws_ptr, ws_bytes, stream)
+
+
+def rope_sdpa_debug_quantize_qk(args, q_codes_ptr, k_codes_ptr, q_scales_ptr, k_scales_ptr, ws_ptr, ws_bytes,
+                                stream) -> int:
+    return _abi.load().rope_sdpa_debug_quantize_qk(args, q_codes_ptr, k_codes_ptr, q_scales_ptr, k_scales_ptr,
+                                                   ws_ptr, ws_bytes, stream)
 
 
 def rope_sdpa_workspace_size(args, backward: int) -> int:

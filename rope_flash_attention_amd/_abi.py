@@ -20,7 +20,7 @@ RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT8_QK = 1, 2
 # Every symbol include/rope_sdpa.h declares.
 EXPORTED = (
     "rope_sdpa_workspace_size", "rope_sdpa_fwd", "rope_sdpa_bwd", "rope_sdpa_status_string",
-    "rope_sdpa_get_stats", "rope_sdpa_reset_stats", "rope_sdpa_abi_version",
+    "rope_sdpa_get_stats", "rope_sdpa_reset_stats", "rope_sdpa_abi_version", "rope_sdpa_debug_quantize_qk",
 )
 
 
@@ -81,6 +81,9 @@ def load(path: str = LIB_PATH):
     lib.rope_sdpa_get_stats.restype = None
     lib.rope_sdpa_reset_stats.argtypes = []
     lib.rope_sdpa_reset_stats.restype = None
+    lib.rope_sdpa_debug_quantize_qk.argtypes = [P(RsArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.rope_sdpa_debug_quantize_qk.restype = ctypes.c_int
     lib.rope_sdpa_abi_version.argtypes = []
     lib.rope_sdpa_abi_version.restype = ctypes.c_int
     _lib = lib

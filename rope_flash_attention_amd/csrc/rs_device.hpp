@@ -57,6 +57,13 @@ __device__ inline f32x16 zero16() {
   return z;
 }
 
+__device__ inline i32x16 izero16() {
+  i32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0;
+  return z;
+}
+
 // Accumulator register i of lane half hh holds row 8*(i/4) + 4*hh + (i%4) of the C block.
 __device__ inline int c_row(int i, int hh) { return 8 * (i >> 2) + 4 * hh + (i & 3); }
 

@@ -78,8 +78,12 @@ constexpr int kSchedDsRead = 0x100;
 constexpr int QK_AHEAD = 8;  // K' fragment reads kept in flight ahead of the QK^T products
 constexpr int PV_AHEAD = 3;  // V^T fragments (two reads each) in flight ahead of the P.V products
 
-template <typename T, int D, int MASK, bool CAUSAL>
+// QI8: blockwise int8 variant.  Q' and K' arrive as int8 codes with one fp32 scale per
+// (b, h, 64-token block), written beforehand by the quantization kernel; Q'K'^T runs on
+// int8 MFMA with exact int32 sums, which are scaled into the fp32 scores once per tile.
+template <typename T, int D, int MASK, bool CAUSAL, bool QI8 = false>
 __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
+  static_assert(!QI8 || (sizeof(T) == 2 && MASK == MASK_NONE && !CAUSAL), "int8 variant: 16-bit, unmasked");
   using M = Mf<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = 2 * KPL;
@@ -98,6 +102,12 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   static_assert(KCPT * NT == BN * CPR, "K tile split");
   constexpr int NW = NT / 64;
   constexpr int VLD = VBYTES / 1024 / NW;  // direct-to-LDS V loads per wave (1 KB each)
+  // int8 K' tiles: BN rows of D code bytes, 16-byte chunks XOR-swizzled per row
+  constexpr int NQ8 = D / 32;              // k-steps of the int8 product (32 codes each)
+  constexpr int K8CH = D / 16;             // 16-byte chunks per code row
+  constexpr int K8RPB = 256 / D;           // code rows per 256-byte bank sweep
+  constexpr int K8LD = BN * D / 1024;      // 1 KB direct-to-LDS loads per code tile
+  static_assert(!QI8 || BN == 64, "int8 tiles coincide with the 64-token quantization blocks");
   static_assert(VLD * NW * 1024 == VBYTES, "V tile split");
 
   // Separate LDS objects per buffer: the compiler can then tell that reads of one V buffer
@@ -128,8 +138,17 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   const float* tab = p.tab.ptr + b * p.tab.sb;  // float2 pairs, row stride D/2 pairs = D floats
 
   // ---- Q: load, rotate in fp32, scale by scale*log2(e), round, keep as B fragments --------
-  frag qf[NQK];
-  {
+  // (int8 variant: the codes of this lane's row; the scales enter once per tile)
+  using QF = typename std::conditional<QI8, i32x4[NQ8], frag[NQK]>::type;
+  QF qf;
+  const int slice = b * p.shp.H + hd;  // (b, h) index into the int8 codes and scales
+  float q8scale = 0.f;
+  if constexpr (QI8) {
+    const int8_t* qrow = p.qc + ((int64_t)slice * p.sp + mc) * D;
+#pragma unroll
+    for (int t = 0; t < NQ8; ++t) qf[t] = *(const i32x4*)(qrow + 32 * t + 16 * hh);
+    q8scale = p.qsc[(int64_t)slice * (p.sp / 64) + mc / 64] * c2;  // mc < S: always a valid block
+  } else {
     const T* qrow = qbase + (int64_t)mc * p.q.ss;
     const float* trow = tab + (int64_t)mc * D;
     if constexpr (KPL == 8) {
@@ -214,7 +233,9 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     v_voff[i] = (uint32_t)(row * (int)p.v.ss * ES + ((pch ^ vsw<CPR>(row)) * 16));
   }
 
-  auto load_tile = [&](int kt, char* sV) {
+  // K (and its table rows) of tile kt into registers
+  auto load_k = [&](int kt) {
+    if constexpr (QI8) return;
     const int kv0 = kt * BN;
     const T* kt_base = kbase + (int64_t)kv0 * p.k.ss;
     const float* tt_base = tab + (int64_t)kv0 * D;
@@ -241,13 +262,35 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         }
       }
     }
-    const uint32_t soff = (uint32_t)((int64_t)kv0 * p.v.ss * ES);
+  };
+  // this wave's share of V of tile kt straight into the LDS buffer sV
+  auto dma_v = [&](int kt, char* sV) {
+    const uint32_t soff = (uint32_t)((int64_t)kt * BN * p.v.ss * ES);
 #pragma unroll
     for (int i = 0; i < VLD; ++i)
       buffer_load_lds16(vrsrc, sV + (wave * VLD + i) * 1024, v_voff[i], soff);
   };
 
+  // int8 variant: K' code tile straight into LDS.  LDS row j holds key perm_row(j) (the
+  // row order the score fragments need, as for the rotated K' tiles), its 16-byte chunk c
+  // at c ^ k8sw(j); code rows past the padded sequence read as zero.
+  auto k8sw = [](int row) { return (row / K8RPB) & (K8CH - 1); };
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(QI8 ? p.kc + (int64_t)slice * p.sp * D : nullptr), (short)0, QI8 ? p.sp * D : 0, 0x00020000);
+  uint32_t k8_voff = 0;
+  if constexpr (QI8) {
+    const int byte = wave * 1024 + lane * 16;  // this wave's 1 KB share of a code tile
+    const int row = byte / D, pch = (byte % D) / 16;
+    k8_voff = (uint32_t)(perm_row(row) * D + ((pch ^ k8sw(row)) << 4));
+  }
+  auto dma_k = [&](int kt, char* sK) {
+    if constexpr (QI8) {
+      if (wave < K8LD) buffer_load_lds16(krsrc, sK + wave * 1024, k8_voff, (uint32_t)(kt * BN * D));
+    }
+  };
+
   auto store_tile = [&](char* sK) {
+    if constexpr (QI8) return;
 #pragma unroll
     for (int it = 0; it < KCPT; ++it) {
       const float* tf = (const float*)&kt4[it][0];  // (c, s) per pair
@@ -303,49 +346,56 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     v_rd[db] = v_row_l * VRB + ((chunk ^ vsw<CPR>(v_row_l)) * 16) + (v_colb & 15);
   }
 
-  int kt = next_tile(0);
-  if (kt < kt_end) {
-    load_tile(kt, sv0);
-    store_tile(sk0);
-  }
-  wait_vmem_and_sync();
-
-  auto body = [&](auto stage_c) {
-    constexpr int stage = decltype(stage_c)::value;
-    const char* sK = stage ? sk1 : sk0;
-    const char* sV = stage ? sv1 : sv0;
-    char* sKn = stage ? sk0 : sk1;
-    char* sVn = stage ? sv0 : sv1;
-    const int ktn = next_tile(kt + 1);
-    if (ktn < kt_end) load_tile(ktn, sVn);
-    const int kv0 = kt * BN;
-
-    // S^T - m_base = K' Q'^T + C : rows = keys, columns = this wave's 32 queries
-    f32x16 sacc[NKB];
+  // S^T - m_base = K' Q'^T + C for one tile: rows = keys, columns = this wave's 32 queries
+  auto qk = [&](const char* sK, f32x16* sacc, int kt) {
+    if constexpr (QI8) {
+      // exact integer sums, then s = sum * scale_q * scale_k * scale * log2(e) - m_base
+      const float f = q8scale * p.ksc[(int64_t)slice * (p.sp / 64) + kt];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      // all fragments of the 32-key block are requested before the first product, so the
-      // LDS latency is paid once per block rather than once per k-step
-      frag ka[NQK];
+      for (int kb = 0; kb < NKB; ++kb) {
+        i32x4 ka[NQ8];
+        const int row = 32 * kb + r;
 #pragma unroll
-      for (int t = 0; t < NQK; ++t) ka[t] = *(const frag*)(sK + k_rd + (32 * kb) * KP + t * KSTEP * ES);
+        for (int t = 0; t < NQ8; ++t)
+          ka[t] = *(const i32x4*)(sK + row * D + (((2 * t + hh) ^ k8sw(row)) << 4));
+        i32x16 acc;
 #pragma unroll
-      for (int t = 0; t < NQK; ++t) sacc[kb] = M::mma(ka[t], qf[t], t == 0 ? negm : sacc[kb]);
-    }
-    if constexpr (KPL == 8) {
-      // keep QK_AHEAD fragment reads in flight ahead of the products (the scheduler would
-      // otherwise pair each read with its product and wait out every LDS round trip)
-      constexpr int NR = NKB * NQK;
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, QK_AHEAD, 0);
+        for (int t = 0; t < NQ8; ++t)
+          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[t], qf[t], t == 0 ? izero16() : acc, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < NR - QK_AHEAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = fmaf((float)acc[i], f, -m_base);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, QK_AHEAD, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NKB * NQ8, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NKB * NQ8, 0);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        // all fragments of the 32-key block are requested before the first product, so the
+        // LDS latency is paid once per block rather than once per k-step
+        frag ka[NQK];
+#pragma unroll
+        for (int t = 0; t < NQK; ++t) ka[t] = *(const frag*)(sK + k_rd + (32 * kb) * KP + t * KSTEP * ES);
+#pragma unroll
+        for (int t = 0; t < NQK; ++t) sacc[kb] = M::mma(ka[t], qf[t], t == 0 ? negm : sacc[kb]);
+      }
+      if constexpr (KPL == 8) {
+        // keep QK_AHEAD fragment reads in flight ahead of the products (the scheduler would
+        // otherwise pair each read with its product and wait out every LDS round trip)
+        constexpr int NR = NKB * NQK;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, QK_AHEAD, 0);
+#pragma unroll
+        for (int i = 0; i < NR - QK_AHEAD; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, QK_AHEAD, 0);
+      }
     }
+  };
 
-    // exclusions: sequence tail, causal diagonal, masks
+  // exclusions of one tile: sequence tail, causal diagonal, masks
+  auto fixup = [&](int kt, f32x16* sacc) {
+    const int kv0 = kt * BN;
     const bool tail = kv0 + BN > S;
     const bool diag = CAUSAL && (kv0 + BN - 1 > q0);
     uint32_t st = TILE_ALL_TRUE;
@@ -388,8 +438,11 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
           }
         }
     }
+  };
 
-    // lazy online softmax: rescale only when some row max grows by more than 2^8
+  // lazy online softmax, part 1: rescale only when some row max grows by more than 2^8
+  // (wave-uniform branch)
+  auto rescale = [&](f32x16* sacc) {
     float mx = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -416,22 +469,37 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) negm[i] = -m_base;
     }
+  };
+
+  // part 2: P = exp2(S), rounded to T into MFMA fragments for 16-bit types, and row sums
+  using PT = typename std::conditional<KPL == 8, frag[NKB][2], f32x16[NKB]>::type;
+  auto probs = [&](f32x16* sacc, PT& pt) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = fast_exp2(sacc[kb][i]);
-
-    // O^T += V^T P^T
     if constexpr (KPL == 8) {
-      frag pf[NKB][2];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pf[kb][c][e] = from_f<T>(sacc[kb][8 * c + e]);
-          l_run = frag_sum(pf[kb][c], l_run);
+          for (int e = 0; e < 8; ++e) pt[kb][c][e] = from_f<T>(sacc[kb][8 * c + e]);
+          l_run = frag_sum(pt[kb][c], l_run);
         }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) l_run += sacc[kb][i];
+        pt[kb] = sacc[kb];
+      }
+    }
+  };
+
+  // O^T += V^T P^T
+  auto pv = [&](const char* sV, PT& pt) {
+    if constexpr (KPL == 8) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -447,7 +515,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
             frag a;
             *(s4*)&a = lo;
             *((s4*)&a + 1) = hi;
-            oacc[db] = M::mma(a, pf[kb][c], oacc[db]);
+            oacc[db] = M::mma(a, pt[kb][c], oacc[db]);
           }
       }
       // V^T fragments: PV_AHEAD products' worth of transposed reads in flight
@@ -461,10 +529,6 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, PV_AHEAD, 1);
     } else {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) l_run += sacc[kb][i];
-#pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -473,16 +537,44 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
             const int key = 32 * kb + c_idx_sig(i, hh);
             const int col = 4 * (32 * db + r);  // byte column of element d = 32db + r
             const float a = *(const float*)(sV + key * VRB + (((col >> 4) ^ vsw<CPR>(key)) << 4) + (col & 15));
-            oacc[db] = M::mma(a, sacc[kb][i], oacc[db]);
+            oacc[db] = M::mma(a, pt[kb][i], oacc[db]);
           }
       }
     }
+  };
 
+  // ---- key-tile loop: double-buffered over K' and V ------------------------------------------
+  int kt = next_tile(0);
+  if (kt < kt_end) {
+    load_k(kt);
+    dma_k(kt, sk0);
+    dma_v(kt, sv0);
+    store_tile(sk0);
+  }
+  wait_vmem_and_sync();
+  auto body = [&](auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
+    const char* sK = stage ? sk1 : sk0;
+    const char* sV = stage ? sv1 : sv0;
+    char* sKn = stage ? sk0 : sk1;
+    char* sVn = stage ? sv0 : sv1;
+    const int ktn = next_tile(kt + 1);
+    if (ktn < kt_end) {
+      load_k(ktn);
+      dma_k(ktn, sKn);
+      dma_v(ktn, sVn);
+    }
+    f32x16 sacc[NKB];
+    qk(sK, sacc, kt);
+    fixup(kt, sacc);
+    rescale(sacc);
+    PT pt;
+    probs(sacc, pt);
+    pv(sV, pt);
     if (ktn < kt_end) store_tile(sKn);
     wait_vmem_and_sync();
     kt = ktn;
   };
-
   while (kt < kt_end) {
     body(std::integral_constant<int, 0>{});
     if (kt >= kt_end) break;
@@ -517,10 +609,10 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   }
 }
 
-template <typename T, int D, int MASK, bool CAUSAL>
+template <typename T, int D, int MASK, bool CAUSAL, bool QI8 = false>
 static int launch_fwd_t(const FwdParams& p, void* stream) {
   const int grid = p.num_qt * p.shp.H * p.shp.B;
-  hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
+  hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL, QI8>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
                      (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
@@ -541,10 +633,14 @@ static int launch_fwd_dt(int D, int mask_kind, bool causal, const FwdParams& p, 
                  : launch_fwd_d<T, 128>(mask_kind, causal, p, stream);
 }
 
-int launch_fwd_int8(int dtype, int D, const FwdParams& p, void* stream);
+template <typename T>
+static int launch_fwd_int8(int D, const FwdParams& p, void* stream) {
+  return D == 64 ? launch_fwd_t<T, 64, MASK_NONE, false, true>(p, stream)
+                 : launch_fwd_t<T, 128, MASK_NONE, false, true>(p, stream);
+}
 
 int launch_fwd(int dtype, int D, int mask_kind, bool causal, bool int8, const FwdParams& p, void* stream) {
-  if (int8) return launch_fwd_int8(dtype, D, p, stream);
+  if (int8) return dtype == F16 ? launch_fwd_int8<_Float16>(D, p, stream) : launch_fwd_int8<__bf16>(D, p, stream);
   switch (dtype) {
     case F32: return launch_fwd_dt<float>(D, mask_kind, causal, p, stream);
     case F16: return launch_fwd_dt<_Float16>(D, mask_kind, causal, p, stream);

@@ -60,7 +60,6 @@ rs_status check_bhsd(const rs_tensor* t, int dtype, const int64_t* size) {
   return RS_OK;
 }
 
-constexpr bool kInt8Available = false;
 
 struct Shape {
   int64_t B, H, S, D;
@@ -151,7 +150,7 @@ rs_status validate_args(const rs_args* a, Shape* out) {
     return RS_ERR_INVALID;
   }
   if (a->flags & RS_FLAG_QUANT_INT8_QK) {
-    if (!kInt8Available || dt == RS_F32) return RS_ERR_UNSUPPORTED;
+    if (dt == RS_F32) return RS_ERR_UNSUPPORTED;
     if (a->mask_kind != RS_MASK_NONE || causal) return RS_ERR_UNSUPPORTED;
   }
   if (a->mask_kind == RS_MASK_BOOL) {
@@ -163,11 +162,12 @@ rs_status validate_args(const rs_args* a, Shape* out) {
 }
 
 struct Layout {
-  size_t ctrl, table, tiles, delta, total;
+  size_t ctrl, table, tiles, delta, qc, kc, qs, ks, total;
   int64_t nqt, nkt;
+  int64_t sp, nblk;  // int8 variant: padded rows per (b, h) slice and 64-token blocks
 };
 
-Layout layout(const Shape& s, int mask_kind, bool backward) {
+Layout layout(const Shape& s, int mask_kind, bool backward, bool int8) {
   Layout L{};
   size_t off = 0;
   L.ctrl = off;
@@ -182,6 +182,20 @@ Layout layout(const Shape& s, int mask_kind, bool backward) {
   }
   L.delta = off;
   if (backward) off += round_up((size_t)(s.B * s.H * s.S) * sizeof(float), 256);
+  if (int8) {
+    L.nblk = (s.S + 63) / 64;
+    L.sp = L.nblk * 64;
+    const size_t codes = round_up((size_t)(s.B * s.H * L.sp * s.D), 256);
+    const size_t scales = round_up((size_t)(s.B * s.H * L.nblk) * sizeof(float), 256);
+    L.qc = off;
+    off += codes;
+    L.kc = off;
+    off += codes;
+    L.qs = off;
+    off += scales;
+    L.ks = off;
+    off += scales;
+  }
   L.total = off;
   return L;
 }
@@ -276,6 +290,28 @@ Opnd opnd(const rs_tensor* t) {
   return o;
 }
 
+QuantParams quant_params(const rs_args* a, const Shape& s, const Layout& L, char* ws, int8_t* qc,
+                         int8_t* kc, float* qs, float* ks, int64_t rows) {
+  QuantParams qp{};
+  qp.x[0] = opnd(a->q);
+  qp.x[1] = opnd(a->k);
+  qp.tab.ptr = (const float*)(ws + L.table);
+  qp.tab.sb = s.Bt > 1 ? s.S * s.D : 0;
+  qp.codes[0] = qc;
+  qp.codes[1] = kc;
+  qp.c_sh = rows * s.D;
+  qp.c_sb = s.H * rows * s.D;
+  qp.rows = (int)rows;
+  qp.scales[0] = qs;
+  qp.scales[1] = ks;
+  qp.B = (int)s.B;
+  qp.H = (int)s.H;
+  qp.S = (int)s.S;
+  qp.D = (int)s.D;
+  qp.nblk = (int)((s.S + 63) / 64);
+  return qp;
+}
+
 rs_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
   if (!ws || ws_bytes < L.total) return RS_ERR_WORKSPACE;
   if (((uintptr_t)ws) % 256 != 0) return RS_ERR_ALIGN;
@@ -310,7 +346,7 @@ rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* by
   Shape s;
   rs_status st = validate_args(args, &s);
   if (st != RS_OK) return fail(st);
-  *bytes = layout(s, args->mask_kind, backward != 0).total;
+  *bytes = layout(s, args->mask_kind, backward != 0, (args->flags & RS_FLAG_QUANT_INT8_QK) != 0).total;
   return RS_OK;
 }
 
@@ -324,13 +360,19 @@ rs_status rope_sdpa_fwd(const rs_args* a, const rs_tensor* o, float* lse, void* 
   if (o->data && o->dtype != s.dtype) return fail(RS_ERR_DTYPE);
   if ((st = check_bhsd(o, s.dtype, sz)) != RS_OK) return fail(st);
   if (lse && ((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
-  const Layout L = layout(s, a->mask_kind, false);
+  const bool int8 = (a->flags & RS_FLAG_QUANT_INT8_QK) != 0;
+  const Layout L = layout(s, a->mask_kind, false, int8);
   if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
   if ((st = current_device_ok()) != RS_OK) return fail(st);
 
   char* w = (char*)ws;
   hipStream_t strm = (hipStream_t)stream;
   if ((st = prepare(a, s, L, w, strm)) != RS_OK) return fail(st);
+  if (int8) {
+    const QuantParams qp = quant_params(a, s, L, w, (int8_t*)(w + L.qc), (int8_t*)(w + L.kc),
+                                        (float*)(w + L.qs), (float*)(w + L.ks), L.sp);
+    if (launch_quant_int8(s.dtype, qp, strm) != 0) return fail(RS_ERR_LAUNCH);
+  }
   FwdParams p{};
   p.q = opnd(a->q);
   p.k = opnd(a->k);
@@ -347,7 +389,13 @@ rs_status rope_sdpa_fwd(const rs_args* a, const rs_tensor* o, float* lse, void* 
   const int bm = fwd_block_m(s.dtype);
   p.num_qt = (int)((s.S + bm - 1) / bm);
   const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
-  const bool int8 = (a->flags & RS_FLAG_QUANT_INT8_QK) != 0;
+  if (int8) {
+    p.qc = (const int8_t*)(w + L.qc);
+    p.kc = (const int8_t*)(w + L.kc);
+    p.qsc = (const float*)(w + L.qs);
+    p.ksc = (const float*)(w + L.ks);
+    p.sp = (int)L.sp;
+  }
   if (launch_fwd(s.dtype, (int)s.D, a->mask_kind, causal, int8, p, strm) != 0) return fail(RS_ERR_LAUNCH);
 
   (lse ? g_ctr.fwd_autograd : g_ctr.fwd_instream).fetch_add(1, std::memory_order_relaxed);
@@ -355,6 +403,26 @@ rs_status rope_sdpa_fwd(const rs_args* a, const rs_tensor* o, float* lse, void* 
   if (a->mask_kind == RS_MASK_ADDITIVE) g_ctr.masked_additive.fetch_add(1, std::memory_order_relaxed);
   if (causal) g_ctr.causal.fetch_add(1, std::memory_order_relaxed);
   if (int8) g_ctr.quant_int8.fetch_add(1, std::memory_order_relaxed);
+  return RS_OK;
+}
+
+rs_status rope_sdpa_debug_quantize_qk(const rs_args* a, int8_t* q_codes, int8_t* k_codes, float* q_scales,
+                                      float* k_scales, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  rs_status st = validate_args(a, &s);
+  if (st != RS_OK) return fail(st);
+  if (!(a->flags & RS_FLAG_QUANT_INT8_QK)) return fail(RS_ERR_INVALID);
+  if (!q_codes || !k_codes || !q_scales || !k_scales) return fail(RS_ERR_NULL);
+  if (((uintptr_t)q_codes) % 8 != 0 || ((uintptr_t)k_codes) % 8 != 0) return fail(RS_ERR_ALIGN);
+  if (((uintptr_t)q_scales) % 4 != 0 || ((uintptr_t)k_scales) % 4 != 0) return fail(RS_ERR_ALIGN);
+  const Layout L = layout(s, a->mask_kind, false, true);
+  if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
+  if ((st = current_device_ok()) != RS_OK) return fail(st);
+  char* w = (char*)ws;
+  hipStream_t strm = (hipStream_t)stream;
+  if ((st = prepare(a, s, L, w, strm)) != RS_OK) return fail(st);
+  const QuantParams qp = quant_params(a, s, L, w, q_codes, k_codes, q_scales, k_scales, s.S);
+  if (launch_quant_int8(s.dtype, qp, strm) != 0) return fail(RS_ERR_LAUNCH);
   return RS_OK;
 }
 
@@ -373,7 +441,7 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
     if ((st = check_bhsd(t, s.dtype, sz)) != RS_OK) return fail(st);
   }
   if (((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
-  const Layout L = layout(s, a->mask_kind, true);
+  const Layout L = layout(s, a->mask_kind, true, false);
   if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
   if ((st = current_device_ok()) != RS_OK) return fail(st);
 

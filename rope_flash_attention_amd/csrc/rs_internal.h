@@ -54,6 +54,13 @@ struct FwdParams {
   MaskView mask;
   AttnShape shp;
   int num_qt;  // query tiles per (b, h)
+  // blockwise int8 variant: codes of the rotated Q and K, [B][H][sp][D] int8 with sp = S
+  // rounded up to 64 (padding rows zero), and their fp32 scales [B][H][sp / 64]
+  const int8_t* qc;
+  const int8_t* kc;
+  const float* qsc;
+  const float* ksc;
+  int sp;
 };
 
 struct BwdParams {
@@ -71,7 +78,6 @@ struct BwdParams {
   AttnShape shp;
 };
 
-// int8 variant: per-(b, h, 64-token block) codes are recomputed in-stream; nothing persists.
 struct PackParams {
   const float* cos;
   const float* sin;
@@ -79,6 +85,17 @@ struct PackParams {
   float* out;                      // float2 pairs [Bt][S][D/2]
   int Bt, S, D;
   unsigned* ctrl;                  // control words cleared for the mask classifier
+};
+
+// Rotation + blockwise int8 quantization of Q (x[0]) and K (x[1]).
+struct QuantParams {
+  Opnd x[2];
+  Table tab;
+  int8_t* codes[2];     // [B][H][rows][D] with the strides below
+  int64_t c_sb, c_sh;   // element strides of the codes over b and h
+  int rows;             // allocated rows per (b, h) slice (>= S); rows past S are written as 0
+  float* scales[2];     // [B][H][nblk]
+  int B, H, S, D, nblk;
 };
 
 struct ClassifyParams {
@@ -94,6 +111,7 @@ int launch_pack_tables(const PackParams& p, void* stream);
 int launch_classify(const ClassifyParams& p, void* stream);
 int fwd_block_m(int dtype);  // query rows per forward workgroup
 int launch_fwd(int dtype, int D, int mask_kind, bool causal, bool int8, const FwdParams& p, void* stream);
+int launch_quant_int8(int dtype, const QuantParams& p, void* stream);
 int launch_bwd(int dtype, int D, int mask_kind, bool causal, const BwdParams& p, void* stream);
 // Reads (and optionally clears) the device-side count of all-true bool masks.
 int read_all_true_counter(uint64_t* value, bool reset);

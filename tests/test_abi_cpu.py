@@ -161,6 +161,46 @@ def test_int8_flag_limits():
     c = Call()
     c.flags = RS_FLAG_QUANT_INT8_QK | RS_FLAG_CAUSAL
     assert c.fwd() == ERR["RS_ERR_UNSUPPORTED"]
+    c = Call()
+    _bool_mask(c, (2, 1, 1, 100), (112, 0, 0, 1))
+    c.flags = RS_FLAG_QUANT_INT8_QK
+    assert c.fwd() == ERR["RS_ERR_UNSUPPORTED"]
+    c = Call()
+    c.flags = RS_FLAG_QUANT_INT8_QK  # a valid int8 request: only the missing device stops it
+    assert c.fwd() == ERR["RS_ERR_NO_DEVICE"]
+
+
+def test_int8_workspace_layout():
+    c = Call(B=2, H=3, S=100, D=128)
+    st, n = c.ws_size(0)
+    c.flags = RS_FLAG_QUANT_INT8_QK
+    st8, n8 = c.ws_size(0)
+    assert st == 0 and st8 == 0
+    codes = 2 * 3 * 128 * 128  # S padded to 128 rows, one byte per element
+    scales = -(-(2 * 3 * 2 * 4) // 256) * 256
+    assert n8 == n + 2 * codes + 2 * scales
+
+
+def test_debug_quantize_validation():
+    L = lib()
+    c = Call(B=2, H=3, S=100, D=128)
+    c.flags = RS_FLAG_QUANT_INT8_QK
+    a = c.args()
+    ptr = lambda i: BASE + (20 + i) * (1 << 32)
+    st = L.rope_sdpa_debug_quantize_qk(ctypes.byref(a), ptr(0), ptr(1), ptr(2), ptr(3), c.ws, c.ws_bytes, None)
+    assert st == ERR["RS_ERR_NO_DEVICE"]
+    st = L.rope_sdpa_debug_quantize_qk(ctypes.byref(a), None, ptr(1), ptr(2), ptr(3), c.ws, c.ws_bytes, None)
+    assert st == ERR["RS_ERR_NULL"]
+    st = L.rope_sdpa_debug_quantize_qk(ctypes.byref(a), ptr(0) + 4, ptr(1), ptr(2), ptr(3), c.ws, c.ws_bytes, None)
+    assert st == ERR["RS_ERR_ALIGN"]
+    st = L.rope_sdpa_debug_quantize_qk(ctypes.byref(a), ptr(0), ptr(1), ptr(2) + 2, ptr(3), c.ws, c.ws_bytes, None)
+    assert st == ERR["RS_ERR_ALIGN"]
+    st = L.rope_sdpa_debug_quantize_qk(ctypes.byref(a), ptr(0), ptr(1), ptr(2), ptr(3), c.ws, 64, None)
+    assert st == ERR["RS_ERR_WORKSPACE"]
+    c.flags = 0
+    a = c.args()
+    st = L.rope_sdpa_debug_quantize_qk(ctypes.byref(a), ptr(0), ptr(1), ptr(2), ptr(3), c.ws, c.ws_bytes, None)
+    assert st == ERR["RS_ERR_INVALID"]
 
 
 def test_strided_views_are_accepted():
