@@ -51,11 +51,18 @@ def _events_time(fn, steps, warmup, stream):
 
 
 def _source_hash():
+    """Hash of the kernel and host sources with comments and blank lines removed (a comment
+    edit does not invalidate counters taken on the same code)."""
+    import re
+
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rope_flash_attention_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+            text = open(os.path.join(csrc, name)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", "", text)
+            h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
@@ -103,6 +110,115 @@ def cpu_baseline(budget_s=10.0):
     }
 
 
+def _train_case(w, steps, dev, stream, causal):
+    """Forward with LSE + backward (the training step) and the backward alone."""
+    import rope_flash_attention_amd as rfa
+
+    B, H, S, D = w.q.shape
+    tq, tk, tv, tdo = (t.to(dev) for t in (w.q, w.k, w.v, w.do))
+    tc, ts = w.cos.to(dev), w.sin.to(dev)
+    res = {}
+
+    def fwd_lse():
+        res["o"], res["lse"] = rfa.rope_sdpa_fwd_with_lse(tq, tk, tv, tc, ts, is_causal=causal)
+
+    def bwd():
+        rfa.rope_sdpa_bwd_explicit(tq, tk, tv, tc, ts, res["o"], res["lse"], tdo, is_causal=causal)
+
+    def step():
+        fwd_lse()
+        bwd()
+
+    fwd_lse()
+    n = max(5, steps // 2)
+    ms_bwd = _events_time(bwd, n, 2, stream)
+    ms_train = _events_time(step, n, 2, stream)
+    fl_f = flops_fwd(B, H, S, D, causal)
+    return {
+        "ms_fwd_bwd": round(ms_train, 4),
+        "ms_bwd": round(ms_bwd, 4),
+        "tflops_fwd_bwd": round(3.5 * fl_f / (ms_train * 1e-3) / 1e12, 2),
+        "tflops_bwd": round(2.5 * fl_f / (ms_bwd * 1e-3) / 1e12, 2),
+    }
+
+
+def _extra_cases(steps, dev, stream):
+    """Masked FLUX forwards (B=2) and the long-sequence forward in bf16 and int8 (no-grad)."""
+    import torch
+
+    import synthetic as syn
+    import rope_flash_attention_amd as rfa
+
+    out = {}
+    n = max(5, steps // 3)
+
+    def timed(name, w_dev, mask=None, quant=None, note=""):
+        q, k, v, c, s = w_dev
+        B, H, S, D = q.shape
+
+        def f():
+            rfa.rope_scaled_dot_product_attention(q, k, v, c, s, attn_mask=mask, quantization=quant)
+
+        with torch.no_grad():
+            ms = _events_time(f, n, 2, stream)
+        out[name] = {"ms": round(ms, 4), "tflops": round(flops_fwd(B, H, S, D) / (ms * 1e-3) / 1e12, 2),
+                     "shape": f"B={B},H={H},S={S},D={D}"}
+        if note:
+            out[name]["note"] = note
+
+    w = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=3000)
+    S = w.q.shape[2]
+    wd = tuple(t.to(dev) for t in (w.q, w.k, w.v, w.cos, w.sin))
+    lens = syn.key_padding_lengths(3000, 2)
+    bm = syn.key_padding_mask(lens, 512, S).to(dev)
+    timed("mask_bool_key_padding", wd, bm, note="bool [2,1,1,S]; dense flop count")
+    timed("mask_all_true", wd, torch.ones_like(bm), note="bool [2,1,1,S] all True (skip path)")
+    add = torch.where(bm, torch.zeros((), dtype=torch.bfloat16, device=dev),
+                      torch.full((), float("-inf"), dtype=torch.bfloat16, device=dev)).expand(2, 24, S, S).contiguous()
+    timed("mask_additive_4d", wd, add, note="bf16 [2,24,S,S] 0/-inf, 2.04 GB read")
+    del add, wd
+    torch.cuda.empty_cache()
+
+    w = syn.flux(batch=1, heads=48, grid=128, dtype="bf16", seed=5000)
+    wd = tuple(t.to(dev) for t in (w.q, w.k, w.v, w.cos, w.sin))
+    del w
+    timed("long_bf16", wd)
+    timed("long_int8", wd, quant="int8", note="int8 Q'K'^T + bf16 P.V; flops counted as the dense formula")
+    del wd
+    torch.cuda.empty_cache()
+    return out
+
+
+def traffic_from_counters(fetch_db, write_db, command):
+    """HBM bytes per launch of the forward kernel from two rocprofv3 --pmc runs of
+    `bench.py --copy-probe` (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch).  Each
+    counter is scaled by what it reads for the 256 MiB device copy of the same run (a copy
+    reads and writes 256 MiB)."""
+    import sqlite3
+
+    def per_kernel(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select kernel_name, avg(value), count(*) from counters_collection "
+                           "where counter_name = ? group by kernel_name, grid_size", (counter,)).fetchall()
+        return rows
+
+    copy_bytes = 256 << 20
+    out = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        rows = per_kernel(db, counter)
+        probe = max((v for n, v, c in rows if "copyBuffer" in n), default=None)
+        fwd = [(n, v, c) for n, v, c in rows if "fwd_kernel" in n]
+        if probe is None or not fwd:
+            raise SystemExit(f"{db}: no copy probe or forward kernel with {counter}")
+        scale = copy_bytes / (probe * 1024.0)
+        name, v, c = max(fwd, key=lambda x: x[2])
+        out[counter] = {"kiB_per_dispatch": v, "copy_probe_kiB": probe, "scale": scale,
+                        "bytes_per_launch": v * 1024.0 * scale, "kernel": name, "dispatches": c}
+    total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    return {"fwd_bf16_d128_flux_b1": {"bytes_per_launch": total, "source_hash": _source_hash(),
+                                      "command": command, "counters": out}}
+
+
 def summarize_rocpd(db_path, command):
     """Text summary of a rocprofv3 kernel trace: per kernel and grid size, calls and durations."""
     import sqlite3
@@ -125,14 +241,20 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-train", action="store_true", help="skip the training-step timing")
+    ap.add_argument("--no-train", action="store_true", help="skip the training-step timings")
+    ap.add_argument("--no-extra", action="store_true", help="skip the masked / long / int8 forward timings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--summarize", metavar="DB", help="print a summary of a rocprofv3 results database and exit")
     ap.add_argument("--command", default="", help="command line recorded in the --summarize output")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="print HBM bytes per forward launch from two rocprofv3 --pmc results databases and exit")
     args = ap.parse_args()
     if args.summarize:
         print(summarize_rocpd(args.summarize, args.command))
+        return
+    if args.traffic:
+        print(json.dumps(traffic_from_counters(args.traffic[0], args.traffic[1], args.command), indent=1))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
@@ -186,32 +308,18 @@ def main():
     # ---- training step, FLUX B=2 ------------------------------------------------------------
     train = None
     if not args.no_train:
-        wt = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=4100, with_grad=True)
-        tq, tk, tv, tdo = (t.to(dev) for t in (wt.q, wt.k, wt.v, wt.do))
-        tc, ts = wt.cos.to(dev), wt.sin.to(dev)
-        res = {}
+        train = _train_case(syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=4100, with_grad=True),
+                            args.steps, dev, stream, causal=False)
+        train["config"] = "FLUX B=2,H=24,S=4608,D=128,bf16"
+        ct = _train_case(syn.causal_1axis(batch=4, heads=16, seq=2048, dim=128, dtype="bf16", seed=4200),
+                         args.steps, dev, stream, causal=True)
+        ct["config"] = "causal B=4,H=16,S=2048,D=128,bf16, 1-axis RoPE"
+        train["causal"] = ct
 
-        def fwd_lse():
-            res["o"], res["lse"] = rfa.rope_sdpa_fwd_with_lse(tq, tk, tv, tc, ts)
-
-        def bwd():
-            rfa.rope_sdpa_bwd_explicit(tq, tk, tv, tc, ts, res["o"], res["lse"], tdo)
-
-        def step():
-            fwd_lse()
-            bwd()
-
-        fwd_lse()
-        ms_bwd = _events_time(bwd, max(5, args.steps // 2), 2, stream)
-        ms_train = _events_time(step, max(5, args.steps // 2), 2, stream)
-        fl_f = flops_fwd(2, 24, S, D)
-        train = {
-            "config": "B=2,H=24,S=4608,D=128,bf16",
-            "ms_fwd_bwd": round(ms_train, 4),
-            "ms_bwd": round(ms_bwd, 4),
-            "tflops_fwd_bwd": round(3.5 * fl_f / (ms_train * 1e-3) / 1e12, 2),
-            "tflops_bwd": round(2.5 * fl_f / (ms_bwd * 1e-3) / 1e12, 2),
-        }
+    # ---- the other forward workloads: masks at the FLUX shape, long sequence bf16 and int8 ----
+    extra = None
+    if not args.no_extra:
+        extra = _extra_cases(args.steps, dev, stream)
 
     line = {
         "metric": METRIC,
@@ -237,9 +345,11 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": _traffic("fwd_bf16_d128_flux_b1"),
-            "kernel": "fwd_kernel<bf16,128,nomask> (+ table pack kernel inside the timed call)",
+            "kernel": "fwd_kernel<bf16,128,nomask>; achieved = algorithmic flops over the event-timed forward call "
+                      "(table packing launch + attention kernel)",
         },
         "train": train,
+        "forward_variants": extra,
         "parity_rel_err": err,
         "cpu_baseline": base,
     }

@@ -107,6 +107,24 @@ __device__ inline void wait_vmem_but_and_sync() {
   __syncthreads();
 }
 
+// Instruction schedule for a chain of N matrix products fed from LDS, each product
+// consuming RPM LDS reads: AHEAD products' worth of reads are issued first, then each
+// product is followed by the reads of the product AHEAD places later.  Without it the
+// scheduler tends to pair every read with its product and wait out each LDS round trip.
+// Must follow the reads and products it orders, in the same basic block; SYNC separates
+// independent chains of one block.
+template <int N, int RPM, int AHEAD, int SYNC>
+__device__ inline void sched_reads_ahead() {
+  static_assert(AHEAD >= 1 && AHEAD <= N, "read-ahead depth");
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * RPM, SYNC);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, SYNC);  // one matrix product
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, SYNC);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, SYNC);
+}
+
 // Interleaved-pair rotation with each product and sum rounded to fp32 (no fused
 // multiply-add), so that quantized codes computed from it are reproducible exactly.
 __device__ inline float2 rot_pair(float x0, float x1, float c, float s) {

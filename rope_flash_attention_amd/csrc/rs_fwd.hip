@@ -12,8 +12,9 @@
 //    (cos, sin) table, multiplied by scale*log2(e) (scores come out in log2 units), rounded
 //    to the input dtype and kept in registers as MFMA B fragments;
 //  * K/V tiles of BN keys stream through LDS, double buffered: K is rotated in registers on
-//    its way in (never written back to memory), V is transposed into 128-byte rows with an
-//    XOR swizzle so the P.V operand is one 16-byte LDS read per lane;
+//    its way in (never written back to memory); V goes from memory straight into a
+//    row-major LDS tile (buffer loads with an LDS destination, chunks XOR-swizzled per row)
+//    and the P.V operand is read transposed from it;
 //  * S^T = K' Q'^T lands with one query per lane, so the row max needs one exchange between
 //    wave halves and the P^T fragments feed O^T += V^T P^T directly from registers;
 //  * the running row max m enters the S product through the MFMA accumulator (C = -m), so
@@ -72,9 +73,6 @@ __device__ inline float2 rot_pair_fma(float x0, float x1, float c, float s) {
   return r;
 }
 
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
 constexpr int QK_AHEAD = 8;  // K' fragment reads kept in flight ahead of the QK^T products
 constexpr int PV_AHEAD = 3;  // V^T fragments (two reads each) in flight ahead of the P.V products
 
@@ -365,8 +363,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][i] = fmaf((float)acc[i], f, -m_base);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NKB * NQ8, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NKB * NQ8, 0);
+      sched_reads_ahead<NKB * NQ8, 1, NKB * NQ8, 0>();
     } else {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -378,18 +375,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int t = 0; t < NQK; ++t) sacc[kb] = M::mma(ka[t], qf[t], t == 0 ? negm : sacc[kb]);
       }
-      if constexpr (KPL == 8) {
-        // keep QK_AHEAD fragment reads in flight ahead of the products (the scheduler would
-        // otherwise pair each read with its product and wait out every LDS round trip)
-        constexpr int NR = NKB * NQK;
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, QK_AHEAD, 0);
-#pragma unroll
-        for (int i = 0; i < NR - QK_AHEAD; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, QK_AHEAD, 0);
-      }
+      if constexpr (KPL == 8) sched_reads_ahead<NKB * NQK, 1, QK_AHEAD, 0>();
     }
   };
 
@@ -519,14 +505,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
           }
       }
       // V^T fragments: PV_AHEAD products' worth of transposed reads in flight
-      constexpr int NP = NDB * NKB * 2;
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PV_AHEAD, 1);
-#pragma unroll
-      for (int i = 0; i < NP - PV_AHEAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, PV_AHEAD, 1);
+      sched_reads_ahead<NDB * NKB * 2, 2, PV_AHEAD, 1>();
     } else {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
