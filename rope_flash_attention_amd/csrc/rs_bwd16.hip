@@ -1,0 +1,627 @@
+// Backward kernels for 16-bit inputs at D = 128 on 16x16x32 MFMA.
+//
+// Same mathematics as rs_bwd.hip (page "Metal Flash Attention", section "Fused RoPE +
+// SDPA": gradients with respect to the pre-rotation Q and K through the inverse rotation):
+//    P = exp2(S' - LSE log2 e) with S' = scale log2(e) Q'K'^T,  dP = dO V^T,
+//    dS = P o (dP - delta),  dV = P^T dO,  dK = R^T (scale dS^T Q'),  dQ = R^T (scale dS K').
+//
+// The 16x16 products keep a wave's accumulators small (a 16 x 128 block is 32 registers
+// instead of 64 for 32 rows), so eight waves of one workgroup fit two per SIMD:
+//  * dq16:   workgroup = 128 queries (16 per wave, one per lane column); Q' (times
+//            scale log2 e) and dO stay in registers as B operands; K' is rotated on its way
+//            into LDS and V goes straight from memory into LDS; per 64-key tile
+//            S'^T = K' Q'^T, dP^T = V dO^T (row reads), dQ'^T += K'^T dS^T (transposed reads).
+//  * dkdv16: workgroup = 128 keys (16 per wave); K' (times scale log2 e) and V stay in
+//            registers; Q' (rotated) and dO tiles of 64 queries stream through LDS; per tile
+//            S' = Q' K'^T, dP = dO V^T, dV^T += dO^T P, dK'^T += Q'^T dS.
+// The score rows are read in a permuted order so that the four accumulator rows a lane holds
+// in two consecutive 16-row blocks are eight consecutive contraction indices of the next
+// product: P and dS go from accumulators to B operands without leaving registers.
+// LDS tiles are 64 rows of 256 bytes with 16-byte chunks XOR-swizzled per row so that both
+// the row reads (16 lanes x 16 bytes) and the transposed reads (32 lanes x 8 bytes) touch
+// distinct banks.  Deterministic: no atomics.
+#include "rs_device.hpp"
+
+namespace rs {
+
+namespace {
+
+constexpr float kL2e = 1.4426950408889634f;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct M16;
+template <>
+struct M16<__bf16> {
+  __device__ static inline f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct M16<_Float16> {
+  __device__ static inline f32x4 mma(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Swizzle of 256-byte LDS rows: logical 16-byte chunk ch of row r sits at ch ^ msk16(r).
+__device__ inline int msk16(int row) { return ((row & 3) << 2) | ((row >> 2) & 2) | ((row >> 4) & 1); }
+__device__ inline int lds_off(int row, int byte) { return row * 256 + (((byte >> 4) ^ msk16(row)) << 4) + (byte & 15); }
+
+// Row of a 64-row tile that lane row rho of 16-row block kb reads.  With this order the
+// accumulator rows 4g..4g+3 of blocks 2s and 2s+1 are tile rows 32s + 8g + 0..7.
+__device__ inline int blk_row(int kb, int rho) { return 32 * (kb >> 1) + 8 * (rho >> 2) + 4 * (kb & 1) + (rho & 3); }
+
+// Per-lane LDS byte offsets of the two access patterns.  The swizzle only depends on row
+// bits 0, 1, 3 and 4, which the lane fixes; block and k-step terms are plain additions,
+// so one register per pattern serves every block and buffer.
+//  * row reads: lane (c, g) reads 16 bytes of row blk_row(kb, c) at column 64t + 16g:
+//      offset = row_rd[t] + 256 (32 (kb >> 1) + 4 (kb & 1));
+//  * transposed reads: rows r0 + 4h + (c >> 2) (r0 = 32s + 8g), 8 bytes at column
+//    16db + 4(c & 3) (16-bit elements): offset = tr_rd[db] + 256 (32 s + 4 h).
+struct LaneOffsets {
+  int row_rd[4];
+  int tr_rd[8];
+  __device__ void init(int c, int g) {
+    const int rl = 8 * (c >> 2) + (c & 3);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) row_rd[t] = lds_off(rl, 64 * t + 16 * g);
+    const int rt = 8 * g + (c >> 2);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) tr_rd[db] = lds_off(rt, 2 * (16 * db + 4 * (c & 3)));
+  }
+};
+__device__ inline int blk_off(int kb) { return 256 * (32 * (kb >> 1) + 4 * (kb & 1)); }
+
+// A fragment of a transposed operand: element e = tile[32s + 8g + e][16db + c] (16-bit
+// elements), from two transposed 8-byte reads per lane.
+template <typename F>
+__device__ inline F tr_frag(const char* tile, const LaneOffsets& lo_, int s, int db) {
+  const char* a = tile + lo_.tr_rd[db] + 256 * 32 * s;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a + 256 * 4));
+  F f;
+  *(s16x4*)&f = lo;
+  *((s16x4*)&f + 1) = hi;
+  return f;
+}
+
+// Rotation of one pair with fused multiply-adds (the forward's form for Q and K).
+__device__ inline float2 rot_fma(float x0, float x1, float c, float s) {
+  float2 r;
+  r.x = fmaf(x0, c, -x1 * s);
+  r.y = fmaf(x0, s, x1 * c);
+  return r;
+}
+
+// B fragments of one row (D = 128): element e of fragment t = row[32t + 8g + e], rotated
+// with the packed table row and multiplied by `mul` when ROT.
+template <typename T, bool ROT>
+__device__ inline void row_frags(typename Mf<T>::frag* f, const T* row, const float* trow, int g, float mul) {
+  typedef T v8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int d0 = 32 * t + 8 * g;
+    v8 x = *(const v8*)(row + d0);
+    if constexpr (ROT) {
+      const float4 a = *(const float4*)(trow + d0), b = *(const float4*)(trow + d0 + 4);
+      const float cc[4] = {a.x, a.z, b.x, b.z}, ss[4] = {a.y, a.w, b.y, b.w};
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const float2 r = rot_fma(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), cc[pp], ss[pp]);
+        x[2 * pp] = from_f<T>(r.x * mul);
+        x[2 * pp + 1] = from_f<T>(r.y * mul);
+      }
+    }
+    f[t] = x;
+  }
+}
+
+// Staging of a 64-row tile that needs rotation (K for dq16, Q for dkdv16): each of the 512
+// threads loads two 16-byte chunks and their table pairs into registers, rotates them and
+// writes them swizzled.
+template <typename T>
+struct RotStager {
+  uint4 x[2];
+  float4 t[2][2];
+  int row, ch;
+  __device__ void init(int tid) {
+    row = tid >> 4;
+    ch = tid & 15;
+  }
+  __device__ void load(const T* base, int64_t ss, const float* tab, int row0, int S) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int j = row0 + row + 32 * it;
+      if (row0 + 64 <= S || j < S) {
+        x[it] = *(const uint4*)(base + (int64_t)j * ss + 8 * ch);
+        const float* tr = tab + (int64_t)j * 128 + 8 * ch;
+        t[it][0] = *(const float4*)tr;
+        t[it][1] = *(const float4*)(tr + 4);
+      } else {
+        x[it] = make_uint4(0, 0, 0, 0);
+        t[it][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+        t[it][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
+  __device__ void store(char* tile) {
+    typedef T v8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const float* tf = (const float*)&t[it][0];
+      v8 v = *(const v8*)&x[it];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const float2 r = rot_fma(to_f(v[2 * pp]), to_f(v[2 * pp + 1]), tf[2 * pp], tf[2 * pp + 1]);
+        v[2 * pp] = from_f<T>(r.x);
+        v[2 * pp + 1] = from_f<T>(r.y);
+      }
+      *(uint4*)(tile + lds_off(row + 32 * it, 16 * ch)) = *(const uint4*)&v;
+    }
+  }
+};
+
+// Direct-to-LDS loads of a 64-row tile of a [*, 128] 16-bit operand (rows past the end of
+// the slice read as zero): each wave issues two 1 KB loads.
+struct DmaTile {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[2];
+  uint32_t row_bytes;
+  __device__ void init(const void* base, int64_t ss, int S, int wave, int lane) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(((int64_t)(S - 1) * ss + 128) * 2), 0x00020000);
+    row_bytes = (uint32_t)(ss * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int byte = (wave * 2 + i) * 1024 + lane * 16;
+      const int row = byte >> 8, pch = (byte & 255) >> 4;
+      voff[i] = (uint32_t)(row * (int)row_bytes + ((pch ^ msk16(row)) << 4));
+    }
+  }
+  __device__ void issue(char* tile, int row0, int wave) {
+    const uint32_t soff = (uint32_t)row0 * row_bytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) buffer_load_lds16(rsrc, tile + (wave * 2 + i) * 1024, voff[i], soff);
+  }
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+template <typename T, int MASK, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
+  using frag = typename Mf<T>::frag;
+  using M = M16<T>;
+  constexpr int D = 128, BM = 128, BN = 64, TILE = BN * 256;
+  __shared__ __attribute__((aligned(16))) char sk0[TILE];
+  __shared__ __attribute__((aligned(16))) char sk1[TILE];
+  __shared__ __attribute__((aligned(16))) char sv0[TILE];
+  __shared__ __attribute__((aligned(16))) char sv1[TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int S = p.shp.S;
+  const int nqt = (S + BM - 1) / BM;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  int qt = item % nqt;
+  const int bh = item / nqt;
+  const int hd = bh % p.shp.H, b = bh / p.shp.H;
+  if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
+  const int q0 = qt * BM;
+  const int m = q0 + 16 * wave + c;
+  const int mc = m < S ? m : S - 1;
+
+  const T* kbase = (const T*)p.k.ptr + b * p.k.sb + hd * p.k.sh;
+  const T* vbase = (const T*)p.v.ptr + b * p.v.sb + hd * p.v.sh;
+  const float* tab = p.tab.ptr + b * p.tab.sb;
+
+  frag qf[4], gf[4];
+  row_frags<T, true>(qf, (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh + (int64_t)mc * p.q.ss, tab + (int64_t)mc * D,
+                     g, p.shp.scale_log2);
+  row_frags<T, false>(gf, (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh + (int64_t)mc * p.dout.ss, nullptr,
+                      g, 1.f);
+  const int64_t rowid = ((int64_t)b * p.shp.H + hd) * S + mc;
+  const float lse_v = p.lse[rowid];
+  const float l2 = (m >= S || lse_v == -INFINITY) ? INFINITY : lse_v * kL2e;
+  const float dlt = p.delta[rowid];
+  const f32x4 cinit = {-l2, -l2, -l2, -l2};  // S'^T - LSE log2 e through the accumulator
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+  f32x4 dq[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dq[i] = z4;
+
+  const int nkt = (S + BN - 1) / BN;
+  int kt_end = nkt;
+  if (CAUSAL) kt_end = min(nkt, (min(q0 + BM, S) - 1) / BN + 1);
+  auto tile_state = [&](int kt) -> uint32_t {
+    if constexpr (MASK == MASK_BOOL) {
+      const int bm = p.mask.t_sb ? b : 0, hm = p.mask.t_sh ? hd : 0;
+      uint32_t st = mask_tile_state(p.mask, bm, hm, 2 * qt, kt);
+      if (2 * qt + 1 < (S + kMaskTile - 1) / kMaskTile) st |= mask_tile_state(p.mask, bm, hm, 2 * qt + 1, kt);
+      return st;
+    } else {
+      return TILE_MIXED;
+    }
+  };
+  auto next_tile = [&](int kt) -> int {
+    if constexpr (MASK == MASK_BOOL) {
+      while (kt < kt_end && tile_state(kt) == TILE_ALL_FALSE) ++kt;
+    }
+    return kt;
+  };
+
+  LaneOffsets lo;
+  lo.init(c, g);
+  RotStager<T> sk;
+  sk.init(tid);
+  DmaTile dv;
+  dv.init(vbase, p.v.ss, S, wave, lane);
+  const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
+
+  int kt = next_tile(0);
+  if (kt < kt_end) {
+    sk.load(kbase, p.k.ss, tab, kt * BN, S);
+    dv.issue(sv0, kt * BN, wave);
+    sk.store(sk0);
+  }
+  wait_vmem_and_sync();
+
+  auto body = [&](auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
+    const char* sK = stage ? sk1 : sk0;
+    const char* sV = stage ? sv1 : sv0;
+    char* sKn = stage ? sk0 : sk1;
+    char* sVn = stage ? sv0 : sv1;
+    const int ktn = next_tile(kt + 1);
+    if (ktn < kt_end) {
+      sk.load(kbase, p.k.ss, tab, ktn * BN, S);
+      dv.issue(sVn, ktn * BN, wave);
+    }
+    const int kv0 = kt * BN;
+
+    // S'^T - l2 and dP^T: rows = keys (permuted order), column = this lane's query
+    f32x4 sacc[4], dpacc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      frag ka[4], va[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ka[t] = *(const frag*)(sK + lo.row_rd[t] + blk_off(kb));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) va[t] = *(const frag*)(sV + lo.row_rd[t] + blk_off(kb));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sacc[kb] = M::mma(ka[t], qf[t], t == 0 ? cinit : sacc[kb]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dpacc[kb] = M::mma(va[t], gf[t], t == 0 ? z4 : dpacc[kb]);
+    }
+    sched_reads_ahead<32, 1, 8, 0>();
+
+    // exclusions (keys past the end, causal, masks), P and dS
+    if constexpr (MASK == MASK_ADD) {
+      const int esz = p.mask.dtype == F32 ? 4 : 2;
+      const char* mrow = mask_row_ptr(p.mask, bm, hm, p.mask.sq ? mc : 0, esz);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float mv[8];
+        mask_add8<T>(p.mask, mrow, kv0 + 32 * half + 8 * g, S, mv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sacc[2 * half + (e >> 2)][e & 3] = fmaf(mv[e], kL2e, sacc[2 * half + (e >> 2)][e & 3]);
+      }
+    }
+    uint32_t st = TILE_ALL_TRUE;
+    if constexpr (MASK == MASK_BOOL) st = tile_state(kt);
+    const bool check = kv0 + BN > S || (CAUSAL && kv0 + BN - 1 > q0) || (MASK == MASK_BOOL && st != TILE_ALL_TRUE);
+    uint32_t bits[2] = {0xffu, 0xffu};
+    if (check) {
+      if constexpr (MASK == MASK_BOOL) {
+        if (st != TILE_ALL_TRUE) {
+          const uint8_t* brow = (const uint8_t*)mask_row_ptr(p.mask, bm, hm, p.mask.sq ? mc : 0, 1);
+          bits[0] = mask_bits8(p.mask, brow, kv0 + 8 * g, S);
+          bits[1] = mask_bits8(p.mask, brow, kv0 + 32 + 8 * g, S);
+        }
+      }
+    }
+    frag dsf[2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float pv = fast_exp2(sacc[kb][i]);
+        if (check) {
+          const int e = 4 * (kb & 1) + i;  // key = kv0 + 32 (kb >> 1) + 8 g + e
+          const int j = kv0 + 32 * (kb >> 1) + 8 * g + e;
+          bool ok = j < S && ((bits[kb >> 1] >> e) & 1u);
+          if (CAUSAL) ok = ok && j <= m;
+          if (!ok) pv = 0.f;
+        }
+        dsf[kb >> 1][4 * (kb & 1) + i] = from_f<T>(pv * (dpacc[kb][i] - dlt));
+      }
+
+    // dQ'^T += K'^T dS^T: rows = head dim, column = this lane's query
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) dq[db] = M::mma(tr_frag<frag>(sK, lo, ks, db), dsf[ks], dq[db]);
+    sched_reads_ahead<16, 2, 3, 1>();
+
+    if (ktn < kt_end) sk.store(sKn);
+    wait_vmem_and_sync();
+    kt = ktn;
+  };
+  while (kt < kt_end) {
+    body(std::integral_constant<int, 0>{});
+    if (kt >= kt_end) break;
+    body(std::integral_constant<int, 1>{});
+  }
+
+  // dQ = R^T (scale dQ'): lane holds d = 16 db + 4 g + i of its query row
+  if (m < S) {
+    char* orow = (char*)p.dq + ((int64_t)b * p.dq_sb + (int64_t)hd * p.dq_sh + (int64_t)m * p.dq_ss) * 2;
+    const float* trow = tab + (int64_t)m * D;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int d0 = 16 * db + 4 * g;
+      const float4 cs = *(const float4*)(trow + d0);  // pairs d0/2, d0/2 + 1
+      const float sc = p.shp.scale;
+      const float2 a = rot_pair_t(dq[db][0] * sc, dq[db][1] * sc, cs.x, cs.y);
+      const float2 e = rot_pair_t(dq[db][2] * sc, dq[db][3] * sc, cs.z, cs.w);
+      typedef T v4 __attribute__((ext_vector_type(4)));
+      v4 w;
+      w[0] = from_f<T>(a.x);
+      w[1] = from_f<T>(a.y);
+      w[2] = from_f<T>(e.x);
+      w[3] = from_f<T>(e.y);
+      *(v4*)(orow + d0 * 2) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <typename T, int MASK, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
+  using frag = typename Mf<T>::frag;
+  using M = M16<T>;
+  constexpr int D = 128, BNK = 128, BMQ = 64, TILE = BMQ * 256;
+  __shared__ __attribute__((aligned(16))) char sq0[TILE];
+  __shared__ __attribute__((aligned(16))) char sq1[TILE];
+  __shared__ __attribute__((aligned(16))) char sd0[TILE];
+  __shared__ __attribute__((aligned(16))) char sd1[TILE];
+  __shared__ __attribute__((aligned(16))) float sl0[2 * BMQ];  // l2 then delta per query
+  __shared__ __attribute__((aligned(16))) float sl1[2 * BMQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int S = p.shp.S;
+  const int nkt = (S + BNK - 1) / BNK;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = item % nkt;
+  const int bh = item / nkt;
+  const int hd = bh % p.shp.H, b = bh / p.shp.H;
+  const int k0 = kt * BNK;
+  const int j = k0 + 16 * wave + c;  // this lane's key
+  const int jc = j < S ? j : S - 1;
+
+  const T* qbase = (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh;
+  const T* dobase = (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh;
+  const float* tab = p.tab.ptr + b * p.tab.sb;
+  const float* lse = p.lse + ((int64_t)b * p.shp.H + hd) * S;
+  const float* dlt = p.delta + ((int64_t)b * p.shp.H + hd) * S;
+
+  // K' (times scale log2 e) and V of this lane's key as B fragments
+  frag kf[4], vf[4];
+  row_frags<T, true>(kf, (const T*)p.k.ptr + b * p.k.sb + hd * p.k.sh + (int64_t)jc * p.k.ss, tab + (int64_t)jc * D,
+                     g, p.shp.scale_log2);
+  row_frags<T, false>(vf, (const T*)p.v.ptr + b * p.v.sb + hd * p.v.sh + (int64_t)jc * p.v.ss, nullptr, g, 1.f);
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 dv[8], dk[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    dv[i] = z4;
+    dk[i] = z4;
+  }
+
+  const int nqt = (S + BMQ - 1) / BMQ;
+  const int qt_begin = CAUSAL ? k0 / BMQ : 0;
+  auto tile_state = [&](int qt) -> uint32_t {
+    if constexpr (MASK == MASK_BOOL) {
+      const int bm = p.mask.t_sb ? b : 0, hm = p.mask.t_sh ? hd : 0;
+      const int nk64 = (S + kMaskTile - 1) / kMaskTile;
+      uint32_t st = mask_tile_state(p.mask, bm, hm, qt, 2 * kt);
+      if (2 * kt + 1 < nk64) st |= mask_tile_state(p.mask, bm, hm, qt, 2 * kt + 1);
+      return st;
+    } else {
+      return TILE_MIXED;
+    }
+  };
+  auto next_tile = [&](int qt) -> int {
+    if constexpr (MASK == MASK_BOOL) {
+      while (qt < nqt && tile_state(qt) == TILE_ALL_FALSE) ++qt;
+    }
+    return qt;
+  };
+
+  LaneOffsets lo;
+  lo.init(c, g);
+  RotStager<T> sq;
+  sq.init(tid);
+  DmaTile dd;
+  dd.init(dobase, p.dout.ss, S, wave, lane);
+  float lreg = 0.f;  // thread t < 64: l2 of query q0 + t; 64 <= t < 128: delta of q0 + t - 64
+  auto load_tile = [&](int qt, char* sD) {
+    const int q0 = qt * BMQ;
+    sq.load(qbase, p.q.ss, tab, q0, S);
+    dd.issue(sD, q0, wave);
+    if (tid < 2 * BMQ) {
+      const int i = q0 + (tid & (BMQ - 1));
+      if (tid < BMQ) {
+        const float lv = i < S ? lse[i] : -INFINITY;
+        lreg = lv == -INFINITY ? INFINITY : lv * kL2e;  // +inf makes P = 0 for empty rows
+      } else {
+        lreg = i < S ? dlt[i] : 0.f;
+      }
+    }
+  };
+  auto store_tile = [&](char* sQ, float* sL) {
+    sq.store(sQ);
+    if (tid < 2 * BMQ) sL[tid] = lreg;
+  };
+  const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
+
+  int qt = next_tile(qt_begin);
+  if (qt < nqt) {
+    load_tile(qt, sd0);
+    store_tile(sq0, sl0);
+  }
+  wait_vmem_and_sync();
+
+  auto body = [&](auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
+    const char* sQ = stage ? sq1 : sq0;
+    const char* sD = stage ? sd1 : sd0;
+    const float* sL = stage ? sl1 : sl0;
+    char* sQn = stage ? sq0 : sq1;
+    char* sDn = stage ? sd0 : sd1;
+    float* sLn = stage ? sl0 : sl1;
+    const int qtn = next_tile(qt + 1);
+    if (qtn < nqt) load_tile(qtn, sDn);
+    const int q0 = qt * BMQ;
+
+    // S' and dP: rows = queries (permuted order), column = this lane's key
+    f32x4 sacc[4], dpacc[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      frag qa[4], ga[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qa[t] = *(const frag*)(sQ + lo.row_rd[t] + blk_off(qb));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ga[t] = *(const frag*)(sD + lo.row_rd[t] + blk_off(qb));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sacc[qb] = M::mma(qa[t], kf[t], t == 0 ? z4 : sacc[qb]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dpacc[qb] = M::mma(ga[t], vf[t], t == 0 ? z4 : dpacc[qb]);
+    }
+    sched_reads_ahead<32, 1, 8, 0>();
+
+    // accumulator row 4g + i of block qb is query q0 + 32 (qb >> 1) + 8 g + 4 (qb & 1) + i
+    if constexpr (MASK == MASK_ADD) {
+      const int jj = p.mask.key_bcast ? 0 : jc;
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int qi = min(q0 + 32 * (qb >> 1) + 8 * g + 4 * (qb & 1) + i, S - 1);
+          float mvv;
+          if (p.mask.dtype == F32)
+            mvv = ((const float*)mask_row_ptr(p.mask, bm, hm, p.mask.sq ? qi : 0, 4))[jj];
+          else
+            mvv = to_f(((const T*)mask_row_ptr(p.mask, bm, hm, p.mask.sq ? qi : 0, 2))[jj]);
+          sacc[qb][i] = fmaf(mvv, kL2e, sacc[qb][i]);
+        }
+    }
+    uint32_t st = TILE_ALL_TRUE;
+    if constexpr (MASK == MASK_BOOL) st = tile_state(qt);
+    const bool check = (CAUSAL && q0 < k0 + BNK - 1) || (MASK == MASK_BOOL && st != TILE_ALL_TRUE);
+    frag pf[2], sf[2];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int r0 = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);  // tile-local query of register 0
+      const float4 lv = *(const float4*)(sL + r0);
+      const float4 dl = *(const float4*)(sL + BMQ + r0);
+      const float l4[4] = {lv.x, lv.y, lv.z, lv.w}, d4[4] = {dl.x, dl.y, dl.z, dl.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float pv = fast_exp2(sacc[qb][i] - l4[i]);
+        if (check) {
+          const int qi = q0 + r0 + i;
+          bool ok = true;
+          if (CAUSAL) ok = j <= qi;
+          if constexpr (MASK == MASK_BOOL) {
+            if (st != TILE_ALL_TRUE && ok && qi < S) {
+              const uint8_t* brow = (const uint8_t*)mask_row_ptr(p.mask, bm, hm, p.mask.sq ? qi : 0, 1);
+              ok = brow[p.mask.key_bcast ? 0 : jc] != 0;
+            }
+          }
+          if (!ok) pv = 0.f;
+        }
+        pf[qb >> 1][4 * (qb & 1) + i] = from_f<T>(pv);
+        sf[qb >> 1][4 * (qb & 1) + i] = from_f<T>(pv * (dpacc[qb][i] - d4[i]));
+      }
+    }
+
+    // dV^T += dO^T P, dK'^T += Q'^T dS: rows = head dim, column = this lane's key
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        dv[db] = M::mma(tr_frag<frag>(sD, lo, qs, db), pf[qs], dv[db]);
+        dk[db] = M::mma(tr_frag<frag>(sQ, lo, qs, db), sf[qs], dk[db]);
+      }
+    sched_reads_ahead<32, 2, 3, 1>();
+
+    if (qtn < nqt) store_tile(sQn, sLn);
+    wait_vmem_and_sync();
+    qt = qtn;
+  };
+  while (qt < nqt) {
+    body(std::integral_constant<int, 0>{});
+    if (qt >= nqt) break;
+    body(std::integral_constant<int, 1>{});
+  }
+
+  if (j < S) {
+    char* vrow = (char*)p.dv + ((int64_t)b * p.dv_sb + (int64_t)hd * p.dv_sh + (int64_t)j * p.dv_ss) * 2;
+    char* krow = (char*)p.dk + ((int64_t)b * p.dk_sb + (int64_t)hd * p.dk_sh + (int64_t)j * p.dk_ss) * 2;
+    const float* trow = tab + (int64_t)j * D;
+    typedef T v4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int d0 = 16 * db + 4 * g;
+      v4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = from_f<T>(dv[db][i]);
+      *(v4*)(vrow + d0 * 2) = w;
+      const float4 cs = *(const float4*)(trow + d0);
+      const float sc = p.shp.scale;
+      const float2 a = rot_pair_t(dk[db][0] * sc, dk[db][1] * sc, cs.x, cs.y);
+      const float2 e = rot_pair_t(dk[db][2] * sc, dk[db][3] * sc, cs.z, cs.w);
+      w[0] = from_f<T>(a.x);
+      w[1] = from_f<T>(a.y);
+      w[2] = from_f<T>(e.x);
+      w[3] = from_f<T>(e.y);
+      *(v4*)(krow + d0 * 2) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <typename T, int MASK, bool CAUSAL>
+static int launch_bwd16_t(const BwdParams& p, void* stream) {
+  const int S = p.shp.S, BH = p.shp.B * p.shp.H;
+  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL>), dim3(((S + 127) / 128) * BH), dim3(512), 0,
+                     (hipStream_t)stream, p);
+  int e = (int)hipGetLastError();
+  if (e) return e;
+  hipLaunchKernelGGL((dq16_kernel<T, MASK, CAUSAL>), dim3(((S + 127) / 128) * BH), dim3(512), 0,
+                     (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+
+template <typename T>
+static int launch_bwd16_dt(int mask_kind, bool causal, const BwdParams& p, void* stream) {
+  if (causal) return launch_bwd16_t<T, MASK_NONE, true>(p, stream);
+  switch (mask_kind) {
+    case MASK_BOOL: return launch_bwd16_t<T, MASK_BOOL, false>(p, stream);
+    case MASK_ADD: return launch_bwd16_t<T, MASK_ADD, false>(p, stream);
+    default: return launch_bwd16_t<T, MASK_NONE, false>(p, stream);
+  }
+}
+
+// dK/dV and dQ for 16-bit inputs at D = 128 (after the delta pre-pass).
+int launch_bwd16(int dtype, int mask_kind, bool causal, const BwdParams& p, void* stream) {
+  return dtype == F16 ? launch_bwd16_dt<_Float16>(mask_kind, causal, p, stream)
+                      : launch_bwd16_dt<__bf16>(mask_kind, causal, p, stream);
+}
+
+}  // namespace rs
