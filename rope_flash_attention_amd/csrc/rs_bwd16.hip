@@ -47,7 +47,13 @@ struct M16<_Float16> {
 };
 
 // Swizzle of 256-byte LDS rows: logical 16-byte chunk ch of row r sits at ch ^ msk16(r).
-__device__ inline int msk16(int row) { return ((row & 3) << 2) | ((row >> 2) & 2) | ((row >> 4) & 1); }
+// Row bits 0-1 go to mask bits 1-2, bit 3 to mask bit 0, bit 3 xor bit 4 to mask bit 3:
+// the row reads (rows r0 + {0..3, 8..11, 16..19, 24..27}) and the transposed reads (four
+// consecutive rows, two 16-lane groups eight rows apart) then hit distinct banks whether a
+// pass serves 128 or 256 bytes.
+__device__ inline int msk16(int row) {
+  return ((row & 3) << 1) | ((row >> 3) & 1) | ((((row >> 3) ^ (row >> 4)) & 1) << 3);
+}
 __device__ inline int lds_off(int row, int byte) { return row * 256 + (((byte >> 4) ^ msk16(row)) << 4) + (byte & 15); }
 
 // Row of a 64-row tile that lane row rho of 16-row block kb reads.  With this order the
