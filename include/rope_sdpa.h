@@ -88,7 +88,8 @@ typedef struct {
   const rs_tensor* sin;
   /* Optional mask, sizes [Bm, Hm, Sqm, Skm] with each dimension 1 (broadcast) or full
    * (B, H, S, S).  RS_MASK_BOOL: dtype RS_BOOL (one byte, nonzero = attend).
-   * RS_MASK_ADDITIVE: dtype RS_F32 or the dtype of q.  Must be NULL for RS_MASK_NONE. */
+   * RS_MASK_ADDITIVE: dtype RS_F32 or the dtype of q.  Must be NULL for RS_MASK_NONE.
+   * With RS_MASK_BOOL, S <= 262144 (else RS_ERR_SHAPE). */
   const rs_tensor* mask;
   int32_t mask_kind;     /* rs_mask_kind */
   uint32_t flags;        /* RS_FLAG_* */

@@ -27,6 +27,7 @@ namespace rs {
 namespace {
 
 constexpr float kL2e = 1.4426950408889634f;
+constexpr int kMaxStateTiles16 = kMaxBoolMaskSeq / 64;  // 64-row tiles of a bool-masked call
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -242,12 +243,21 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
   const int nkt = (S + BN - 1) / BN;
   int kt_end = nkt;
   if (CAUSAL) kt_end = min(nkt, (min(q0 + BM, S) - 1) / BN + 1);
+  auto tile_state_mem = [&](int kt) -> uint32_t {
+    const int bm = p.mask.t_sb ? b : 0, hm = p.mask.t_sh ? hd : 0;
+    uint32_t st = mask_tile_state(p.mask, bm, hm, 2 * qt, kt);
+    if (2 * qt + 1 < (S + kMaskTile - 1) / kMaskTile) st |= mask_tile_state(p.mask, bm, hm, 2 * qt + 1, kt);
+    return st;
+  };
+  // tile states gathered once into LDS (see the forward kernel)
+  __shared__ uint8_t s_tstate[MASK == MASK_BOOL ? kMaxStateTiles16 : 1];
+  if constexpr (MASK == MASK_BOOL) {
+    for (int i = tid; i < kt_end; i += 512) s_tstate[i] = (uint8_t)tile_state_mem(i);
+    __syncthreads();
+  }
   auto tile_state = [&](int kt) -> uint32_t {
     if constexpr (MASK == MASK_BOOL) {
-      const int bm = p.mask.t_sb ? b : 0, hm = p.mask.t_sh ? hd : 0;
-      uint32_t st = mask_tile_state(p.mask, bm, hm, 2 * qt, kt);
-      if (2 * qt + 1 < (S + kMaskTile - 1) / kMaskTile) st |= mask_tile_state(p.mask, bm, hm, 2 * qt + 1, kt);
-      return st;
+      return (uint32_t)s_tstate[kt];
     } else {
       return TILE_MIXED;
     }
@@ -430,13 +440,21 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
 
   const int nqt = (S + BMQ - 1) / BMQ;
   const int qt_begin = CAUSAL ? k0 / BMQ : 0;
+  auto tile_state_mem = [&](int qt) -> uint32_t {
+    const int bm = p.mask.t_sb ? b : 0, hm = p.mask.t_sh ? hd : 0;
+    const int nk64 = (S + kMaskTile - 1) / kMaskTile;
+    uint32_t st = mask_tile_state(p.mask, bm, hm, qt, 2 * kt);
+    if (2 * kt + 1 < nk64) st |= mask_tile_state(p.mask, bm, hm, qt, 2 * kt + 1);
+    return st;
+  };
+  __shared__ uint8_t s_tstate[MASK == MASK_BOOL ? kMaxStateTiles16 : 1];
+  if constexpr (MASK == MASK_BOOL) {
+    for (int i = tid; i < nqt; i += 512) s_tstate[i] = (uint8_t)tile_state_mem(i);
+    __syncthreads();
+  }
   auto tile_state = [&](int qt) -> uint32_t {
     if constexpr (MASK == MASK_BOOL) {
-      const int bm = p.mask.t_sb ? b : 0, hm = p.mask.t_sh ? hd : 0;
-      const int nk64 = (S + kMaskTile - 1) / kMaskTile;
-      uint32_t st = mask_tile_state(p.mask, bm, hm, qt, 2 * kt);
-      if (2 * kt + 1 < nk64) st |= mask_tile_state(p.mask, bm, hm, qt, 2 * kt + 1);
-      return st;
+      return (uint32_t)s_tstate[qt];
     } else {
       return TILE_MIXED;
     }

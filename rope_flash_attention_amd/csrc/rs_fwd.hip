@@ -73,6 +73,7 @@ __device__ inline float2 rot_pair_fma(float x0, float x1, float c, float s) {
   return r;
 }
 
+constexpr int kMaxStateTiles = kMaxBoolMaskSeq / 32;  // key tiles (32 keys or more) of a bool-masked call
 constexpr int QK_AHEAD = 8;  // K' fragment reads kept in flight ahead of the QK^T products
 constexpr int PV_AHEAD = 3;  // V^T fragments (two reads each) in flight ahead of the P.V products
 
@@ -186,17 +187,28 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   }
   // bool masks: per-tile states over 64x64 blocks; this workgroup covers BM/64 of them
   // along the queries.
+  auto tile_state_mem = [&](int kt) -> uint32_t {
+    const int kt64 = (kt * BN) / kMaskTile;
+    const int bm = p.mask.t_sb ? b : 0, hm = p.mask.t_sh ? hd : 0;
+    const int nq64 = (S + kMaskTile - 1) / kMaskTile;
+    uint32_t st = 0;
+    for (int u = 0; u < BM / kMaskTile; ++u) {
+      const int q64 = (q0 / kMaskTile) + u;
+      if (q64 < nq64) st |= mask_tile_state(p.mask, bm, hm, q64, kt64);
+    }
+    return st;
+  };
+  // the workgroup's combined tile states, gathered once into LDS (scalar loads in the loop
+  // would make every wait for them also wait for all outstanding LDS reads)
+  // (the host limits bool-masked sequences to kMaxStateTiles key tiles)
+  __shared__ uint8_t s_tstate[MASK == MASK_BOOL ? kMaxStateTiles : 1];
+  if constexpr (MASK == MASK_BOOL) {
+    for (int i = tid; i < kt_end; i += NT) s_tstate[i] = (uint8_t)tile_state_mem(i);
+    __syncthreads();
+  }
   auto tile_state = [&](int kt) -> uint32_t {
     if constexpr (MASK == MASK_BOOL) {
-      const int kt64 = (kt * BN) / kMaskTile;
-      const int bm = p.mask.t_sb ? b : 0, hm = p.mask.t_sh ? hd : 0;
-      const int nq64 = (S + kMaskTile - 1) / kMaskTile;
-      uint32_t st = 0;
-      for (int u = 0; u < BM / kMaskTile; ++u) {
-        const int q64 = (q0 / kMaskTile) + u;
-        if (q64 < nq64) st |= mask_tile_state(p.mask, bm, hm, q64, kt64);
-      }
-      return st;
+      return (uint32_t)s_tstate[kt];
     } else {
       return TILE_MIXED;
     }

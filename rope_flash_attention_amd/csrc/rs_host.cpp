@@ -154,6 +154,7 @@ rs_status validate_args(const rs_args* a, Shape* out) {
     if (a->mask_kind != RS_MASK_NONE || causal) return RS_ERR_UNSUPPORTED;
   }
   if (a->mask_kind == RS_MASK_BOOL) {
+    if (s.S > kMaxBoolMaskSeq) return RS_ERR_SHAPE;
     // grid limits of the tile classifier (y: query tiles, z: mask batch x heads)
     if ((s.mQ + kMaskTile - 1) / kMaskTile > 65535 || s.mB * s.mH > 65535) return RS_ERR_SHAPE;
   }

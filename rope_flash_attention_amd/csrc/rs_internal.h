@@ -13,6 +13,9 @@ enum MaskKind : int { MASK_NONE = 0, MASK_BOOL = 1, MASK_ADD = 2 };
 // bit1 = some key excluded.  OR-ing states combines blocks.
 enum : uint8_t { TILE_ALL_TRUE = 1, TILE_ALL_FALSE = 2, TILE_MIXED = 3 };
 constexpr int kMaskTile = 64;
+// Longest sequence accepted with a bool mask: the kernels keep the mask's tile states of a
+// whole key (or query) range in LDS.
+constexpr int kMaxBoolMaskSeq = 262144;
 
 // A [B, H, S, D] operand: base pointer and element strides of dims 0..2 (dim 3 is contiguous).
 struct Opnd {
