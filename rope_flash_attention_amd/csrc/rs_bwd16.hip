@@ -174,11 +174,13 @@ struct RotStager {
 // Direct-to-LDS loads of a 64-row tile of a [*, 128] 16-bit operand (rows past the end of
 // the slice read as zero): each wave issues two 1 KB loads.
 struct DmaTile {
-  __amdgpu_buffer_rsrc_t rsrc;
+  const void* base;
+  int64_t total;  // bytes of the (b, h) slice
   uint32_t voff[2];
   uint32_t row_bytes;
-  __device__ void init(const void* base, int64_t ss, int S, int wave, int lane) {
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(((int64_t)(S - 1) * ss + 128) * 2), 0x00020000);
+  __device__ void init(const void* base_, int64_t ss, int S, int wave, int lane) {
+    base = base_;
+    total = ((int64_t)(S - 1) * ss + 128) * 2;
     row_bytes = (uint32_t)(ss * 2);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -188,9 +190,9 @@ struct DmaTile {
     }
   }
   __device__ void issue(char* tile, int row0, int wave) {
-    const uint32_t soff = (uint32_t)row0 * row_bytes;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(base, (int64_t)row0 * row_bytes, total);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) buffer_load_lds16(rsrc, tile + (wave * 2 + i) * 1024, voff[i], soff);
+    for (int i = 0; i < 2; ++i) buffer_load_lds16(rs, tile + (wave * 2 + i) * 1024, voff[i], 0);
   }
 };
 

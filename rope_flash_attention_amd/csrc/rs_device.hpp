@@ -92,6 +92,16 @@ __device__ inline void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, char* lds, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
+// Buffer descriptor for one tile of a buffer-loaded operand: base = the tile's first byte,
+// range = the bytes of the operand that remain from there.  The per-lane offset then
+// covers the whole distance from the base, so every read of the tile is range-checked and
+// bytes at or past the operand's end read as zero (the scalar offset stays 0).
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int64_t tile_off, int64_t total) {
+  const int64_t rem = total - tile_off;
+  const int n = rem <= 0 ? 0 : (rem >= 0x7fffffff ? 0x7fffffff : (int)rem);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)base + tile_off), (short)0, n, 0x00020000);
+}
+
 // Waits for this wave's outstanding memory loads (including loads that write LDS directly)
 // and then for every wave of the workgroup.
 __device__ inline void wait_vmem_and_sync() {

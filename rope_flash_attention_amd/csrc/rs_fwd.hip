@@ -115,6 +115,12 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) char sk1[KBYTES];
   __shared__ __attribute__((aligned(16))) char sv0[VBYTES];
   __shared__ __attribute__((aligned(16))) char sv1[VBYTES];
+  // additive masks in the input's 16-bit dtype: the [BM x BN] mask tile goes straight into
+  // LDS with the K/V tile (rows of BN * 2 bytes, 16-byte chunks swizzled per row)
+  constexpr bool kMaskTileLds = MASK == MASK_ADD && ES == 2;
+  constexpr int MROW = BN * 2, MBYTES = kMaskTileLds ? BM * MROW : 16;
+  __shared__ __attribute__((aligned(16))) char sm0[MBYTES];
+  __shared__ __attribute__((aligned(16))) char sm1[MBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hh = lane >> 5;
@@ -233,8 +239,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // destination: lane i of a load writes bytes [16i, 16i+16) of a 1 KB block).  The byte
   // range check of the buffer turns rows at or past S into zeros.  16-byte chunks of row j
   // sit at chunk ^ vsw(j) so that the transposed reads below touch distinct banks.
-  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)vbase, (short)0, (int)(((int64_t)(S - 1) * p.v.ss + D) * ES), 0x00020000);
+  const int64_t vtotal = ((int64_t)(S - 1) * p.v.ss + D) * ES;  // bytes of this (b, h) slice of V
   uint32_t v_voff[VLD];
 #pragma unroll
   for (int i = 0; i < VLD; ++i) {
@@ -242,6 +247,42 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     const int row = byte / VRB, pch = (byte % VRB) / 16;
     v_voff[i] = (uint32_t)(row * (int)p.v.ss * ES + ((pch ^ vsw<CPR>(row)) * 16));
   }
+
+  // additive mask tiles (see sm0/sm1): used when the mask is in the input dtype, not
+  // broadcast over queries or keys, and one (b, h) slice is addressable by a buffer
+  // descriptor; otherwise the mask is read from memory where it is applied
+  bool mask_lds = false;
+  const void* mbase = nullptr;
+  int64_t mspan = 0;
+  uint32_t m_voff[kMaskTileLds ? BM * MROW / 1024 / NW : 1] = {};
+  auto msw = [](int row) { return (row & 7) ^ ((row >> 3) & 1); };
+  if constexpr (kMaskTileLds) {
+    mspan = ((int64_t)(S - 1) * p.mask.sq + S) * 2;
+    // (S % 8 == 0: every 16-byte chunk of a valid key run lies inside the mask's last row)
+    mask_lds = p.mask.dtype != F32 && !p.mask.key_bcast && p.mask.sq != 0 && S % 8 == 0 &&
+               p.mask.sq * 2 * BM < ((int64_t)1 << 31);
+    if (mask_lds) {
+      const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
+      mbase = mask_row_ptr(p.mask, bm, hm, 0, 2);
+      constexpr int ML = BM * MROW / 1024 / NW;
+#pragma unroll
+      for (int i = 0; i < ML; ++i) {
+        const int byte = (wave * ML + i) * 1024 + lane * 16;
+        const int row = byte / MROW, pch = (byte % MROW) / 16;
+        m_voff[i] = (uint32_t)(row * (int)p.mask.sq * 2 + ((pch ^ msw(row)) << 4));
+      }
+    }
+  }
+  auto dma_mask = [&](int kt, char* sM) {
+    if constexpr (kMaskTileLds) {
+      if (mask_lds) {
+        constexpr int ML = BM * MROW / 1024 / NW;
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(mbase, ((int64_t)q0 * p.mask.sq + (int64_t)kt * BN) * 2, mspan);
+#pragma unroll
+        for (int i = 0; i < ML; ++i) buffer_load_lds16(rs, sM + (wave * ML + i) * 1024, m_voff[i], 0);
+      }
+    }
+  };
 
   // K (and its table rows) of tile kt into registers
   auto load_k = [&](int kt) {
@@ -275,18 +316,16 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   };
   // this wave's share of V of tile kt straight into the LDS buffer sV
   auto dma_v = [&](int kt, char* sV) {
-    const uint32_t soff = (uint32_t)((int64_t)kt * BN * p.v.ss * ES);
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vbase, (int64_t)kt * BN * p.v.ss * ES, vtotal);
 #pragma unroll
-    for (int i = 0; i < VLD; ++i)
-      buffer_load_lds16(vrsrc, sV + (wave * VLD + i) * 1024, v_voff[i], soff);
+    for (int i = 0; i < VLD; ++i) buffer_load_lds16(rs, sV + (wave * VLD + i) * 1024, v_voff[i], 0);
   };
 
   // int8 variant: K' code tile straight into LDS.  LDS row j holds key perm_row(j) (the
   // row order the score fragments need, as for the rotated K' tiles), its 16-byte chunk c
   // at c ^ k8sw(j); code rows past the padded sequence read as zero.
   auto k8sw = [](int row) { return (row / K8RPB) & (K8CH - 1); };
-  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(QI8 ? p.kc + (int64_t)slice * p.sp * D : nullptr), (short)0, QI8 ? p.sp * D : 0, 0x00020000);
+  const int8_t* kcodes = QI8 ? p.kc + (int64_t)slice * p.sp * D : nullptr;  // this (b, h) slice
   uint32_t k8_voff = 0;
   if constexpr (QI8) {
     const int byte = wave * 1024 + lane * 16;  // this wave's 1 KB share of a code tile
@@ -295,7 +334,8 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   }
   auto dma_k = [&](int kt, char* sK) {
     if constexpr (QI8) {
-      if (wave < K8LD) buffer_load_lds16(krsrc, sK + wave * 1024, k8_voff, (uint32_t)(kt * BN * D));
+      if (wave < K8LD)
+        buffer_load_lds16(tile_rsrc(kcodes, (int64_t)kt * BN * D, (int64_t)p.sp * D), sK + wave * 1024, k8_voff, 0);
     }
   };
 
@@ -392,25 +432,39 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   };
 
   // exclusions of one tile: sequence tail, causal diagonal, masks
-  auto fixup = [&](int kt, f32x16* sacc) {
+  auto fixup = [&](int kt, f32x16* sacc, const char* sM) {
     const int kv0 = kt * BN;
     const bool tail = kv0 + BN > S;
     const bool diag = CAUSAL && (kv0 + BN - 1 > q0);
     uint32_t st = TILE_ALL_TRUE;
     if constexpr (MASK == MASK_BOOL) st = tile_state(kt);
     if constexpr (MASK == MASK_ADD) {
-      const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
-      const int esz = p.mask.dtype == F32 ? 4 : ES;
-      const char* mrow = mask_row_ptr(p.mask, bm, hm, p.mask.sq ? mc : 0, esz);
+      if (kMaskTileLds && mask_lds) {
+        // row 32 wave + r of the tile, keys 32kb + 16c + 8hh .. +7 = logical chunk 4kb + 2c + hh
+        const int rl = 32 * wave + r;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          float mv[8];
-          mask_add8<T>(p.mask, mrow, kv0 + 32 * kb + 16 * c + 8 * hh, S, mv);
+          for (int c = 0; c < 2; ++c) {
+            typedef T v8 __attribute__((ext_vector_type(8)));
+            const v8 mv = *(const v8*)(sM + rl * MROW + (((4 * kb + 2 * c + hh) ^ msw(rl)) << 4));
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(mv[e], kLog2eF, sacc[kb][8 * c + e]);
-        }
+            for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(to_f(mv[e]), kLog2eF, sacc[kb][8 * c + e]);
+          }
+      } else {
+        const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
+        const int esz = p.mask.dtype == F32 ? 4 : ES;
+        const char* mrow = mask_row_ptr(p.mask, bm, hm, p.mask.sq ? mc : 0, esz);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            float mv[8];
+            mask_add8<T>(p.mask, mrow, kv0 + 32 * kb + 16 * c + 8 * hh, S, mv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(mv[e], kLog2eF, sacc[kb][8 * c + e]);
+          }
+      }
     }
     if (tail || diag || (MASK == MASK_BOOL && st != TILE_ALL_TRUE)) {
       const uint8_t* brow = nullptr;
@@ -540,6 +594,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     load_k(kt);
     dma_k(kt, sk0);
     dma_v(kt, sv0);
+    dma_mask(kt, sm0);
     store_tile(sk0);
   }
   wait_vmem_and_sync();
@@ -549,15 +604,18 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     const char* sV = stage ? sv1 : sv0;
     char* sKn = stage ? sk0 : sk1;
     char* sVn = stage ? sv0 : sv1;
+    const char* sM = stage ? sm1 : sm0;
+    char* sMn = stage ? sm0 : sm1;
     const int ktn = next_tile(kt + 1);
     if (ktn < kt_end) {
       load_k(ktn);
       dma_k(ktn, sKn);
       dma_v(ktn, sVn);
+      dma_mask(ktn, sMn);
     }
     f32x16 sacc[NKB];
     qk(sK, sacc, kt);
-    fixup(kt, sacc);
+    fixup(kt, sacc, sM);
     rescale(sacc);
     PT pt;
     probs(sacc, pt);

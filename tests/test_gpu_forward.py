@@ -234,3 +234,20 @@ def test_long_sequence_sampled():
     rows = _sample_rows(w.q.shape[2], 26, 3)
     _compare(w, rows=rows, pairs=[(0, 0), (0, 47)])
 
+
+
+# ---- additive masks in the input dtype, S a multiple of 8 -----------------------------------
+# Such masks go from memory straight into LDS with the K/V tiles.  S = 328: two query tiles
+# of the 16-bit kernel and a ragged last key tile of 8 keys.
+@pytest.mark.parametrize("case", ["full_bf16", "bcast_b_bf16", "padded_rows_bf16", "full_f16"])
+def test_additive_mask_tile_path(case):
+    dtype = "f16" if case == "full_f16" else "bf16"
+    B, H, S = 2, 3, 328
+    shape = (1, H, S, S) if case == "bcast_b_bf16" else (B, H, S, S)
+    w = syn.random_small(B, H, S, 128, dtype=dtype, seed=120, mask_kind="additive", mask_shape=shape)
+    if case == "padded_rows_bf16":
+        # rows 16 elements longer than S: the mask is a view with row stride S + 16
+        wide = torch.zeros((*w.mask.shape[:3], S + 16), dtype=w.mask.dtype)
+        wide[..., :S] = w.mask
+        w.mask = wide[..., :S]
+    _compare(w)
