@@ -30,6 +30,10 @@
  *    error nothing is launched, outputs are untouched and a negative rs_status is returned.
  *    Faults during execution surface at the caller's next synchronisation, as in HIP.
  *  - Thread safety: all entry points are re-entrant; there is no global mode.
+ *  - Empty inputs: B, H or S may be 0.  Such a call checks dtypes, sizes, flags and the
+ *    mask kind as any other; since no element is addressed, data pointers may be NULL and
+ *    strides and alignment are not checked.  It returns RS_OK without launching anything or
+ *    touching the workspace (which may be NULL; its size is then 0).
  */
 #ifndef ROPE_SDPA_H
 #define ROPE_SDPA_H
@@ -96,8 +100,9 @@ typedef struct {
   float scale;           /* softmax scale; 0 means 1/sqrt(D); otherwise finite and > 0 */
 } rs_args;
 
-/* Bytes of device workspace a call needs (0 is never returned: the rotation tables are
- * repacked into it).  `backward` = 0 for rope_sdpa_fwd, 1 for rope_sdpa_bwd. */
+/* Bytes of device workspace a call needs (0 only for an empty call, B, H or S = 0; otherwise
+ * the rotation tables are repacked into it).  `backward` = 0 for rope_sdpa_fwd, 1 for
+ * rope_sdpa_bwd. */
 rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* bytes);
 
 /*

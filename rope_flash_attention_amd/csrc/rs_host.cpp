@@ -40,12 +40,13 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Checks a [B,H,S,D]-like operand: pointer, dtype, exact sizes, contiguous last dim,
 // 16-byte base alignment and 16-byte multiples for the strides of non-trivial dims.
-rs_status check_bhsd(const rs_tensor* t, int dtype, const int64_t* size) {
-  if (!t || !t->data) return RS_ERR_NULL;
+rs_status check_bhsd(const rs_tensor* t, int dtype, const int64_t* size, bool empty = false) {
+  if (!t || (!t->data && !empty)) return RS_ERR_NULL;
   if (t->dtype != dtype) return RS_ERR_DTYPE;
   if (t->reserved != 0) return RS_ERR_INVALID;
   for (int i = 0; i < 4; ++i)
     if (t->size[i] != size[i]) return RS_ERR_SHAPE;
+  if (empty) return RS_OK;  // no element is addressed: strides and base are not looked at
   if (t->stride[3] != 1) return RS_ERR_STRIDE;
   const int64_t es = (int64_t)elem_size(dtype);
   for (int i = 0; i < 3; ++i) {
@@ -63,6 +64,7 @@ rs_status check_bhsd(const rs_tensor* t, int dtype, const int64_t* size) {
 
 struct Shape {
   int64_t B, H, S, D;
+  bool empty;  // B, H or S is 0: a valid call with nothing to compute
   int dtype;
   float scale;
   int64_t Bt;
@@ -70,11 +72,13 @@ struct Shape {
 };
 
 rs_status check_table(const rs_tensor* t, const Shape& s, int64_t* bt) {
-  if (!t || !t->data) return RS_ERR_NULL;
+  if (!t || (!t->data && !s.empty)) return RS_ERR_NULL;
   if (t->dtype != RS_F32) return RS_ERR_DTYPE;
   if (t->reserved != 0) return RS_ERR_INVALID;
   if (!(t->size[0] == 1 || t->size[0] == s.B) || t->size[1] != 1 || t->size[2] != s.S || t->size[3] != s.D)
     return RS_ERR_SHAPE;
+  *bt = t->size[0];
+  if (s.empty) return RS_OK;  // not read
   if (t->stride[3] != 1) return RS_ERR_STRIDE;
   if (t->stride[0] < 0 || t->stride[2] < 0) return RS_ERR_STRIDE;
   if (((uintptr_t)t->data) % 4 != 0) return RS_ERR_ALIGN;
@@ -86,7 +90,6 @@ rs_status check_table(const rs_tensor* t, const Shape& s, int64_t* bt) {
 rs_status validate_args(const rs_args* a, Shape* out) {
   if (!a || !a->q || !a->k || !a->v || !a->cos || !a->sin) return RS_ERR_NULL;
   const rs_tensor* q = a->q;
-  if (!q->data) return RS_ERR_NULL;
   const int dt = q->dtype;
   if (dt != RS_F32 && dt != RS_F16 && dt != RS_BF16) return RS_ERR_DTYPE;
   Shape s{};
@@ -95,18 +98,20 @@ rs_status validate_args(const rs_args* a, Shape* out) {
   s.S = q->size[2];
   s.D = q->size[3];
   s.dtype = dt;
-  if (s.B < 1 || s.H < 1 || s.S < 1) return RS_ERR_SHAPE;
+  if (s.B < 0 || s.H < 0 || s.S < 0) return RS_ERR_SHAPE;
+  s.empty = s.B == 0 || s.H == 0 || s.S == 0;
+  if (!q->data && !s.empty) return RS_ERR_NULL;
   if (s.D != 64 && s.D != 128) return RS_ERR_SHAPE;
   if (s.S > (int64_t)1 << 24) return RS_ERR_SHAPE;
   const int64_t nqt = (s.S + 127) / 128;
   if (s.B * s.H * nqt >= ((int64_t)1 << 31) || s.B * s.H * s.S >= ((int64_t)1 << 31)) return RS_ERR_SHAPE;
   const int64_t sz[4] = {s.B, s.H, s.S, s.D};
   rs_status st;
-  if ((st = check_bhsd(q, dt, sz)) != RS_OK) return st;
+  if ((st = check_bhsd(q, dt, sz, s.empty)) != RS_OK) return st;
   // K and V: same dtype as Q (mixed dtypes, e.g. fp32 Q/K with bf16 V, are rejected)
   if (a->k->dtype != dt || a->v->dtype != dt) return RS_ERR_DTYPE;
-  if ((st = check_bhsd(a->k, dt, sz)) != RS_OK) return st;
-  if ((st = check_bhsd(a->v, dt, sz)) != RS_OK) return st;
+  if ((st = check_bhsd(a->k, dt, sz, s.empty)) != RS_OK) return st;
+  if ((st = check_bhsd(a->v, dt, sz, s.empty)) != RS_OK) return st;
   int64_t bt_c = 0, bt_s = 0;
   if ((st = check_table(a->cos, s, &bt_c)) != RS_OK) return st;
   if ((st = check_table(a->sin, s, &bt_s)) != RS_OK) return st;
@@ -122,7 +127,7 @@ rs_status validate_args(const rs_args* a, Shape* out) {
     if (a->mask) return RS_ERR_INVALID;
   } else if (a->mask_kind == RS_MASK_BOOL || a->mask_kind == RS_MASK_ADDITIVE) {
     const rs_tensor* m = a->mask;
-    if (!m || !m->data) return RS_ERR_NULL;
+    if (!m || (!m->data && !s.empty)) return RS_ERR_NULL;
     if (causal) return RS_ERR_INVALID;
     if (m->reserved != 0) return RS_ERR_INVALID;
     if (a->mask_kind == RS_MASK_BOOL) {
@@ -134,14 +139,16 @@ rs_status validate_args(const rs_args* a, Shape* out) {
     for (int i = 0; i < 4; ++i)
       if (m->size[i] != 1 && m->size[i] != full[i]) return RS_ERR_SHAPE;
     const int64_t es = (int64_t)elem_size(m->dtype);
-    if (m->size[3] > 1 && m->stride[3] != 1) return RS_ERR_STRIDE;
-    for (int i = 0; i < 3; ++i) {
-      if (m->size[i] <= 1) continue;
-      if (m->stride[i] < 0) return RS_ERR_STRIDE;
-      if (m->size[3] > 1 && (m->stride[i] * es) % 16 != 0) return RS_ERR_STRIDE;
+    if (!s.empty) {  // an empty call reads no mask element
+      if (m->size[3] > 1 && m->stride[3] != 1) return RS_ERR_STRIDE;
+      for (int i = 0; i < 3; ++i) {
+        if (m->size[i] <= 1) continue;
+        if (m->stride[i] < 0) return RS_ERR_STRIDE;
+        if (m->size[3] > 1 && (m->stride[i] * es) % 16 != 0) return RS_ERR_STRIDE;
+      }
+      if (m->size[3] > 1 && ((uintptr_t)m->data) % 16 != 0) return RS_ERR_ALIGN;
+      if (((uintptr_t)m->data) % es != 0) return RS_ERR_ALIGN;
     }
-    if (m->size[3] > 1 && ((uintptr_t)m->data) % 16 != 0) return RS_ERR_ALIGN;
-    if (((uintptr_t)m->data) % es != 0) return RS_ERR_ALIGN;
     s.mB = m->size[0];
     s.mH = m->size[1];
     s.mQ = m->size[2];
@@ -347,7 +354,7 @@ rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* by
   Shape s;
   rs_status st = validate_args(args, &s);
   if (st != RS_OK) return fail(st);
-  *bytes = layout(s, args->mask_kind, backward != 0, (args->flags & RS_FLAG_QUANT_INT8_QK) != 0).total;
+  *bytes = s.empty ? 0 : layout(s, args->mask_kind, backward != 0, (args->flags & RS_FLAG_QUANT_INT8_QK) != 0).total;
   return RS_OK;
 }
 
@@ -359,8 +366,9 @@ rs_status rope_sdpa_fwd(const rs_args* a, const rs_tensor* o, float* lse, void* 
   const int64_t sz[4] = {s.B, s.H, s.S, s.D};
   if (!o) return fail(RS_ERR_NULL);
   if (o->data && o->dtype != s.dtype) return fail(RS_ERR_DTYPE);
-  if ((st = check_bhsd(o, s.dtype, sz)) != RS_OK) return fail(st);
+  if ((st = check_bhsd(o, s.dtype, sz, s.empty)) != RS_OK) return fail(st);
   if (lse && ((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
+  if (s.empty) return RS_OK;  // nothing to compute: no workspace or device needed
   const bool int8 = (a->flags & RS_FLAG_QUANT_INT8_QK) != 0;
   const Layout L = layout(s, a->mask_kind, false, int8);
   if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
@@ -413,6 +421,7 @@ rs_status rope_sdpa_debug_quantize_qk(const rs_args* a, int8_t* q_codes, int8_t*
   rs_status st = validate_args(a, &s);
   if (st != RS_OK) return fail(st);
   if (!(a->flags & RS_FLAG_QUANT_INT8_QK)) return fail(RS_ERR_INVALID);
+  if (s.empty) return RS_OK;
   if (!q_codes || !k_codes || !q_scales || !k_scales) return fail(RS_ERR_NULL);
   if (((uintptr_t)q_codes) % 8 != 0 || ((uintptr_t)k_codes) % 8 != 0) return fail(RS_ERR_ALIGN);
   if (((uintptr_t)q_scales) % 4 != 0 || ((uintptr_t)k_scales) % 4 != 0) return fail(RS_ERR_ALIGN);
@@ -435,13 +444,14 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   if (st != RS_OK) return fail(st);
   if (a->flags & RS_FLAG_QUANT_INT8_QK) return fail(RS_ERR_UNSUPPORTED);
   const int64_t sz[4] = {s.B, s.H, s.S, s.D};
-  if (!o || !dout || !dq || !dk || !dv || !lse) return fail(RS_ERR_NULL);
+  if (!o || !dout || !dq || !dk || !dv || (!lse && !s.empty)) return fail(RS_ERR_NULL);
   const rs_tensor* ts[5] = {o, dout, dq, dk, dv};
   for (const rs_tensor* t : ts) {
     if (t->data && t->dtype != s.dtype) return fail(RS_ERR_DTYPE);
-    if ((st = check_bhsd(t, s.dtype, sz)) != RS_OK) return fail(st);
+    if ((st = check_bhsd(t, s.dtype, sz, s.empty)) != RS_OK) return fail(st);
   }
   if (((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
+  if (s.empty) return RS_OK;
   const Layout L = layout(s, a->mask_kind, true, false);
   if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
   if ((st = current_device_ok()) != RS_OK) return fail(st);

@@ -257,3 +257,44 @@ def test_backward_validation_and_error_counter():
     s = RsStats()
     L.rope_sdpa_get_stats(ctypes.byref(s))
     assert s.errors == 4 and s.bwd_calls == 0 and s.fwd_instream == 0
+
+
+@pytest.mark.parametrize("dims", [dict(B=0), dict(H=0), dict(S=0)])
+def test_empty_calls_are_valid_no_ops(dims):
+    """B, H or S = 0: validated like any call, NULL data accepted, RS_OK with no device."""
+    L = lib()
+    c = Call(**dims)
+    for t in (c.q, c.k, c.v, c.o, c.cos, c.sin):
+        t.data = None
+    c.lse, c.ws, c.ws_bytes = None, None, 0
+    c.q.stride[3] = 0  # an empty tensor's strides are not looked at (torch may hand any)
+    _bool_mask(c, (1, 1, 1, c.S), (0, 0, 0, 3))
+    c.mask.data = None
+    assert c.ws_size(0) == (0, 0) and c.ws_size(1) == (0, 0)
+    assert c.fwd() == 0
+    a = c.args()
+    shape = (c.B, c.H, c.S, c.D)
+    t = lambda: make_tensor(None, RS_BF16, shape, (c.H * c.S * c.D, c.S * c.D, c.D, 1))
+    do, dq, dk, dv = t(), t(), t(), t()
+    st = L.rope_sdpa_bwd(ctypes.byref(a), ctypes.byref(c.o), None, ctypes.byref(do), ctypes.byref(dq),
+                         ctypes.byref(dk), ctypes.byref(dv), None, 0, None)
+    assert st == 0
+    c.mask, c.kind = None, RS_MASK_NONE
+    c.flags = RS_FLAG_QUANT_INT8_QK
+    assert c.fwd() == 0
+    a = c.args()
+    assert L.rope_sdpa_debug_quantize_qk(ctypes.byref(a), None, None, None, None, None, 0, None) == 0
+    # still validated: a wrong dtype or size is an error even with nothing to compute
+    c.flags = 0
+    c.v.dtype = RS_F16
+    assert c.fwd() == ERR["RS_ERR_DTYPE"]
+    c.v.dtype = RS_BF16
+    c.k.size[3] = 64
+    assert c.fwd() == ERR["RS_ERR_SHAPE"]
+
+
+def test_negative_sizes_are_rejected():
+    c = Call()
+    for t in (c.q, c.k, c.v, c.o):
+        t.size[2] = -1
+    assert c.fwd() == ERR["RS_ERR_SHAPE"]

@@ -113,3 +113,21 @@ def test_causal_training_full_size_two_heads():
     """B=4, H=16, S=2048, D=128, bf16, 1-axis RoPE theta=10000, causal."""
     w = syn.causal_1axis(batch=4, heads=16, seq=2048, dim=128, dtype="bf16", seed=4200)
     _compare(w, pairs=[(0, 0), (3, 15)])
+
+
+@pytest.mark.parametrize("shape", [(0, 2, 16, 64), (1, 0, 16, 128), (2, 3, 0, 128)])
+def test_empty_inputs_forward_and_backward(shape):
+    """B, H or S = 0: the calls succeed and return empty results of the right shapes."""
+    d = dev()
+    B, H, S, D = shape
+    q, k, v = (torch.randn(shape, dtype=torch.bfloat16, device=d, requires_grad=True) for _ in range(3))
+    cos = torch.ones(S, D, device=d)
+    sin = torch.zeros(S, D, device=d)
+    o = rfa.rope_scaled_dot_product_attention(q, k, v, cos, sin)
+    assert o.shape == shape and o.dtype == torch.bfloat16
+    o.float().sum().backward()
+    assert q.grad.shape == shape and k.grad.shape == shape and v.grad.shape == shape
+    with torch.no_grad():
+        o2, lse = rfa.rope_sdpa_fwd_with_lse(q, k, v, cos, sin, quantization="int8")
+    torch.cuda.synchronize()
+    assert o2.shape == shape and lse.shape == shape[:3]
