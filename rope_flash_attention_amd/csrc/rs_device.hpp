@@ -96,10 +96,16 @@ __device__ inline void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, char* lds, u
 // range = the bytes of the operand that remain from there.  The per-lane offset then
 // covers the whole distance from the base, so every read of the tile is range-checked and
 // bytes at or past the operand's end read as zero (the scalar offset stays 0).
+// Callers pass workgroup-uniform values only; they are read from the first lane so that the
+// descriptor stays in scalar registers even where the compiler cannot prove uniformity
+// (it would otherwise loop over the distinct descriptors of the lanes on every load).
 __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int64_t tile_off, int64_t total) {
   const int64_t rem = total - tile_off;
-  const int n = rem <= 0 ? 0 : (rem >= 0x7fffffff ? 0x7fffffff : (int)rem);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)base + tile_off), (short)0, n, 0x00020000);
+  const int n = __builtin_amdgcn_readfirstlane(rem <= 0 ? 0 : (rem >= 0x7fffffff ? 0x7fffffff : (int)rem));
+  const uint64_t a = (uint64_t)((const char*)base + tile_off);
+  const uint64_t au = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)au, (short)0, n, 0x00020000);
 }
 
 // Waits for this wave's outstanding memory loads (including loads that write LDS directly)
@@ -108,15 +114,6 @@ __device__ inline void wait_vmem_and_sync() {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt(7), lgkmcnt(15)
   __syncthreads();
 }
-// Same, but the N most recently issued loads may still be in flight (loads complete in
-// issue order for the counter).
-template <int N>
-__device__ inline void wait_vmem_but_and_sync() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
-  __syncthreads();
-}
-
 // Instruction schedule for a chain of N matrix products fed from LDS, each product
 // consuming RPM LDS reads: AHEAD products' worth of reads are issued first, then each
 // product is followed by the reads of the product AHEAD places later.  Without it the
@@ -133,6 +130,39 @@ __device__ inline void sched_reads_ahead() {
     __builtin_amdgcn_sched_group_barrier(0x100, RPM, SYNC);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, SYNC);
+}
+
+// Instruction schedule interleaving a chain of N matrix products fed from LDS (RPM reads
+// each; AHEAD products' reads are issued first) with up to VPM vector-ALU instructions after
+// each product, so that the wave's own vector work runs in the shadow of its matrix work.
+// Same placement rules as sched_reads_ahead.
+template <int N, int RPM, int AHEAD, int VPM, int SYNC>
+__device__ inline void sched_mfma_interleave() {
+  static_assert(AHEAD >= 1 && AHEAD <= N, "read-ahead depth");
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * RPM, SYNC);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, SYNC);  // one matrix product
+    if (i < N - AHEAD) __builtin_amdgcn_sched_group_barrier(0x100, RPM, SYNC);
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, SYNC);  // vector ALU
+  }
+}
+
+// As sched_mfma_interleave, with the wave's vector-memory loads spread through the chain:
+// LEAD of them before the first product, then one after every second product.  (All waves
+// issuing a tile's loads at once stall at issue until the load pipeline drains.)
+template <int N, int RPM, int AHEAD, int VPM, int LEAD, int SYNC>
+__device__ inline void sched_mfma_interleave_loads() {
+  static_assert(AHEAD >= 1 && AHEAD <= N, "read-ahead depth");
+  __builtin_amdgcn_sched_group_barrier(0x020, LEAD, SYNC);         // vector-memory loads
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * RPM, SYNC);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, SYNC);  // one matrix product
+    if (i < N - AHEAD) __builtin_amdgcn_sched_group_barrier(0x100, RPM, SYNC);
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, SYNC);  // vector ALU
+    if (i % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, SYNC);
+  }
 }
 
 // Interleaved-pair rotation with each product and sum rounded to fp32 (no fused

@@ -74,7 +74,7 @@ __device__ inline float2 rot_pair_fma(float x0, float x1, float c, float s) {
 }
 
 constexpr int kMaxStateTiles = kMaxBoolMaskSeq / 32;  // key tiles (32 keys or more) of a bool-masked call
-constexpr int QK_AHEAD = 8;  // K' fragment reads kept in flight ahead of the QK^T products
+constexpr int QK_AHEAD = 4;  // K' fragment reads kept in flight ahead of the QK^T products
 constexpr int PV_AHEAD = 3;  // V^T fragments (two reads each) in flight ahead of the P.V products
 
 // QI8: blockwise int8 variant.  Q' and K' arrive as int8 codes with one fp32 scale per
@@ -117,7 +117,17 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) char sv1[VBYTES];
   // additive masks in the input's 16-bit dtype: the [BM x BN] mask tile goes straight into
   // LDS with the K/V tile (rows of BN * 2 bytes, 16-byte chunks swizzled per row)
-  constexpr bool kMaskTileLds = MASK == MASK_ADD && ES == 2;
+  // MASK_ADD_TILE: an additive mask whose [BM x BN] tiles go straight into LDS with the K/V
+  // tiles (the launcher picks it when the mask is in the input's 16-bit dtype, broadcast over
+  // neither queries nor keys, S % 8 == 0 and a slice fits a buffer descriptor); MASK_ADD reads
+  // the mask from memory where it is applied.  Separate instantiations keep the registers of
+  // one path out of the other.
+  constexpr bool kMaskTileLds = MASK == MASK_ADD_TILE;
+  // additive masks: the running max is subtracted where the mask is added (one more vector
+  // operation per score) instead of entering through the accumulator, which frees the 16
+  // registers of that accumulator image
+  constexpr bool kAddMask = MASK == MASK_ADD || MASK == MASK_ADD_TILE;
+  static_assert(!kMaskTileLds || ES == 2, "mask tiles in LDS: 16-bit inputs");
   constexpr int MROW = BN * 2, MBYTES = kMaskTileLds ? BM * MROW : 16;
   __shared__ __attribute__((aligned(16))) char sm0[MBYTES];
   __shared__ __attribute__((aligned(16))) char sm1[MBYTES];
@@ -193,7 +203,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   }
   // bool masks: per-tile states over 64x64 blocks; this workgroup covers BM/64 of them
   // along the queries.
-  auto tile_state_mem = [&](int kt) -> uint32_t {
+  auto tile_state_mem = [&](int kt) __attribute__((always_inline)) -> uint32_t {
     const int kt64 = (kt * BN) / kMaskTile;
     const int bm = p.mask.t_sb ? b : 0, hm = p.mask.t_sh ? hd : 0;
     const int nq64 = (S + kMaskTile - 1) / kMaskTile;
@@ -212,16 +222,19 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     for (int i = tid; i < kt_end; i += NT) s_tstate[i] = (uint8_t)tile_state_mem(i);
     __syncthreads();
   }
-  auto tile_state = [&](int kt) -> uint32_t {
+  auto tile_state = [&](int kt) __attribute__((always_inline)) -> uint32_t {
     if constexpr (MASK == MASK_BOOL) {
       return (uint32_t)s_tstate[kt];
     } else {
       return TILE_MIXED;
     }
   };
-  auto next_tile = [&](int kt) -> int {
+  // (the states are read from LDS, which the compiler takes for per-lane values: the
+  // result, the same in every lane, is read from the first lane to keep it scalar)
+  auto next_tile = [&](int kt) __attribute__((always_inline)) -> int {
     if constexpr (MASK == MASK_BOOL) {
       while (kt < kt_end && tile_state(kt) == TILE_ALL_FALSE) ++kt;
+      kt = __builtin_amdgcn_readfirstlane(kt);
     }
     return kt;
   };
@@ -248,74 +261,63 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     v_voff[i] = (uint32_t)(row * (int)p.v.ss * ES + ((pch ^ vsw<CPR>(row)) * 16));
   }
 
-  // additive mask tiles (see sm0/sm1): used when the mask is in the input dtype, not
-  // broadcast over queries or keys, and one (b, h) slice is addressable by a buffer
-  // descriptor; otherwise the mask is read from memory where it is applied
-  bool mask_lds = false;
+  // additive mask tiles (see sm0/sm1)
   const void* mbase = nullptr;
   int64_t mspan = 0;
-  uint32_t m_voff[kMaskTileLds ? BM * MROW / 1024 / NW : 1] = {};
-  auto msw = [](int row) { return (row & 7) ^ ((row >> 3) & 1); };
+  auto msw = [](int row) __attribute__((always_inline)) { return (row & 7) ^ ((row >> 3) & 1); };
   if constexpr (kMaskTileLds) {
-    mspan = ((int64_t)(S - 1) * p.mask.sq + S) * 2;
     // (S % 8 == 0: every 16-byte chunk of a valid key run lies inside the mask's last row)
-    mask_lds = p.mask.dtype != F32 && !p.mask.key_bcast && p.mask.sq != 0 && S % 8 == 0 &&
-               p.mask.sq * 2 * BM < ((int64_t)1 << 31);
-    if (mask_lds) {
-      const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
-      mbase = mask_row_ptr(p.mask, bm, hm, 0, 2);
+    mspan = ((int64_t)(S - 1) * p.mask.sq + S) * 2;
+    const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
+    mbase = mask_row_ptr(p.mask, bm, hm, 0, 2);
+  }
+  auto dma_mask = [&](int kt, char* sM) __attribute__((always_inline)) {
+    if constexpr (kMaskTileLds) {
       constexpr int ML = BM * MROW / 1024 / NW;
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(mbase, ((int64_t)q0 * p.mask.sq + (int64_t)kt * BN) * 2, mspan);
+      // per-lane offsets recomputed here (cheap) rather than held in registers throughout
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int i = 0; i < ML; ++i) {
-        const int byte = (wave * ML + i) * 1024 + lane * 16;
+        const int byte = (wave * ML + i) * 1024 + ln * 16;
         const int row = byte / MROW, pch = (byte % MROW) / 16;
-        m_voff[i] = (uint32_t)(row * (int)p.mask.sq * 2 + ((pch ^ msw(row)) << 4));
-      }
-    }
-  }
-  auto dma_mask = [&](int kt, char* sM) {
-    if constexpr (kMaskTileLds) {
-      if (mask_lds) {
-        constexpr int ML = BM * MROW / 1024 / NW;
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(mbase, ((int64_t)q0 * p.mask.sq + (int64_t)kt * BN) * 2, mspan);
-#pragma unroll
-        for (int i = 0; i < ML; ++i) buffer_load_lds16(rs, sM + (wave * ML + i) * 1024, m_voff[i], 0);
+        const uint32_t off = (uint32_t)(row * (int)p.mask.sq * 2 + ((pch ^ msw(row)) << 4));
+        buffer_load_lds16(rs, sM + (wave * ML + i) * 1024, off, 0);
       }
     }
   };
 
-  // K (and its table rows) of tile kt into registers
-  auto load_k = [&](int kt) {
+  // K of tile kt and its table rows into registers, through buffer descriptors: rows at or
+  // past S read as zeros, and every call issues the same loads (so the wait for them can
+  // let later loads stay in flight)
+  const int64_t ktotal = ((int64_t)(S - 1) * p.k.ss + D) * ES;  // bytes of this (b, h) slice of K
+  const int64_t ttotal = (int64_t)S * D * 4;                     // bytes of this sample's table rows
+  auto load_k_rows = [&](int kt) __attribute__((always_inline)) {
     if constexpr (QI8) return;
-    const int kv0 = kt * BN;
-    const T* kt_base = kbase + (int64_t)kv0 * p.k.ss;
-    const float* tt_base = tab + (int64_t)kv0 * D;
-    if (kv0 + BN <= S) {
+    const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kbase, (int64_t)kt * BN * p.k.ss * ES, ktotal);
 #pragma unroll
-      for (int it = 0; it < KCPT; ++it) {
-        kx[it] = *(const uint4*)(kt_base + k_off + it * KROWS_PER_IT * (int)p.k.ss);
-        const float* tr = tt_base + t_off + it * KROWS_PER_IT * D;
-#pragma unroll
-        for (int u = 0; u < EPC / 4; ++u) kt4[it][u] = *(const float4*)(tr + 4 * u);
-      }
-    } else {
-#pragma unroll
-      for (int it = 0; it < KCPT; ++it) {
-        if (kv0 + k_key0 + it * KROWS_PER_IT < S) {
-          kx[it] = *(const uint4*)(kt_base + k_off + it * KROWS_PER_IT * (int)p.k.ss);
-          const float* tr = tt_base + t_off + it * KROWS_PER_IT * D;
-#pragma unroll
-          for (int u = 0; u < EPC / 4; ++u) kt4[it][u] = *(const float4*)(tr + 4 * u);
-        } else {
-          kx[it] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-          for (int u = 0; u < EPC / 4; ++u) kt4[it][u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-    }
+    for (int it = 0; it < KCPT; ++it)
+      kx[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             krs, (uint32_t)((k_off + it * KROWS_PER_IT * (int)p.k.ss) * ES), 0, 0));
   };
+  auto load_k_tab = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (QI8) return;
+    const __amdgpu_buffer_rsrc_t trs = tile_rsrc(tab, (int64_t)kt * BN * D * 4, ttotal);
+#pragma unroll
+    for (int it = 0; it < KCPT; ++it)
+#pragma unroll
+      for (int u = 0; u < EPC / 4; ++u)
+        kt4[it][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    trs, (uint32_t)((t_off + it * KROWS_PER_IT * D + 4 * u) * 4), 0, 0));
+  };
+  auto load_k = [&](int kt) __attribute__((always_inline)) {
+    load_k_rows(kt);
+    load_k_tab(kt);
+  };
+
   // this wave's share of V of tile kt straight into the LDS buffer sV
-  auto dma_v = [&](int kt, char* sV) {
+  auto dma_v = [&](int kt, char* sV) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vbase, (int64_t)kt * BN * p.v.ss * ES, vtotal);
 #pragma unroll
     for (int i = 0; i < VLD; ++i) buffer_load_lds16(rs, sV + (wave * VLD + i) * 1024, v_voff[i], 0);
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // int8 variant: K' code tile straight into LDS.  LDS row j holds key perm_row(j) (the
   // row order the score fragments need, as for the rotated K' tiles), its 16-byte chunk c
   // at c ^ k8sw(j); code rows past the padded sequence read as zero.
-  auto k8sw = [](int row) { return (row / K8RPB) & (K8CH - 1); };
+  auto k8sw = [](int row) __attribute__((always_inline)) { return (row / K8RPB) & (K8CH - 1); };
   const int8_t* kcodes = QI8 ? p.kc + (int64_t)slice * p.sp * D : nullptr;  // this (b, h) slice
   uint32_t k8_voff = 0;
   if constexpr (QI8) {
@@ -332,14 +334,14 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     const int row = byte / D, pch = (byte % D) / 16;
     k8_voff = (uint32_t)(perm_row(row) * D + ((pch ^ k8sw(row)) << 4));
   }
-  auto dma_k = [&](int kt, char* sK) {
+  auto dma_k = [&](int kt, char* sK) __attribute__((always_inline)) {
     if constexpr (QI8) {
       if (wave < K8LD)
         buffer_load_lds16(tile_rsrc(kcodes, (int64_t)kt * BN * D, (int64_t)p.sp * D), sK + wave * 1024, k8_voff, 0);
     }
   };
 
-  auto store_tile = [&](char* sK) {
+  auto store_tile = [&](char* sK) __attribute__((always_inline)) {
     if constexpr (QI8) return;
 #pragma unroll
     for (int it = 0; it < KCPT; ++it) {
@@ -396,11 +398,11 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     v_rd[db] = v_row_l * VRB + ((chunk ^ vsw<CPR>(v_row_l)) * 16) + (v_colb & 15);
   }
 
-  // S^T - m_base = K' Q'^T + C for one tile: rows = keys, columns = this wave's 32 queries
-  auto qk = [&](const char* sK, f32x16* sacc, int kt) {
+  // S^T - m_base = K' Q'^T + C for one tile: rows = keys, columns = this wave's 32 queries.
+  // (int8 variant: exact integer sums into ia; qk_scale turns them into scores.)
+  i32x16 ia[QI8 ? NKB : 1];
+  auto qk = [&](const char* sK, f32x16* sacc) __attribute__((always_inline)) {
     if constexpr (QI8) {
-      // exact integer sums, then s = sum * scale_q * scale_k * scale * log2(e) - m_base
-      const float f = q8scale * p.ksc[(int64_t)slice * (p.sp / 64) + kt];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         i32x4 ka[NQ8];
@@ -408,49 +410,55 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int t = 0; t < NQ8; ++t)
           ka[t] = *(const i32x4*)(sK + row * D + (((2 * t + hh) ^ k8sw(row)) << 4));
-        i32x16 acc;
 #pragma unroll
         for (int t = 0; t < NQ8; ++t)
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[t], qf[t], t == 0 ? izero16() : acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = fmaf((float)acc[i], f, -m_base);
+          ia[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[t], qf[t], t == 0 ? izero16() : ia[kb], 0, 0, 0);
       }
-      sched_reads_ahead<NKB * NQ8, 1, NKB * NQ8, 0>();
     } else {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        // all fragments of the 32-key block are requested before the first product, so the
-        // LDS latency is paid once per block rather than once per k-step
         frag ka[NQK];
 #pragma unroll
         for (int t = 0; t < NQK; ++t) ka[t] = *(const frag*)(sK + k_rd + (32 * kb) * KP + t * KSTEP * ES);
 #pragma unroll
-        for (int t = 0; t < NQK; ++t) sacc[kb] = M::mma(ka[t], qf[t], t == 0 ? negm : sacc[kb]);
+        for (int t = 0; t < NQK; ++t) sacc[kb] = M::mma(ka[t], qf[t], t == 0 ? (kAddMask ? zero16() : negm) : sacc[kb]);
       }
-      if constexpr (KPL == 8) sched_reads_ahead<NKB * NQK, 1, QK_AHEAD, 0>();
+    }
+  };
+  // int8 variant: s = sum * scale_q * scale_k * scale * log2(e) - m_base
+  auto qk_scale = [&](f32x16* sacc, int kt) __attribute__((always_inline)) {
+    if constexpr (QI8) {
+      const float f = q8scale * p.ksc[(int64_t)slice * (p.sp / 64) + kt];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = fmaf((float)ia[kb][i], f, -m_base);
     }
   };
 
   // exclusions of one tile: sequence tail, causal diagonal, masks
-  auto fixup = [&](int kt, f32x16* sacc, const char* sM) {
+  auto fixup = [&](int kt, f32x16* sacc, const char* sM) __attribute__((always_inline)) {
     const int kv0 = kt * BN;
     const bool tail = kv0 + BN > S;
     const bool diag = CAUSAL && (kv0 + BN - 1 > q0);
     uint32_t st = TILE_ALL_TRUE;
     if constexpr (MASK == MASK_BOOL) st = tile_state(kt);
-    if constexpr (MASK == MASK_ADD) {
-      if (kMaskTileLds && mask_lds) {
+    if constexpr (MASK == MASK_ADD || MASK == MASK_ADD_TILE) {
+      if constexpr (kMaskTileLds) {
         // row 32 wave + r of the tile, keys 32kb + 16c + 8hh .. +7 = logical chunk 4kb + 2c + hh
-        const int rl = 32 * wave + r;
+        // (addresses recomputed per tile, not held in registers across the loop)
+        int rl = 32 * wave + r;
+        asm volatile("" : "+v"(rl));
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             typedef T v8 __attribute__((ext_vector_type(8)));
             const v8 mv = *(const v8*)(sM + rl * MROW + (((4 * kb + 2 * c + hh) ^ msw(rl)) << 4));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(to_f(mv[e]), kLog2eF, sacc[kb][8 * c + e]);
+            for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(to_f(mv[e]), kLog2eF, sacc[kb][8 * c + e]) - m_base;
           }
+        }
       } else {
         const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
         const int esz = p.mask.dtype == F32 ? 4 : ES;
@@ -462,7 +470,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
             float mv[8];
             mask_add8<T>(p.mask, mrow, kv0 + 32 * kb + 16 * c + 8 * hh, S, mv);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(mv[e], kLog2eF, sacc[kb][8 * c + e]);
+            for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(mv[e], kLog2eF, sacc[kb][8 * c + e]) - m_base;
           }
       }
     }
@@ -492,40 +500,41 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     }
   };
 
-  // lazy online softmax, part 1: rescale only when some row max grows by more than 2^8
-  // (wave-uniform branch)
-  auto rescale = [&](f32x16* sacc) {
-    float mx = sacc[0][0];
+  // lazy online softmax, part 1: the tile's row max (mx, log2 units relative to m_base) and
+  // whether some row max grows by more than 2^8 (wave-uniform); only then is m rescaled
+  auto check = [&](const f32x16* sacc, float& mx) __attribute__((always_inline)) -> bool {
+    float x = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = (kb == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = xhalf_max(mx);  // max of (s - m_base) over this tile's keys
-    const bool need = mx > (m_run - m_base) + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = fmaxf(m_run, mx + m_base);
-      const bool dead = m_new == -INFINITY;  // no attended key so far
-      const float alpha = dead ? 1.f : fast_exp2(m_run - m_new);
-      const float shift = dead ? 0.f : m_new - m_base;
-      l_run *= alpha;
+      for (int i = (kb == 0 ? 1 : 0); i < 16; ++i) x = fmaxf(x, sacc[kb][i]);
+    x = xhalf_max(x);
+    mx = x;
+    return __builtin_amdgcn_ballot_w64(x > (m_run - m_base) + kRescaleLog2) != 0;
+  };
+  auto rescale = [&](f32x16* sacc, float mx) __attribute__((always_inline)) {
+    const float m_new = fmaxf(m_run, mx + m_base);
+    const bool dead = m_new == -INFINITY;  // no attended key so far
+    const float alpha = dead ? 1.f : fast_exp2(m_run - m_new);
+    const float shift = dead ? 0.f : m_new - m_base;
+    l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] -= shift;
-      m_run = m_new;
-      m_base = dead ? 0.f : m_new;
+      for (int i = 0; i < 16; ++i) sacc[kb][i] -= shift;
+    m_run = m_new;
+    m_base = dead ? 0.f : m_new;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) negm[i] = -m_base;
-    }
+    for (int i = 0; i < 16; ++i) negm[i] = -m_base;
   };
 
   // part 2: P = exp2(S), rounded to T into MFMA fragments for 16-bit types, and row sums
   using PT = typename std::conditional<KPL == 8, frag[NKB][2], f32x16[NKB]>::type;
-  auto probs = [&](f32x16* sacc, PT& pt) {
+  auto probs = [&](f32x16* sacc, PT& pt) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -550,7 +559,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   };
 
   // O^T += V^T P^T
-  auto pv = [&](const char* sV, PT& pt) {
+  auto pv = [&](const char* sV, PT& pt) __attribute__((always_inline)) {
     if constexpr (KPL == 8) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -570,8 +579,6 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
             oacc[db] = M::mma(a, pt[kb][c], oacc[db]);
           }
       }
-      // V^T fragments: PV_AHEAD products' worth of transposed reads in flight
-      sched_reads_ahead<NDB * NKB * 2, 2, PV_AHEAD, 1>();
     } else {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -588,41 +595,105 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     }
   };
 
-  // ---- key-tile loop: double-buffered over K' and V ------------------------------------------
+  // ---- key-tile loop: software pipelined over the visiting order t_0 < t_1 < ... ----------
+  // Iteration i:
+  //   (rare) rescale for S(t_i), as its check decided;
+  //   phase A: S(t_{i+1}) = K'(t_{i+1}) Q'^T on MFMA, interleaved with P(t_i) = exp2(S(t_i))
+  //            and its row sums, and with the loads of K(t_{i+2}) into registers and of
+  //            V(t_{i+1}) and the mask tile of t_{i+2} into LDS;
+  //   phase B: O^T += V(t_i)^T P(t_i)^T on MFMA, interleaved with the rotation of K(t_{i+2})
+  //            into LDS and the max check of S(t_{i+1}) (after its exclusions);
+  //   wait for the loads issued, barrier.
+  // Tile t_j uses buffer j & 1 of each pair (sk, sv, sm): phase A reads K' of t_{i+1} while
+  // phase B writes K' of t_{i+2}; V of t_i is read while V of t_{i+1} arrives; the mask tile
+  // of t_{i+1} is read while that of t_{i+2} arrives.  A wave's matrix and vector work thus
+  // overlap whatever phase the other wave of its SIMD is in.
+  f32x16 sacc[2][NKB];
+  float mx = 0.f;     // row max of the current tile's scores (valid where need was computed)
+  bool need = false;  // the current tile raises some row max by more than 2^8
   int kt = next_tile(0);
+  int kt1 = kt < kt_end ? next_tile(kt + 1) : kt_end;
   if (kt < kt_end) {
     load_k(kt);
     dma_k(kt, sk0);
     dma_v(kt, sv0);
     dma_mask(kt, sm0);
     store_tile(sk0);
+    if (kt1 < kt_end) {
+      load_k(kt1);
+      dma_k(kt1, sk1);
+      dma_mask(kt1, sm1);
+      store_tile(sk1);
+    }
   }
   wait_vmem_and_sync();
-  auto body = [&](auto stage_c) {
-    constexpr int stage = decltype(stage_c)::value;
-    const char* sK = stage ? sk1 : sk0;
-    const char* sV = stage ? sv1 : sv0;
-    char* sKn = stage ? sk0 : sk1;
-    char* sVn = stage ? sv0 : sv1;
-    const char* sM = stage ? sm1 : sm0;
-    char* sMn = stage ? sm0 : sm1;
-    const int ktn = next_tile(kt + 1);
-    if (ktn < kt_end) {
-      load_k(ktn);
-      dma_k(ktn, sKn);
-      dma_v(ktn, sVn);
-      dma_mask(ktn, sMn);
-    }
-    f32x16 sacc[NKB];
-    qk(sK, sacc, kt);
-    fixup(kt, sacc, sM);
-    rescale(sacc);
+  if (kt < kt_end) {
+    qk(sk0, sacc[0]);
+    qk_scale(sacc[0], kt);
+    fixup(kt, sacc[0], sm0);
+    need = check(sacc[0], mx);
+  }
+  __syncthreads();  // sk0 and sm0 are refilled in the first iteration
+  auto body = [&](auto stage_c) __attribute__((always_inline)) {
+    constexpr int st = decltype(stage_c)::value;  // i & 1
+    f32x16* s_cur = sacc[st];
+    f32x16* s_nxt = sacc[st ^ 1];
+    const char* sKr = st ? sk0 : sk1;  // K' of t_{i+1}
+    char* sKw = st ? sk1 : sk0;        // K' of t_{i+2}
+    const char* sVr = st ? sv1 : sv0;  // V of t_i
+    char* sVw = st ? sv0 : sv1;        // V of t_{i+1}
+    const char* sMr = st ? sm0 : sm1;  // mask tile of t_{i+1}
+    char* sMw = st ? sm1 : sm0;        // mask tile of t_{i+2}
+    if (need) rescale(s_cur, mx);
+    const bool has1 = kt1 < kt_end;
+    const int kt2 = has1 ? next_tile(kt1 + 1) : kt_end;
+    // issued whether or not t_{i+1} and t_{i+2} exist (tile kt_end then: in range or read
+    // as zeros, into buffers that are not read again), so the counts of loads in flight are
+    // the same on every path and the wait for K(t_{i+2}) leaves the V loads in flight; the
+    // mask tile (additive masks in LDS) goes first, as it comes from memory rather than L2
+    dma_mask(kt2, sMw);
+    load_k(kt2);
+    dma_v(kt1, sVw);
+    dma_k(kt2, sKw);
+
+    // phase A (one straight block: without t_{i+1} the products run on a stale K' buffer
+    // and their result is ignored)
     PT pt;
-    probs(sacc, pt);
-    pv(sV, pt);
-    if (ktn < kt_end) store_tile(sKn);
+    qk(sKr, s_nxt);
+    probs(s_cur, pt);
+    if constexpr (KPL == 8) {
+      if constexpr (QI8) {
+        sched_mfma_interleave<NKB * NQ8, 1, NKB * NQ8, 8, 0>();
+      } else {
+        sched_mfma_interleave_loads<NKB * NQK, 1, QK_AHEAD, 4, kMaskTileLds ? 6 : 2, 0>();
+      }
+      // keep P(t_i) and its row sums here: left alone, the compiler moves them next to
+      // their use in phase B, out of the shadow of these products
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          i32x4 w = __builtin_bit_cast(i32x4, pt[kb][c]);
+          asm volatile("" : "+v"(w));
+          pt[kb][c] = __builtin_bit_cast(frag, w);
+        }
+      asm volatile("" : "+v"(l_run));
+    }
+    // (additive mask tiles: the compiler barrier keeps the mask reads of phase B from being
+    // hoisted into phase A, where their registers would add to its peak)
+    if constexpr (kMaskTileLds) asm volatile("" ::: "memory");
+    // phase B
+    if (has1) {
+      qk_scale(s_nxt, kt1);
+      fixup(kt1, s_nxt, sMr);
+    }
+    pv(sVr, pt);
+    store_tile(sKw);  // (stale registers when there is no t_{i+2}: the buffer is not read)
+    need = check(s_nxt, mx) && has1;
+    if constexpr (KPL == 8) sched_mfma_interleave<NDB * NKB * 2, 2, PV_AHEAD, 6, 1>();
     wait_vmem_and_sync();
-    kt = ktn;
+    kt = kt1;
+    kt1 = kt2;
   };
   while (kt < kt_end) {
     body(std::integral_constant<int, 0>{});
@@ -671,7 +742,13 @@ static int launch_fwd_d(int mask_kind, bool causal, const FwdParams& p, void* st
   if (causal) return launch_fwd_t<T, D, MASK_NONE, true>(p, stream);
   switch (mask_kind) {
     case MASK_BOOL: return launch_fwd_t<T, D, MASK_BOOL, false>(p, stream);
-    case MASK_ADD: return launch_fwd_t<T, D, MASK_ADD, false>(p, stream);
+    case MASK_ADD:
+      if constexpr (sizeof(T) == 2) {
+        if (p.mask.dtype != F32 && !p.mask.key_bcast && p.mask.sq != 0 && p.shp.S % 8 == 0 &&
+            p.mask.sq * 2 * FwdCfg<T>::BM < ((int64_t)1 << 31))
+          return launch_fwd_t<T, D, MASK_ADD_TILE, false>(p, stream);
+      }
+      return launch_fwd_t<T, D, MASK_ADD, false>(p, stream);
     default: return launch_fwd_t<T, D, MASK_NONE, false>(p, stream);
   }
 }

@@ -8,6 +8,8 @@ namespace rs {
 
 enum DType : int { F32 = 0, F16 = 1, BF16 = 2, BOOL8 = 3 };
 enum MaskKind : int { MASK_NONE = 0, MASK_BOOL = 1, MASK_ADD = 2 };
+// Forward kernel only: an additive mask staged through LDS in tiles (chosen by the launcher).
+constexpr int MASK_ADD_TILE = 3;
 
 // Tile states of a bool mask over 64 x 64 (query x key) blocks: bit0 = some key attended,
 // bit1 = some key excluded.  OR-ing states combines blocks.
