@@ -108,6 +108,16 @@ __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int64_t til
   return __builtin_amdgcn_make_buffer_rsrc((void*)au, (short)0, n, 0x00020000);
 }
 
+// Descriptor for the tile of rows row0.. of a row-major operand of nrows rows (stride_bytes
+// apart, the last row_bytes long): bytes at or past the operand's end read as zero.  Takes
+// 32-bit sizes only, so nothing 64-bit is held in scalar registers between tiles.
+__device__ inline __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int row0, int nrows, int stride_bytes,
+                                                   int row_bytes) {
+  const int64_t off = (int64_t)row0 * stride_bytes;
+  const int64_t total = (int64_t)(nrows - 1) * stride_bytes + row_bytes;
+  return tile_rsrc(base, off, total);
+}
+
 // Waits for this wave's outstanding memory loads (including loads that write LDS directly)
 // and then for every wave of the workgroup.
 __device__ inline void wait_vmem_and_sync() {

@@ -26,6 +26,7 @@
 //  * the all-true / all-false state of each 64x64 bool-mask tile (computed beforehand on the
 //    device) lets all-false tiles be skipped and all-true tiles run without mask reads;
 //    causal tiles above the diagonal are never visited.
+#include <algorithm>
 #include <type_traits>
 
 #include "rs_device.hpp"
@@ -137,8 +138,21 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   const int S = p.shp.S;
   const float c2 = p.shp.scale_log2;
 
-  // ---- work item -------------------------------------------------------------------------
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  // ---- work decomposition ----------------------------------------------------------------
+  // A unit is one (b, h, query tile) over all its key tiles.  Without split, workgroup w
+  // runs unit w.  With split (uniform key-tile counts: no causal, no bool mask), the first
+  // split_full workgroups run one whole unit each and the remaining units' (unit, key tile)
+  // iterations are cut into split_grid equal contiguous ranges, one per further workgroup
+  // (these start as the whole units finish, so the cut units' work is spread over the whole
+  // GPU instead of leaving it part-idle in a last round); a unit cut between workgroups is
+  // processed as pieces, each writing its normalized output and row log-sum-exp to a slot,
+  // which fwd_merge_kernel then combines.
+  const int nkt_all = (S + BN - 1) / BN;
+  constexpr bool kCanSplit = !CAUSAL && MASK != MASK_BOOL;
+
+  // one piece: key tiles [t0, t1) of unit `item` (t1 < 0: the unit's whole range); a cut
+  // piece writes to slot `slot` (workgroup w of the ranges owns slots 2w and 2w + 1)
+  auto piece = [&](const int item, const int t0, const int t1, const int slot) __attribute__((always_inline)) {
   int qt = item % p.num_qt;
   const int bh = item / p.num_qt;
   const int hd = bh % p.shp.H, b = bh / p.shp.H;
@@ -195,8 +209,8 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   }
 
   // ---- KV tile range -----------------------------------------------------------------------
-  const int nkt = (S + BN - 1) / BN;
-  int kt_end = nkt;
+  const int nkt = nkt_all;
+  int kt_end = t1 >= 0 ? t1 : nkt;
   if (CAUSAL) {
     const int last_row = min(q0 + BM, S) - 1;
     kt_end = min(nkt, last_row / BN + 1);
@@ -252,7 +266,6 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // destination: lane i of a load writes bytes [16i, 16i+16) of a 1 KB block).  The byte
   // range check of the buffer turns rows at or past S into zeros.  16-byte chunks of row j
   // sit at chunk ^ vsw(j) so that the transposed reads below touch distinct banks.
-  const int64_t vtotal = ((int64_t)(S - 1) * p.v.ss + D) * ES;  // bytes of this (b, h) slice of V
   uint32_t v_voff[VLD];
 #pragma unroll
   for (int i = 0; i < VLD; ++i) {
@@ -263,18 +276,17 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 
   // additive mask tiles (see sm0/sm1)
   const void* mbase = nullptr;
-  int64_t mspan = 0;
   auto msw = [](int row) __attribute__((always_inline)) { return (row & 7) ^ ((row >> 3) & 1); };
   if constexpr (kMaskTileLds) {
     // (S % 8 == 0: every 16-byte chunk of a valid key run lies inside the mask's last row)
-    mspan = ((int64_t)(S - 1) * p.mask.sq + S) * 2;
     const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
     mbase = mask_row_ptr(p.mask, bm, hm, 0, 2);
   }
   auto dma_mask = [&](int kt, char* sM) __attribute__((always_inline)) {
     if constexpr (kMaskTileLds) {
       constexpr int ML = BM * MROW / 1024 / NW;
-      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(mbase, ((int64_t)q0 * p.mask.sq + (int64_t)kt * BN) * 2, mspan);
+      const __amdgpu_buffer_rsrc_t rs =
+          rows_rsrc((const char*)mbase + kt * BN * 2, q0, S, (int)p.mask.sq * 2, (S - kt * BN) * 2);
       // per-lane offsets recomputed here (cheap) rather than held in registers throughout
       int ln = lane;
       asm volatile("" : "+v"(ln));
@@ -291,11 +303,9 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // K of tile kt and its table rows into registers, through buffer descriptors: rows at or
   // past S read as zeros, and every call issues the same loads (so the wait for them can
   // let later loads stay in flight)
-  const int64_t ktotal = ((int64_t)(S - 1) * p.k.ss + D) * ES;  // bytes of this (b, h) slice of K
-  const int64_t ttotal = (int64_t)S * D * 4;                     // bytes of this sample's table rows
   auto load_k_rows = [&](int kt) __attribute__((always_inline)) {
     if constexpr (QI8) return;
-    const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kbase, (int64_t)kt * BN * p.k.ss * ES, ktotal);
+    const __amdgpu_buffer_rsrc_t krs = rows_rsrc(kbase, kt * BN, S, (int)p.k.ss * ES, D * ES);
 #pragma unroll
     for (int it = 0; it < KCPT; ++it)
       kx[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -303,7 +313,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   };
   auto load_k_tab = [&](int kt) __attribute__((always_inline)) {
     if constexpr (QI8) return;
-    const __amdgpu_buffer_rsrc_t trs = tile_rsrc(tab, (int64_t)kt * BN * D * 4, ttotal);
+    const __amdgpu_buffer_rsrc_t trs = rows_rsrc(tab, kt * BN, S, D * 4, D * 4);
 #pragma unroll
     for (int it = 0; it < KCPT; ++it)
 #pragma unroll
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 
   // this wave's share of V of tile kt straight into the LDS buffer sV
   auto dma_v = [&](int kt, char* sV) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vbase, (int64_t)kt * BN * p.v.ss * ES, vtotal);
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(vbase, kt * BN, S, (int)p.v.ss * ES, D * ES);
 #pragma unroll
     for (int i = 0; i < VLD; ++i) buffer_load_lds16(rs, sV + (wave * VLD + i) * 1024, v_voff[i], 0);
   };
@@ -611,7 +621,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   f32x16 sacc[2][NKB];
   float mx = 0.f;     // row max of the current tile's scores (valid where need was computed)
   bool need = false;  // the current tile raises some row max by more than 2^8
-  int kt = next_tile(0);
+  int kt = next_tile(t0);
   int kt1 = kt < kt_end ? next_tile(kt + 1) : kt_end;
   if (kt < kt_end) {
     load_k(kt);
@@ -702,10 +712,14 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   }
 
   // ---- epilogue ------------------------------------------------------------------------------
+  // (a piece of a cut unit writes its normalized output and row log-sum-exp to its slot, in
+  // the same form as a whole unit does; fwd_merge_kernel combines the pieces)
   const float l = xhalf_sum(l_run);
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   if (m < S) {
-    char* orow = (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)hd * p.o_sh + (int64_t)m * p.o_ss) * ES;
+    char* orow = slot >= 0 ? (char*)p.part_o + ((int64_t)slot * BM + (m - q0)) * D * ES
+                           : (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)hd * p.o_sh +
+                                                 (int64_t)m * p.o_ss) * ES;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -723,17 +737,126 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
           *(float4*)(orow + d0 * ES) = w;
         }
       }
-    if (p.lse && hh == 0) {
-      p.lse[((int64_t)b * p.shp.H + hd) * S + m] = l > 0.f ? (m_run + __log2f(l)) * kLn2F : -INFINITY;
+    float* lse = slot >= 0 ? p.part_lse + (int64_t)slot * BM + (m - q0)
+                           : p.lse ? p.lse + ((int64_t)b * p.shp.H + hd) * S + m : nullptr;
+    if (lse && hh == 0) {
+      *lse = l > 0.f ? (m_run + __log2f(l)) * kLn2F : -INFINITY;
     }
   }
+  };
+
+  // pieces of this workgroup, one call site (the body is inlined once)
+  int whole_unit = -1;  // >= 0: this workgroup runs that one unit whole
+  int w = 0;
+  int64_t it = 0, it_end = 0;
+  const int64_t G = p.split_grid, W = p.split_iters;
+  if (!kCanSplit || p.split_iters == 0) {
+    whole_unit = xcd_remap(blockIdx.x, gridDim.x);
+  } else if ((int)blockIdx.x < p.split_full) {
+    whole_unit = xcd_remap(blockIdx.x, p.split_full);
+  } else {
+    // (split_full is a multiple of 8, so tail workgroup tw sits on XCD tw % 8 like the others)
+    w = __builtin_amdgcn_readfirstlane(xcd_remap((int)blockIdx.x - p.split_full, p.split_grid));
+    it = (int64_t)w * W / G;
+    it_end = (int64_t)(w + 1) * W / G;
+  }
+  // (the piece coordinates are the same in every lane: read from the first lane they stay in
+  // scalar registers, not in vector registers held through the whole piece)
+  auto uni = [](int x) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(x); };
+  for (int n = 0;; ++n) {
+    int item, t0 = 0, t1 = -1, slot = -1;
+    if (whole_unit >= 0) {
+      if (n > 0) break;
+      item = whole_unit;
+    } else {
+      if (it >= it_end) break;
+      const int u = uni((int)(it / nkt_all));
+      t0 = uni((int)(it - (int64_t)u * nkt_all));
+      const int te = uni((int)min((int64_t)nkt_all, t0 + (it_end - it)));
+      item = p.split_full + u;
+      if (t0 > 0 || te < nkt_all) {  // a cut piece: first one in slot 2w, a later one in 2w + 1
+        t1 = te;
+        slot = 2 * w + (n > 0 ? 1 : 0);
+      }
+      it += te - t0;
+    }
+    if (n > 0) __syncthreads();  // LDS of the previous piece
+    piece(uni(item), uni(t0), uni(t1), uni(slot));
+  }
+}
+
+// Combines the pieces of the cut units: per row, LSE = log sum_s exp(LSE_s) and
+// O = sum_s exp(LSE_s - LSE) O_s over the pieces in range order (a fixed order: the result
+// does not depend on timing).  One workgroup per (cut unit, 32 rows); 8 threads per row, 16
+// elements of the head dimension each.  A unit has at most kMaxPieces pieces (the planner
+// keeps at least 8 key tiles per range), so all loads of a row can be issued together.
+constexpr int kMaxPieces = 4;
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p) {
+  constexpr int BM = FwdCfg<T>::BM;
+  constexpr int PER = D / 8;  // elements per thread
+  const int u = blockIdx.x / (BM / 32);
+  const int r = (blockIdx.x % (BM / 32)) * 32 + (threadIdx.x >> 3), c = (threadIdx.x & 7) * PER;
+  const int S = p.shp.S, nkt = (S + FwdCfg<T>::BN - 1) / FwdCfg<T>::BN;
+  const int item = p.split_full + u;
+  const int qt = item % p.num_qt, bh = item / p.num_qt;
+  const int hd = bh % p.shp.H, b = bh / p.shp.H;
+  const int m = qt * BM + r;
+  if (m >= S) return;
+  const int64_t G = p.split_grid, W = p.split_iters, u0 = (int64_t)u * nkt;
+  const int w_lo = (int)(((u0 + 1) * G + W - 1) / W) - 1;
+  const int w_hi = (int)(((u0 + nkt) * G + W - 1) / W) - 1;
+  const int n = min(w_hi - w_lo + 1, kMaxPieces);
+  int sl[kMaxPieces];
+  float ls[kMaxPieces];
+  typedef T vp __attribute__((ext_vector_type(PER)));
+  vp o[kMaxPieces];
+#pragma unroll
+  for (int j = 0; j < kMaxPieces; ++j) {
+    const int w = w_lo + j;
+    sl[j] = 2 * w + ((int)(((int64_t)w * W / G) / nkt) == u ? 0 : 1);
+    if (j < n) {
+      ls[j] = p.part_lse[(int64_t)sl[j] * BM + r];
+      o[j] = *(const vp*)((const T*)p.part_o + ((int64_t)sl[j] * BM + r) * D + c);
+    } else {
+      ls[j] = -INFINITY;
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMaxPieces; ++j) mx = fmaxf(mx, ls[j]);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float sum = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < kMaxPieces; ++j) {
+      if (j >= n) break;
+      const float f = __expf(ls[j] - mx);  // 0 for a piece with no attended key
+      sum += f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(f, to_f(o[j][e]), acc[e]);
+    }
+  }
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  vp outv;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) outv[e] = from_f<T>(acc[e] * inv);
+  *(vp*)((T*)p.o + (int64_t)b * p.o_sb + (int64_t)hd * p.o_sh + (int64_t)m * p.o_ss + c) = outv;
+  if (p.lse && c == 0) p.lse[((int64_t)b * p.shp.H + hd) * S + m] = sum > 0.f ? mx + __logf(sum) : -INFINITY;
 }
 
 template <typename T, int D, int MASK, bool CAUSAL, bool QI8 = false>
 static int launch_fwd_t(const FwdParams& p, void* stream) {
-  const int grid = p.num_qt * p.shp.H * p.shp.B;
+  const int grid = p.split_iters > 0 ? p.split_full + p.split_grid : p.num_qt * p.shp.H * p.shp.B;
   hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL, QI8>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
                      (hipStream_t)stream, p);
+  if (p.split_iters > 0) {
+    const int cut = p.num_qt * p.shp.H * p.shp.B - p.split_full;
+    hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3(cut * (FwdCfg<T>::BM / 32)), dim3(256), 0,
+                       (hipStream_t)stream, p);
+  }
   return (int)hipGetLastError();
 }
 
@@ -775,5 +898,51 @@ int launch_fwd(int dtype, int D, int mask_kind, bool causal, bool int8, const Fw
 }
 
 int fwd_block_m(int dtype) { return dtype == F32 ? FwdCfg<float>::BM : FwdCfg<__bf16>::BM; }
+int fwd_block_n(int dtype) { return dtype == F32 ? FwdCfg<float>::BN : FwdCfg<__bf16>::BN; }
+int fwd_waves(int dtype) { return (dtype == F32 ? FwdCfg<float>::NT : FwdCfg<__bf16>::NT) / 64; }
+
+template <typename T, int D, bool QI8>
+static int resident_per_cu() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<T, D, MASK_NONE, false, QI8>, FwdCfg<T>::NT, 0) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+
+SplitPlan fwd_split_plan(int dtype, int D, bool int8, bool causal, int mask_kind, int64_t units, int nkt) {
+  SplitPlan sp{};
+  if (causal || mask_kind == MASK_BOOL || units <= 0 || nkt < 16) return sp;
+  int dev = -1, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return sp;
+  const bool d64 = D == 64;
+  int per = 0;
+  if (dtype == F32) per = d64 ? resident_per_cu<float, 64, false>() : resident_per_cu<float, 128, false>();
+  else if (dtype == F16) per = int8 ? (d64 ? resident_per_cu<_Float16, 64, true>() : resident_per_cu<_Float16, 128, true>())
+                                    : (d64 ? resident_per_cu<_Float16, 64, false>() : resident_per_cu<_Float16, 128, false>());
+  else per = int8 ? (d64 ? resident_per_cu<__bf16, 64, true>() : resident_per_cu<__bf16, 128, true>())
+                  : (d64 ? resident_per_cu<__bf16, 64, false>() : resident_per_cu<__bf16, 128, false>());
+  const int64_t g = (int64_t)cus * per & ~(int64_t)7;  // resident workgroups, a multiple of 8
+  if (g < 8) return sp;
+  const int64_t full = units / g * g, cut = units - full;
+  if (cut == 0) return sp;
+  const int64_t iters = cut * nkt;
+  // at least nkt / (kMaxPieces - 1) key tiles per range: a unit then meets at most
+  // kMaxPieces ranges (fwd_merge_kernel relies on it)
+  const int64_t grid = std::min<int64_t>(g, iters / std::max<int64_t>(8, (nkt + kMaxPieces - 2) / (kMaxPieces - 1)));
+  if (grid <= cut) return sp;  // no more workgroups than units: nothing gained
+  // time in key-tile steps: one unit per workgroup, against whole units plus an equal share
+  // of the rest (plus about two steps for publishing and merging the pieces)
+  const int64_t plain = (units + g - 1) / g * nkt;
+  const int64_t split = full / g * nkt + (iters + grid - 1) / grid + 2;
+  if (split * 100 > plain * 97) return sp;  // keep the plain schedule unless ~3% is gained
+  sp.full = (int)full;
+  sp.grid = (int)grid;
+  sp.iters = iters;
+  sp.cut_units = cut;
+  sp.slot_bytes = (size_t)fwd_block_m(dtype) * D * (dtype == F32 ? 4 : 2);  // normalized O rows
+  return sp;
+}
 
 }  // namespace rs

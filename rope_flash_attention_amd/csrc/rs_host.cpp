@@ -170,12 +170,13 @@ rs_status validate_args(const rs_args* a, Shape* out) {
 }
 
 struct Layout {
-  size_t ctrl, table, tiles, delta, qc, kc, qs, ks, total;
+  size_t ctrl, table, tiles, delta, qc, kc, qs, ks, part, cnt, total;
   int64_t nqt, nkt;
   int64_t sp, nblk;  // int8 variant: padded rows per (b, h) slice and 64-token blocks
+  SplitPlan split;   // forward only: work split over the current device's workgroups
 };
 
-Layout layout(const Shape& s, int mask_kind, bool backward, bool int8) {
+Layout layout(const Shape& s, int mask_kind, bool backward, bool int8, bool causal) {
   Layout L{};
   size_t off = 0;
   L.ctrl = off;
@@ -203,6 +204,17 @@ Layout layout(const Shape& s, int mask_kind, bool backward, bool int8) {
     off += scales;
     L.ks = off;
     off += scales;
+  }
+  if (!backward) {
+    const int64_t bm = fwd_block_m(s.dtype), bn = fwd_block_n(s.dtype);
+    const int64_t units = s.B * s.H * ((s.S + bm - 1) / bm);
+    L.split = fwd_split_plan(s.dtype, (int)s.D, int8, causal, mask_kind, units, (int)((s.S + bn - 1) / bn));
+    if (L.split.iters > 0) {
+      L.part = off;
+      off += round_up(2 * (size_t)L.split.grid * L.split.slot_bytes, 256);
+      L.cnt = off;  // the pieces' row log-sum-exp
+      off += round_up(2 * (size_t)L.split.grid * bm * sizeof(float), 256);
+    }
   }
   L.total = off;
   return L;
@@ -354,7 +366,10 @@ rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* by
   Shape s;
   rs_status st = validate_args(args, &s);
   if (st != RS_OK) return fail(st);
-  *bytes = s.empty ? 0 : layout(s, args->mask_kind, backward != 0, (args->flags & RS_FLAG_QUANT_INT8_QK) != 0).total;
+  *bytes = s.empty ? 0
+                   : layout(s, args->mask_kind, backward != 0, (args->flags & RS_FLAG_QUANT_INT8_QK) != 0,
+                            (args->flags & RS_FLAG_CAUSAL) != 0)
+                         .total;
   return RS_OK;
 }
 
@@ -370,7 +385,7 @@ rs_status rope_sdpa_fwd(const rs_args* a, const rs_tensor* o, float* lse, void* 
   if (lse && ((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
   if (s.empty) return RS_OK;  // nothing to compute: no workspace or device needed
   const bool int8 = (a->flags & RS_FLAG_QUANT_INT8_QK) != 0;
-  const Layout L = layout(s, a->mask_kind, false, int8);
+  const Layout L = layout(s, a->mask_kind, false, int8, (a->flags & RS_FLAG_CAUSAL) != 0);
   if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
   if ((st = current_device_ok()) != RS_OK) return fail(st);
 
@@ -405,6 +420,13 @@ rs_status rope_sdpa_fwd(const rs_args* a, const rs_tensor* o, float* lse, void* 
     p.ksc = (const float*)(w + L.ks);
     p.sp = (int)L.sp;
   }
+  if (L.split.iters > 0) {
+    p.split_full = L.split.full;
+    p.split_grid = L.split.grid;
+    p.split_iters = L.split.iters;
+    p.part_o = w + L.part;
+    p.part_lse = (float*)(w + L.cnt);
+  }
   if (launch_fwd(s.dtype, (int)s.D, a->mask_kind, causal, int8, p, strm) != 0) return fail(RS_ERR_LAUNCH);
 
   (lse ? g_ctr.fwd_autograd : g_ctr.fwd_instream).fetch_add(1, std::memory_order_relaxed);
@@ -425,7 +447,7 @@ rs_status rope_sdpa_debug_quantize_qk(const rs_args* a, int8_t* q_codes, int8_t*
   if (!q_codes || !k_codes || !q_scales || !k_scales) return fail(RS_ERR_NULL);
   if (((uintptr_t)q_codes) % 8 != 0 || ((uintptr_t)k_codes) % 8 != 0) return fail(RS_ERR_ALIGN);
   if (((uintptr_t)q_scales) % 4 != 0 || ((uintptr_t)k_scales) % 4 != 0) return fail(RS_ERR_ALIGN);
-  const Layout L = layout(s, a->mask_kind, false, true);
+  const Layout L = layout(s, a->mask_kind, false, true, false);
   if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
   if ((st = current_device_ok()) != RS_OK) return fail(st);
   char* w = (char*)ws;
@@ -452,7 +474,7 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   }
   if (((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
   if (s.empty) return RS_OK;
-  const Layout L = layout(s, a->mask_kind, true, false);
+  const Layout L = layout(s, a->mask_kind, true, false, (a->flags & RS_FLAG_CAUSAL) != 0);
   if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
   if ((st = current_device_ok()) != RS_OK) return fail(st);
 

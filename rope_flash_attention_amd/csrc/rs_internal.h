@@ -66,6 +66,12 @@ struct FwdParams {
   const float* qsc;
   const float* ksc;
   int sp;
+  // split of the work (see the forward kernel): split_iters = 0 for one workgroup per unit
+  int split_full;       // units run whole by the first workgroups (a multiple of 8)
+  int split_grid;       // further workgroups sharing the remaining units' key tiles
+  int64_t split_iters;  // (unit, key tile) iterations of the remaining units
+  void* part_o;         // pieces' normalized outputs: two slots of [BM][D] per further workgroup
+  float* part_lse;      // pieces' row log-sum-exp: two slots of [BM] per further workgroup
 };
 
 struct BwdParams {
@@ -115,6 +121,15 @@ struct ClassifyParams {
 int launch_pack_tables(const PackParams& p, void* stream);
 int launch_classify(const ClassifyParams& p, void* stream);
 int fwd_block_m(int dtype);  // query rows per forward workgroup
+int fwd_block_n(int dtype);  // keys per forward tile
+// Split plan of a forward call on the current device (all zero: one workgroup per unit).
+struct SplitPlan {
+  int full, grid;
+  int64_t iters;
+  size_t slot_bytes;  // bytes of one partial-state slot
+  int64_t cut_units;  // units whose key tiles are shared out
+};
+SplitPlan fwd_split_plan(int dtype, int D, bool int8, bool causal, int mask_kind, int64_t units, int nkt);
 int launch_fwd(int dtype, int D, int mask_kind, bool causal, bool int8, const FwdParams& p, void* stream);
 int launch_quant_int8(int dtype, const QuantParams& p, void* stream);
 int launch_bwd(int dtype, int D, int mask_kind, bool causal, const BwdParams& p, void* stream);

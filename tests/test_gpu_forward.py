@@ -251,3 +251,18 @@ def test_additive_mask_tile_path(case):
         wide[..., :S] = w.mask
         w.mask = wide[..., :S]
     _compare(w)
+
+
+@pytest.mark.parametrize("case", ["bf16", "f16", "f32", "additive_bf16", "d64_bf16"])
+def test_split_key_ranges(case):
+    """Few units for the GPU: the units' key ranges are cut into pieces spread over all
+    workgroups, each piece writes its normalized output and row log-sum-exp, and a merge
+    kernel combines them.  S = 1104: 5 (16-bit) or 9 (fp32) query tiles per head and 18 or
+    35 key tiles, cut at tile boundaries inside units."""
+    dtype = case.split("_")[-1]
+    D = 64 if case.startswith("d64") else 128
+    kw = dict(mask_kind="additive", mask_shape=(1, 3, 1104, 1104)) if case.startswith("additive") else {}
+    w = syn.random_small(1, 3, 1104, D, dtype=dtype, seed=130, **kw)
+    _compare(w)
+    if case == "bf16":
+        _compare(w, need_lse=False)

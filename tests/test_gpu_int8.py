@@ -172,3 +172,15 @@ def test_int8_long_full_size_sampled():
     """Long FLUX sequence B=1, H=48, S=16896 (512 text + 128x128 image), D=128: heads 0 and 47."""
     w = syn.flux(batch=1, heads=48, grid=128, dtype="bf16", seed=5000)
     _sampled_full(w, (0, 47), [0, 511, 512, 9000, 16895])
+
+
+def test_int8_split_key_ranges():
+    """int8 forward on a shape whose units' key ranges are split and merged (S = 1104)."""
+    w = syn.random_small(1, 3, 1104, 128, dtype="bf16", seed=131)
+    codes = _gpu_codes(w.q, w.k, w.cos, w.sin)
+    o, lse = _run_int8(w)
+    qc, qs, kc, ks = codes
+    O_ref, L_ref = rope_sdpa_forward_int8(w.q, w.k, w.v, w.cos, w.sin, scale=w.scale,
+                                          codes=((qc, qs), (kc, ks)), workers=8)
+    check_out("O", to64(o), O_ref, "bf16")
+    check_lse(to64(lse), L_ref, "bf16")
