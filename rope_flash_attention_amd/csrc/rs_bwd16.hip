@@ -495,27 +495,8 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   };
   const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
 
-  int qt = next_tile(qt_begin);
-  if (qt < nqt) {
-    load_tile(qt, sd0);
-    store_tile(sq0, sl0);
-  }
-  wait_vmem_and_sync();
-
-  auto body = [&](auto stage_c) {
-    constexpr int stage = decltype(stage_c)::value;
-    const char* sQ = stage ? sq1 : sq0;
-    const char* sD = stage ? sd1 : sd0;
-    const float* sL = stage ? sl1 : sl0;
-    char* sQn = stage ? sq0 : sq1;
-    char* sDn = stage ? sd0 : sd1;
-    float* sLn = stage ? sl0 : sl1;
-    const int qtn = next_tile(qt + 1);
-    if (qtn < nqt) load_tile(qtn, sDn);
-    const int q0 = qt * BMQ;
-
-    // S' and dP: rows = queries (permuted order), column = this lane's key
-    f32x4 sacc[4], dpacc[4];
+  // S' and dP of one query tile: rows = queries (permuted order), column = this lane's key
+  auto rows = [&](const char* sQ, const char* sD, f32x4* sacc, f32x4* dpacc) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       frag qa[4], ga[4];
@@ -529,7 +510,12 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
       for (int t = 0; t < 4; ++t) dpacc[qb] = M::mma(ga[t], vf[t], t == 0 ? z4 : dpacc[qb]);
     }
     sched_reads_ahead<32, 1, 8, 0>();
-
+  };
+  // P and dS of query tile qt (l2 and delta in sL) as B fragments
+  auto softmax = [&](int qt, const float* sL, f32x4* sacc, f32x4* dpacc, frag* pf_out, frag* sf_out)
+                     __attribute__((always_inline)) {
+    const int q0 = qt * BMQ;
+    frag pf[2], sf[2];  // built from scratch: every element is written
     // accumulator row 4g + i of block qb is query q0 + 32 (qb >> 1) + 8 g + 4 (qb & 1) + i
     if constexpr (MASK == MASK_ADD) {
       const int jj = p.mask.key_bcast ? 0 : jc;
@@ -549,7 +535,6 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
     uint32_t st = TILE_ALL_TRUE;
     if constexpr (MASK == MASK_BOOL) st = tile_state(qt);
     const bool check = (CAUSAL && q0 < k0 + BNK - 1) || (MASK == MASK_BOOL && st != TILE_ALL_TRUE);
-    frag pf[2], sf[2];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int r0 = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);  // tile-local query of register 0
@@ -575,8 +560,20 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
         sf[qb >> 1][4 * (qb & 1) + i] = from_f<T>(pv * (dpacc[qb][i] - d4[i]));
       }
     }
-
-    // dV^T += dO^T P, dK'^T += Q'^T dS: rows = head dim, column = this lane's key
+    // computed here: left alone, the compiler sinks this arithmetic to the products that
+    // use it (after the barrier), which keeps the fp32 scores alive instead
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      i32x4 w = __builtin_bit_cast(i32x4, pf[h]);
+      asm volatile("" : "+v"(w));
+      pf_out[h] = __builtin_bit_cast(frag, w);
+      w = __builtin_bit_cast(i32x4, sf[h]);
+      asm volatile("" : "+v"(w));
+      sf_out[h] = __builtin_bit_cast(frag, w);
+    }
+  };
+  // dV^T += dO^T P, dK'^T += Q'^T dS: rows = head dim, column = this lane's key
+  auto cols = [&](const char* sQ, const char* sD, const frag* pf, const frag* sf) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
@@ -585,15 +582,80 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
         dk[db] = M::mma(tr_frag<frag>(sQ, lo, qs, db), sf[qs], dk[db]);
       }
     sched_reads_ahead<32, 2, 3, 1>();
-
-    if (qtn < nqt) store_tile(sQn, sLn);
-    wait_vmem_and_sync();
-    qt = qtn;
   };
-  while (qt < nqt) {
-    body(std::integral_constant<int, 0>{});
-    if (qt >= nqt) break;
-    body(std::integral_constant<int, 1>{});
+
+  // The two waves of a SIMD work half a tile apart.  A step has two halves separated by a
+  // barrier: waves 0-3 take the tile's scores (row reads) and then its gradient products
+  // (transposed reads); waves 4-7 first finish the previous tile's gradient products, then
+  // take this tile's scores, whose P and dS stay in registers across the barrier.  Each half
+  // then has one wave per SIMD on each kind of product, and the LDS serves both kinds of
+  // reads at once.  The previous tile's buffer is free after the first half: the next tile
+  // is loaded into it during the second.  The two wave groups run separate loops (one
+  // branch outside), so that neither carries the other's registers; both pass the same
+  // barriers: two per tile.
+  int qt = next_tile(qt_begin);
+  if (qt < nqt) {
+    load_tile(qt, sd0);
+    store_tile(sq0, sl0);
+  }
+  wait_vmem_and_sync();
+  frag pf[2], sf[2];
+  if (__builtin_amdgcn_readfirstlane(wave) < 4) {
+    auto body = [&](auto stage_c) __attribute__((always_inline)) {
+      constexpr int stage = decltype(stage_c)::value;
+      char* sQ = stage ? sq1 : sq0;
+      char* sD = stage ? sd1 : sd0;
+      float* sL = stage ? sl1 : sl0;
+      char* sQn = stage ? sq0 : sq1;
+      char* sDn = stage ? sd0 : sd1;
+      float* sLn = stage ? sl0 : sl1;
+      f32x4 sacc[4], dpacc[4];
+      rows(sQ, sD, sacc, dpacc);
+      softmax(qt, sL, sacc, dpacc, pf, sf);
+      __syncthreads();
+      const int qtn = next_tile(qt + 1);
+      if (qtn < nqt) load_tile(qtn, sDn);
+      cols(sQ, sD, pf, sf);
+      if (qtn < nqt) store_tile(sQn, sLn);
+      wait_vmem_and_sync();
+      qt = qtn;
+    };
+    while (qt < nqt) {
+      body(std::integral_constant<int, 0>{});
+      if (qt >= nqt) break;
+      body(std::integral_constant<int, 1>{});
+    }
+  } else {
+    bool has_prev = false;
+    auto body = [&](auto stage_c) __attribute__((always_inline)) {
+      constexpr int stage = decltype(stage_c)::value;
+      char* sQ = stage ? sq1 : sq0;
+      char* sD = stage ? sd1 : sd0;
+      float* sL = stage ? sl1 : sl0;
+      char* sQp = stage ? sq0 : sq1;  // the previous tile, then the next one
+      char* sDp = stage ? sd0 : sd1;
+      float* sLp = stage ? sl0 : sl1;
+      if (has_prev) cols(sQp, sDp, pf, sf);
+      __syncthreads();
+      const int qtn = next_tile(qt + 1);
+      if (qtn < nqt) load_tile(qtn, sDp);
+      f32x4 sacc[4], dpacc[4];
+      rows(sQ, sD, sacc, dpacc);
+      softmax(qt, sL, sacc, dpacc, pf, sf);
+      if (qtn < nqt) store_tile(sQp, sLp);
+      wait_vmem_and_sync();
+      has_prev = true;
+      qt = qtn;
+    };
+    int last = 0;  // buffer of the last tile
+    while (qt < nqt) {
+      body(std::integral_constant<int, 0>{});
+      last = 0;
+      if (qt >= nqt) break;
+      body(std::integral_constant<int, 1>{});
+      last = 1;
+    }
+    if (has_prev) cols(last ? sq1 : sq0, last ? sd1 : sd0, pf, sf);
   }
 
   if (j < S) {
