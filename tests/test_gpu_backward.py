@@ -103,6 +103,17 @@ def test_fully_masked_rows_have_zero_query_gradient():
     _compare(w)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [64, 65, 128, 192, 256])
+def test_query_tile_counts_16bit(S, causal):
+    """bf16, D=128: 1 to 4 query tiles of 64 rows, exact and with a 1-row tail.  The dK/dV
+    kernel runs its two wave groups half a tile apart (the second group finishes each tile's
+    gradient products one step later), so the first and last tiles of every key range are
+    the cases where the two loops differ."""
+    w = syn.random_small(2, 2, S, 128, "bf16", seed=900 + S, causal=causal, with_grad=True)
+    _compare(w)
+
+
 def test_flux_training_full_size_two_heads():
     """B=2, H=24, S=512+4096, D=128, bf16, 3-axis RoPE; dO ~ N(0,1)."""
     w = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=4100, with_grad=True)
