@@ -219,6 +219,95 @@ def traffic_from_counters(fetch_db, write_db, command):
                                       "command": command, "counters": out}}
 
 
+def pmc_legs(reps):
+    """Workloads for rocprofv3 --pmc passes, each forward call run `reps` times: the tiny fp32
+    case (B=1, H=2, S=128, D=64), the FLUX forward (B=1, no mask) and the FLUX forward with
+    the additive 4-D bf16 mask (B=2), then a 256 MiB device copy whose byte counters scale
+    the others."""
+    import torch
+
+    import synthetic as syn
+    import rope_flash_attention_amd as rfa
+
+    dev = torch.device("cuda:0")
+    w = syn.tiny_fp32()
+    t = [x.to(dev) for x in (w.q, w.k, w.v, w.cos, w.sin)]
+    with torch.no_grad():
+        for _ in range(reps):
+            rfa.rope_scaled_dot_product_attention(*t)
+    w = syn.flux(batch=1, heads=24, grid=64, dtype="bf16", seed=2000)
+    t = [x.to(dev) for x in (w.q, w.k, w.v, w.cos, w.sin)]
+    with torch.no_grad():
+        for _ in range(reps):
+            rfa.rope_scaled_dot_product_attention(*t)
+    w = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=3000)
+    S = w.q.shape[2]
+    t = [x.to(dev) for x in (w.q, w.k, w.v, w.cos, w.sin)]
+    bm = syn.key_padding_mask(syn.key_padding_lengths(3000, 2), 512, S).to(dev)
+    add = torch.where(bm, torch.zeros((), dtype=torch.bfloat16, device=dev),
+                      torch.full((), float("-inf"), dtype=torch.bfloat16, device=dev)).expand(2, 24, S, S).contiguous()
+    with torch.no_grad():
+        for _ in range(reps):
+            rfa.rope_scaled_dot_product_attention(*t, attn_mask=add)
+    del add
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_legs": ["tiny_fp32", "flux_fwd_b1", "flux_fwd_b2_additive_4d", "copy_256MiB"],
+                      "reps": reps}))
+
+
+def summarize_counters(mfma_db, fetch_db, write_db, command):
+    """Per forward kernel launch (kernel, grid): matrix-core busy fraction and HBM bytes from
+    three rocprofv3 --pmc runs of `bench.py --pmc-legs` (SQ_VALU_MFMA_BUSY_CYCLES with
+    GRBM_GUI_ACTIVE; FETCH_SIZE; WRITE_SIZE).  SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of
+    all 1024 SIMDs and GRBM_GUI_ACTIVE the active cycles of the 8 XCDs, so the busy fraction
+    is (MFMA_BUSY / 1024) / (GRBM_GUI_ACTIVE / 8), at the clock the GPU actually ran; that
+    clock is GRBM_GUI_ACTIVE / 8 over the dispatch's duration.  Byte counters (KiB per
+    dispatch) are scaled by what they read for the 256 MiB copy of the same run."""
+    import sqlite3
+
+    def rows(db, counters):
+        con = sqlite3.connect(db)
+        q = ("select kernel_name, grid_size, counter_name, avg(value), avg(duration) from counters_collection "
+             "where counter_name in (%s) group by kernel_name, grid_size, counter_name" % ",".join("?" * len(counters)))
+        return con.execute(q, counters).fetchall()
+
+    data = {}
+    for db, counters in ((mfma_db, ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")), (fetch_db, ("FETCH_SIZE",)),
+                         (write_db, ("WRITE_SIZE",))):
+        for name, grid, cname, val, dur in rows(db, counters):
+            e = data.setdefault((name, grid), {})
+            e[cname] = val
+            e.setdefault("dur_ns", dur)
+    probe = max(((n, g) for n, g in data if "copyBuffer" in n and "FETCH_SIZE" in data[(n, g)]),
+                key=lambda k: data[k]["FETCH_SIZE"], default=None)
+    if probe is None:
+        raise SystemExit("no copy probe in the counter runs")
+    fscale = (256 << 20) / (data[probe]["FETCH_SIZE"] * 1024.0)
+    wscale = (256 << 20) / (data[probe]["WRITE_SIZE"] * 1024.0)
+    out = [f"command: {command}", "",
+           f"copy probe: FETCH_SIZE scale {fscale:.3f}, WRITE_SIZE scale {wscale:.3f} (256 MiB copy)", "",
+           f"{'kernel':58s} {'grid':>8s} {'us':>8s} {'GHz':>5s} {'MFMA busy':>9s} {'read MB':>9s} {'write MB':>9s} {'GB/s':>8s}"]
+    for (name, grid), e in sorted(data.items(), key=lambda kv: -kv[1].get("dur_ns", 0)):
+        if not (name.startswith("_ZN2rs") or "rs::" in name):
+            continue
+        us = e["dur_ns"] / 1000.0
+        ghz = e["GRBM_GUI_ACTIVE"] / 8 / e["dur_ns"] if "GRBM_GUI_ACTIVE" in e else float("nan")
+        busy = (e["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024) / (e["GRBM_GUI_ACTIVE"] / 8) if "GRBM_GUI_ACTIVE" in e else float("nan")
+        rd = e.get("FETCH_SIZE", float("nan")) * 1024.0 * fscale / 1e6
+        wr = e.get("WRITE_SIZE", float("nan")) * 1024.0 * wscale / 1e6
+        # (GRBM_GUI_ACTIVE also counts the dispatch's start and drain: clock and busy fraction
+        # are only read for dispatches far longer than that)
+        clk = f"{ghz:5.2f}" if us >= 50 else f"{'-':>5s}"
+        mb = f"{100 * busy:8.1f}%" if us >= 50 else f"{'-':>9s}"
+        out.append(f"{name[:58]:58s} {grid:8d} {us:8.1f} {clk} {mb} {rd:9.1f} {wr:9.1f} "
+                   f"{(rd + wr) * 1e6 / (us * 1e-6) / 1e9:8.0f}")
+    return "\n".join(out)
+
+
 def summarize_rocpd(db_path, command):
     """Text summary of a rocprofv3 kernel trace: per kernel and grid size, calls and durations."""
     import sqlite3
@@ -249,6 +338,10 @@ def main():
                     help="also run a 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--summarize", metavar="DB", help="print a summary of a rocprofv3 results database and exit")
     ap.add_argument("--command", default="", help="command line recorded in the --summarize output")
+    ap.add_argument("--pmc-legs", type=int, metavar="REPS",
+                    help="run the counter workloads (tiny fp32, FLUX, FLUX additive 4-D, copy probe) and exit")
+    ap.add_argument("--counters", nargs=3, metavar=("MFMA_DB", "FETCH_DB", "WRITE_DB"),
+                    help="print matrix-core busy fraction and HBM bytes per forward launch and exit")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="print HBM bytes per forward launch from two rocprofv3 --pmc results databases and exit")
     args = ap.parse_args()
@@ -257,6 +350,12 @@ def main():
         return
     if args.traffic:
         print(json.dumps(traffic_from_counters(args.traffic[0], args.traffic[1], args.command), indent=1))
+        return
+    if args.counters:
+        print(summarize_counters(*args.counters, args.command))
+        return
+    if args.pmc_legs:
+        pmc_legs(args.pmc_legs)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
