@@ -220,10 +220,10 @@ def traffic_from_counters(fetch_db, write_db, command):
 
 
 def pmc_legs(reps):
-    """Workloads for rocprofv3 --pmc passes, each forward call run `reps` times: the tiny fp32
-    case (B=1, H=2, S=128, D=64), the FLUX forward (B=1, no mask) and the FLUX forward with
-    the additive 4-D bf16 mask (B=2), then a 256 MiB device copy whose byte counters scale
-    the others."""
+    """Workloads for rocprofv3 --pmc passes, each call run `reps` times: the tiny fp32 forward
+    (B=1, H=2, S=128, D=64), the FLUX forward (B=1, no mask), the FLUX forward with the
+    additive 4-D bf16 mask (B=2) and the FLUX backward (B=2), then a 256 MiB device copy
+    whose byte counters scale the others."""
     import torch
 
     import synthetic as syn
@@ -250,17 +250,23 @@ def pmc_legs(reps):
         for _ in range(reps):
             rfa.rope_scaled_dot_product_attention(*t, attn_mask=add)
     del add
+    w = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=4100, with_grad=True)
+    t = [x.to(dev) for x in (w.q, w.k, w.v, w.cos, w.sin, w.do)]
+    o, lse = rfa.rope_sdpa_fwd_with_lse(*t[:5])
+    for _ in range(reps):
+        rfa.rope_sdpa_bwd_explicit(*t[:5], o, lse, t[5])
+    del o, lse, t
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_legs": ["tiny_fp32", "flux_fwd_b1", "flux_fwd_b2_additive_4d", "copy_256MiB"],
+    print(json.dumps({"pmc_legs": ["tiny_fp32", "flux_fwd_b1", "flux_fwd_b2_additive_4d", "flux_bwd_b2", "copy_256MiB"],
                       "reps": reps}))
 
 
 def summarize_counters(mfma_db, fetch_db, write_db, command):
-    """Per forward kernel launch (kernel, grid): matrix-core busy fraction and HBM bytes from
+    """Per kernel launch (kernel, grid): matrix-core busy fraction and HBM bytes from
     three rocprofv3 --pmc runs of `bench.py --pmc-legs` (SQ_VALU_MFMA_BUSY_CYCLES with
     GRBM_GUI_ACTIVE; FETCH_SIZE; WRITE_SIZE).  SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of
     all 1024 SIMDs and GRBM_GUI_ACTIVE the active cycles of the 8 XCDs, so the busy fraction
