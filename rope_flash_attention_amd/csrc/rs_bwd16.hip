@@ -13,7 +13,8 @@
 //            S'^T = K' Q'^T, dP^T = V dO^T (row reads), dQ'^T += K'^T dS^T (transposed reads).
 //  * dkdv16: workgroup = 128 keys (16 per wave); K' (times scale log2 e) and V stay in
 //            registers; Q' (rotated) and dO tiles of 64 queries stream through LDS; per tile
-//            S' = Q' K'^T, dP = dO V^T, dV^T += dO^T P, dK'^T += Q'^T dS.
+//            S' = Q' K'^T, dP = dO V^T, dV^T += dO^T P, dK'^T += Q'^T dS; waves 0-3 and
+//            4-7 work half a tile apart (two barriers per tile, see the kernel).
 // The score rows are read in a permuted order so that the four accumulator rows a lane holds
 // in two consecutive 16-row blocks are eight consecutive contraction indices of the next
 // product: P and dS go from accumulators to B operands without leaving registers.
