@@ -750,7 +750,17 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   int w = 0;
   int64_t it = 0, it_end = 0;
   const int64_t G = p.split_grid, W = p.split_iters;
-  if (!kCanSplit || p.split_iters == 0) {
+  // causal: workgroup w runs two units of one head, query tiles num_qt - 1 - i and i (the
+  // longest with the shortest), so that every workgroup has the same number of key tiles
+  // whatever order the workgroups are placed on the CUs in
+  int pair_b = -1;
+  if constexpr (CAUSAL) {
+    const int npairs = (p.num_qt + 1) / 2;
+    const int itemp = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = itemp / npairs, i = itemp % npairs;
+    whole_unit = bh * p.num_qt + i;  // (the unit's query tile is num_qt - 1 - i, see piece)
+    if (i != p.num_qt - 1 - i) pair_b = bh * p.num_qt + (p.num_qt - 1 - i);
+  } else if (!kCanSplit || p.split_iters == 0) {
     whole_unit = xcd_remap(blockIdx.x, gridDim.x);
   } else if ((int)blockIdx.x < p.split_full) {
     whole_unit = xcd_remap(blockIdx.x, p.split_full);
@@ -766,8 +776,8 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   for (int n = 0;; ++n) {
     int item, t0 = 0, t1 = -1, slot = -1;
     if (whole_unit >= 0) {
-      if (n > 0) break;
-      item = whole_unit;
+      if (n > 1 || (n == 1 && pair_b < 0)) break;
+      item = n == 0 ? whole_unit : pair_b;
     } else {
       if (it >= it_end) break;
       const int u = uni((int)(it / nkt_all));
@@ -849,7 +859,9 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p) {
 
 template <typename T, int D, int MASK, bool CAUSAL, bool QI8 = false>
 static int launch_fwd_t(const FwdParams& p, void* stream) {
-  const int grid = p.split_iters > 0 ? p.split_full + p.split_grid : p.num_qt * p.shp.H * p.shp.B;
+  const int grid = p.split_iters > 0 ? p.split_full + p.split_grid
+                   : CAUSAL        ? (p.num_qt + 1) / 2 * p.shp.H * p.shp.B
+                                   : p.num_qt * p.shp.H * p.shp.B;
   hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL, QI8>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
                      (hipStream_t)stream, p);
   if (p.split_iters > 0) {
