@@ -214,11 +214,19 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
   const int c = lane & 15, g = lane >> 4;
   const int S = p.shp.S;
   const int nqt = (S + BM - 1) / BM;
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  int qt = item % nqt;
-  const int bh = item / nqt;
+  // causal: workgroup w runs two query tiles of one head, the longest (nqt - 1 - i) and the
+  // shortest (i), so that every workgroup has the same number of key tiles whatever order
+  // the workgroups are placed on the CUs in
+  const int npairs = (nqt + 1) / 2;
+  const int itemw = xcd_remap(blockIdx.x, gridDim.x);
+#pragma unroll 1
+  for (int pu = 0; pu < (CAUSAL ? 2 : 1); ++pu) {
+  const int ip = CAUSAL ? itemw % npairs : 0;
+  if (CAUSAL && pu == 1 && ip == nqt - 1 - ip) break;
+  const int qt = CAUSAL ? (pu == 0 ? nqt - 1 - ip : ip) : itemw % nqt;
+  const int bh = CAUSAL ? itemw / npairs : itemw / nqt;
   const int hd = bh % p.shp.H, b = bh / p.shp.H;
-  if (CAUSAL) qt = nqt - 1 - qt;  // longest rows first
+  if (pu > 0) __syncthreads();  // LDS of the previous tile
   const int q0 = qt * BM;
   const int m = q0 + 16 * wave + c;
   const int mc = m < S ? m : S - 1;
@@ -394,6 +402,7 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
       w[3] = from_f<T>(e.y);
       *(v4*)(orow + d0 * 2) = w;
     }
+  }
   }
 }
 
@@ -692,7 +701,9 @@ static int launch_bwd16_t(const BwdParams& p, void* stream) {
                      (hipStream_t)stream, p);
   int e = (int)hipGetLastError();
   if (e) return e;
-  hipLaunchKernelGGL((dq16_kernel<T, MASK, CAUSAL>), dim3(((S + 127) / 128) * BH), dim3(512), 0,
+  // causal: two query tiles of one head per workgroup (see the kernel)
+  const int grid_q = CAUSAL ? ((S + 127) / 128 + 1) / 2 * BH : ((S + 127) / 128) * BH;
+  hipLaunchKernelGGL((dq16_kernel<T, MASK, CAUSAL>), dim3(grid_q), dim3(512), 0,
                      (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }

@@ -15,7 +15,7 @@ Sources for the recipes (pages are cited by title and section):
   * same page, section "Enable In SimpleTuner": bool masks (True = attend), additive
     masks, batched [B,H,Sq,Skv] and broadcast [B,1,1,Skv] shapes.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * RoPE frequencies: omega_p = theta ** (-2p/d) for pair p < d/2 of an axis of
     width d, angle = position * omega_p, computed in float64 and rounded to fp32
     once.  Multi-axis tables concatenate the per-axis pairs in axis order.
