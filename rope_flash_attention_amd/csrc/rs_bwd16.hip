@@ -172,6 +172,28 @@ struct RotStager {
   }
 };
 
+// Q' = R(Q) of one row in the input dtype (D = 128; this lane's four 8-element chunks
+// 32t + 8g), as RotStager rounds it: the dQ kernel writes these rows for the dK/dV kernel,
+// whose tiles then hold exactly the values it would rotate itself.
+template <typename T>
+__device__ inline void store_rot_row(T* dst, const T* row, const float* trow, int g) {
+  typedef T v8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int d0 = 32 * t + 8 * g;
+    v8 x = *(const v8*)(row + d0);
+    const float4 a = *(const float4*)(trow + d0), b = *(const float4*)(trow + d0 + 4);
+    const float cc[4] = {a.x, a.z, b.x, b.z}, ss[4] = {a.y, a.w, b.y, b.w};
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const float2 r = rot_fma(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), cc[pp], ss[pp]);
+      x[2 * pp] = from_f<T>(r.x);
+      x[2 * pp + 1] = from_f<T>(r.y);
+    }
+    *(v8*)(dst + d0) = x;
+  }
+}
+
 // Direct-to-LDS loads of a 64-row tile of a [*, 128] 16-bit operand (rows past the end of
 // the slice read as zero): each wave issues two 1 KB loads.
 struct DmaTile {
@@ -236,8 +258,9 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
   const float* tab = p.tab.ptr + b * p.tab.sb;
 
   frag qf[4], gf[4];
-  row_frags<T, true>(qf, (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh + (int64_t)mc * p.q.ss, tab + (int64_t)mc * D,
-                     g, p.shp.scale_log2);
+  const T* qrow = (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh + (int64_t)mc * p.q.ss;
+  row_frags<T, true>(qf, qrow, tab + (int64_t)mc * D, g, p.shp.scale_log2);
+  if (m < S) store_rot_row<T>((T*)p.qrot + ((int64_t)bh * S + m) * D, qrow, tab + (int64_t)mc * D, g);
   row_frags<T, false>(gf, (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh + (int64_t)mc * p.dout.ss, nullptr,
                       g, 1.f);
   const int64_t rowid = ((int64_t)b * p.shp.H + hd) * S + mc;
@@ -431,7 +454,6 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   const int j = k0 + 16 * wave + c;  // this lane's key
   const int jc = j < S ? j : S - 1;
 
-  const T* qbase = (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh;
   const T* dobase = (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh;
   const float* tab = p.tab.ptr + b * p.tab.sb;
   const float* lse = p.lse + ((int64_t)b * p.shp.H + hd) * S;
@@ -480,14 +502,14 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
 
   LaneOffsets lo;
   lo.init(c, g);
-  RotStager<T> sq;
-  sq.init(tid);
+  DmaTile dqr;  // Q' tiles, rotated by the dQ kernel (launched first)
+  dqr.init((const T*)p.qrot + (int64_t)bh * S * D, D, S, wave, lane);
   DmaTile dd;
   dd.init(dobase, p.dout.ss, S, wave, lane);
   float lreg = 0.f;  // thread t < 64: l2 of query q0 + t; 64 <= t < 128: delta of q0 + t - 64
-  auto load_tile = [&](int qt, char* sD) {
+  auto load_tile = [&](int qt, char* sQ, char* sD) {
     const int q0 = qt * BMQ;
-    sq.load(qbase, p.q.ss, tab, q0, S);
+    dqr.issue(sQ, q0, wave);
     dd.issue(sD, q0, wave);
     if (tid < 2 * BMQ) {
       const int i = q0 + (tid & (BMQ - 1));
@@ -499,8 +521,7 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
       }
     }
   };
-  auto store_tile = [&](char* sQ, float* sL) {
-    sq.store(sQ);
+  auto store_tile = [&](float* sL) {
     if (tid < 2 * BMQ) sL[tid] = lreg;
   };
   const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
@@ -605,8 +626,8 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   // barriers: two per tile.
   int qt = next_tile(qt_begin);
   if (qt < nqt) {
-    load_tile(qt, sd0);
-    store_tile(sq0, sl0);
+    load_tile(qt, sq0, sd0);
+    store_tile(sl0);
   }
   wait_vmem_and_sync();
   frag pf[2], sf[2];
@@ -624,9 +645,9 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
       softmax(qt, sL, sacc, dpacc, pf, sf);
       __syncthreads();
       const int qtn = next_tile(qt + 1);
-      if (qtn < nqt) load_tile(qtn, sDn);
+      if (qtn < nqt) load_tile(qtn, sQn, sDn);
       cols(sQ, sD, pf, sf);
-      if (qtn < nqt) store_tile(sQn, sLn);
+      if (qtn < nqt) store_tile(sLn);
       wait_vmem_and_sync();
       qt = qtn;
     };
@@ -648,11 +669,11 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
       if (has_prev) cols(sQp, sDp, pf, sf);
       __syncthreads();
       const int qtn = next_tile(qt + 1);
-      if (qtn < nqt) load_tile(qtn, sDp);
+      if (qtn < nqt) load_tile(qtn, sQp, sDp);
       f32x4 sacc[4], dpacc[4];
       rows(sQ, sD, sacc, dpacc);
       softmax(qt, sL, sacc, dpacc, pf, sf);
-      if (qtn < nqt) store_tile(sQp, sLp);
+      if (qtn < nqt) store_tile(sLp);
       wait_vmem_and_sync();
       has_prev = true;
       qt = qtn;
@@ -697,13 +718,14 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
 template <typename T, int MASK, bool CAUSAL>
 static int launch_bwd16_t(const BwdParams& p, void* stream) {
   const int S = p.shp.S, BH = p.shp.B * p.shp.H;
-  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL>), dim3(((S + 127) / 128) * BH), dim3(512), 0,
+  // dQ first: it also writes Q' for the dK/dV kernel.  Causal: two query tiles of one head
+  // per workgroup (see the kernel)
+  const int grid_q = CAUSAL ? ((S + 127) / 128 + 1) / 2 * BH : ((S + 127) / 128) * BH;
+  hipLaunchKernelGGL((dq16_kernel<T, MASK, CAUSAL>), dim3(grid_q), dim3(512), 0,
                      (hipStream_t)stream, p);
   int e = (int)hipGetLastError();
   if (e) return e;
-  // causal: two query tiles of one head per workgroup (see the kernel)
-  const int grid_q = CAUSAL ? ((S + 127) / 128 + 1) / 2 * BH : ((S + 127) / 128) * BH;
-  hipLaunchKernelGGL((dq16_kernel<T, MASK, CAUSAL>), dim3(grid_q), dim3(512), 0,
+  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL>), dim3(((S + 127) / 128) * BH), dim3(512), 0,
                      (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }

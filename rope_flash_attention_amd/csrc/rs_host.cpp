@@ -170,7 +170,7 @@ rs_status validate_args(const rs_args* a, Shape* out) {
 }
 
 struct Layout {
-  size_t ctrl, table, tiles, delta, qc, kc, qs, ks, part, cnt, total;
+  size_t ctrl, table, tiles, delta, qrot, qc, kc, qs, ks, part, cnt, total;
   int64_t nqt, nkt;
   int64_t sp, nblk;  // int8 variant: padded rows per (b, h) slice and 64-token blocks
   SplitPlan split;   // forward only: work split over the current device's workgroups
@@ -191,6 +191,8 @@ Layout layout(const Shape& s, int mask_kind, bool backward, bool int8, bool caus
   }
   L.delta = off;
   if (backward) off += round_up((size_t)(s.B * s.H * s.S) * sizeof(float), 256);
+  L.qrot = off;
+  if (backward && s.dtype != F32 && s.D == 128) off += round_up((size_t)(s.B * s.H * s.S * s.D) * 2, 256);
   if (int8) {
     L.nblk = (s.S + 63) / 64;
     L.sp = L.nblk * 64;
@@ -501,6 +503,7 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   p.dv_ss = dv->stride[2];
   p.lse = lse;
   p.delta = (float*)(w + L.delta);
+  p.qrot = w + L.qrot;
   p.tab.ptr = (const float*)(w + L.table);
   p.tab.sb = s.Bt > 1 ? s.S * s.D : 0;
   p.mask = mask_view(a, s, L, w);

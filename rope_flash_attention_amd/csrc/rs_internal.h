@@ -84,6 +84,8 @@ struct BwdParams {
   int64_t dv_sb, dv_sh, dv_ss;
   const float* lse;  // contiguous [B, H, S]
   float* delta;      // workspace, contiguous [B, H, S]
+  void* qrot;        // workspace (16-bit inputs, D = 128): Q' = R(Q) [B, H, S, D] in the input
+                     // dtype, written by the dQ kernel and read by the dK/dV kernel
   Table tab;
   MaskView mask;
   AttnShape shp;

@@ -220,7 +220,12 @@ def test_workspace_size_layout():
     table = 100 * 128 * 4  # (cos, sin) pairs: D/2 float2 per position
     assert n == 256 + -(-table // 256) * 256
     st, nb = c.ws_size(1)
-    assert st == 0 and nb == n + -(-(2 * 3 * 100 * 4) // 256) * 256
+    # backward: + delta (fp32 per row) + Q' = R(Q) in the input dtype (16-bit, D = 128)
+    assert st == 0 and nb == n + -(-(2 * 3 * 100 * 4) // 256) * 256 + -(-(2 * 3 * 100 * 128 * 2) // 256) * 256
+    f = Call(B=2, H=3, S=100, D=128, dt=RS_F32, es=4)
+    st, nf = f.ws_size(0)
+    st2, nfb = f.ws_size(1)
+    assert st == 0 and st2 == 0 and nfb == nf + -(-(2 * 3 * 100 * 4) // 256) * 256  # fp32: no Q'
     _bool_mask(c, (2, 1, 1, 100), (112, 0, 0, 1))
     st, nm = c.ws_size(0)
     assert st == 0 and nm == n + 256  # 2 x 1 x 1 x 2 tile states, padded
