@@ -172,25 +172,38 @@ struct RotStager {
   }
 };
 
-// Q' = R(Q) of one row in the input dtype (D = 128; this lane's four 8-element chunks
-// 32t + 8g), as RotStager rounds it: the dQ kernel writes these rows for the dK/dV kernel,
-// whose tiles then hold exactly the values it would rotate itself.
+// row_frags<T, true> for a Q row that also writes Q' = R(Q) (unscaled, in the input dtype,
+// rounded as RotStager rounds it) to `dst` unless it is null: the dQ kernel writes these rows
+// for the dK/dV kernel, whose tiles then hold exactly the values it would rotate itself.
+// Every load is issued before the first store (a store in between would make the compiler
+// issue the later loads again, one round trip each).
 template <typename T>
-__device__ inline void store_rot_row(T* dst, const T* row, const float* trow, int g) {
+__device__ inline void row_frags_qrot(typename Mf<T>::frag* f, T* dst, const T* row, const float* trow, int g,
+                                      float mul) {
   typedef T v8 __attribute__((ext_vector_type(8)));
+  v8 x[4];
+  float4 ta[4], tb[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int d0 = 32 * t + 8 * g;
-    v8 x = *(const v8*)(row + d0);
-    const float4 a = *(const float4*)(trow + d0), b = *(const float4*)(trow + d0 + 4);
-    const float cc[4] = {a.x, a.z, b.x, b.z}, ss[4] = {a.y, a.w, b.y, b.w};
+    x[t] = *(const v8*)(row + d0);
+    ta[t] = *(const float4*)(trow + d0);
+    tb[t] = *(const float4*)(trow + d0 + 4);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float cc[4] = {ta[t].x, ta[t].z, tb[t].x, tb[t].z}, ss[4] = {ta[t].y, ta[t].w, tb[t].y, tb[t].w};
+    v8 y, z;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      const float2 r = rot_fma(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), cc[pp], ss[pp]);
-      x[2 * pp] = from_f<T>(r.x);
-      x[2 * pp + 1] = from_f<T>(r.y);
+      const float2 r = rot_fma(to_f(x[t][2 * pp]), to_f(x[t][2 * pp + 1]), cc[pp], ss[pp]);
+      y[2 * pp] = from_f<T>(r.x * mul);
+      y[2 * pp + 1] = from_f<T>(r.y * mul);
+      z[2 * pp] = from_f<T>(r.x);
+      z[2 * pp + 1] = from_f<T>(r.y);
     }
-    *(v8*)(dst + d0) = x;
+    f[t] = y;
+    if (dst) *(v8*)(dst + 32 * t + 8 * g) = z;
   }
 }
 
@@ -258,9 +271,9 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
   const float* tab = p.tab.ptr + b * p.tab.sb;
 
   frag qf[4], gf[4];
-  const T* qrow = (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh + (int64_t)mc * p.q.ss;
-  row_frags<T, true>(qf, qrow, tab + (int64_t)mc * D, g, p.shp.scale_log2);
-  if (m < S) store_rot_row<T>((T*)p.qrot + ((int64_t)bh * S + m) * D, qrow, tab + (int64_t)mc * D, g);
+  row_frags_qrot<T>(qf, m < S ? (T*)p.qrot + ((int64_t)bh * S + m) * D : nullptr,
+                    (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh + (int64_t)mc * p.q.ss, tab + (int64_t)mc * D, g,
+                    p.shp.scale_log2);
   row_frags<T, false>(gf, (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh + (int64_t)mc * p.dout.ss, nullptr,
                       g, 1.f);
   const int64_t rowid = ((int64_t)b * p.shp.H + hd) * S + mc;
