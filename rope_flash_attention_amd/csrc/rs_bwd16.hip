@@ -11,10 +11,12 @@
 //            scale log2 e) and dO stay in registers as B operands; K' is rotated on its way
 //            into LDS and V goes straight from memory into LDS; per 64-key tile
 //            S'^T = K' Q'^T, dP^T = V dO^T (row reads), dQ'^T += K'^T dS^T (transposed reads).
+//            Launched first: it also writes its rows of Q' (unscaled, in the input dtype) to
+//            the workspace for dkdv16.
 //  * dkdv16: workgroup = 128 keys (16 per wave); K' (times scale log2 e) and V stay in
-//            registers; Q' (rotated) and dO tiles of 64 queries stream through LDS; per tile
-//            S' = Q' K'^T, dP = dO V^T, dV^T += dO^T P, dK'^T += Q'^T dS; waves 0-3 and
-//            4-7 work half a tile apart (two barriers per tile, see the kernel).
+//            registers; Q' (from dq16) and dO tiles of 64 queries go straight from memory
+//            into LDS; per tile S' = Q' K'^T, dP = dO V^T, dV^T += dO^T P, dK'^T += Q'^T dS;
+//            waves 0-3 and 4-7 work half a tile apart (two barriers per tile, see the kernel).
 // The score rows are read in a permuted order so that the four accumulator rows a lane holds
 // in two consecutive 16-row blocks are eight consecutive contraction indices of the next
 // product: P and dS go from accumulators to B operands without leaving registers.
@@ -127,7 +129,7 @@ __device__ inline void row_frags(typename Mf<T>::frag* f, const T* row, const fl
   }
 }
 
-// Staging of a 64-row tile that needs rotation (K for dq16, Q for dkdv16): each of the 512
+// Staging of a 64-row tile that needs rotation (K for dq16): each of the 512
 // threads loads two 16-byte chunks and their table pairs into registers, rotates them and
 // writes them swizzled.
 template <typename T>
