@@ -555,7 +555,7 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) dpacc[qb] = M::mma(ga[t], vf[t], t == 0 ? z4 : dpacc[qb]);
     }
-    sched_reads_ahead<32, 1, 8, 0>();
+    sched_reads_ahead<32, 1, 16, 0>();
   };
   // P and dS of query tile qt (l2 and delta in sL) as B fragments
   auto softmax = [&](int qt, const float* sL, f32x4* sacc, f32x4* dpacc, frag* pf_out, frag* sf_out)
