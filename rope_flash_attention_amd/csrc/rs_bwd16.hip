@@ -361,7 +361,7 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) dpacc[kb] = M::mma(va[t], gf[t], t == 0 ? z4 : dpacc[kb]);
     }
-    sched_reads_ahead<32, 1, 8, 0>();
+    sched_reads_ahead<32, 1, 12, 0>();
 
     // exclusions (keys past the end, causal, masks), P and dS
     if constexpr (MASK == MASK_ADD) {
