@@ -10,10 +10,12 @@
  *
  * with M from a bool mask (True = attend) or an additive float mask, broadcast over up to
  * four dimensions (same page, section "Enable In SimpleTuner"), or a causal (top-left,
- * key j > query i excluded) pattern.  The rotation happens inside the attention kernels:
- * no rotated copy of Q or K is ever written to memory.  The backward returns gradients
- * with respect to the unrotated Q and K (the inverse rotation, i.e. the same rotation with
- * sin negated, applied to dQ' and dK'), and V.
+ * key j > query i excluded) pattern.  The forward rotates Q and K inside the attention
+ * kernel, in registers: it writes no rotated copy of Q or K to memory.  The backward rotates
+ * each Q row once, in its dQ kernel, and leaves Q' = R(Q), rounded to the input dtype, in the
+ * caller's workspace ([B, H, S, D], 16-bit inputs at D = 128) for its dK/dV kernel; K' is
+ * never written.  The backward returns gradients with respect to the unrotated Q and K (the
+ * inverse rotation, i.e. the same rotation with sin negated, applied to dQ' and dK'), and V.
  *
  * Conventions for every entry point
  *  - All tensors are described by rs_tensor: a DEVICE pointer, a dtype and four sizes and

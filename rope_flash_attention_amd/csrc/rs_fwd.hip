@@ -27,6 +27,7 @@
 //    device) lets all-false tiles be skipped and all-true tiles run without mask reads;
 //    causal tiles above the diagonal are never visited.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "rs_device.hpp"
@@ -140,7 +141,9 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 
   // ---- work decomposition ----------------------------------------------------------------
   // A unit is one (b, h, query tile) over all its key tiles.  Without split, workgroup w
-  // runs unit w.  With split (uniform key-tile counts: no causal, no bool mask), the first
+  // runs unit w.  With split (no causal; bool masks may skip all-false key tiles, so their
+  // pieces can be shorter than planned, or empty: an empty piece writes O = 0 and LSE = -inf,
+  // which the merge weighs as zero), the first
   // split_full workgroups run one whole unit each and the remaining units' (unit, key tile)
   // iterations are cut into split_grid equal contiguous ranges, one per further workgroup
   // (these start as the whole units finish, so the cut units' work is spread over the whole
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // processed as pieces, each writing its normalized output and row log-sum-exp to a slot,
   // which fwd_merge_kernel then combines.
   const int nkt_all = (S + BN - 1) / BN;
-  constexpr bool kCanSplit = !CAUSAL && MASK != MASK_BOOL;
+  constexpr bool kCanSplit = !CAUSAL;
 
   // one piece: key tiles [t0, t1) of unit `item` (t1 < 0: the unit's whole range); a cut
   // piece writes to slot `slot` (workgroup w of the ranges owns slots 2w and 2w + 1)
@@ -922,19 +925,50 @@ static int resident_per_cu() {
   return n;
 }
 
+// Resident forward workgroups per CU and CU count, queried once per (device, variant) and
+// kept: the split planner runs on every forward call (and on every workspace query).
+static int resident_per_cu_query(int dtype, int D, bool int8) {
+  const bool d64 = D == 64;
+  if (dtype == F32) return d64 ? resident_per_cu<float, 64, false>() : resident_per_cu<float, 128, false>();
+  if (dtype == F16)
+    return int8 ? (d64 ? resident_per_cu<_Float16, 64, true>() : resident_per_cu<_Float16, 128, true>())
+                : (d64 ? resident_per_cu<_Float16, 64, false>() : resident_per_cu<_Float16, 128, false>());
+  return int8 ? (d64 ? resident_per_cu<__bf16, 64, true>() : resident_per_cu<__bf16, 128, true>())
+              : (d64 ? resident_per_cu<__bf16, 64, false>() : resident_per_cu<__bf16, 128, false>());
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_occ_mu;
+int g_occ_cus[kMaxDevices] = {0};
+int g_occ_per[kMaxDevices][12] = {{0}};  // [dtype (3) x D (2) x int8 (2)], 0 = not queried yet
+}  // namespace
+
+static bool occupancy(int dtype, int D, bool int8, int* cus, int* per) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  const int key = (dtype % 3) * 4 + (D == 64 ? 2 : 0) + (int8 ? 1 : 0);
+  std::lock_guard<std::mutex> lk(g_occ_mu);
+  if (g_occ_cus[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) return false;
+    g_occ_cus[dev] = c;
+  }
+  if (g_occ_per[dev][key] == 0) {
+    const int n = resident_per_cu_query(dtype, D, int8);
+    if (n <= 0) return false;
+    g_occ_per[dev][key] = n;
+  }
+  *cus = g_occ_cus[dev];
+  *per = g_occ_per[dev][key];
+  return true;
+}
+
 SplitPlan fwd_split_plan(int dtype, int D, bool int8, bool causal, int mask_kind, int64_t units, int nkt) {
   SplitPlan sp{};
-  if (causal || mask_kind == MASK_BOOL || units <= 0 || nkt < 16) return sp;
-  int dev = -1, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return sp;
-  const bool d64 = D == 64;
-  int per = 0;
-  if (dtype == F32) per = d64 ? resident_per_cu<float, 64, false>() : resident_per_cu<float, 128, false>();
-  else if (dtype == F16) per = int8 ? (d64 ? resident_per_cu<_Float16, 64, true>() : resident_per_cu<_Float16, 128, true>())
-                                    : (d64 ? resident_per_cu<_Float16, 64, false>() : resident_per_cu<_Float16, 128, false>());
-  else per = int8 ? (d64 ? resident_per_cu<__bf16, 64, true>() : resident_per_cu<__bf16, 128, true>())
-                  : (d64 ? resident_per_cu<__bf16, 64, false>() : resident_per_cu<__bf16, 128, false>());
+  if (causal || units <= 0 || nkt < 16) return sp;
+  int cus = 0, per = 0;
+  if (!occupancy(dtype, D, int8, &cus, &per)) return sp;
   const int64_t g = (int64_t)cus * per & ~(int64_t)7;  // resident workgroups, a multiple of 8
   if (g < 8) return sp;
   const int64_t full = units / g * g, cut = units - full;

@@ -27,3 +27,20 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With RS_GRAD_REPORT=<path>, write the achieved gradient error ratios of every bf16/fp16
+    gradient check (test, tensor, max|err|/RMS, RMS(err)/RMS, bf16 rounding floor)."""
+    path = os.environ.get("RS_GRAD_REPORT")
+    if not path:
+        return
+    try:
+        from parity_util import GRAD_REPORT
+    except Exception:
+        return
+    import json
+
+    with open(path, "w") as f:
+        for row in GRAD_REPORT:
+            f.write(json.dumps(row) + "\n")

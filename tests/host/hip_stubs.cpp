@@ -1,0 +1,121 @@
+// Host-only stand-ins for the HIP runtime calls and kernel launchers of the library, so that
+// its host code (argument validation, workspace layout, parameter blocks) can be built with
+// g++ under AddressSanitizer / UndefinedBehaviorSanitizer and run without a GPU.
+//
+// The launchers launch nothing.  They count calls and check that every pointer the host code
+// derived from the caller's workspace lies inside it, with room for what the kernel writes
+// or reads there; a violation aborts the run.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "rs_internal.h"
+
+namespace stub {
+const char* ws_lo = nullptr;  // the workspace of the call in progress (set by the driver)
+size_t ws_bytes = 0;
+int launches = 0;
+bool no_device = false;
+
+void need(const void* p, size_t bytes, const char* what) {
+  const char* c = (const char*)p;
+  if (!ws_lo || c < ws_lo || c + bytes > ws_lo + ws_bytes) {
+    std::fprintf(stderr, "workspace range violated: %s [%p, +%zu) outside [%p, +%zu)\n", what, p, bytes,
+                 (const void*)ws_lo, ws_bytes);
+    std::abort();
+  }
+}
+}  // namespace stub
+
+extern "C" {
+hipError_t hipGetDevice(int* dev) {
+  if (stub::no_device) return hipErrorNoDevice;
+  *dev = 0;
+  return hipSuccess;
+}
+hipError_t hipGetDevicePropertiesR0600(hipDeviceProp_tR0600* prop, int) {
+  std::memset(prop, 0, sizeof(*prop));
+  std::strcpy(prop->gcnArchName, "gfx950:sramecc+:xnack-");
+  return hipSuccess;
+}
+hipError_t hipDeviceSynchronize(void) { return hipSuccess; }
+}
+
+namespace rs {
+
+int fwd_block_m(int dtype) { return dtype == F32 ? 128 : 256; }
+int fwd_block_n(int dtype) { return dtype == F32 ? 32 : 64; }
+
+// A split plan of the same form as the device planner's (whole units, then ranges of the
+// remaining units' key tiles over further workgroups) on a pretend 8-workgroup device, so
+// that the layout of the pieces' slots is exercised.
+SplitPlan fwd_split_plan(int dtype, int D, bool, bool causal, int, int64_t units, int nkt) {
+  SplitPlan sp{};
+  if (causal || units <= 8 || units % 8 == 0 || nkt < 4) return sp;
+  sp.full = (int)(units / 8 * 8);
+  sp.cut_units = units - sp.full;
+  sp.grid = 8;
+  sp.iters = sp.cut_units * nkt;
+  sp.slot_bytes = (size_t)fwd_block_m(dtype) * D * (dtype == F32 ? 4 : 2);
+  return sp;
+}
+
+int launch_pack_tables(const PackParams& p, void*) {
+  ++stub::launches;
+  stub::need(p.out, (size_t)p.Bt * p.S * p.D * sizeof(float), "packed tables");
+  stub::need(p.ctrl, 2 * sizeof(unsigned), "control words");
+  return 0;
+}
+
+int launch_classify(const ClassifyParams& p, void*) {
+  ++stub::launches;
+  const int64_t nq = (p.Sq + kMaskTile - 1) / kMaskTile, nk = (p.Sk + kMaskTile - 1) / kMaskTile;
+  stub::need(p.tiles, (size_t)(p.nb * p.nh * nq * nk), "mask tile states");
+  stub::need(p.ctrl, 2 * sizeof(unsigned), "control words");
+  if (p.total_blocks != p.nb * p.nh * nq * nk) std::abort();
+  return 0;
+}
+
+int launch_fwd(int dtype, int D, int, bool, bool int8, const FwdParams& p, void*) {
+  ++stub::launches;
+  const int B = p.shp.B, H = p.shp.H, S = p.shp.S;
+  stub::need(p.tab.ptr, (size_t)(p.tab.sb ? B : 1) * S * D * sizeof(float), "packed tables");
+  if (p.mask.tiles) stub::need(p.mask.tiles, 1, "mask tile states");
+  if (int8) {
+    const size_t codes = (size_t)B * H * p.sp * D;
+    stub::need(p.qc, codes, "q codes");
+    stub::need(p.kc, codes, "k codes");
+    stub::need(p.qsc, (size_t)B * H * (p.sp / 64) * sizeof(float), "q scales");
+    stub::need(p.ksc, (size_t)B * H * (p.sp / 64) * sizeof(float), "k scales");
+  }
+  if (p.split_iters > 0) {
+    const size_t bm = (size_t)fwd_block_m(dtype), es = dtype == F32 ? 4 : 2;
+    stub::need(p.part_o, 2 * (size_t)p.split_grid * bm * D * es, "pieces' outputs");
+    stub::need(p.part_lse, 2 * (size_t)p.split_grid * bm * sizeof(float), "pieces' LSE");
+  }
+  return 0;
+}
+
+int launch_quant_int8(int, const QuantParams& p, void*) {
+  ++stub::launches;
+  stub::need(p.tab.ptr, (size_t)(p.tab.sb ? p.B : 1) * p.S * p.D * sizeof(float), "packed tables");
+  return 0;
+}
+
+int launch_bwd(int dtype, int D, int, bool, const BwdParams& p, void*) {
+  ++stub::launches;
+  const int B = p.shp.B, H = p.shp.H, S = p.shp.S;
+  stub::need(p.tab.ptr, (size_t)(p.tab.sb ? B : 1) * S * D * sizeof(float), "packed tables");
+  stub::need(p.delta, (size_t)B * H * S * sizeof(float), "delta");
+  if (dtype != F32 && D == 128) stub::need(p.qrot, (size_t)B * H * S * D * 2, "rotated Q");
+  return 0;
+}
+
+int read_all_true_counter(uint64_t* value, bool) {
+  *value = 0;
+  return 0;
+}
+
+}  // namespace rs

@@ -4,8 +4,10 @@ with the CPU float64 oracle on identical seeded inputs.
 Tolerances (per tensor, in the tests):
   fp32 outputs/LSE : max|gpu - ref| <= 1e-5 * max|ref|
   bf16/fp16 outputs: max|gpu - ref| <= 2e-2 * max|ref|   (fp16 uses the bf16 bound)
-  bf16/fp16 grads  : rms(gpu - ref) <= 5e-2 * rms(ref), and max|gpu - ref| <= 0.5 * rms(ref)
-                     (the bound is read as an RMS ratio: see tests/test_tolerance_reading.py)
+  bf16/fp16 grads  : rms(gpu - ref) <= 5e-2 * rms(ref), and
+                     max|gpu - ref| <= 2 max(5e-2, floor) * rms(ref), floor = the bf16 rounding
+                     error of the exact gradient (see check_grad and
+                     tests/test_tolerance_reading.py)
   fp32 grads       : max|gpu - ref| <= 1e-5 * max|ref|
 """
 from __future__ import annotations
@@ -17,7 +19,6 @@ import rope_flash_attention_amd as rfa
 
 OUT_TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2}
 GRAD_TOL = {"bf16": 5e-2, "f16": 5e-2}
-GRAD_MAX_GUARD = 0.5
 GRAD_TOL_F32 = 1e-5
 
 
@@ -82,18 +83,39 @@ def check_lse(got, ref, dtype):
     return 0.0
 
 
+GRAD_REPORT = []  # (test, tensor, max|err|/RMS, RMS(err)/RMS, bf16 rounding floor) per check
+
+
+def _bf16_floor(ref, rms):
+    """max|bf16(ref) - ref| / RMS(ref): the error of the best bf16 answer."""
+    r = torch.from_numpy(np.ascontiguousarray(ref)).to(torch.float32).to(torch.bfloat16).double().numpy()
+    return float(np.abs(r - ref).max() / rms)
+
+
 def check_grad(name, got, ref, dtype):
+    """fp32: max|err| <= 1e-5 max|grad|.  bf16/fp16: RMS(err) <= 5e-2 RMS(grad), and
+    max|err| <= 2 max(5e-2, floor) RMS(grad) with floor = max|bf16(grad) - grad| / RMS(grad).
+    The stated max|err| <= 5e-2 RMS reading is out of reach of a backward on bf16 matrix
+    products: tests/test_tolerance_reading.py shows the exact arithmetic with only the bf16
+    operand and output roundings such products force already exceeding it (FLUX training
+    shape), and the bf16 rounding of the exact gradient alone exceeding it (causal shape)."""
+    import os
+
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     if dtype == "f32":
         e = rel_max_err(got, ref)
         assert e <= GRAD_TOL_F32, f"{name}: relative max error {e:.3e} > {GRAD_TOL_F32}"
-    else:
-        ref = np.asarray(ref, dtype=np.float64)
-        rms = np.sqrt((ref ** 2).mean())
-        rms = rms if rms > 0 else 1.0
-        d = np.asarray(got, dtype=np.float64) - ref
-        e = np.sqrt((d ** 2).mean()) / rms
-        emax = np.abs(d).max() / rms
-        assert e <= GRAD_TOL[dtype], f"{name}: error RMS {e:.3e} of the gradient RMS > {GRAD_TOL[dtype]}"
-        assert emax <= GRAD_MAX_GUARD, f"{name}: max error {emax:.3e} of the gradient RMS > {GRAD_MAX_GUARD}"
+        return e
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt((ref ** 2).mean())
+    rms = rms if rms > 0 else 1.0
+    d = np.asarray(got, dtype=np.float64) - ref
+    e = np.sqrt((d ** 2).mean()) / rms
+    emax = np.abs(d).max() / rms
+    floor = _bf16_floor(ref, rms)
+    GRAD_REPORT.append((os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], name, emax, e, floor))
+    guard = 2.0 * max(GRAD_TOL[dtype], floor)
+    assert e <= GRAD_TOL[dtype], f"{name}: error RMS {e:.3e} of the gradient RMS > {GRAD_TOL[dtype]}"
+    assert emax <= guard, (f"{name}: max error {emax:.3e} of the gradient RMS > {guard:.3e} "
+                           f"(bf16 rounding of the exact gradient alone: {floor:.3e})")
     return e

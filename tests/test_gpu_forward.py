@@ -162,15 +162,17 @@ def test_forward_is_deterministic():
 
 
 def test_large_logits_stress():
-    """Q, K ~ N(0, 4^2): logits 16x larger.  Rounding the rotated Q', K' to bf16 perturbs each
-    logit in proportion to its size, so the output bound scales with the input spread:
-    2e-2 * 4 here."""
+    """Q, K ~ N(0, 4^2): logits 16x larger.  Any kernel that feeds the rotated, scaled Q' and
+    K' to bf16 matrix cores perturbs each logit in proportion to its size; the CPU pin
+    tests/test_tolerance_reading.py::test_large_logit_output_bound shows that this rounding
+    alone moves O by more than the 2e-2 bound (between 2e-2 and 4e-2 of max|O|), so O is held
+    to twice the pinned rounding error, 8e-2.  LSE keeps the stated 2e-2 bound."""
     w = syn.random_small(1, 2, 200, 128, "bf16", seed=26, std=4.0)
     o, lse = gpu_forward(w)
     O_ref, L_ref = rope_sdpa_forward(w.q, w.k, w.v, w.cos, w.sin)
     e = np.abs(to64(o) - O_ref).max() / np.abs(O_ref).max()
     assert e <= 8e-2, e
-    assert np.abs(to64(lse) - L_ref).max() / np.abs(L_ref).max() <= 8e-2
+    check_lse(to64(lse), L_ref, "bf16")
 
 
 def test_explicit_scale():
@@ -198,12 +200,6 @@ def test_rejects_mixed_dtypes_without_launching():
 
 # ---- full-size FLUX shapes: every head runs on the GPU, sampled rows are checked -----------
 
-def _sample_rows(S, n, seed):
-    rs = np.random.default_rng(seed)
-    fixed = [0, 1, 511, 512, 513, S - 1]
-    return np.unique(np.concatenate([fixed, rs.choice(S, n, replace=False)]))
-
-
 def test_flux_forward_full_size_all_heads():
     """The timed workload in full: B=1, H=24, S=512+4096, D=128, bf16, every head and row of
     O and LSE against the oracle (the launch the benchmark times, with LSE requested)."""
@@ -212,8 +208,10 @@ def test_flux_forward_full_size_all_heads():
 
 
 @pytest.mark.parametrize("variant", ["bool_padding", "additive_4d", "all_true"])
-def test_flux_masked_full_size_sampled(variant):
-    """B=2 FLUX shape with a key-padding mask on the text tokens (lengths U{64..512})."""
+def test_flux_masked_full_size_all_heads(variant):
+    """B=2 FLUX shape with a key-padding mask on the text tokens (lengths U{64..512}): every
+    (b, h) and every row of O and LSE against the oracle, for the bool [B,1,1,S] mask, the
+    same pattern as an additive 0/-inf bf16 [B,H,S,S] mask, and an all-true bool mask."""
     w = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=3000)
     S = w.q.shape[2]
     lens = syn.key_padding_lengths(3000, 2)
@@ -224,16 +222,24 @@ def test_flux_masked_full_size_sampled(variant):
         w.mask, w.mask_kind = syn.expand_additive(m, 24, S, "bf16"), "additive"
     else:
         w.mask, w.mask_kind = torch.ones_like(m), "bool"
-    rows = _sample_rows(S, 26, 2)
-    _compare(w, rows=rows, pairs=[(0, 3), (1, 17)])
+    _compare(w)
 
 
-def test_long_sequence_sampled():
-    """B=1, H=48, S=512+16384, D=128, bf16, 3-axis RoPE."""
+def test_flux_all_true_mask_full_size_is_bitwise_no_mask():
+    """At the FLUX B=2 shape an all-true bool mask takes the unmasked schedule (same cut of
+    the last round's units): O and LSE equal the unmasked call's bit for bit."""
+    w = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=3000)
+    o0, l0 = gpu_forward(w)
+    w.mask, w.mask_kind = torch.ones(2, 1, 1, w.q.shape[2], dtype=torch.bool), "bool"
+    o1, l1 = gpu_forward(w)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+def test_long_sequence_two_full_heads():
+    """B=1, H=48, S=512+16384, D=128, bf16, 3-axis RoPE: all 48 heads run on the GPU; heads
+    0 and 47 are compared whole (every row of O and LSE) against the oracle."""
     w = syn.flux(batch=1, heads=48, grid=128, dtype="bf16", seed=5000)
-    rows = _sample_rows(w.q.shape[2], 26, 3)
-    _compare(w, rows=rows, pairs=[(0, 0), (0, 47)])
-
+    _compare(w, pairs=[(0, 0), (0, 47)])
 
 
 # ---- additive masks in the input dtype, S a multiple of 8 -----------------------------------

@@ -146,3 +146,52 @@ def test_f32_rotation_close_to_f64():
     r64 = rope_rotate(x.astype(np.float64), cos, sin)
     assert r32.dtype == np.float32
     np.testing.assert_allclose(r32, r64, rtol=0, atol=4 * np.finfo(np.float32).eps * np.abs(x).max())
+
+
+def _rot_f32_torch(x, c, s):
+    """The fp32 rotation evaluated independently with torch float32 elementwise operations on
+    the CPU: two products, each rounded to fp32, then their difference / sum, rounded once."""
+    x = torch.as_tensor(np.asarray(x, dtype=np.float32))
+    c = torch.as_tensor(np.asarray(c, dtype=np.float32))
+    s = torch.as_tensor(np.asarray(s, dtype=np.float32))
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    c0, s0 = c[..., 0::2], s[..., 0::2]
+    out = torch.empty_like(x)
+    p0, p1 = torch.mul(x0, c0), torch.mul(x1, s0)
+    out[..., 0::2] = torch.sub(p0, p1)
+    p2, p3 = torch.mul(x0, s0), torch.mul(x1, c0)
+    out[..., 1::2] = torch.add(p2, p3)
+    return out.numpy()
+
+
+def test_f32_rotation_bitwise_matches_torch_float32_ops():
+    """rope_rotate_f32 decides the int8 codes, so its exact rounding is pinned, not only its
+    closeness to float64: bit for bit against torch float32 elementwise ops."""
+    rs = np.random.default_rng(81)
+    x = rs.standard_normal((2, 3, 96, 128)).astype(np.float32) * rs.uniform(0.01, 50, (2, 3, 1, 1)).astype(np.float32)
+    cos, sin = syn.rope_tables(syn.flux_ids(32, 8), (16, 56, 56), 10000.0)
+    got = rope_rotate_f32(x, cos, sin)[0:2]
+    ref = _rot_f32_torch(x, cos.numpy()[None, None], sin.numpy()[None, None])
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_f32_rotation_rounds_each_product_no_fma():
+    """Inputs built so that one rounding of a fused multiply-add and two roundings of
+    product-then-difference give different fp32 results:
+      x0 = c = 1 + 2^-12: x0 c = 1 + 2^-11 + 2^-24 is a tie in fp32 and rounds to even,
+      1 + 2^-11; x1 = 1 + 2^-11, s = 1.  Rounded products: x0 c - x1 s = 0 exactly, while a
+      fused form would keep the 2^-24.  The second element: x0 s + x1 c with the same values
+      = (1 + 2^-12) + (1 + 2^-11)(1 + 2^-12), product 1 + 2^-11 + 2^-12 + 2^-23 rounded
+      to fp32 (exact: it has 24 significant bits), sum 2 + 2^-11 + 2^-11 + 2^-23, rounded
+      to fp32 at spacing 2^-22: 2 + 2^-10 + 2^-23 is a tie, to even gives 2 + 2^-10."""
+    a = np.float32(1 + 2.0 ** -12)
+    b = np.float32(1 + 2.0 ** -11)
+    x = np.array([[[[a, b]]]], dtype=np.float32)
+    cos = np.array([[a, a]], dtype=np.float32)
+    sin = np.array([[1.0, 1.0]], dtype=np.float32)
+    got = rope_rotate_f32(x, cos, sin)[0, 0, 0]
+    assert got[0] == np.float32(0.0)
+    assert got[1] == np.float32(2 + 2.0 ** -10)
+    # a fused evaluation differs on the first element
+    fused0 = np.float32(float(a) * float(a) - float(b) * 1.0)
+    assert fused0 != got[0]

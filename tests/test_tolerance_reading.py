@@ -1,12 +1,17 @@
-"""Why the bf16 gradient tolerance is read as an RMS ratio (CPU only).
+"""Pins behind the tolerance readings of the GPU parity tests (CPU only).
 
-The parity bound for bf16 gradients is 5e-2 relative to the gradient RMS.  Read as
-max|error| / RMS(gradient), it cannot be met by ANY implementation that returns bf16
-gradients on the causal training shape: rounding the exact float64 gradient itself to
-bf16 already exceeds it, because a few gradient entries (e.g. dV of the first keys, which
-every causal query attends) are tens of RMS in size.  The tests therefore check
-RMS(error) / RMS(gradient) <= 5e-2, plus a max|error| <= 0.5 RMS guard against localized
-faults; this file pins the fact behind that choice.
+Gradients.  The parity bound for bf16 gradients is 5e-2 relative to the gradient RMS.
+Read as max|error| / RMS(gradient), it cannot be met by ANY implementation that returns
+bf16 gradients on the causal training shape: rounding the exact float64 gradient itself
+to bf16 already exceeds it, because a few gradient entries (e.g. dV of the first keys,
+which every causal query attends) are tens of RMS in size.  On the FLUX training shape
+the rounded exact gradient fits, but a backward on bf16 matrix products (which must round
+Q', K', P and dS to bf16) does not.  The tests therefore check RMS(error) / RMS(gradient)
+<= 5e-2, plus max|error| <= 2 max(5e-2, floor) RMS(gradient) against localized faults
+(floor = the bf16 rounding error of the exact gradient).
+
+Outputs.  With Q, K ~ N(0, 4^2) the bf16 rounding of the rotated Q' and K' alone moves O
+past the stated 2e-2 of max|O|; see test_large_logit_output_bound.
 """
 import numpy as np
 import torch
@@ -26,3 +31,67 @@ def test_exact_gradient_rounded_to_bf16_fails_max_reading_but_not_rms_reading():
         rms_ratio.append(np.sqrt(((gb - g) ** 2).mean()) / rms)
     assert max(max_ratio) > 5e-2          # the max reading is infeasible for bf16 outputs
     assert max(rms_ratio) < 5e-3          # output rounding alone uses < 1/10 of the RMS budget
+
+
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(torch.bfloat16).double().numpy()
+
+
+def test_large_logit_output_bound():
+    """Q, K ~ N(0, 4^2) (the large-logit GPU case): a bf16 matrix-core kernel must round the
+    rotated Q' (times scale log2 e) and K' to bf16 before QK^T.  That rounding alone, with
+    everything else exact, moves O by more than the stated 2e-2 of max|O| (so the stated
+    bound cannot hold there for any such kernel), but by less than 4e-2: the GPU test bounds
+    O by twice that, 8e-2.  LSE moves by far less, and keeps the stated 2e-2."""
+    import math
+
+    from oracle import attention_forward, rope_rotate, rope_sdpa_forward
+
+    w = syn.random_small(1, 2, 200, 128, "bf16", seed=26, std=4.0)
+    O_ref, L_ref = rope_sdpa_forward(w.q, w.k, w.v, w.cos, w.sin)
+    scale = 1.0 / math.sqrt(128)
+    c2 = scale * math.log2(math.e)
+    qr = rope_rotate(w.q, w.cos, w.sin)
+    kr = rope_rotate(w.k, w.cos, w.sin)
+    O_p, L_p = attention_forward(_bf16(qr * c2) / c2, _bf16(kr), w.v.double().numpy(), scale)
+    e_o = np.abs(O_p - O_ref).max() / np.abs(O_ref).max()
+    e_l = np.abs(L_p - L_ref).max() / np.abs(L_ref).max()
+    assert 2e-2 < e_o < 4e-2, e_o
+    assert e_l < 2e-2 / 4, e_l
+
+
+def test_bf16_matrix_operands_exceed_max_reading_on_flux_training_shape():
+    """On the non-causal FLUX training shape (B=2, H=24, S=4608, D=128) the exact gradient
+    rounded to bf16 stays within max|error| <= 5e-2 RMS(gradient), but a backward built on
+    bf16 matrix products cannot: it must round its operands Q' and K' (as the forward does),
+    P (for dV = P^T dO) and dS (for dQ' = dS K', dK' = dS^T Q') to bf16.  Emulated here in
+    float64 with exactly those roundings and bf16 outputs, everything else exact, head
+    (b, h) = (1, 5) exceeds the max reading on dK, while its RMS error stays near 4e-3."""
+    import math
+
+    from oracle import attention_forward, rope_rotate, rope_rotate_vjp, rope_sdpa_backward
+
+    w = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=4100, with_grad=True)
+    b, h = 1, 5
+    q, k, v, do = (t[b:b + 1, h:h + 1].double().numpy() for t in (w.q, w.k, w.v, w.do))
+    dq_ref, dk_ref, dv_ref = rope_sdpa_backward(q, k, v, w.cos, w.sin, do)
+    scale = 1.0 / math.sqrt(128)
+    qr, kr = rope_rotate(q, w.cos, w.sin)[0, 0], rope_rotate(k, w.cos, w.sin)[0, 0]
+    _, lse = attention_forward(qr[None, None], kr[None, None], v, scale)
+    qb, kb = _bf16(qr), _bf16(kr)
+    V, dO = v[0, 0], do[0, 0]
+    P = np.exp(scale * (qb @ kb.T) - lse[0, 0][:, None])
+    dP = dO @ V.T
+    delta = (P * dP).sum(axis=1)
+    dS = _bf16(P * (dP - delta[:, None]))
+    dq = _bf16(rope_rotate_vjp((scale * (dS @ kb))[None, None], w.cos, w.sin)[0, 0])
+    dk = _bf16(rope_rotate_vjp((scale * (dS.T @ qb))[None, None], w.cos, w.sin)[0, 0])
+    dv = _bf16(_bf16(P).T @ dO)
+    ratios = {}
+    for name, g, r in (("dQ", dq, dq_ref[0, 0]), ("dK", dk, dk_ref[0, 0]), ("dV", dv, dv_ref[0, 0])):
+        rms = np.sqrt((r ** 2).mean())
+        ratios[name] = (np.abs(g - r).max() / rms, np.sqrt(((g - r) ** 2).mean()) / rms,
+                        np.abs(_bf16(r) - r).max() / rms)
+    assert all(floor < 5e-2 for _, _, floor in ratios.values()), ratios
+    assert max(m for m, _, _ in ratios.values()) > 5e-2, ratios
+    assert all(e < 1e-2 for _, e, _ in ratios.values()), ratios
