@@ -7,8 +7,10 @@ to bf16 already exceeds it, because a few gradient entries (e.g. dV of the first
 which every causal query attends) are tens of RMS in size.  On the FLUX training shape
 the rounded exact gradient fits, but a backward on bf16 matrix products (which must round
 Q', K', P and dS to bf16) does not.  The tests therefore check RMS(error) / RMS(gradient)
-<= 5e-2, plus max|error| <= 2 max(5e-2, floor) RMS(gradient) against localized faults
-(floor = the bf16 rounding error of the exact gradient).
+<= 5e-2, plus max|error| <= 3 max(5e-2, floor) RMS(gradient) against localized faults
+(floor = the bf16 rounding error of the exact gradient; an otherwise exact bf16-product
+backward reaches up to ~2.5x the larger of the two, and a localized fault, e.g. a wrong
+tile, gives errors of the order of the gradient itself).
 
 Outputs.  With Q, K ~ N(0, 4^2) the bf16 rounding of the rotated Q' and K' alone moves O
 past the stated 2e-2 of max|O|; see test_large_logit_output_bound.
@@ -60,38 +62,67 @@ def test_large_logit_output_bound():
     assert e_l < 2e-2 / 4, e_l
 
 
-def test_bf16_matrix_operands_exceed_max_reading_on_flux_training_shape():
-    """On the non-causal FLUX training shape (B=2, H=24, S=4608, D=128) the exact gradient
-    rounded to bf16 stays within max|error| <= 5e-2 RMS(gradient), but a backward built on
-    bf16 matrix products cannot: it must round its operands Q' and K' (as the forward does),
-    P (for dV = P^T dO) and dS (for dQ' = dS K', dK' = dS^T Q') to bf16.  Emulated here in
-    float64 with exactly those roundings and bf16 outputs, everything else exact, head
-    (b, h) = (1, 5) exceeds the max reading on dK, while its RMS error stays near 4e-3."""
+def _ideal_bf16_backward_ratios(w, b, h, causal):
+    """Gradient errors of a backward on bf16 matrix products that is otherwise exact: float64
+    arithmetic with only the roundings such products force (Q' and K' rounded to bf16 as the
+    forward rounds them, P rounded for dV = P^T dO, dS rounded for dQ' = dS K' and
+    dK' = dS^T Q', outputs rounded to bf16).  Per tensor: (max|err| / RMS, RMS(err) / RMS,
+    floor = max|bf16(grad) - grad| / RMS)."""
     import math
 
     from oracle import attention_forward, rope_rotate, rope_rotate_vjp, rope_sdpa_backward
 
-    w = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=4100, with_grad=True)
-    b, h = 1, 5
     q, k, v, do = (t[b:b + 1, h:h + 1].double().numpy() for t in (w.q, w.k, w.v, w.do))
-    dq_ref, dk_ref, dv_ref = rope_sdpa_backward(q, k, v, w.cos, w.sin, do)
-    scale = 1.0 / math.sqrt(128)
-    qr, kr = rope_rotate(q, w.cos, w.sin)[0, 0], rope_rotate(k, w.cos, w.sin)[0, 0]
-    _, lse = attention_forward(qr[None, None], kr[None, None], v, scale)
+    cos = w.cos[b:b + 1] if w.cos.shape[0] > 1 else w.cos
+    sin = w.sin[b:b + 1] if w.sin.shape[0] > 1 else w.sin
+    dq_ref, dk_ref, dv_ref = rope_sdpa_backward(q, k, v, cos, sin, do, causal=causal)
+    S, D = q.shape[2], q.shape[3]
+    scale = 1.0 / math.sqrt(D)
+    qr, kr = rope_rotate(q, cos, sin)[0, 0], rope_rotate(k, cos, sin)[0, 0]
+    _, lse = attention_forward(qr[None, None], kr[None, None], v, scale, causal=causal)
     qb, kb = _bf16(qr), _bf16(kr)
+    s = scale * (qb @ kb.T)
+    if causal:
+        s = np.where(np.arange(S)[None, :] > np.arange(S)[:, None], -np.inf, s)
+    P = np.exp(s - lse[0, 0][:, None])
     V, dO = v[0, 0], do[0, 0]
-    P = np.exp(scale * (qb @ kb.T) - lse[0, 0][:, None])
     dP = dO @ V.T
     delta = (P * dP).sum(axis=1)
     dS = _bf16(P * (dP - delta[:, None]))
-    dq = _bf16(rope_rotate_vjp((scale * (dS @ kb))[None, None], w.cos, w.sin)[0, 0])
-    dk = _bf16(rope_rotate_vjp((scale * (dS.T @ qb))[None, None], w.cos, w.sin)[0, 0])
+    dq = _bf16(rope_rotate_vjp((scale * (dS @ kb))[None, None], cos, sin)[0, 0])
+    dk = _bf16(rope_rotate_vjp((scale * (dS.T @ qb))[None, None], cos, sin)[0, 0])
     dv = _bf16(_bf16(P).T @ dO)
-    ratios = {}
+    out = {}
     for name, g, r in (("dQ", dq, dq_ref[0, 0]), ("dK", dk, dk_ref[0, 0]), ("dV", dv, dv_ref[0, 0])):
         rms = np.sqrt((r ** 2).mean())
-        ratios[name] = (np.abs(g - r).max() / rms, np.sqrt(((g - r) ** 2).mean()) / rms,
-                        np.abs(_bf16(r) - r).max() / rms)
+        out[name] = (np.abs(g - r).max() / rms, np.sqrt(((g - r) ** 2).mean()) / rms,
+                     np.abs(_bf16(r) - r).max() / rms)
+    return out
+
+
+def test_bf16_matrix_operands_exceed_max_reading_on_flux_training_shape():
+    """On the non-causal FLUX training shape (B=2, H=24, S=4608, D=128) the exact gradient
+    rounded to bf16 stays within max|error| <= 5e-2 RMS(gradient), but a backward built on
+    bf16 matrix products cannot: with only the roundings such products force, head
+    (b, h) = (1, 5) exceeds the max reading on dK, while its RMS error stays near 4e-3."""
+    w = syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=4100, with_grad=True)
+    ratios = _ideal_bf16_backward_ratios(w, 1, 5, causal=False)
     assert all(floor < 5e-2 for _, _, floor in ratios.values()), ratios
     assert max(m for m, _, _ in ratios.values()) > 5e-2, ratios
     assert all(e < 1e-2 for _, e, _ in ratios.values()), ratios
+    assert all(m <= 3 * max(5e-2, floor) for m, _, floor in ratios.values()), ratios
+
+
+def test_max_error_guard_admits_an_ideal_bf16_backward():
+    """The parity tests' max-error guard, 3 max(5e-2, floor) RMS(gradient): on a small causal
+    case (B=2, H=2, S=300, D=128, the GPU test's seed) an otherwise exact backward on bf16
+    matrix products already reaches more than twice the floor and 1.8x the stated bound, so a
+    guard of twice the larger would reject the ideal kernel; three times admits it."""
+    w = syn.random_small(2, 2, 300, 128, "bf16", seed=5 + 300 + 128, causal=True, with_grad=True)
+    worst = 0.0
+    for b in range(2):
+        for h in range(2):
+            for m, e, floor in _ideal_bf16_backward_ratios(w, b, h, causal=True).values():
+                worst = max(worst, m / max(5e-2, floor))
+                assert m <= 3 * max(5e-2, floor) and e < 1e-2
+    assert worst > 1.5, worst
