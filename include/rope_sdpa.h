@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ROPE_SDPA_ABI_VERSION 1
+#define ROPE_SDPA_ABI_VERSION 2
 
 typedef enum {
   RS_OK = 0,
@@ -60,7 +60,8 @@ typedef enum {
   RS_ERR_WORKSPACE = -7,   /* workspace NULL or smaller than rope_sdpa_workspace_size() */
   RS_ERR_INVALID = -8,     /* bad flag, mask kind, scale, or causal together with a mask */
   RS_ERR_NO_DEVICE = -9,   /* no usable gfx950 device is current */
-  RS_ERR_LAUNCH = -10      /* the HIP launch itself failed */
+  RS_ERR_LAUNCH = -10,     /* the HIP launch itself failed */
+  RS_ERR_SCRATCH = -11     /* rope_sdpa_fwd_noalloc: the call needs more than its static scratch */
 } rs_status;
 
 typedef enum { RS_F32 = 0, RS_F16 = 1, RS_BF16 = 2, RS_BOOL = 3 } rs_dtype;
@@ -122,6 +123,23 @@ rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* by
  */
 rs_status rope_sdpa_fwd(const rs_args* args, const rs_tensor* o, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * checks and results as rope_sdpa_fwd (bit for bit: the same kernels), without the
+ * workspace: the library keeps a device scratch array of rope_sdpa_noalloc_scratch_bytes()
+ * bytes (64 MiB) per device, held from the first call on that device until the process ends,
+ * and this call allocates nothing (no hipMalloc, no allocating library routine).  A call whose
+ * workspace would exceed that size returns RS_ERR_SCRATCH and launches nothing.  The caller
+ * still owns and passes inputs, o and lse.  Every call on one device shares that device's
+ * scratch: calls that overlap on one device (enqueued on different streams without ordering
+ * between them, or from several threads onto unordered streams) race and give undefined
+ * results; calls on one stream are ordered and safe.  Nothing in the scratch is assumed to
+ * start at zero (the kernels clear what they count).
+ */
+rs_status rope_sdpa_fwd_noalloc(const rs_args* args, const rs_tensor* o, float* lse, void* stream);
+size_t rope_sdpa_noalloc_scratch_bytes(void);
 
 /*
  * Backward of rope_sdpa_fwd (section "Fused RoPE + SDPA": gradients with respect to the

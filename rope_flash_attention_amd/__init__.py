@@ -29,6 +29,7 @@ __all__ = [
     "rope_scaled_dot_product_attention", "rope_sdpa_fwd", "rope_sdpa_bwd", "rope_sdpa_workspace_size",
     "rope_sdpa_get_stats", "rope_sdpa_reset_stats", "rope_sdpa_abi_version", "rope_sdpa_status_string",
     "get_dispatch_stats", "RopeSdpaError", "library_path", "rope_sdpa_debug_quantize_qk", "debug_quantize_qk",
+    "rope_sdpa_fwd_noalloc", "rope_sdpa_noalloc_scratch_bytes",
 ]
 
 _DT = {torch.float32: RS_F32, torch.float16: RS_F16, torch.bfloat16: RS_BF16, torch.bool: RS_BOOL}
@@ -232,6 +233,14 @@ def rope_sdpa_bwd_explicit(query, key, value, rope_cos, rope_sin, out, lse, dout
 # ---- C-ABI names, re-exported -------------------------------------------------------------
 def rope_sdpa_fwd(args, o, lse_ptr, ws_ptr, ws_bytes, stream) -> int:
     return _abi.load().rope_sdpa_fwd(args, o, lse_ptr, ws_ptr, ws_bytes, stream)
+
+
+def rope_sdpa_fwd_noalloc(args, o, lse_ptr, stream) -> int:
+    return _abi.load().rope_sdpa_fwd_noalloc(args, o, lse_ptr, stream)
+
+
+def rope_sdpa_noalloc_scratch_bytes() -> int:
+    return int(_abi.load().rope_sdpa_noalloc_scratch_bytes())
 
 
 def rope_sdpa_bwd(args, o, lse_ptr, dout, dq, dk, dv, ws_ptr, ws_bytes, stream) -> int:

@@ -11,7 +11,7 @@ RS_OK = 0
 STATUS_NAMES = {
     0: "RS_OK", -1: "RS_ERR_NULL", -2: "RS_ERR_DTYPE", -3: "RS_ERR_SHAPE", -4: "RS_ERR_STRIDE",
     -5: "RS_ERR_ALIGN", -6: "RS_ERR_UNSUPPORTED", -7: "RS_ERR_WORKSPACE", -8: "RS_ERR_INVALID",
-    -9: "RS_ERR_NO_DEVICE", -10: "RS_ERR_LAUNCH",
+    -9: "RS_ERR_NO_DEVICE", -10: "RS_ERR_LAUNCH", -11: "RS_ERR_SCRATCH",
 }
 RS_F32, RS_F16, RS_BF16, RS_BOOL = 0, 1, 2, 3
 RS_MASK_NONE, RS_MASK_BOOL, RS_MASK_ADDITIVE = 0, 1, 2
@@ -21,6 +21,7 @@ RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT8_QK = 1, 2
 EXPORTED = (
     "rope_sdpa_workspace_size", "rope_sdpa_fwd", "rope_sdpa_bwd", "rope_sdpa_status_string",
     "rope_sdpa_get_stats", "rope_sdpa_reset_stats", "rope_sdpa_abi_version", "rope_sdpa_debug_quantize_qk",
+    "rope_sdpa_fwd_noalloc", "rope_sdpa_noalloc_scratch_bytes",
 )
 
 
@@ -72,6 +73,10 @@ def load(path: str = LIB_PATH):
     lib.rope_sdpa_fwd.argtypes = [P(RsArgs), P(RsTensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.c_void_p]
     lib.rope_sdpa_fwd.restype = ctypes.c_int
+    lib.rope_sdpa_fwd_noalloc.argtypes = [P(RsArgs), P(RsTensor), ctypes.c_void_p, ctypes.c_void_p]
+    lib.rope_sdpa_fwd_noalloc.restype = ctypes.c_int
+    lib.rope_sdpa_noalloc_scratch_bytes.argtypes = []
+    lib.rope_sdpa_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.rope_sdpa_bwd.argtypes = [P(RsArgs), P(RsTensor), ctypes.c_void_p, P(RsTensor), P(RsTensor), P(RsTensor),
                                   P(RsTensor), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.rope_sdpa_bwd.restype = ctypes.c_int

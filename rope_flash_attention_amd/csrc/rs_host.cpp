@@ -359,6 +359,9 @@ const char* rope_sdpa_status_string(rs_status st) {
     case RS_ERR_INVALID: return "RS_ERR_INVALID: bad flags, mask kind, scale, or causal with a mask";
     case RS_ERR_NO_DEVICE: return "RS_ERR_NO_DEVICE: no current gfx950 device";
     case RS_ERR_LAUNCH: return "RS_ERR_LAUNCH: kernel launch failed";
+    case RS_ERR_SCRATCH:
+      return "RS_ERR_SCRATCH: the call needs more device scratch than rope_sdpa_fwd_noalloc has "
+             "(rope_sdpa_noalloc_scratch_bytes()); use rope_sdpa_fwd with a workspace";
   }
   return "unknown rs_status";
 }
@@ -375,8 +378,15 @@ rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* by
   return RS_OK;
 }
 
-rs_status rope_sdpa_fwd(const rs_args* a, const rs_tensor* o, float* lse, void* ws, size_t ws_bytes,
-                        void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward of both entry points: `ws` is the caller's workspace (rope_sdpa_fwd) or, when
+// `scratch` is set, the library's device scratch (rope_sdpa_fwd_noalloc), looked up after
+// validation and the device check.
+rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, size_t ws_bytes, void* stream,
+                   bool scratch) {
   Shape s;
   rs_status st = validate_args(a, &s);
   if (st != RS_OK) return fail(st);
@@ -388,6 +398,12 @@ rs_status rope_sdpa_fwd(const rs_args* a, const rs_tensor* o, float* lse, void* 
   if (s.empty) return RS_OK;  // nothing to compute: no workspace or device needed
   const bool int8 = (a->flags & RS_FLAG_QUANT_INT8_QK) != 0;
   const Layout L = layout(s, a->mask_kind, false, int8, (a->flags & RS_FLAG_CAUSAL) != 0);
+  if (scratch) {
+    if (L.total > kScratchBytes) return fail(RS_ERR_SCRATCH);
+    if ((st = current_device_ok()) != RS_OK) return fail(st);
+    if (scratch_address(&ws) != 0) return fail(RS_ERR_NO_DEVICE);
+    ws_bytes = kScratchBytes;
+  }
   if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
   if ((st = current_device_ok()) != RS_OK) return fail(st);
 
@@ -438,6 +454,21 @@ rs_status rope_sdpa_fwd(const rs_args* a, const rs_tensor* o, float* lse, void* 
   if (int8) g_ctr.quant_int8.fetch_add(1, std::memory_order_relaxed);
   return RS_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+rs_status rope_sdpa_fwd(const rs_args* a, const rs_tensor* o, float* lse, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return fwd_impl(a, o, lse, ws, ws_bytes, stream, false);
+}
+
+rs_status rope_sdpa_fwd_noalloc(const rs_args* a, const rs_tensor* o, float* lse, void* stream) {
+  return fwd_impl(a, o, lse, nullptr, 0, stream, true);
+}
+
+size_t rope_sdpa_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 rs_status rope_sdpa_debug_quantize_qk(const rs_args* a, int8_t* q_codes, int8_t* k_codes, float* q_scales,
                                       float* k_scales, void* ws, size_t ws_bytes, void* stream) {

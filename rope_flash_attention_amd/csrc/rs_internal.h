@@ -138,4 +138,9 @@ int launch_bwd(int dtype, int D, int mask_kind, bool causal, const BwdParams& p,
 // Reads (and optionally clears) the device-side count of all-true bool masks.
 int read_all_true_counter(uint64_t* value, bool reset);
 
+// Library-owned device scratch of rope_sdpa_fwd_noalloc (rs_scratch.hip): its size, and its
+// device address on the current device (looked up once per device); 0 or a HIP error.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+int scratch_address(void** ptr);
+
 }  // namespace rs

@@ -118,4 +118,15 @@ int read_all_true_counter(uint64_t* value, bool) {
   return 0;
 }
 
+// The library's device scratch: host memory standing in for it, registered with the range
+// checks of the launchers when looked up.
+int scratch_address(void** ptr) {
+  static char* mem = nullptr;
+  if (!mem) mem = (char*)std::aligned_alloc(256, kScratchBytes);
+  stub::ws_lo = mem;
+  stub::ws_bytes = kScratchBytes;
+  *ptr = mem;
+  return 0;
+}
+
 }  // namespace rs

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = lib()
-    assert L.rope_sdpa_abi_version() == 1
+    assert L.rope_sdpa_abi_version() == 2
     for code, name in _abi.STATUS_NAMES.items():
         assert _abi.status_string(code).startswith(name)
     assert "unknown" in _abi.status_string(-99)
@@ -303,3 +303,22 @@ def test_negative_sizes_are_rejected():
     for t in (c.q, c.k, c.v, c.o):
         t.size[2] = -1
     assert c.fwd() == ERR["RS_ERR_SHAPE"]
+
+
+def test_noalloc_forward_validates_and_bounds_its_scratch():
+    """The allocation-free forward runs the forward's checks; a call whose workspace would
+    exceed the library's static scratch returns RS_ERR_SCRATCH before any device access."""
+    L = lib()
+    assert L.rope_sdpa_noalloc_scratch_bytes() == 64 << 20
+    c = Call()
+    a = c.args()
+    assert L.rope_sdpa_fwd_noalloc(ctypes.byref(a), ctypes.byref(c.o), c.lse, None) == ERR["RS_ERR_NO_DEVICE"]
+    c.k.dtype = RS_F32
+    a = c.args()
+    assert L.rope_sdpa_fwd_noalloc(ctypes.byref(a), ctypes.byref(c.o), c.lse, None) == ERR["RS_ERR_DTYPE"]
+    # per-sample tables of 64 samples at S = 4608: 151 MB of packed tables > 64 MiB
+    big = Call(B=64, H=1, S=4608, D=128)
+    big.cos = make_tensor(BASE + 4 * (1 << 32), RS_F32, (64, 1, 4608, 128), (4608 * 128, 4608 * 128, 128, 1))
+    big.sin = make_tensor(BASE + 5 * (1 << 32), RS_F32, (64, 1, 4608, 128), (4608 * 128, 4608 * 128, 128, 1))
+    a = big.args()
+    assert L.rope_sdpa_fwd_noalloc(ctypes.byref(a), ctypes.byref(big.o), big.lse, None) == ERR["RS_ERR_SCRATCH"]
