@@ -86,8 +86,13 @@ typedef struct {
 
 typedef struct {
   const rs_tensor* q;    /* [B, H, S, D]  f32 | f16 | bf16 */
-  const rs_tensor* k;    /* [B, H, S, D]  same dtype as q */
-  const rs_tensor* v;    /* [B, H, S, D]  same dtype as q */
+  /* K and V: [B, Hkv, S, D], same dtype as q, with H % Hkv == 0.  Hkv < H is grouped-query
+   * (Hkv == 1: multi-query) attention: query head h reads K/V head h / (H / Hkv), and K is
+   * rotated at its own head count (section "Fused RoPE + SDPA": GQA inputs are rotated at
+   * the K/V head count and expanded afterwards); dK and dV of the backward have Hkv heads,
+   * each the sum over the query heads that read it. */
+  const rs_tensor* k;
+  const rs_tensor* v;
   /* Pair-duplicated rotation tables (cos[2i] == cos[2i+1]), fp32, sizes [Bt, 1, S, D] with
    * Bt == 1 (shared) or Bt == B (per sample), stride[3] == 1.  Only the even entries are
    * read; duplication is the caller's precondition (section "Fused RoPE + SDPA"). */
@@ -144,7 +149,8 @@ size_t rope_sdpa_noalloc_scratch_bytes(void);
 /*
  * Backward of rope_sdpa_fwd (section "Fused RoPE + SDPA": gradients with respect to the
  * pre-rotation Q and K).  Inputs: the same args as the forward, its o and lse, and the
- * upstream gradient dout (sizes and dtype of o).  Writes dq, dk, dv (dtype of q, sizes of q).
+ * upstream gradient dout (sizes and dtype of o).  Writes dq (sizes of q), dk and dv (sizes of k),
+ * all in the dtype of q.
  * The mask (if any) is a constant: no mask gradient.  Not available with RS_FLAG_QUANT_INT8_QK.
  */
 rs_status rope_sdpa_bwd(const rs_args* args, const rs_tensor* o, const float* lse,
@@ -155,8 +161,9 @@ rs_status rope_sdpa_bwd(const rs_args* args, const rs_tensor* o, const float* ls
 /*
  * Test-only export of the int8 quantization that rope_sdpa_fwd performs under
  * RS_FLAG_QUANT_INT8_QK (same reading, same kernel): writes the int8 codes of the rotated Q and
- * K into q_codes / k_codes, contiguous [B, H, S, D] DEVICE buffers (8-byte aligned), and their
- * fp32 scales into q_scales / k_scales, contiguous [B, H, ceil(S / 64)] DEVICE buffers.  args
+ * K into q_codes / k_codes, contiguous [B, H, S, D] / [B, Hkv, S, D] DEVICE buffers (8-byte
+ * aligned), and their fp32 scales into q_scales / k_scales, contiguous [B, H, ceil(S / 64)] /
+ * [B, Hkv, ceil(S / 64)] DEVICE buffers.  args
  * must carry RS_FLAG_QUANT_INT8_QK (else RS_ERR_INVALID) and pass the same validation as the
  * forward; the workspace is the forward's (rope_sdpa_workspace_size(args, 0, ...)).  It lets a
  * test compare the integer decisions bit for bit and run a reference from exactly these

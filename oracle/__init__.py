@@ -11,8 +11,9 @@ What it computes is the plain definition on the page "Metal Flash Attention"
 
 with R the interleaved-pair rotation driven by caller-supplied cos/sin tables, masks
 as in the section "Enable In SimpleTuner" (bool True = attend, additive float,
-broadcast up to 4-D), a causal mode, and gradients with respect to the unrotated Q
-and K (the inverse rotation applied to dQ/dK).  The blockwise int8 variant follows
+broadcast up to 4-D), a causal mode, grouped-query attention (K/V with fewer heads,
+rotated at their own head count and expanded), and gradients with respect to the
+unrotated Q and K (the inverse rotation applied to dQ/dK).  The blockwise int8 variant follows
 the quantizer step by step and then applies the same definition to the dequantized
 rotated Q and K.
 
@@ -32,4 +33,6 @@ from .rope_sdpa_ref import (  # noqa: F401
     rope_rotate_f32,
     quantize_blockwise_int8,
     rope_sdpa_forward_int8,
+    expand_kv,
+    reduce_kv,
 )

@@ -284,12 +284,37 @@ def _resolve_scale(scale, D):
         return float(Decimal(1) / Decimal(int(D)).sqrt())
 
 
+def _kv_group(H, Hkv):
+    """Query heads per K/V head (grouped-query attention, [FR]): query head h reads K/V head
+    h // (H / Hkv) = h Hkv / H.  Hkv == H is ordinary multi-head attention."""
+    if Hkv <= 0 or H % Hkv != 0:
+        raise ValueError(f"{H} query heads cannot share {Hkv} K/V heads evenly")
+    return H // Hkv
+
+
+def expand_kv(x, H):
+    """[B, Hkv, S, D] -> [B, H, S, D]: each K/V head repeated for the query heads that read it
+    ([FR]: GQA inputs are rotated at the K/V head count and expanded afterwards)."""
+    G = _kv_group(H, x.shape[1])
+    return np.repeat(x, G, axis=1) if G > 1 else x
+
+
+def reduce_kv(g, Hkv):
+    """Gradient of expand_kv: [B, H, S, D] -> [B, Hkv, S, D], summing each group's heads."""
+    B, H = g.shape[:2]
+    G = _kv_group(H, Hkv)
+    return g.reshape(B, Hkv, G, *g.shape[2:]).sum(axis=2) if G > 1 else g
+
+
 def rope_sdpa_forward(q, k, v, cos, sin, mask=None, mask_kind="none", causal=False, scale=None,
                       rows=None, pairs=None, workers=1):
-    """Fused RoPE + SDPA forward [FR]: rotate Q and K, then exact attention.  Returns (O, LSE)."""
+    """Fused RoPE + SDPA forward [FR]: rotate Q and K, then exact attention.  K and V may have
+    fewer heads than Q (grouped-query attention): they are rotated at their own head count and
+    expanded afterwards.  Returns (O, LSE)."""
     q64, k64, v64 = _np64(q), _np64(k), _np64(v)
     qr = rope_rotate(q64, cos, sin)
-    kr = rope_rotate(k64, cos, sin)
+    kr = expand_kv(rope_rotate(k64, cos, sin), q64.shape[1])
+    v64 = expand_kv(v64, q64.shape[1])
     madd = mask_to_additive(mask, mask_kind)
     return attention_forward(qr, kr, v64, _resolve_scale(scale, q64.shape[-1]), madd, causal,
                              rows=rows, pairs=pairs, workers=workers)
@@ -299,15 +324,22 @@ def rope_sdpa_backward(q, k, v, cos, sin, do, mask=None, mask_kind="none", causa
                        pairs=None, workers=1):
     """Gradients w.r.t. the unrotated Q, K and V [FR]: attention backward in the rotated frame,
     then the exact VJP of the rotation on dQ' and dK'.  The mask and tables get no gradient.
-    Returns (dQ, dK, dV).
+    Returns (dQ, dK, dV).  With grouped-query attention (K, V with Hkv < H heads) dK and dV
+    have Hkv heads: the gradients of the expanded heads are summed over each group (the VJP of
+    the expansion) before the inverse rotation; `pairs` is then not accepted.
     """
     q64, k64, v64, do64 = _np64(q), _np64(k), _np64(v), _np64(do)
+    H, Hkv = q64.shape[1], k64.shape[1]
     qr = rope_rotate(q64, cos, sin)
-    kr = rope_rotate(k64, cos, sin)
+    kr = expand_kv(rope_rotate(k64, cos, sin), H)
+    v64 = expand_kv(v64, H)
     madd = mask_to_additive(mask, mask_kind)
+    if Hkv != H and pairs is not None:
+        raise ValueError("pairs are not supported with grouped-query attention")
     dqr, dkr, dv = attention_backward(qr, kr, v64, do64, _resolve_scale(scale, q64.shape[-1]), madd,
                                       causal, pairs=pairs, workers=workers)
     if pairs is None:
+        dkr, dv = reduce_kv(dkr, Hkv), reduce_kv(dv, Hkv)
         return rope_rotate_vjp(dqr, cos, sin), rope_rotate_vjp(dkr, cos, sin), dv
     # per-pair tables: index the batch of each (b, h)
     c, s = _np64(cos), _np64(sin)
@@ -395,8 +427,8 @@ def rope_sdpa_forward_int8(q, k, v, cos, sin, scale=None, rows=None, pairs=None,
     else:
         (qc, qs), (kc, ks) = codes
     qh = dequantize_blockwise(qc, qs, block)
-    kh = dequantize_blockwise(kc, ks, block)
-    v64 = _np64(v)
+    kh = expand_kv(dequantize_blockwise(kc, ks, block), qh.shape[1])  # K quantized at its own head count
+    v64 = expand_kv(_np64(v), qh.shape[1])
     return attention_forward(qh, kh, v64, _resolve_scale(scale, qh.shape[-1]), None, False,
                              rows=rows, pairs=pairs, workers=workers)
 

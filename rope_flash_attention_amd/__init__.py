@@ -10,7 +10,9 @@ Entry point (page "Metal Flash Attention", SimpleTuner docs, section "Fused RoPE
     rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin,
                                       attn_mask=None, is_causal=False, scale=None)
 
-query/key/value are BHSD (strided views accepted), rope_cos/rope_sin are pair-duplicated
+query/key/value are BHSD (strided views accepted); key and value may have fewer heads than
+query (grouped-query / multi-query attention: query head h reads K/V head h * Hkv / H, and K is
+rotated at its own head count); rope_cos/rope_sin are pair-duplicated
 tables of shape [S, D], [1, S, D] or [B, S, D] in any float dtype (normalised to fp32),
 masks are bool (True = attend) or additive float, broadcastable, up to 4-D.  Gradients
 flow to query, key (pre-rotation) and value.
@@ -139,8 +141,8 @@ def _backward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, o, lse, do):
     lib = _abi.load()
     call = _Call(q, k, v, cos4, sin4, mask, mask_kind, causal, scale)
     dq = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    dk = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    dv = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    dk = torch.empty(k.shape, dtype=q.dtype, device=q.device)  # K/V heads (grouped-query attention)
+    dv = torch.empty(v.shape, dtype=q.dtype, device=q.device)
     ws = call.workspace(True, q.device)
     tdo, tdq, tdk, tdv, to = _desc(do), _desc(dq), _desc(dk), _desc(dv), _desc(o)
     _check(lib.rope_sdpa_bwd(ctypes.byref(call.args), ctypes.byref(to), lse.data_ptr(), ctypes.byref(tdo),
@@ -205,17 +207,18 @@ def rope_sdpa_fwd_with_lse(query, key, value, rope_cos, rope_sin, attn_mask=None
 def debug_quantize_qk(query, key, rope_cos, rope_sin):
     """The int8 codes and scales the int8 forward computes, for tests.
 
-    Returns (q_codes, q_scales, k_codes, k_scales): int8 [B, H, S, D] and fp32 [B, H, ceil(S/64)].
+    Returns (q_codes, q_scales, k_codes, k_scales): int8 [B, H|Hkv, S, D] and fp32 [B, H|Hkv, ceil(S/64)].
     """
     lib = _abi.load()
     cos4, sin4 = _tables4(rope_cos, query.device), _tables4(rope_sin, query.device)
     call = _Call(query, key, key, cos4, sin4, None, 0, False, None, int8=True)
     B, H, S, D = query.shape
     nb = -(-S // 64)
+    Hkv = key.shape[1]
     qc = torch.empty((B, H, S, D), dtype=torch.int8, device=query.device)
-    kc = torch.empty_like(qc)
+    kc = torch.empty((B, Hkv, S, D), dtype=torch.int8, device=query.device)
     qs = torch.empty((B, H, nb), dtype=torch.float32, device=query.device)
-    ks = torch.empty_like(qs)
+    ks = torch.empty((B, Hkv, nb), dtype=torch.float32, device=query.device)
     ws = call.workspace(False, query.device)
     _check(lib.rope_sdpa_debug_quantize_qk(ctypes.byref(call.args), qc.data_ptr(), kc.data_ptr(), qs.data_ptr(),
                                            ks.data_ptr(), ws.data_ptr(), ws.numel(), _stream(query.device)))

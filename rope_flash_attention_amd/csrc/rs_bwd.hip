@@ -268,26 +268,36 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   const int r = lane & 31, hh = lane >> 5;
   const int S = p.shp.S;
   const int nkt = (S + BNK - 1) / BNK;
+  // workgroup = one key tile of one (b, K/V head); with grouped-query attention it runs the
+  // query tiles of every query head of the group, dK and dV accumulating across them
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = item % nkt;
   const int bh = item / nkt;
-  const int hd = bh % p.shp.H, b = bh / p.shp.H;
+  const int hk = bh % p.shp.Hkv, b = bh / p.shp.Hkv;
   const int k0 = kt * BNK;
   const int j = k0 + 32 * wave + r;  // this lane's key
   const int jc = j < S ? j : S - 1;
 
-  const T* qbase = (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh;
-  const T* dobase = (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh;
   const float* tab = p.tab.ptr + b * p.tab.sb;
-  const float* lse = p.lse + ((int64_t)b * p.shp.H + hd) * S;
-  const float* dlt = p.delta + ((int64_t)b * p.shp.H + hd) * S;
+  int hd = 0;  // the query head whose tiles are being run
+  const T* qbase = nullptr;
+  const T* dobase = nullptr;
+  const float* lse = nullptr;
+  const float* dlt = nullptr;
+  auto set_head = [&](int h) {
+    hd = h;
+    qbase = (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh;
+    dobase = (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh;
+    lse = p.lse + ((int64_t)b * p.shp.H + hd) * S;
+    dlt = p.delta + ((int64_t)b * p.shp.H + hd) * S;
+  };
 
   // K' and V of this lane's key as B fragments (column = key)
   frag kf[NQK], vf[NQK];
   if (j < S) {
-    load_row_frags<T, D, true>(kf, (const T*)p.k.ptr + b * p.k.sb + hd * p.k.sh + (int64_t)j * p.k.ss,
+    load_row_frags<T, D, true>(kf, (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh + (int64_t)j * p.k.ss,
                                tab + (int64_t)j * D, hh);
-    load_row_frags<T, D, false>(vf, (const T*)p.v.ptr + b * p.v.sb + hd * p.v.sh + (int64_t)j * p.v.ss,
+    load_row_frags<T, D, false>(vf, (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh + (int64_t)j * p.v.ss,
                                 nullptr, hh);
   } else {
     zero_frags<T, D>(kf);
@@ -356,6 +366,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   };
 
   const float c2 = p.shp.scale_log2;
+#pragma unroll 1
+  for (int g = 0; g < p.shp.group; ++g) {
+  set_head(hk * p.shp.group + g);
+  if (g > 0) __syncthreads();  // LDS of the previous head's last tile
   int qt = next_tile(qt_begin);
   if (qt < nqt) {
     load_tile(qt);
@@ -499,11 +513,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     stage ^= 1;
     qt = qtn;
   }
+  }  // query heads of the group
 
   if (j < S) {
-    char* dvrow = (char*)p.dv + ((int64_t)b * p.dv_sb + (int64_t)hd * p.dv_sh + (int64_t)j * p.dv_ss) * ES;
+    char* dvrow = (char*)p.dv + ((int64_t)b * p.dv_sb + (int64_t)hk * p.dv_sh + (int64_t)j * p.dv_ss) * ES;
     store_acc_row<T, D, false>(dvrow, dv_acc, 1.f, nullptr, hh);
-    char* dkrow = (char*)p.dk + ((int64_t)b * p.dk_sb + (int64_t)hd * p.dk_sh + (int64_t)j * p.dk_ss) * ES;
+    char* dkrow = (char*)p.dk + ((int64_t)b * p.dk_sb + (int64_t)hk * p.dk_sh + (int64_t)j * p.dk_ss) * ES;
     store_acc_row<T, D, true>(dkrow, dk_acc, p.shp.scale, tab + (int64_t)j * D, hh);
   }
 }
@@ -543,8 +558,9 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
   const int m = q0 + 32 * wave + r;
   const int mc = m < S ? m : S - 1;
 
-  const T* kbase = (const T*)p.k.ptr + b * p.k.sb + hd * p.k.sh;
-  const T* vbase = (const T*)p.v.ptr + b * p.v.sb + hd * p.v.sh;
+  const int hk = hd / p.shp.group;  // K/V head (grouped-query attention)
+  const T* kbase = (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh;
+  const T* vbase = (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh;
   const float* tab = p.tab.ptr + b * p.tab.sb;
 
   frag qf[NQK], gf[NQK];
@@ -733,7 +749,7 @@ static int launch_bwd_t(const BwdParams& p, hipStream_t s) {
   int e = (int)hipGetLastError();
   if (e) return e;
   const int nk = (p.shp.S + DkdvCfg<T>::BNK - 1) / DkdvCfg<T>::BNK;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, MASK, CAUSAL>), dim3(nk * p.shp.H * p.shp.B), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((dkdv_kernel<T, D, MASK, CAUSAL>), dim3(nk * p.shp.Hkv * p.shp.B), dim3(256), 0, s, p);
   e = (int)hipGetLastError();
   if (e) return e;
   const int nq = (p.shp.S + DqCfg<T>::BM - 1) / DqCfg<T>::BM;

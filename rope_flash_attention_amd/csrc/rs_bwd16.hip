@@ -268,8 +268,9 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
   const int m = q0 + 16 * wave + c;
   const int mc = m < S ? m : S - 1;
 
-  const T* kbase = (const T*)p.k.ptr + b * p.k.sb + hd * p.k.sh;
-  const T* vbase = (const T*)p.v.ptr + b * p.v.sb + hd * p.v.sh;
+  const int hk = hd / p.shp.group;  // K/V head (grouped-query attention)
+  const T* kbase = (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh;
+  const T* vbase = (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh;
   const float* tab = p.tab.ptr + b * p.tab.sb;
 
   frag qf[4], gf[4];
@@ -461,24 +462,27 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   const int c = lane & 15, g = lane >> 4;
   const int S = p.shp.S;
   const int nkt = (S + BNK - 1) / BNK;
+  // workgroup = one key tile of one (b, K/V head); with grouped-query attention it runs the
+  // query tiles of every query head of the group, dK and dV accumulating across them
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = item % nkt;
   const int bh = item / nkt;
-  const int hd = bh % p.shp.H, b = bh / p.shp.H;
+  const int hk = bh % p.shp.Hkv, b = bh / p.shp.Hkv;
   const int k0 = kt * BNK;
   const int j = k0 + 16 * wave + c;  // this lane's key
   const int jc = j < S ? j : S - 1;
 
-  const T* dobase = (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh;
   const float* tab = p.tab.ptr + b * p.tab.sb;
-  const float* lse = p.lse + ((int64_t)b * p.shp.H + hd) * S;
-  const float* dlt = p.delta + ((int64_t)b * p.shp.H + hd) * S;
+  int hd = 0;  // the query head whose tiles are being run
+  const T* dobase = nullptr;
+  const float* lse = nullptr;
+  const float* dlt = nullptr;
 
   // K' (times scale log2 e) and V of this lane's key as B fragments
   frag kf[4], vf[4];
-  row_frags<T, true>(kf, (const T*)p.k.ptr + b * p.k.sb + hd * p.k.sh + (int64_t)jc * p.k.ss, tab + (int64_t)jc * D,
+  row_frags<T, true>(kf, (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh + (int64_t)jc * p.k.ss, tab + (int64_t)jc * D,
                      g, p.shp.scale_log2);
-  row_frags<T, false>(vf, (const T*)p.v.ptr + b * p.v.sb + hd * p.v.sh + (int64_t)jc * p.v.ss, nullptr, g, 1.f);
+  row_frags<T, false>(vf, (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh + (int64_t)jc * p.v.ss, nullptr, g, 1.f);
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 dv[8], dk[8];
 #pragma unroll
@@ -497,10 +501,6 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
     return st;
   };
   __shared__ uint8_t s_tstate[MASK == MASK_BOOL ? kMaxStateTiles16 : 1];
-  if constexpr (MASK == MASK_BOOL) {
-    for (int i = tid; i < nqt; i += 512) s_tstate[i] = (uint8_t)tile_state_mem(i);
-    __syncthreads();
-  }
   auto tile_state = [&](int qt) -> uint32_t {
     if constexpr (MASK == MASK_BOOL) {
       return (uint32_t)s_tstate[qt];
@@ -518,9 +518,7 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   LaneOffsets lo;
   lo.init(c, g);
   DmaTile dqr;  // Q' tiles, rotated by the dQ kernel (launched first)
-  dqr.init((const T*)p.qrot + (int64_t)bh * S * D, D, S, wave, lane);
   DmaTile dd;
-  dd.init(dobase, p.dout.ss, S, wave, lane);
   float lreg = 0.f;  // thread t < 64: l2 of query q0 + t; 64 <= t < 128: delta of q0 + t - 64
   auto load_tile = [&](int qt, char* sQ, char* sD) {
     const int q0 = qt * BMQ;
@@ -539,7 +537,8 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   auto store_tile = [&](float* sL) {
     if (tid < 2 * BMQ) sL[tid] = lreg;
   };
-  const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
+  const int bm = p.mask.sb ? b : 0;
+  int hm = 0;
 
   // S' and dP of one query tile: rows = queries (permuted order), column = this lane's key
   auto rows = [&](const char* sQ, const char* sD, f32x4* sacc, f32x4* dpacc) __attribute__((always_inline)) {
@@ -639,6 +638,20 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   // is loaded into it during the second.  The two wave groups run separate loops (one
   // branch outside), so that neither carries the other's registers; both pass the same
   // barriers: two per tile.
+#pragma unroll 1
+  for (int gq = 0; gq < p.shp.group; ++gq) {
+  hd = hk * p.shp.group + gq;
+  dobase = (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh;
+  lse = p.lse + ((int64_t)b * p.shp.H + hd) * S;
+  dlt = p.delta + ((int64_t)b * p.shp.H + hd) * S;
+  hm = p.mask.sh ? hd : 0;
+  dqr.init((const T*)p.qrot + ((int64_t)b * p.shp.H + hd) * S * D, D, S, wave, lane);
+  dd.init(dobase, p.dout.ss, S, wave, lane);
+  if (gq > 0) __syncthreads();  // LDS of the previous head's last tile and tile states
+  if constexpr (MASK == MASK_BOOL) {
+    for (int i = tid; i < nqt; i += 512) s_tstate[i] = (uint8_t)tile_state_mem(i);
+    __syncthreads();
+  }
   int qt = next_tile(qt_begin);
   if (qt < nqt) {
     load_tile(qt, sq0, sd0);
@@ -703,10 +716,11 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
     }
     if (has_prev) cols(last ? sq1 : sq0, last ? sd1 : sd0, pf, sf);
   }
+  }  // query heads of the group
 
   if (j < S) {
-    char* vrow = (char*)p.dv + ((int64_t)b * p.dv_sb + (int64_t)hd * p.dv_sh + (int64_t)j * p.dv_ss) * 2;
-    char* krow = (char*)p.dk + ((int64_t)b * p.dk_sb + (int64_t)hd * p.dk_sh + (int64_t)j * p.dk_ss) * 2;
+    char* vrow = (char*)p.dv + ((int64_t)b * p.dv_sb + (int64_t)hk * p.dv_sh + (int64_t)j * p.dv_ss) * 2;
+    char* krow = (char*)p.dk + ((int64_t)b * p.dk_sb + (int64_t)hk * p.dk_sh + (int64_t)j * p.dk_ss) * 2;
     const float* trow = tab + (int64_t)j * D;
     typedef T v4 __attribute__((ext_vector_type(4)));
 #pragma unroll
@@ -740,7 +754,7 @@ static int launch_bwd16_t(const BwdParams& p, void* stream) {
                      (hipStream_t)stream, p);
   int e = (int)hipGetLastError();
   if (e) return e;
-  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL>), dim3(((S + 127) / 128) * BH), dim3(512), 0,
+  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL>), dim3(((S + 127) / 128) * p.shp.B * p.shp.Hkv), dim3(512), 0,
                      (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }

@@ -164,9 +164,10 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   const int m = q0 + wave * 32 + r;
   const int mc = m < S ? m : S - 1;
 
+  const int hk = hd / p.shp.group;  // K/V head (grouped-query attention)
   const T* qbase = (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh;
-  const T* kbase = (const T*)p.k.ptr + b * p.k.sb + hd * p.k.sh;
-  const T* vbase = (const T*)p.v.ptr + b * p.v.sb + hd * p.v.sh;
+  const T* kbase = (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh;
+  const T* vbase = (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh;
   const float* tab = p.tab.ptr + b * p.tab.sb;  // float2 pairs, row stride D/2 pairs = D floats
 
   // ---- Q: load, rotate in fp32, scale by scale*log2(e), round, keep as B fragments --------
@@ -340,7 +341,8 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // row order the score fragments need, as for the rotated K' tiles), its 16-byte chunk c
   // at c ^ k8sw(j); code rows past the padded sequence read as zero.
   auto k8sw = [](int row) __attribute__((always_inline)) { return (row / K8RPB) & (K8CH - 1); };
-  const int8_t* kcodes = QI8 ? p.kc + (int64_t)slice * p.sp * D : nullptr;  // this (b, h) slice
+  const int slice_k = b * p.shp.Hkv + hk;  // (b, K/V head) index into the K codes and scales
+  const int8_t* kcodes = QI8 ? p.kc + (int64_t)slice_k * p.sp * D : nullptr;
   uint32_t k8_voff = 0;
   if constexpr (QI8) {
     const int byte = wave * 1024 + lane * 16;  // this wave's 1 KB share of a code tile
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // int8 variant: s = sum * scale_q * scale_k * scale * log2(e) - m_base
   auto qk_scale = [&](f32x16* sacc, int kt) __attribute__((always_inline)) {
     if constexpr (QI8) {
-      const float f = q8scale * p.ksc[(int64_t)slice * (p.sp / 64) + kt];
+      const float f = q8scale * p.ksc[(int64_t)slice_k * (p.sp / 64) + kt];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll

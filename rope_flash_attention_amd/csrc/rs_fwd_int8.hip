@@ -30,6 +30,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantParams p) {
   static_assert(UPT * 256 == kQuantBlock * UPR, "block split");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z >> 1, which = blockIdx.z & 1;
+  if (h >= p.Hx[which]) return;  // K with fewer heads than Q (grouped-query attention)
   const Opnd x = p.x[which];
   const T* xb = (const T*)x.ptr + b * x.sb + h * x.sh;
   const float* tab = p.tab.ptr + b * p.tab.sb;  // (cos, sin) pairs, D floats per row
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantParams p) {
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float inv = amax > 0.f ? 127.f / amax : 0.f;
 
-  int8_t* cb = p.codes[which] + b * p.c_sb + h * p.c_sh;
+  int8_t* cb = p.codes[which] + b * p.c_sb[which] + h * p.c_sh[which];
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const int u = tid + 256 * i, row = u / UPR, ch = u % UPR;
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantParams p) {
     }
     *(uint2*)(cb + (int64_t)s * D + ch * 8) = make_uint2(w[0], w[1]);
   }
-  if (tid == 0) p.scales[which][((int64_t)b * p.H + h) * p.nblk + blk] = amax > 0.f ? amax / 127.f : 0.f;
+  if (tid == 0) p.scales[which][((int64_t)b * p.Hx[which] + h) * p.nblk + blk] = amax > 0.f ? amax / 127.f : 0.f;
 }
 
 template <typename T>

@@ -64,6 +64,7 @@ rs_status check_bhsd(const rs_tensor* t, int dtype, const int64_t* size, bool em
 
 struct Shape {
   int64_t B, H, S, D;
+  int64_t Hkv;  // heads of K and V (grouped-query attention: H % Hkv == 0)
   bool empty;  // B, H or S is 0: a valid call with nothing to compute
   int dtype;
   float scale;
@@ -108,10 +109,14 @@ rs_status validate_args(const rs_args* a, Shape* out) {
   const int64_t sz[4] = {s.B, s.H, s.S, s.D};
   rs_status st;
   if ((st = check_bhsd(q, dt, sz, s.empty)) != RS_OK) return st;
-  // K and V: same dtype as Q (mixed dtypes, e.g. fp32 Q/K with bf16 V, are rejected)
+  // K and V: same dtype as Q (mixed dtypes, e.g. fp32 Q/K with bf16 V, are rejected), and
+  // Hkv heads with H % Hkv == 0 (grouped-query attention when Hkv < H)
   if (a->k->dtype != dt || a->v->dtype != dt) return RS_ERR_DTYPE;
-  if ((st = check_bhsd(a->k, dt, sz, s.empty)) != RS_OK) return st;
-  if ((st = check_bhsd(a->v, dt, sz, s.empty)) != RS_OK) return st;
+  s.Hkv = a->k->size[1];
+  if (s.H == 0 ? s.Hkv != 0 : (s.Hkv <= 0 || s.H % s.Hkv != 0)) return RS_ERR_SHAPE;
+  const int64_t szkv[4] = {s.B, s.Hkv, s.S, s.D};
+  if ((st = check_bhsd(a->k, dt, szkv, s.empty)) != RS_OK) return st;
+  if ((st = check_bhsd(a->v, dt, szkv, s.empty)) != RS_OK) return st;
   int64_t bt_c = 0, bt_s = 0;
   if ((st = check_table(a->cos, s, &bt_c)) != RS_OK) return st;
   if ((st = check_table(a->sin, s, &bt_s)) != RS_OK) return st;
@@ -196,16 +201,16 @@ Layout layout(const Shape& s, int mask_kind, bool backward, bool int8, bool caus
   if (int8) {
     L.nblk = (s.S + 63) / 64;
     L.sp = L.nblk * 64;
-    const size_t codes = round_up((size_t)(s.B * s.H * L.sp * s.D), 256);
-    const size_t scales = round_up((size_t)(s.B * s.H * L.nblk) * sizeof(float), 256);
+    const size_t qcodes = round_up((size_t)(s.B * s.H * L.sp * s.D), 256);
+    const size_t kcodes = round_up((size_t)(s.B * s.Hkv * L.sp * s.D), 256);
     L.qc = off;
-    off += codes;
+    off += qcodes;
     L.kc = off;
-    off += codes;
+    off += kcodes;
     L.qs = off;
-    off += scales;
+    off += round_up((size_t)(s.B * s.H * L.nblk) * sizeof(float), 256);
     L.ks = off;
-    off += scales;
+    off += round_up((size_t)(s.B * s.Hkv * L.nblk) * sizeof(float), 256);
   }
   if (!backward) {
     const int64_t bm = fwd_block_m(s.dtype), bn = fwd_block_n(s.dtype);
@@ -267,6 +272,8 @@ AttnShape attn_shape(const Shape& s) {
   a.B = (int)s.B;
   a.H = (int)s.H;
   a.S = (int)s.S;
+  a.Hkv = (int)s.Hkv;
+  a.group = s.Hkv > 0 ? (int)(s.H / s.Hkv) : 1;
   a.scale = s.scale;
   a.scale_log2 = (float)((double)s.scale * 1.4426950408889634);
   a.inv_scale = (float)(1.0 / (double)s.scale);
@@ -321,11 +328,14 @@ QuantParams quant_params(const rs_args* a, const Shape& s, const Layout& L, char
   qp.tab.sb = s.Bt > 1 ? s.S * s.D : 0;
   qp.codes[0] = qc;
   qp.codes[1] = kc;
-  qp.c_sh = rows * s.D;
-  qp.c_sb = s.H * rows * s.D;
+  qp.c_sh[0] = qp.c_sh[1] = rows * s.D;
+  qp.c_sb[0] = s.H * rows * s.D;
+  qp.c_sb[1] = s.Hkv * rows * s.D;
   qp.rows = (int)rows;
   qp.scales[0] = qs;
   qp.scales[1] = ks;
+  qp.Hx[0] = (int)s.H;
+  qp.Hx[1] = (int)s.Hkv;
   qp.B = (int)s.B;
   qp.H = (int)s.H;
   qp.S = (int)s.S;
@@ -499,11 +509,12 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   if (st != RS_OK) return fail(st);
   if (a->flags & RS_FLAG_QUANT_INT8_QK) return fail(RS_ERR_UNSUPPORTED);
   const int64_t sz[4] = {s.B, s.H, s.S, s.D};
+  const int64_t szkv[4] = {s.B, s.Hkv, s.S, s.D};
   if (!o || !dout || !dq || !dk || !dv || (!lse && !s.empty)) return fail(RS_ERR_NULL);
   const rs_tensor* ts[5] = {o, dout, dq, dk, dv};
   for (const rs_tensor* t : ts) {
     if (t->data && t->dtype != s.dtype) return fail(RS_ERR_DTYPE);
-    if ((st = check_bhsd(t, s.dtype, sz, s.empty)) != RS_OK) return fail(st);
+    if ((st = check_bhsd(t, s.dtype, (t == dk || t == dv) ? szkv : sz, s.empty)) != RS_OK) return fail(st);
   }
   if (((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
   if (s.empty) return RS_OK;

@@ -39,6 +39,8 @@ struct MaskView {
 
 struct AttnShape {
   int B, H, S;
+  int Hkv, group;    // K/V heads and query heads per K/V head (grouped-query attention:
+                     // query head h reads K/V head h / group); Hkv == H, group == 1 otherwise
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   float inv_scale;   // 1 / scale
@@ -104,10 +106,11 @@ struct PackParams {
 struct QuantParams {
   Opnd x[2];
   Table tab;
-  int8_t* codes[2];     // [B][H][rows][D] with the strides below
-  int64_t c_sb, c_sh;   // element strides of the codes over b and h
-  int rows;             // allocated rows per (b, h) slice (>= S); rows past S are written as 0
-  float* scales[2];     // [B][H][nblk]
+  int8_t* codes[2];        // [B][Hx][rows][D] with the strides below
+  int64_t c_sb[2], c_sh[2];  // element strides of the codes over b and h
+  int rows;                // allocated rows per (b, h) slice (>= S); rows past S are written as 0
+  float* scales[2];        // [B][Hx][nblk]
+  int Hx[2];               // heads of Q (H) and of K (Hkv)
   int B, H, S, D, nblk;
 };
 

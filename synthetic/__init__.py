@@ -33,7 +33,7 @@ import torch
 
 # Independent random streams per tensor role, so that changing one tensor's shape
 # never changes another tensor's values.
-STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_LEN = 1, 2, 3, 4, 5
+STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_LEN, STREAM_TAB = 1, 2, 3, 4, 5, 6
 
 _TORCH_DTYPES = {
     "f32": torch.float32,
@@ -150,20 +150,40 @@ def tiny_fp32(seed: int = 1000) -> Workload:
 
 
 def flux(batch: int = 1, heads: int = 24, n_text: int = 512, grid: int = 64, dtype: str = "bf16",
-         seed: int = 2000, with_grad: bool = False) -> Workload:
-    """FLUX-style joint text+image attention: S = n_text + grid^2, D = 128, 3-axis RoPE (16,56,56)."""
+         seed: int = 2000, with_grad: bool = False, kv_heads: int | None = None,
+         per_sample_tables: bool = False) -> Workload:
+    """FLUX-style joint text+image attention: S = n_text + grid^2, D = 128, 3-axis RoPE (16,56,56).
+
+    kv_heads: K/V head count for grouped-query attention (default: heads).
+    per_sample_tables: one table per batch item ([B, S, D]); item b's image ids are shifted by
+    a seeded offset (r0_b, c0_b) in [0, 64), as for crops taken at different positions.
+    """
     S = n_text + grid * grid
     D = 128
-    cos, sin = rope_tables(flux_ids(n_text, grid), (16, 56, 56), 10000.0)
+    if per_sample_tables:
+        offs = rng(seed, STREAM_TAB).integers(0, 64, size=(batch, 2))
+        tabs = []
+        for b in range(batch):
+            ids = flux_ids(n_text, grid)
+            ids[n_text:, 1] += offs[b, 0]
+            ids[n_text:, 2] += offs[b, 1]
+            tabs.append(rope_tables(ids, (16, 56, 56), 10000.0))
+        cos = torch.stack([t[0] for t in tabs])
+        sin = torch.stack([t[1] for t in tabs])
+    else:
+        c, s = rope_tables(flux_ids(n_text, grid), (16, 56, 56), 10000.0)
+        cos, sin = c[None], s[None]
+    hkv = heads if kv_heads is None else kv_heads
     shape = (batch, heads, S, D)
+    kv_shape = (batch, hkv, S, D)
     w = Workload(
-        f"flux_b{batch}h{heads}s{S}d{D}_{dtype}",
+        f"flux_b{batch}h{heads}kv{hkv}s{S}d{D}_{dtype}",
         normal(seed, STREAM_Q, shape, dtype),
-        normal(seed, STREAM_K, shape, dtype),
-        normal(seed, STREAM_V, shape, dtype),
-        cos[None], sin[None],
+        normal(seed, STREAM_K, kv_shape, dtype),
+        normal(seed, STREAM_V, kv_shape, dtype),
+        cos, sin,
         do=normal(seed, STREAM_DO, shape, dtype) if with_grad else None,
-        meta={"axes": (16, 56, 56), "theta": 10000.0, "n_text": n_text, "grid": grid},
+        meta={"axes": (16, 56, 56), "theta": 10000.0, "n_text": n_text, "grid": grid, "kv_heads": hkv},
     )
     return w
 
@@ -185,8 +205,10 @@ def causal_1axis(batch: int = 4, heads: int = 16, seq: int = 2048, dim: int = 12
 
 
 def random_small(B, H, S, D, dtype="f32", seed=7, mask_kind="none", mask_shape=None, causal=False,
-                 per_sample_tables=False, with_grad=False, std=1.0, theta=10000.0, p_keep=0.7) -> Workload:
-    """Small general case for parity tests: 1-axis RoPE, optional random mask of any broadcast shape."""
+                 per_sample_tables=False, with_grad=False, std=1.0, theta=10000.0, p_keep=0.7,
+                 kv_heads=None) -> Workload:
+    """Small general case for parity tests: 1-axis RoPE, optional random mask of any broadcast
+    shape, optional grouped-query K/V (kv_heads < H)."""
     r = rng(seed, 99)
     if per_sample_tables:
         offs = r.integers(0, 1000, size=B)
@@ -208,11 +230,12 @@ def random_small(B, H, S, D, dtype="f32", seed=7, mask_kind="none", mask_shape=N
         else:
             raise ValueError(mask_kind)
     shape = (B, H, S, D)
+    kv_shape = (B, H if kv_heads is None else kv_heads, S, D)
     return Workload(
         f"small_b{B}h{H}s{S}d{D}_{dtype}_{mask_kind}{'_causal' if causal else ''}",
         normal(seed, STREAM_Q, shape, dtype, std),
-        normal(seed, STREAM_K, shape, dtype, std),
-        normal(seed, STREAM_V, shape, dtype),
+        normal(seed, STREAM_K, kv_shape, dtype, std),
+        normal(seed, STREAM_V, kv_shape, dtype),
         cos, sin, mask=mask, mask_kind=mask_kind, causal=causal,
         do=normal(seed, STREAM_DO, shape, dtype) if with_grad else None,
     )

@@ -59,15 +59,16 @@ struct Case {
   rs_tensor q, k, v, cos, sin, mask, o, dout, dq, dk, dv;
   rs_args a{};
   bool has_mask = false;
-  Case(int dt, int64_t B, int64_t H, int64_t S, int64_t D, int64_t Bt = 1) {
+  Case(int dt, int64_t B, int64_t H, int64_t S, int64_t D, int64_t Bt = 1, int64_t Hkv = -1) {
+    if (Hkv < 0) Hkv = H;
     q = tensor(dt, B, H, S, D);
-    k = tensor(dt, B, H, S, D);
-    v = tensor(dt, B, H, S, D);
+    k = tensor(dt, B, Hkv, S, D);
+    v = tensor(dt, B, Hkv, S, D);
     o = tensor(dt, B, H, S, D);
     dout = tensor(dt, B, H, S, D);
     dq = tensor(dt, B, H, S, D);
-    dk = tensor(dt, B, H, S, D);
-    dv = tensor(dt, B, H, S, D);
+    dk = tensor(dt, B, Hkv, S, D);
+    dv = tensor(dt, B, Hkv, S, D);
     cos = tensor(RS_F32, Bt, 1, S, D);
     sin = tensor(RS_F32, Bt, 1, S, D);
     link();
@@ -136,6 +137,16 @@ int main() {
                   (int)st);
             CHECK(stub::launches > before, "valid call launched nothing");
           }
+  // grouped-query attention: 6 query heads over 3, 2 or 1 K/V heads
+  for (int dt : dts)
+    for (int Hkv : {3, 2, 1})
+      for (int bwd = 0; bwd < 2; ++bwd) {
+        Case c(dt, 2, 6, 300, 128, 1, Hkv);
+        CHECK(run(c, bwd != 0) == RS_OK, "GQA dt=%d Hkv=%d bwd=%d", dt, Hkv, bwd);
+        Case ci(dt == RS_F32 ? RS_BF16 : dt, 2, 6, 300, 128, 1, Hkv);
+        ci.a.flags = RS_FLAG_QUANT_INT8_QK;
+        CHECK(run(ci, false) == RS_OK, "GQA int8 Hkv=%d", Hkv);
+      }
   for (int dt : {RS_F16, RS_BF16})
     for (int S : {64, 77, 4608}) {
       Case c(dt, 1, 4, S, 128);
@@ -166,6 +177,9 @@ int main() {
   { Case c(RS_BF16, 1, 2, 128, 64); c.o.dtype = RS_F16; expect_error(c, false, RS_ERR_DTYPE, "output dtype"); }
   { Case c(RS_BOOL, 1, 2, 128, 64); expect_error(c, false, RS_ERR_DTYPE, "bool q"); }
   { Case c(RS_BF16, 1, 2, 128, 96); expect_error(c, false, RS_ERR_SHAPE, "D = 96"); }
+  { Case c(RS_BF16, 1, 6, 128, 64, 1, 4); expect_error(c, false, RS_ERR_SHAPE, "H % Hkv != 0"); }
+  { Case c(RS_BF16, 1, 6, 128, 64, 1, 2); c.v.size[1] = 3; expect_error(c, false, RS_ERR_SHAPE, "V heads differ from K"); }
+  { Case c(RS_BF16, 1, 6, 128, 64, 1, 2); c.dk.size[1] = 6; expect_error(c, true, RS_ERR_SHAPE, "dK at the query head count"); }
   { Case c(RS_BF16, 1, 2, 128, 64); c.k.size[2] = 127; expect_error(c, false, RS_ERR_SHAPE, "K rows"); }
   { Case c(RS_BF16, 1, 2, 128, 64); c.q.stride[3] = 2; expect_error(c, false, RS_ERR_STRIDE, "stride[3]"); }
   { Case c(RS_BF16, 1, 2, 128, 64); c.v.stride[2] = 65; expect_error(c, false, RS_ERR_STRIDE, "row stride"); }

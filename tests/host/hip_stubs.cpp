@@ -83,12 +83,13 @@ int launch_fwd(int dtype, int D, int, bool, bool int8, const FwdParams& p, void*
   const int B = p.shp.B, H = p.shp.H, S = p.shp.S;
   stub::need(p.tab.ptr, (size_t)(p.tab.sb ? B : 1) * S * D * sizeof(float), "packed tables");
   if (p.mask.tiles) stub::need(p.mask.tiles, 1, "mask tile states");
+  if (p.shp.Hkv <= 0 || H % p.shp.Hkv != 0 || p.shp.group != H / p.shp.Hkv) std::abort();
   if (int8) {
-    const size_t codes = (size_t)B * H * p.sp * D;
-    stub::need(p.qc, codes, "q codes");
-    stub::need(p.kc, codes, "k codes");
+    const int Hkv = p.shp.Hkv;
+    stub::need(p.qc, (size_t)B * H * p.sp * D, "q codes");
+    stub::need(p.kc, (size_t)B * Hkv * p.sp * D, "k codes");
     stub::need(p.qsc, (size_t)B * H * (p.sp / 64) * sizeof(float), "q scales");
-    stub::need(p.ksc, (size_t)B * H * (p.sp / 64) * sizeof(float), "k scales");
+    stub::need(p.ksc, (size_t)B * Hkv * (p.sp / 64) * sizeof(float), "k scales");
   }
   if (p.split_iters > 0) {
     const size_t bm = (size_t)fwd_block_m(dtype), es = dtype == F32 ? 4 : 2;
@@ -107,6 +108,7 @@ int launch_quant_int8(int, const QuantParams& p, void*) {
 int launch_bwd(int dtype, int D, int, bool, const BwdParams& p, void*) {
   ++stub::launches;
   const int B = p.shp.B, H = p.shp.H, S = p.shp.S;
+  if (p.shp.Hkv <= 0 || H % p.shp.Hkv != 0 || p.shp.group != H / p.shp.Hkv) std::abort();
   stub::need(p.tab.ptr, (size_t)(p.tab.sb ? B : 1) * S * D * sizeof(float), "packed tables");
   stub::need(p.delta, (size_t)B * H * S * sizeof(float), "delta");
   if (dtype != F32 && D == 128) stub::need(p.qrot, (size_t)B * H * S * D * 2, "rotated Q");
