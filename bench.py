@@ -168,6 +168,11 @@ def _prepare(dev, extra, train):
                                        torch.full((), float("-inf"), dtype=torch.bfloat16, device=dev)
                                        ).expand(2, 24, S, S).contiguous()
         prep["long"] = to_dev(syn.flux(batch=1, heads=48, grid=128, dtype="bf16", seed=5000), qkvcs)
+        c = syn.zimage_chain()
+        prep["chain"] = (c.x0.to(dev), [k.to(dev) for k in c.ks], [v.to(dev) for v in c.vs], c.cos.to(dev),
+                         c.sin.to(dev))
+        prep["gqa"] = to_dev(syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=740, kv_heads=6,
+                                      per_sample_tables=True), qkvcs)
     if train:
         prep["train_flux"] = to_dev(syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=4100, with_grad=True),
                                     qkvcs + ("do",))
@@ -200,15 +205,53 @@ def _extra_cases(prep, steps, warmup, stream):
         if note:
             out[name]["note"] = note
 
+    timed("long_bf16", prep["long"])  # first: its seconds of work bring the clock to its steady value
     wd, bm = prep["flux_b2"], prep["mask_bool"]
     timed("no_mask_b2", wd, note="reference for the masked B=2 calls")
     timed("mask_bool_key_padding", wd, bm, note="bool [2,1,1,S]; dense flop count")
     timed("mask_all_true", wd, torch.ones_like(bm), note="bool [2,1,1,S] all True (skip path)")
     timed("mask_additive_4d", wd, prep["mask_add"], note="bf16 [2,24,S,S] 0/-inf, 2.04 GB read")
     out["mask_additive_4d"]["mask_read_tb_s"] = round(prep["mask_add"].numel() * 2 / (out["mask_additive_4d"]["ms"] * 1e-3) / 1e12, 3)
-    timed("long_bf16", prep["long"])
     timed("long_int8", prep["long"], quant="int8", note="int8 Q'K'^T + bf16 P.V; flops counted as the dense formula")
+    timed("gqa_per_sample_tables", prep["gqa"],
+          note="B=2, 24 query heads over 6 K/V heads, per-sample 3-axis tables; flops as the dense formula")
+    out["chain_zimage"] = _chain_case(prep["chain"], n, warmup, stream)
     return out
+
+
+def _chain_case(c, steps, warmup, stream):
+    """The pages' chain benchmark: 12 attention layers at the Z-Image shape (1, 30, 4128, 128)
+    bf16, each layer's output the next layer's query.  Fused: one fused RoPE + attention call
+    per layer.  Eager: the rotation pass on the query and on the layer's keys (rope_sdpa_rotate,
+    written to memory), then plain attention on the rotated tensors (the same kernels without
+    rotation).  A step is the whole 12-layer chain."""
+    import torch
+
+    import rope_flash_attention_amd as rfa
+
+    x0, ks, vs, cos, sin = c
+    B, H, S, D = x0.shape
+
+    def fused():
+        x = x0
+        for k, v in zip(ks, vs):
+            x = rfa.rope_scaled_dot_product_attention(x, k, v, cos, sin)
+
+    def eager():
+        x = x0
+        for k, v in zip(ks, vs):
+            x = rfa.scaled_dot_product_attention(rfa.rope_rotate(x, cos, sin), rfa.rope_rotate(k, cos, sin), v)
+
+    with torch.no_grad():  # two interleaved rounds, each variant's mean reported
+        t = [(_events_time(fused, steps, warmup, stream), _events_time(eager, steps, warmup, stream))
+             for _ in range(2)]
+    ms_f = sum(a for a, _ in t) / 2
+    ms_e = sum(b for _, b in t) / 2
+    L = len(ks)
+    return {"layers": L, "shape": f"B={B},H={H},S={S},D={D}", "ms_per_layer_fused": round(ms_f / L, 4),
+            "ms_per_layer_eager": round(ms_e / L, 4), "ms_per_layer_saved": round((ms_e - ms_f) / L, 4),
+            "tflops_fused": round(flops_fwd(B, H, S, D) * L / (ms_f * 1e-3) / 1e12, 2),
+            "tflops_eager": round(flops_fwd(B, H, S, D) * L / (ms_e * 1e-3) / 1e12, 2)}
 
 
 def traffic_from_counters(fetch_db, write_db, command):

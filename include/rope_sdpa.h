@@ -95,7 +95,10 @@ typedef struct {
   const rs_tensor* v;
   /* Pair-duplicated rotation tables (cos[2i] == cos[2i+1]), fp32, sizes [Bt, 1, S, D] with
    * Bt == 1 (shared) or Bt == B (per sample), stride[3] == 1.  Only the even entries are
-   * read; duplication is the caller's precondition (section "Fused RoPE + SDPA"). */
+   * read; duplication is the caller's precondition (section "Fused RoPE + SDPA").
+   * Both NULL: plain attention with Q and K used as given (no rotation; the attention half of
+   * the eager path, e.g. after rope_sdpa_rotate).  rope_sdpa_fwd only: rope_sdpa_bwd and
+   * RS_FLAG_QUANT_INT8_QK then return RS_ERR_UNSUPPORTED.  Exactly one NULL: RS_ERR_NULL. */
   const rs_tensor* cos;
   const rs_tensor* sin;
   /* Optional mask, sizes [Bm, Hm, Sqm, Skm] with each dimension 1 (broadcast) or full
@@ -172,6 +175,19 @@ rs_status rope_sdpa_bwd(const rs_args* args, const rs_tensor* o, const float* ls
 rs_status rope_sdpa_debug_quantize_qk(const rs_args* args, int8_t* q_codes, int8_t* k_codes,
                                       float* q_scales, float* k_scales, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/*
+ * The eager rotation pass on its own: out = R(x) for a [B, H, S, D] operand x (f32, f16 or
+ * bf16, D = 64 or 128) with the same pair-duplicated fp32 tables as rs_args ([Bt, 1, S, D],
+ * Bt == 1 or B): out_2i = x_2i c - x_2i+1 s, out_2i+1 = x_2i s + x_2i+1 c, each product and
+ * sum rounded to fp32 (no fused multiply-add), then the result rounded to the dtype of x.
+ * out has the sizes and dtype of x, any valid strides (it may alias x exactly: in place).
+ * This is the separate pass that the fused forward makes unnecessary (section "Fused RoPE +
+ * SDPA"); it serves callers that keep rotated keys, and the fused-versus-eager comparison.
+ * Same conventions as the other calls (validated first, asynchronous on `stream`).
+ */
+rs_status rope_sdpa_rotate(const rs_tensor* x, const rs_tensor* cos, const rs_tensor* sin, const rs_tensor* out,
+                           void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* rope_sdpa_status_string(rs_status status);

@@ -31,7 +31,8 @@ __all__ = [
     "rope_scaled_dot_product_attention", "rope_sdpa_fwd", "rope_sdpa_bwd", "rope_sdpa_workspace_size",
     "rope_sdpa_get_stats", "rope_sdpa_reset_stats", "rope_sdpa_abi_version", "rope_sdpa_status_string",
     "get_dispatch_stats", "RopeSdpaError", "library_path", "rope_sdpa_debug_quantize_qk", "debug_quantize_qk",
-    "rope_sdpa_fwd_noalloc", "rope_sdpa_noalloc_scratch_bytes",
+    "rope_sdpa_fwd_noalloc", "rope_sdpa_noalloc_scratch_bytes", "rope_sdpa_rotate", "rope_rotate",
+    "scaled_dot_product_attention",
 ]
 
 _DT = {torch.float32: RS_F32, torch.float16: RS_F16, torch.bfloat16: RS_BF16, torch.bool: RS_BOOL}
@@ -102,11 +103,13 @@ class _Call:
 
     def __init__(self, q, k, v, cos4, sin4, mask, mask_kind, causal, scale, int8=False):
         self.tq, self.tk, self.tv = _desc(q), _desc(k), _desc(v)
-        self.tc, self.ts = _desc(cos4), _desc(sin4)
+        self.tc = _desc(cos4) if cos4 is not None else None  # no tables: plain attention
+        self.ts = _desc(sin4) if sin4 is not None else None
         self.tm = _desc(mask) if mask is not None else None
         a = RsArgs()
         a.q, a.k, a.v = ctypes.pointer(self.tq), ctypes.pointer(self.tk), ctypes.pointer(self.tv)
-        a.cos, a.sin = ctypes.pointer(self.tc), ctypes.pointer(self.ts)
+        a.cos = ctypes.pointer(self.tc) if self.tc is not None else None
+        a.sin = ctypes.pointer(self.ts) if self.ts is not None else None
         a.mask = ctypes.pointer(self.tm) if self.tm is not None else None
         a.mask_kind = mask_kind
         a.flags = (RS_FLAG_CAUSAL if causal else 0) | (RS_FLAG_QUANT_INT8_QK if int8 else 0)
@@ -204,6 +207,28 @@ def rope_sdpa_fwd_with_lse(query, key, value, rope_cos, rope_sin, attn_mask=None
                     mask, kind, bool(is_causal), scale, need_lse=True, int8=quantization == "int8")
 
 
+def rope_rotate(x, rope_cos, rope_sin, out=None):
+    """The eager rotation pass: R(x) for a BHSD tensor (its own HIP kernel, rope_sdpa_rotate).
+    Each product and sum in fp32 without fused multiply-add, rounded to x's dtype."""
+    lib = _abi.load()
+    cos4, sin4 = _tables4(rope_cos, x.device), _tables4(rope_sin, x.device)
+    if out is None:
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    tx, tc, ts, to = _desc(x), _desc(cos4), _desc(sin4), _desc(out)
+    _check(lib.rope_sdpa_rotate(ctypes.byref(tx), ctypes.byref(tc), ctypes.byref(ts), ctypes.byref(to),
+                                _stream(x.device)))
+    return out
+
+
+def scaled_dot_product_attention(query, key, value, attn_mask=None, is_causal=False, scale=None):
+    """Plain attention, no rotation (the same HIP forward kernels without the tables): the
+    attention half of the eager path.  Forward only: gradients are not available here."""
+    if torch.is_grad_enabled() and (query.requires_grad or key.requires_grad or value.requires_grad):
+        raise RopeSdpaError(-6)
+    mask, kind = _mask4(attn_mask, query.dtype)
+    return _forward(query, key, value, None, None, mask, kind, bool(is_causal), scale, need_lse=False)[0]
+
+
 def debug_quantize_qk(query, key, rope_cos, rope_sin):
     """The int8 codes and scales the int8 forward computes, for tests.
 
@@ -254,6 +279,10 @@ def rope_sdpa_debug_quantize_qk(args, q_codes_ptr, k_codes_ptr, q_scales_ptr, k_
                                 stream) -> int:
     return _abi.load().rope_sdpa_debug_quantize_qk(args, q_codes_ptr, k_codes_ptr, q_scales_ptr, k_scales_ptr,
                                                    ws_ptr, ws_bytes, stream)
+
+
+def rope_sdpa_rotate(x, cos, sin, out, stream) -> int:
+    return _abi.load().rope_sdpa_rotate(x, cos, sin, out, stream)
 
 
 def rope_sdpa_workspace_size(args, backward: int) -> int:

@@ -21,7 +21,7 @@ RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT8_QK = 1, 2
 EXPORTED = (
     "rope_sdpa_workspace_size", "rope_sdpa_fwd", "rope_sdpa_bwd", "rope_sdpa_status_string",
     "rope_sdpa_get_stats", "rope_sdpa_reset_stats", "rope_sdpa_abi_version", "rope_sdpa_debug_quantize_qk",
-    "rope_sdpa_fwd_noalloc", "rope_sdpa_noalloc_scratch_bytes",
+    "rope_sdpa_fwd_noalloc", "rope_sdpa_noalloc_scratch_bytes", "rope_sdpa_rotate",
 )
 
 
@@ -77,6 +77,8 @@ def load(path: str = LIB_PATH):
     lib.rope_sdpa_fwd_noalloc.restype = ctypes.c_int
     lib.rope_sdpa_noalloc_scratch_bytes.argtypes = []
     lib.rope_sdpa_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.rope_sdpa_rotate.argtypes = [P(RsTensor), P(RsTensor), P(RsTensor), P(RsTensor), ctypes.c_void_p]
+    lib.rope_sdpa_rotate.restype = ctypes.c_int
     lib.rope_sdpa_bwd.argtypes = [P(RsArgs), P(RsTensor), ctypes.c_void_p, P(RsTensor), P(RsTensor), P(RsTensor),
                                   P(RsTensor), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.rope_sdpa_bwd.restype = ctypes.c_int

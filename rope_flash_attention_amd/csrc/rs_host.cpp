@@ -64,6 +64,7 @@ rs_status check_bhsd(const rs_tensor* t, int dtype, const int64_t* size, bool em
 
 struct Shape {
   int64_t B, H, S, D;
+  bool rope;    // rotation tables given (both NULL: plain attention, forward only)
   int64_t Hkv;  // heads of K and V (grouped-query attention: H % Hkv == 0)
   bool empty;  // B, H or S is 0: a valid call with nothing to compute
   int dtype;
@@ -89,7 +90,8 @@ rs_status check_table(const rs_tensor* t, const Shape& s, int64_t* bt) {
 
 // Validates everything both directions share: Q/K/V, tables, mask, flags and scale.
 rs_status validate_args(const rs_args* a, Shape* out) {
-  if (!a || !a->q || !a->k || !a->v || !a->cos || !a->sin) return RS_ERR_NULL;
+  if (!a || !a->q || !a->k || !a->v) return RS_ERR_NULL;
+  if ((a->cos == nullptr) != (a->sin == nullptr)) return RS_ERR_NULL;  // both or neither
   const rs_tensor* q = a->q;
   const int dt = q->dtype;
   if (dt != RS_F32 && dt != RS_F16 && dt != RS_BF16) return RS_ERR_DTYPE;
@@ -117,11 +119,16 @@ rs_status validate_args(const rs_args* a, Shape* out) {
   const int64_t szkv[4] = {s.B, s.Hkv, s.S, s.D};
   if ((st = check_bhsd(a->k, dt, szkv, s.empty)) != RS_OK) return st;
   if ((st = check_bhsd(a->v, dt, szkv, s.empty)) != RS_OK) return st;
-  int64_t bt_c = 0, bt_s = 0;
-  if ((st = check_table(a->cos, s, &bt_c)) != RS_OK) return st;
-  if ((st = check_table(a->sin, s, &bt_s)) != RS_OK) return st;
-  if (bt_c != bt_s) return RS_ERR_SHAPE;
-  s.Bt = bt_c;
+  s.rope = a->cos != nullptr;
+  if (s.rope) {
+    int64_t bt_c = 0, bt_s = 0;
+    if ((st = check_table(a->cos, s, &bt_c)) != RS_OK) return st;
+    if ((st = check_table(a->sin, s, &bt_s)) != RS_OK) return st;
+    if (bt_c != bt_s) return RS_ERR_SHAPE;
+    s.Bt = bt_c;
+  } else {
+    s.Bt = 0;  // no packed tables
+  }
 
   if (a->flags & ~(uint32_t)(RS_FLAG_CAUSAL | RS_FLAG_QUANT_INT8_QK)) return RS_ERR_INVALID;
   const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
@@ -162,7 +169,7 @@ rs_status validate_args(const rs_args* a, Shape* out) {
     return RS_ERR_INVALID;
   }
   if (a->flags & RS_FLAG_QUANT_INT8_QK) {
-    if (dt == RS_F32) return RS_ERR_UNSUPPORTED;
+    if (dt == RS_F32 || !s.rope) return RS_ERR_UNSUPPORTED;
     if (a->mask_kind != RS_MASK_NONE || causal) return RS_ERR_UNSUPPORTED;
   }
   if (a->mask_kind == RS_MASK_BOOL) {
@@ -282,13 +289,15 @@ AttnShape attn_shape(const Shape& s) {
 
 // Enqueues the preparation kernels shared by both directions.
 rs_status prepare(const rs_args* a, const Shape& s, const Layout& L, char* ws, hipStream_t stream) {
-  PackParams pp{};
-  pp.cos = (const float*)a->cos->data;
-  pp.sin = (const float*)a->sin->data;
-  pp.c_sb = a->cos->size[0] > 1 ? a->cos->stride[0] : 0;
-  pp.c_ss = a->cos->stride[2];
-  pp.s_sb = a->sin->size[0] > 1 ? a->sin->stride[0] : 0;
-  pp.s_ss = a->sin->stride[2];
+  PackParams pp{};  // (no tables, Bt = 0: the launch only clears the control words)
+  if (s.rope) {
+    pp.cos = (const float*)a->cos->data;
+    pp.sin = (const float*)a->sin->data;
+    pp.c_sb = a->cos->size[0] > 1 ? a->cos->stride[0] : 0;
+    pp.c_ss = a->cos->stride[2];
+    pp.s_sb = a->sin->size[0] > 1 ? a->sin->stride[0] : 0;
+    pp.s_ss = a->sin->stride[2];
+  }
   pp.out = (float*)(ws + L.table);
   pp.Bt = (int)s.Bt;
   pp.S = (int)s.S;
@@ -434,7 +443,7 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
   p.o_sh = o->stride[1];
   p.o_ss = o->stride[2];
   p.lse = lse;
-  p.tab.ptr = (const float*)(w + L.table);
+  p.tab.ptr = s.rope ? (const float*)(w + L.table) : nullptr;
   p.tab.sb = s.Bt > 1 ? s.S * s.D : 0;
   p.mask = mask_view(a, s, L, w);
   p.shp = attn_shape(s);
@@ -455,7 +464,9 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
     p.part_o = w + L.part;
     p.part_lse = (float*)(w + L.cnt);
   }
-  if (launch_fwd(s.dtype, (int)s.D, a->mask_kind, causal, int8, p, strm) != 0) return fail(RS_ERR_LAUNCH);
+  const int lerr = s.rope ? launch_fwd(s.dtype, (int)s.D, a->mask_kind, causal, int8, p, strm)
+                         : launch_fwd_plain(s.dtype, (int)s.D, a->mask_kind, causal, p, strm);
+  if (lerr != 0) return fail(RS_ERR_LAUNCH);
 
   (lse ? g_ctr.fwd_autograd : g_ctr.fwd_instream).fetch_add(1, std::memory_order_relaxed);
   if (a->mask_kind == RS_MASK_BOOL) g_ctr.masked_bool.fetch_add(1, std::memory_order_relaxed);
@@ -508,6 +519,7 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   rs_status st = validate_args(a, &s);
   if (st != RS_OK) return fail(st);
   if (a->flags & RS_FLAG_QUANT_INT8_QK) return fail(RS_ERR_UNSUPPORTED);
+  if (!s.rope) return fail(RS_ERR_UNSUPPORTED);  // the backward is the fused one: tables required
   const int64_t sz[4] = {s.B, s.H, s.S, s.D};
   const int64_t szkv[4] = {s.B, s.Hkv, s.S, s.D};
   if (!o || !dout || !dq || !dk || !dv || (!lse && !s.empty)) return fail(RS_ERR_NULL);
@@ -557,6 +569,52 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   if (a->mask_kind == RS_MASK_BOOL) g_ctr.masked_bool.fetch_add(1, std::memory_order_relaxed);
   if (a->mask_kind == RS_MASK_ADDITIVE) g_ctr.masked_additive.fetch_add(1, std::memory_order_relaxed);
   if (causal) g_ctr.causal.fetch_add(1, std::memory_order_relaxed);
+  return RS_OK;
+}
+
+rs_status rope_sdpa_rotate(const rs_tensor* x, const rs_tensor* cos, const rs_tensor* sin, const rs_tensor* out,
+                           void* stream) {
+  if (!x || !cos || !sin || !out) return fail(RS_ERR_NULL);
+  const int dt = x->dtype;
+  if (dt != RS_F32 && dt != RS_F16 && dt != RS_BF16) return fail(RS_ERR_DTYPE);
+  Shape s{};
+  s.B = x->size[0];
+  s.H = x->size[1];
+  s.S = x->size[2];
+  s.D = x->size[3];
+  s.dtype = dt;
+  if (s.B < 0 || s.H < 0 || s.S < 0) return fail(RS_ERR_SHAPE);
+  s.empty = s.B == 0 || s.H == 0 || s.S == 0;
+  if (s.D != 64 && s.D != 128) return fail(RS_ERR_SHAPE);
+  if (s.B * s.H * s.S >= ((int64_t)1 << 31)) return fail(RS_ERR_SHAPE);
+  const int64_t sz[4] = {s.B, s.H, s.S, s.D};
+  rs_status st;
+  if ((st = check_bhsd(x, dt, sz, s.empty)) != RS_OK) return fail(st);
+  if (out->data && out->dtype != dt) return fail(RS_ERR_DTYPE);
+  if ((st = check_bhsd(out, dt, sz, s.empty)) != RS_OK) return fail(st);
+  int64_t bt_c = 0, bt_s = 0;
+  if ((st = check_table(cos, s, &bt_c)) != RS_OK) return fail(st);
+  if ((st = check_table(sin, s, &bt_s)) != RS_OK) return fail(st);
+  if (bt_c != bt_s) return fail(RS_ERR_SHAPE);
+  if (s.empty) return RS_OK;
+  if ((st = current_device_ok()) != RS_OK) return fail(st);
+  RotateParams rp{};
+  rp.x = opnd(x);
+  rp.out = out->data;
+  rp.o_sb = out->stride[0];
+  rp.o_sh = out->stride[1];
+  rp.o_ss = out->stride[2];
+  rp.cos = (const float*)cos->data;
+  rp.sin = (const float*)sin->data;
+  rp.c_sb = cos->size[0] > 1 ? cos->stride[0] : 0;
+  rp.c_ss = cos->stride[2];
+  rp.s_sb = sin->size[0] > 1 ? sin->stride[0] : 0;
+  rp.s_ss = sin->stride[2];
+  rp.B = (int)s.B;
+  rp.H = (int)s.H;
+  rp.S = (int)s.S;
+  rp.D = (int)s.D;
+  if (launch_rotate(dt, rp, stream) != 0) return fail(RS_ERR_LAUNCH);
   return RS_OK;
 }
 

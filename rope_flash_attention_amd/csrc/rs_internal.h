@@ -114,6 +114,17 @@ struct QuantParams {
   int B, H, S, D, nblk;
 };
 
+// The eager rotation pass (rope_sdpa_rotate): out = R(x) for a [B, H, S, D] operand.
+struct RotateParams {
+  Opnd x;
+  void* out;
+  int64_t o_sb, o_sh, o_ss;
+  const float* cos;
+  const float* sin;
+  int64_t c_sb, c_ss, s_sb, s_ss;  // element strides of the [Bt, 1, S, D] tables (dims 0 and 2)
+  int B, H, S, D;
+};
+
 struct ClassifyParams {
   MaskView mask;  // bool
   int nb, nh, Sq, Sk;  // mask extents (1 on broadcast dimensions)
@@ -136,6 +147,9 @@ struct SplitPlan {
 };
 SplitPlan fwd_split_plan(int dtype, int D, bool int8, bool causal, int mask_kind, int64_t units, int nkt);
 int launch_fwd(int dtype, int D, int mask_kind, bool causal, bool int8, const FwdParams& p, void* stream);
+// The forward without rotation (no tables: plain attention).
+int launch_fwd_plain(int dtype, int D, int mask_kind, bool causal, const FwdParams& p, void* stream);
+int launch_rotate(int dtype, const RotateParams& p, void* stream);
 int launch_quant_int8(int dtype, const QuantParams& p, void* stream);
 int launch_bwd(int dtype, int D, int mask_kind, bool causal, const BwdParams& p, void* stream);
 // Reads (and optionally clears) the device-side count of all-true bool masks.

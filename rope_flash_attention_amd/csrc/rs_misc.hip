@@ -1,4 +1,4 @@
-// Small preparation kernels that run before attention on the caller's stream:
+// Small kernels around attention on the caller's stream:
 //  * table packing: the caller's pair-duplicated fp32 cos/sin tables (page "Metal Flash
 //    Attention", section "Fused RoPE + SDPA": cos[2i] == cos[2i+1]) are repacked into one
 //    array of (cos, sin) pairs per position, halving the table bytes the attention kernels
@@ -36,6 +36,53 @@ int launch_pack_tables(const PackParams& p, void* stream) {
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(pack_tables_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+
+// The eager rotation pass: out = R(x) over a [B, H, S, D] operand, one 16-byte chunk of a row
+// per thread (8 elements of bf16/fp16, 4 of fp32), reading the even entries of the caller's
+// pair-duplicated fp32 tables.  Each product and sum is rounded to fp32 (no fused
+// multiply-add), then the result to the operand's dtype.  Bound by HBM: one read and one
+// write of x (the tables stay in cache across heads).
+template <typename T>
+__global__ __launch_bounds__(256) void rotate_kernel(RotateParams p) {
+  constexpr int EPC = 16 / (int)sizeof(T);
+  const int cpr = p.D / EPC;  // chunks per row
+  const int64_t n = (int64_t)p.B * p.H * p.S * cpr;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int ch = (int)(i % cpr);
+    int64_t r = i / cpr;
+    const int s = (int)(r % p.S);
+    r /= p.S;
+    const int h = (int)(r % p.H);
+    const int b = (int)(r / p.H);
+    typedef T vE __attribute__((ext_vector_type(EPC)));
+    const vE x = *(const vE*)((const T*)p.x.ptr + b * p.x.sb + h * p.x.sh + (int64_t)s * p.x.ss + ch * EPC);
+    const float* cr = p.cos + b * p.c_sb + (int64_t)s * p.c_ss + ch * EPC;
+    const float* sr = p.sin + b * p.s_sb + (int64_t)s * p.s_ss + ch * EPC;
+    vE y;
+#pragma unroll
+    for (int pp = 0; pp < EPC / 2; ++pp) {
+      const float2 rr = rot_pair(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), cr[2 * pp], sr[2 * pp]);
+      y[2 * pp] = from_f<T>(rr.x);
+      y[2 * pp + 1] = from_f<T>(rr.y);
+    }
+    *(vE*)((T*)p.out + b * p.o_sb + h * p.o_sh + (int64_t)s * p.o_ss + ch * EPC) = y;
+  }
+}
+
+int launch_rotate(int dtype, const RotateParams& p, void* stream) {
+  const int epc = dtype == F32 ? 4 : 8;
+  const int64_t n = (int64_t)p.B * p.H * p.S * (p.D / epc);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  const dim3 g((unsigned)blocks), t(256);
+  switch (dtype) {
+    case F32: hipLaunchKernelGGL(rotate_kernel<float>, g, t, 0, (hipStream_t)stream, p); break;
+    case F16: hipLaunchKernelGGL(rotate_kernel<_Float16>, g, t, 0, (hipStream_t)stream, p); break;
+    default: hipLaunchKernelGGL(rotate_kernel<__bf16>, g, t, 0, (hipStream_t)stream, p); break;
+  }
   return (int)hipGetLastError();
 }
 

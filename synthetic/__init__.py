@@ -34,6 +34,7 @@ import torch
 # Independent random streams per tensor role, so that changing one tensor's shape
 # never changes another tensor's values.
 STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_LEN, STREAM_TAB = 1, 2, 3, 4, 5, 6
+STREAM_LAYER = 100  # + 2 * layer (K) and + 2 * layer + 1 (V) of a chain
 
 _TORCH_DTYPES = {
     "f32": torch.float32,
@@ -240,3 +241,36 @@ def random_small(B, H, S, D, dtype="f32", seed=7, mask_kind="none", mask_shape=N
         do=normal(seed, STREAM_DO, shape, dtype) if with_grad else None,
     )
 
+
+
+@dataclass
+class Chain:
+    """A chain of attention layers with no projections between them: layer l attends with
+    query x_l and its own keys/values (K_l, V_l), and its output is the next query,
+    x_{l+1} = attention(R(x_l), R(K_l), V_l).  Everything both sides need, on the CPU."""
+
+    x0: torch.Tensor
+    ks: list
+    vs: list
+    cos: torch.Tensor
+    sin: torch.Tensor
+
+    @property
+    def layers(self):
+        return len(self.ks)
+
+
+def zimage_chain(layers: int = 12, batch: int = 1, heads: int = 30, n_text: int = 32, grid: int = 64,
+                 dtype: str = "bf16", seed: int = 6000) -> Chain:
+    """The pages' chain benchmark at the Z-Image DiT attention shape (B, H, S, D) =
+    (1, 30, 4128, 128), bf16: S = 32 caption tokens + a 64 x 64 image grid.  The pages give the
+    shape but not the model's position ids or frequencies ("the caller adapts" the tables), so
+    the FLUX-style 3-axis tables (16, 56, 56), theta = 10000, are used: text ids (0, 0, 0),
+    image ids (0, r, c)."""
+    S = n_text + grid * grid
+    D = 128
+    cos, sin = rope_tables(flux_ids(n_text, grid), (16, 56, 56), 10000.0)
+    shape = (batch, heads, S, D)
+    ks = [normal(seed, STREAM_LAYER + 2 * l, shape, dtype) for l in range(layers)]
+    vs = [normal(seed, STREAM_LAYER + 2 * l + 1, shape, dtype) for l in range(layers)]
+    return Chain(normal(seed, STREAM_Q, shape, dtype), ks, vs, cos[None], sin[None])

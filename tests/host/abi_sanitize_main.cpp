@@ -153,6 +153,35 @@ int main() {
       c.a.flags = RS_FLAG_QUANT_INT8_QK;
       CHECK(run(c, false) == RS_OK, "int8 forward S=%d", S);
     }
+  // plain attention (no tables): forward only
+  for (int dt : dts)
+    for (int variant = 0; variant < 3; ++variant) {
+      Case c(dt, 2, 3, 300, 128);
+      c.a.cos = c.a.sin = nullptr;
+      if (variant == 1) c.a.flags = RS_FLAG_CAUSAL;
+      if (variant == 2) c.set_mask(RS_MASK_BOOL, RS_BOOL, 2, 1, 1, 300);
+      c.a.cos = c.a.sin = nullptr;  // (set_mask relinks them)
+      CHECK(run(c, false) == RS_OK, "plain forward dt=%d variant=%d", dt, variant);
+      c.a.cos = c.a.sin = nullptr;
+      expect_error(c, true, RS_ERR_UNSUPPORTED, "plain backward");
+    }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.a.sin = nullptr; expect_error(c, false, RS_ERR_NULL, "one table missing"); }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.a.cos = c.a.sin = nullptr; c.a.flags = RS_FLAG_QUANT_INT8_QK;
+    expect_error(c, false, RS_ERR_UNSUPPORTED, "int8 without tables"); }
+  // the eager rotation pass
+  for (int dt : dts) {
+    Case c(dt, 2, 3, 77, 128, 2);
+    const int before = stub::launches;
+    CHECK(rope_sdpa_rotate(&c.q, &c.cos, &c.sin, &c.o, nullptr) == RS_OK, "rotate dt=%d", dt);
+    CHECK(rope_sdpa_rotate(&c.q, &c.cos, &c.sin, &c.q, nullptr) == RS_OK, "rotate in place dt=%d", dt);
+    CHECK(stub::launches == before + 2, "rotate launches");
+    c.o.dtype = dt == RS_F32 ? RS_BF16 : RS_F32;
+    CHECK(rope_sdpa_rotate(&c.q, &c.cos, &c.sin, &c.o, nullptr) == RS_ERR_DTYPE, "rotate out dtype");
+    CHECK(rope_sdpa_rotate(&c.q, &c.cos, nullptr, &c.o, nullptr) == RS_ERR_NULL, "rotate without sin");
+    Case e(dt, 2, 3, 77, 96);
+    CHECK(rope_sdpa_rotate(&e.q, &e.cos, &e.sin, &e.o, nullptr) == RS_ERR_SHAPE, "rotate D = 96");
+    CHECK(stub::launches == before + 2, "rotate launched on error");
+  }
   // empty calls: no workspace, nothing launched, data pointers may be NULL
   for (int e = 0; e < 3; ++e) {
     Case c(RS_BF16, e == 0 ? 0 : 2, e == 1 ? 0 : 3, e == 2 ? 0 : 64, 64);

@@ -99,6 +99,18 @@ int launch_fwd(int dtype, int D, int, bool, bool int8, const FwdParams& p, void*
   return 0;
 }
 
+int launch_fwd_plain(int, int, int, bool, const FwdParams& p, void*) {
+  ++stub::launches;
+  if (p.tab.ptr != nullptr) std::abort();  // plain attention reads no tables
+  return 0;
+}
+
+int launch_rotate(int, const RotateParams& p, void*) {
+  ++stub::launches;
+  if (!p.cos || !p.sin || !p.out || p.B <= 0 || p.H <= 0 || p.S <= 0 || (p.D != 64 && p.D != 128)) std::abort();
+  return 0;
+}
+
 int launch_quant_int8(int, const QuantParams& p, void*) {
   ++stub::launches;
   stub::need(p.tab.ptr, (size_t)(p.tab.sb ? p.B : 1) * p.S * p.D * sizeof(float), "packed tables");
