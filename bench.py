@@ -212,7 +212,11 @@ def _extra_cases(prep, steps, warmup, stream):
     timed("mask_all_true", wd, torch.ones_like(bm), note="bool [2,1,1,S] all True (skip path)")
     timed("mask_additive_4d", wd, prep["mask_add"], note="bf16 [2,24,S,S] 0/-inf, 2.04 GB read")
     out["mask_additive_4d"]["mask_read_tb_s"] = round(prep["mask_add"].numel() * 2 / (out["mask_additive_4d"]["ms"] * 1e-3) / 1e12, 3)
-    timed("long_int8", prep["long"], quant="int8", note="int8 Q'K'^T + bf16 P.V; flops counted as the dense formula")
+    timed("long_int8", prep["long"], quant="int8",
+          note="int8 Q'K'^T (Q', K' quantized in the attention kernel, no codes in memory) + bf16 P.V; "
+               "flops counted as the dense formula")
+    timed("long_int8_prepass", prep["long"], quant="int8_prepass",
+          note="the same int8 forward with a quantizer pass writing the codes first (bit-identical output)")
     timed("gqa_per_sample_tables", prep["gqa"],
           note="B=2, 24 query heads over 6 K/V heads, per-sample 3-axis tables; flops as the dense formula")
     out["chain_zimage"] = _chain_case(prep["chain"], n, warmup, stream)

@@ -72,8 +72,9 @@ typedef enum { RS_F32 = 0, RS_F16 = 1, RS_BF16 = 2, RS_BOOL = 3 } rs_dtype;
 typedef enum { RS_MASK_NONE = 0, RS_MASK_BOOL = 1, RS_MASK_ADDITIVE = 2 } rs_mask_kind;
 
 enum {
-  RS_FLAG_CAUSAL = 1u << 0,       /* exclude key j > query i; cannot be combined with a mask */
-  RS_FLAG_QUANT_INT8_QK = 1u << 1 /* forward only: blockwise int8 Q'/K' (see rope_sdpa_fwd) */
+  RS_FLAG_CAUSAL = 1u << 0,          /* exclude key j > query i; cannot be combined with a mask */
+  RS_FLAG_QUANT_INT8_QK = 1u << 1,   /* forward only: blockwise int8 Q'/K' (see rope_sdpa_fwd) */
+  RS_FLAG_QUANT_INT8_PREPASS = 1u << 2 /* with RS_FLAG_QUANT_INT8_QK: codes from a quantizer pass */
 };
 
 typedef struct {
@@ -123,11 +124,15 @@ rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* by
  * rope_sdpa_bwd needs.  An all-true bool mask is detected on the device and then costs no
  * per-element mask reads.
  * RS_FLAG_QUANT_INT8_QK (bf16/f16 inputs, no mask, no causal, lse may be NULL): after the
- * fp32 rotation, Q' and K' are quantized per (b, h, 64-token block) to int8 codes
- * round-half-even(x * fp32(127/amax)) with scale amax/127, QK^T runs on int8 MFMA with exact
- * int32 accumulation, and P.V stays in the input precision (pages: "Requirements" and
- * "Enable In SimpleTuner" name an int8 blockwise mode; what is quantized is this library's
- * reading).
+ * fp32 rotation (each product and sum rounded), Q' and K' are quantized per (b, h, 64-token
+ * block) to int8 codes round-half-even(x * fp32(127/amax)) with scale amax/127, QK^T runs on
+ * int8 MFMA with exact int32 accumulation, and P.V stays in the input precision (pages:
+ * "Requirements" and "Enable In SimpleTuner" name an int8 blockwise mode; what is quantized
+ * is this library's reading).  The attention kernel quantizes in registers: no code reaches
+ * memory.  With RS_FLAG_QUANT_INT8_PREPASS as well, a quantizer pass writes the codes and
+ * scales of Q' and K' to the workspace first (one byte per element) and the attention kernel
+ * streams them: the same codes and the same results bit for bit, faster, because each K
+ * block is quantized once instead of once per query tile.
  */
 rs_status rope_sdpa_fwd(const rs_args* args, const rs_tensor* o, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);

@@ -24,8 +24,13 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import (RS_BF16, RS_BOOL, RS_F16, RS_F32, RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT8_QK,
-                   RS_MASK_ADDITIVE, RS_MASK_BOOL, RS_MASK_NONE, RsArgs, RsStats, make_tensor)
+from ._abi import (RS_BF16, RS_BOOL, RS_F16, RS_F32, RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT8_PREPASS,
+                   RS_FLAG_QUANT_INT8_QK, RS_MASK_ADDITIVE, RS_MASK_BOOL, RS_MASK_NONE, RsArgs, RsStats,
+                   make_tensor)
+
+# quantization= values -> flags: "int8" quantizes in the attention kernel (no codes in memory),
+# "int8_prepass" has a quantizer pass write the codes first (same results, faster)
+_QUANT_FLAGS = {None: 0, "int8": RS_FLAG_QUANT_INT8_QK, "int8_prepass": RS_FLAG_QUANT_INT8_QK | RS_FLAG_QUANT_INT8_PREPASS}
 
 __all__ = [
     "rope_scaled_dot_product_attention", "rope_sdpa_fwd", "rope_sdpa_bwd", "rope_sdpa_workspace_size",
@@ -101,7 +106,7 @@ def _mask4(mask: torch.Tensor | None, qdtype):
 class _Call:
     """Holds the ctypes descriptors of one call (kept alive for the duration of the call)."""
 
-    def __init__(self, q, k, v, cos4, sin4, mask, mask_kind, causal, scale, int8=False):
+    def __init__(self, q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant=None):
         self.tq, self.tk, self.tv = _desc(q), _desc(k), _desc(v)
         self.tc = _desc(cos4) if cos4 is not None else None  # no tables: plain attention
         self.ts = _desc(sin4) if sin4 is not None else None
@@ -112,7 +117,7 @@ class _Call:
         a.sin = ctypes.pointer(self.ts) if self.ts is not None else None
         a.mask = ctypes.pointer(self.tm) if self.tm is not None else None
         a.mask_kind = mask_kind
-        a.flags = (RS_FLAG_CAUSAL if causal else 0) | (RS_FLAG_QUANT_INT8_QK if int8 else 0)
+        a.flags = (RS_FLAG_CAUSAL if causal else 0) | _QUANT_FLAGS[quant]
         a.scale = 0.0 if scale is None else float(scale)
         self.args = a
 
@@ -126,9 +131,9 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _forward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, need_lse, int8=False):
+def _forward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, need_lse, quant=None):
     lib = _abi.load()
-    call = _Call(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, int8)
+    call = _Call(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant)
     B, H, S, D = q.shape
     o = torch.empty((B, H, S, D), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if need_lse else None
@@ -178,7 +183,9 @@ def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, att
                                       scale=None, quantization=None):
     """softmax(scale * R(Q) R(K)^T + mask) V with R the interleaved-pair rotation of the tables.
 
-    quantization: None, or "int8" for the blockwise int8 Q'/K' forward (no gradient).
+    quantization: None, "int8" for the blockwise int8 Q'/K' forward quantized in the attention
+    kernel, or "int8_prepass" for the same forward with the codes written by a quantizer pass
+    first (bit-identical results, faster); no gradient.
     """
     if not (query.is_cuda and key.is_cuda and value.is_cuda):
         raise ValueError("query, key and value must be device tensors")
@@ -187,13 +194,13 @@ def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, att
     cos4 = _tables4(rope_cos, query.device)
     sin4 = _tables4(rope_sin, query.device)
     mask, kind = _mask4(attn_mask, query.dtype)
-    if quantization not in (None, "int8"):
-        raise ValueError("quantization must be None or 'int8'")
+    if quantization not in _QUANT_FLAGS:
+        raise ValueError("quantization must be None, 'int8' or 'int8_prepass'")
     needs_grad = torch.is_grad_enabled() and (query.requires_grad or key.requires_grad or value.requires_grad)
-    if quantization == "int8":
+    if quantization is not None:
         if needs_grad:
             raise RopeSdpaError(-6)
-        return _forward(query, key, value, cos4, sin4, mask, kind, is_causal, scale, False, int8=True)[0]
+        return _forward(query, key, value, cos4, sin4, mask, kind, is_causal, scale, False, quant=quantization)[0]
     if needs_grad:
         return _RopeSdpaFn.apply(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale)
     return _forward(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale, need_lse=False)[0]
@@ -204,7 +211,7 @@ def rope_sdpa_fwd_with_lse(query, key, value, rope_cos, rope_sin, attn_mask=None
     """Forward returning (O, LSE) without autograd (LSE is fp32 [B, H, S], natural log)."""
     mask, kind = _mask4(attn_mask, query.dtype)
     return _forward(query, key, value, _tables4(rope_cos, query.device), _tables4(rope_sin, query.device),
-                    mask, kind, bool(is_causal), scale, need_lse=True, int8=quantization == "int8")
+                    mask, kind, bool(is_causal), scale, need_lse=True, quant=quantization)
 
 
 def rope_rotate(x, rope_cos, rope_sin, out=None):
@@ -236,7 +243,7 @@ def debug_quantize_qk(query, key, rope_cos, rope_sin):
     """
     lib = _abi.load()
     cos4, sin4 = _tables4(rope_cos, query.device), _tables4(rope_sin, query.device)
-    call = _Call(query, key, key, cos4, sin4, None, 0, False, None, int8=True)
+    call = _Call(query, key, key, cos4, sin4, None, 0, False, None, quant="int8")
     B, H, S, D = query.shape
     nb = -(-S // 64)
     Hkv = key.shape[1]

@@ -7,13 +7,26 @@
 
 namespace rs {
 
-int launch_fwd(int dtype, int D, int mask_kind, bool causal, bool int8, const FwdParams& p, void* stream) {
-  if (int8) return dtype == F16 ? launch_fwd_int8<_Float16>(D, p, stream) : launch_fwd_int8<__bf16>(D, p, stream);
+int launch_fwd(int dtype, int D, int mask_kind, bool causal, int int8, const FwdParams& p, void* stream) {
+  if (int8)
+    return dtype == F16 ? launch_fwd_int8<_Float16>(D, int8, p, stream) : launch_fwd_int8<__bf16>(D, int8, p, stream);
   switch (dtype) {
     case F32: return launch_fwd_dt<float, true>(D, mask_kind, causal, p, stream);
     case F16: return launch_fwd_dt<_Float16, true>(D, mask_kind, causal, p, stream);
     default: return launch_fwd_dt<__bf16, true>(D, mask_kind, causal, p, stream);
   }
+}
+
+// The int8 forward in code export mode (tests): one workgroup per unit, no split, no output.
+template <typename T>
+static int launch_fwd_int8_export_t(int D, const FwdParams& p, void* stream) {
+  return D == 64 ? launch_fwd_t<T, 64, MASK_NONE, false, 1, true, true>(p, stream)
+                 : launch_fwd_t<T, 128, MASK_NONE, false, 1, true, true>(p, stream);
+}
+
+int launch_fwd_int8_export(int dtype, int D, const FwdParams& p, void* stream) {
+  return dtype == F16 ? launch_fwd_int8_export_t<_Float16>(D, p, stream)
+                      : launch_fwd_int8_export_t<__bf16>(D, p, stream);
 }
 
 int fwd_block_m(int dtype) { return dtype == F32 ? FwdCfg<float>::BM : FwdCfg<__bf16>::BM; }
@@ -23,7 +36,7 @@ int fwd_waves(int dtype) { return (dtype == F32 ? FwdCfg<float>::NT : FwdCfg<__b
 template <typename T, int D, bool QI8>
 static int resident_per_cu() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<T, D, MASK_NONE, false, QI8>, FwdCfg<T>::NT, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<T, D, MASK_NONE, false, QI8 ? 1 : 0>, FwdCfg<T>::NT, 0) !=
       hipSuccess)
     return 0;
   return n;

@@ -79,14 +79,20 @@ constexpr int kMaxStateTiles = kMaxBoolMaskSeq / 32;  // key tiles (32 keys or m
 constexpr int QK_AHEAD = 4;  // K' fragment reads kept in flight ahead of the QK^T products
 constexpr int PV_AHEAD = 3;  // V^T fragments (two reads each) in flight ahead of the P.V products
 
-// QI8: blockwise int8 variant.  Q' and K' arrive as int8 codes with one fp32 scale per
-// (b, h, 64-token block), written beforehand by the quantization kernel; Q'K'^T runs on
-// int8 MFMA with exact int32 sums, which are scaled into the fp32 scores once per tile.
+// QI8: blockwise int8 variant; Q'K'^T runs on int8 MFMA with exact int32 sums, scaled into
+// the fp32 scores once per tile.  QI8 = 1: the rotated Q' and K' are quantized here, per
+// (b, h, 64-token block), to int8 codes with one fp32 scale: Q once per workgroup from its
+// own four 64-row blocks, K per 64-key tile (one tile is one block) with the tile's amax
+// reduced over the workgroup through LDS; no code reaches memory.  QI8 = 2: the codes and
+// scales come from the quantizer pass (quant_kernel) and K code tiles go straight into LDS.
+// QEXP (with QI8 = 1): code export mode for tests, which writes the codes and scales
+// instead of the output.
 // ROPE = false: plain attention, Q and K used as given (no tables read, no rotation).
-template <typename T, int D, int MASK, bool CAUSAL, bool QI8 = false, bool ROPE = true>
+template <typename T, int D, int MASK, bool CAUSAL, int QI8 = 0, bool ROPE = true, bool QEXP = false>
 __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   static_assert(!QI8 || (sizeof(T) == 2 && MASK == MASK_NONE && !CAUSAL), "int8 variant: 16-bit, unmasked");
   static_assert(ROPE || !QI8, "the int8 variant rotates");
+  static_assert(!QEXP || QI8 == 1, "code export is the in-kernel int8 mode");
   using M = Mf<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = 2 * KPL;
@@ -136,6 +142,10 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) char sm0[MBYTES];
   __shared__ __attribute__((aligned(16))) char sm1[MBYTES];
 
+  if (p.gate_mode != 0) {  // bool mask: run only if this is the right kernel for the mask
+    const unsigned some_excluded = __builtin_amdgcn_readfirstlane(p.gate[0]);
+    if ((some_excluded == 0u) != (p.gate_mode == 1)) return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, hh = lane >> 5;
   const int S = p.shp.S;
@@ -173,16 +183,75 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   const float* tab = p.tab.ptr + b * p.tab.sb;  // float2 pairs, row stride D/2 pairs = D floats
 
   // ---- Q: load, rotate in fp32, scale by scale*log2(e), round, keep as B fragments --------
-  // (int8 variant: the codes of this lane's row; the scales enter once per tile)
-  using QF = typename std::conditional<QI8, i32x4[NQ8], frag[NQK]>::type;
+  // (int8 variant: rotated, quantized with the amax of its 64-row block, kept as codes; the
+  // scales enter once per tile)
+  using QF = typename std::conditional<QI8 != 0, i32x4[NQ8], frag[NQK]>::type;
   QF qf;
-  const int slice = b * p.shp.H + hd;  // (b, h) index into the int8 codes and scales
   float q8scale = 0.f;
-  if constexpr (QI8) {
+  const int nblk = (S + 63) / 64;  // int8 quantization blocks of a (b, h) slice
+  if constexpr (QI8 == 2) {
+    const int slice = b * p.shp.H + hd;  // (b, h) index into the codes and scales
     const int8_t* qrow = p.qc + ((int64_t)slice * p.sp + mc) * D;
 #pragma unroll
     for (int t = 0; t < NQ8; ++t) qf[t] = *(const i32x4*)(qrow + 32 * t + 16 * hh);
     q8scale = p.qsc[(int64_t)slice * (p.sp / 64) + mc / 64] * c2;  // mc < S: always a valid block
+  } else if constexpr (QI8 == 1) {
+    // this lane holds elements 32t + 16hh + e (e < 16) of row mc, rotated with every product
+    // and sum rounded to fp32 (the quantizer's integer decisions are then reproducible)
+    const T* qrow = qbase + (int64_t)mc * p.q.ss;
+    const float* trow = tab + (int64_t)mc * D;
+    float qv[NQ8][16];
+    float amx = 0.f;
+#pragma unroll
+    for (int t = 0; t < NQ8; ++t) {
+      const int d0 = 32 * t + 16 * hh;
+      typedef T v8 __attribute__((ext_vector_type(8)));
+      const v8 xa = *(const v8*)(qrow + d0), xb = *(const v8*)(qrow + d0 + 8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 cs = *(const float4*)(trow + d0 + 4 * u);  // pairs (d0 + 4u) / 2 + {0, 1}
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          const int e = 4 * u + 2 * w2;
+          const float x0 = to_f(e < 8 ? xa[e] : xb[e - 8]), x1 = to_f(e < 8 ? xa[e + 1] : xb[e - 7]);
+          const float2 rr = rot_pair(x0, x1, w2 ? cs.z : cs.x, w2 ? cs.w : cs.y);
+          qv[t][e] = rr.x;
+          qv[t][e + 1] = rr.y;
+          amx = fmaxf(amx, fmaxf(fabsf(rr.x), fabsf(rr.y)));
+        }
+      }
+    }
+    if (m >= S) amx = 0.f;  // a block's amax is over its valid rows
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amx = fmaxf(amx, __shfl_xor(amx, off, 64));
+    // a 64-row block is the 32 rows of waves 2j and 2j + 1
+    __shared__ float s_qamax[NW];
+    if (lane == 0) s_qamax[wave] = amx;
+    __syncthreads();
+    const float am = fmaxf(s_qamax[wave & ~1], s_qamax[wave | 1]);
+    const float inv = am > 0.f ? 127.f / am : 0.f;
+    const float qsc = am > 0.f ? am / 127.f : 0.f;
+#pragma unroll
+    for (int t = 0; t < NQ8; ++t) {
+      uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float c = fminf(fmaxf(__builtin_rintf(qv[t][e] * inv), -127.f), 127.f);  // half to even
+        wv[e >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (e & 3));
+      }
+      qf[t] = i32x4{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+    }
+    q8scale = qsc * c2;
+    if constexpr (QEXP) {
+      if (m < S) {
+        int8_t* crow = p.xq_codes + (((int64_t)b * p.shp.H + hd) * S + m) * D;
+#pragma unroll
+        for (int t = 0; t < NQ8; ++t) *(i32x4*)(crow + 32 * t + 16 * hh) = qf[t];
+      }
+      const int row0 = q0 + 32 * wave;
+      if (lane == 0 && (wave & 1) == 0 && row0 < S)
+        p.xq_scales[((int64_t)b * p.shp.H + hd) * nblk + row0 / 64] = qsc;
+    }
   } else {
     const T* qrow = qbase + (int64_t)mc * p.q.ss;
     const float* trow = tab + (int64_t)mc * D;
@@ -319,7 +388,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // past S read as zeros, and every call issues the same loads (so the wait for them can
   // let later loads stay in flight)
   auto load_k_rows = [&](int kt) __attribute__((always_inline)) {
-    if constexpr (QI8) return;
+    if constexpr (QI8 == 2) return;
     const __amdgpu_buffer_rsrc_t krs = rows_rsrc(kbase, kt * BN, S, (int)p.k.ss * ES, D * ES);
 #pragma unroll
     for (int it = 0; it < KCPT; ++it)
@@ -327,7 +396,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
                                              krs, (uint32_t)((k_off + it * KROWS_PER_IT * (int)p.k.ss) * ES), 0, 0));
   };
   auto load_k_tab = [&](int kt) __attribute__((always_inline)) {
-    if constexpr (QI8 || !ROPE) return;
+    if constexpr (!ROPE || QI8 == 2) return;
     const __amdgpu_buffer_rsrc_t trs = rows_rsrc(tab, kt * BN, S, D * 4, D * 4);
 #pragma unroll
     for (int it = 0; it < KCPT; ++it)
@@ -348,27 +417,84 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     for (int i = 0; i < VLD; ++i) buffer_load_lds16(rs, sV + (wave * VLD + i) * 1024, v_voff[i], 0);
   };
 
-  // int8 variant: K' code tile straight into LDS.  LDS row j holds key perm_row(j) (the
-  // row order the score fragments need, as for the rotated K' tiles), its 16-byte chunk c
-  // at c ^ k8sw(j); code rows past the padded sequence read as zero.
+  // int8 variant: the K' code tile in LDS.  LDS row j holds key perm_row(j) (the row order
+  // the score fragments need, as for the rotated K' tiles), its 16-byte chunk c (codes
+  // 16c .. 16c + 15) at c ^ k8sw(j).
   auto k8sw = [](int row) __attribute__((always_inline)) { return (row / K8RPB) & (K8CH - 1); };
+  // the amax of the K tile being quantized, one value per wave; two slots, alternating with
+  // the destination buffer, so that a wave writing the next tile's slot never overtakes one
+  // still reading the previous tile's
+  __shared__ float s_kamax[QI8 ? 2 : 1][NW];
+  const int hk_export = QEXP && qt == 0 && hd % p.shp.group == 0;  // one writer per (b, K/V head)
+  // codes from the quantizer pass: this wave's 1 KB share of a code tile straight into LDS
+  // (code rows past the padded sequence read as zero)
   const int slice_k = b * p.shp.Hkv + hk;  // (b, K/V head) index into the K codes and scales
-  const int8_t* kcodes = QI8 ? p.kc + (int64_t)slice_k * p.sp * D : nullptr;
+  const int8_t* kcodes = QI8 == 2 ? p.kc + (int64_t)slice_k * p.sp * D : nullptr;
   uint32_t k8_voff = 0;
-  if constexpr (QI8) {
-    const int byte = wave * 1024 + lane * 16;  // this wave's 1 KB share of a code tile
+  if constexpr (QI8 == 2) {
+    const int byte = wave * 1024 + lane * 16;
     const int row = byte / D, pch = (byte % D) / 16;
     k8_voff = (uint32_t)(perm_row(row) * D + ((pch ^ k8sw(row)) << 4));
   }
   auto dma_k = [&](int kt, char* sK) __attribute__((always_inline)) {
-    if constexpr (QI8) {
+    if constexpr (QI8 == 2) {
       if (wave < K8LD)
         buffer_load_lds16(tile_rsrc(kcodes, (int64_t)kt * BN * D, (int64_t)p.sp * D), sK + wave * 1024, k8_voff, 0);
     }
   };
 
-  auto store_tile = [&](char* sK) __attribute__((always_inline)) {
-    if constexpr (QI8) return;
+  // K' of the tile held in kx/kt4 into LDS buffer sK (tile kt: int8 export only).  int8
+  // variant: rotate (fp32, rounded products), reduce the tile's amax over the workgroup,
+  // quantize, store codes; returns the tile's scale (other variants: 0).
+  auto store_tile = [&](char* sK, int kt) __attribute__((always_inline)) -> float {
+    if constexpr (QI8 == 2) return kt < nkt_all ? p.ksc[(int64_t)slice_k * (p.sp / 64) + kt] : 0.f;
+    if constexpr (QI8 == 1) {
+      float kv[KCPT][8];
+      float amx = 0.f;
+#pragma unroll
+      for (int it = 0; it < KCPT; ++it) {
+        const float* tf = (const float*)&kt4[it][0];
+        typedef T v8 __attribute__((ext_vector_type(8)));
+        const v8 x = *(const v8*)&kx[it];
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const float2 rr = rot_pair(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), tf[2 * pp], tf[2 * pp + 1]);
+          kv[it][2 * pp] = rr.x;
+          kv[it][2 * pp + 1] = rr.y;
+          amx = fmaxf(amx, fmaxf(fabsf(rr.x), fabsf(rr.y)));  // rows past S were read as zeros
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) amx = fmaxf(amx, __shfl_xor(amx, off, 64));
+      const int slot = sK == sk0 ? 0 : 1;
+      if (lane == 0) s_kamax[slot][wave] = amx;
+      __syncthreads();
+      float am = s_kamax[slot][0];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) am = fmaxf(am, s_kamax[slot][w2]);
+      const float inv = am > 0.f ? 127.f / am : 0.f;
+#pragma unroll
+      for (int it = 0; it < KCPT; ++it) {
+        uint32_t wv[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float c = fminf(fmaxf(__builtin_rintf(kv[it][e] * inv), -127.f), 127.f);
+          wv[e >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (e & 3));
+        }
+        const int key = k_key0 + it * KROWS_PER_IT, lrow = perm_row(key);
+        *(uint2*)(sK + lrow * D + (((k_cc >> 1) ^ k8sw(lrow)) << 4) + (k_cc & 1) * 8) = make_uint2(wv[0], wv[1]);
+        if constexpr (QEXP) {
+          const int j = kt * BN + key;
+          if (hk_export && kt < nkt_all && j < S)
+            *(uint2*)(p.xk_codes + (((int64_t)b * p.shp.Hkv + hk) * S + j) * D + k_cc * 8) = make_uint2(wv[0], wv[1]);
+        }
+      }
+      const float ksc = am > 0.f ? am / 127.f : 0.f;
+      if constexpr (QEXP) {
+        if (hk_export && kt < nkt_all && tid == 0) p.xk_scales[((int64_t)b * p.shp.Hkv + hk) * nblk + kt] = ksc;
+      }
+      return ksc;
+    }
 #pragma unroll
     for (int it = 0; it < KCPT; ++it) {
       const float* tf = (const float*)&kt4[it][0];  // (c, s) per pair
@@ -399,6 +525,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
       }
       *(uint4*)(sK + perm_row(k_key0 + it * KROWS_PER_IT) * KP + k_cc * 16) = outw;
     }
+    return 0.f;
   };
 
   // ---- online softmax state ----------------------------------------------------------------
@@ -427,10 +554,11 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   }
 
   // S^T - m_base = K' Q'^T + C for one tile: rows = keys, columns = this wave's 32 queries.
-  // (int8 variant: exact integer sums into ia; qk_scale turns them into scores.)
-  i32x16 ia[QI8 ? NKB : 1];
-  auto qk = [&](const char* sK, f32x16* sacc) __attribute__((always_inline)) {
+  // (int8 variant: exact integer sums per 32-key block, turned into scores right away with
+  // the tile's K scale ksc: s = sum * scale_q * scale_k * scale * log2(e) - m_base.)
+  auto qk = [&](const char* sK, f32x16* sacc, float ksc) __attribute__((always_inline)) {
     if constexpr (QI8) {
+      const float f = q8scale * ksc;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         i32x4 ka[NQ8];
@@ -438,9 +566,11 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int t = 0; t < NQ8; ++t)
           ka[t] = *(const i32x4*)(sK + row * D + (((2 * t + hh) ^ k8sw(row)) << 4));
+        i32x16 ia = izero16();
 #pragma unroll
-        for (int t = 0; t < NQ8; ++t)
-          ia[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[t], qf[t], t == 0 ? izero16() : ia[kb], 0, 0, 0);
+        for (int t = 0; t < NQ8; ++t) ia = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[t], qf[t], ia, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = fmaf((float)ia[i], f, -m_base);
       }
     } else {
 #pragma unroll
@@ -451,16 +581,6 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int t = 0; t < NQK; ++t) sacc[kb] = M::mma(ka[t], qf[t], t == 0 ? (kAddMask ? zero16() : negm) : sacc[kb]);
       }
-    }
-  };
-  // int8 variant: s = sum * scale_q * scale_k * scale * log2(e) - m_base
-  auto qk_scale = [&](f32x16* sacc, int kt) __attribute__((always_inline)) {
-    if constexpr (QI8) {
-      const float f = q8scale * p.ksc[(int64_t)slice_k * (p.sp / 64) + kt];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = fmaf((float)ia[kb][i], f, -m_base);
     }
   };
 
@@ -641,23 +761,23 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   bool need = false;  // the current tile raises some row max by more than 2^8
   int kt = next_tile(t0);
   int kt1 = kt < kt_end ? next_tile(kt + 1) : kt_end;
+  float ks0 = 0.f, ks_t1 = 0.f;  // int8: K scales of tiles t_0 and t_{i+1}
   if (kt < kt_end) {
     load_k(kt);
     dma_k(kt, sk0);
     dma_v(kt, sv0);
     dma_mask(kt, sm0);
-    store_tile(sk0);
+    ks0 = store_tile(sk0, kt);
     if (kt1 < kt_end) {
       load_k(kt1);
       dma_k(kt1, sk1);
       dma_mask(kt1, sm1);
-      store_tile(sk1);
+      ks_t1 = store_tile(sk1, kt1);
     }
   }
   wait_vmem_and_sync();
   if (kt < kt_end) {
-    qk(sk0, sacc[0]);
-    qk_scale(sacc[0], kt);
+    qk(sk0, sacc[0], ks0);
     fixup(kt, sacc[0], sm0);
     need = check(sacc[0], mx);
   }
@@ -687,11 +807,13 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     // phase A (one straight block: without t_{i+1} the products run on a stale K' buffer
     // and their result is ignored)
     PT pt;
-    qk(sKr, s_nxt);
+    qk(sKr, s_nxt, ks_t1);
     probs(s_cur, pt);
     if constexpr (KPL == 8) {
-      if constexpr (QI8) {
+      if constexpr (QI8 == 2) {
         sched_mfma_interleave<NKB * NQ8, 1, NKB * NQ8, 8, 0>();
+      } else if constexpr (QI8 == 1) {
+        sched_mfma_interleave_loads<NKB * NQ8, 1, NKB * NQ8, 8, 4, 0>();
       } else {
         sched_mfma_interleave_loads<NKB * NQK, 1, QK_AHEAD, 4, kMaskTileLds ? 6 : 2, 0>();
       }
@@ -711,17 +833,16 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     // hoisted into phase A, where their registers would add to its peak)
     if constexpr (kMaskTileLds) asm volatile("" ::: "memory");
     // phase B
-    if (has1) {
-      qk_scale(s_nxt, kt1);
-      fixup(kt1, s_nxt, sMr);
-    }
+    if (has1) fixup(kt1, s_nxt, sMr);
     pv(sVr, pt);
-    store_tile(sKw);  // (stale registers when there is no t_{i+2}: the buffer is not read)
+    // (stale registers when there is no t_{i+2}: the buffer is not read)
+    const float ks_t2 = store_tile(sKw, kt2);
     need = check(s_nxt, mx) && has1;
     if constexpr (KPL == 8) sched_mfma_interleave<NDB * NKB * 2, 2, PV_AHEAD, 6, 1>();
     wait_vmem_and_sync();
     kt = kt1;
     kt1 = kt2;
+    ks_t1 = ks_t2;
   };
   while (kt < kt_end) {
     body(std::integral_constant<int, 0>{});
@@ -734,7 +855,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // the same form as a whole unit does; fwd_merge_kernel combines the pieces)
   const float l = xhalf_sum(l_run);
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
-  if (m < S) {
+  if (!QEXP && m < S) {  // (code export mode: no output)
     char* orow = slot >= 0 ? (char*)p.part_o + ((int64_t)slot * BM + (m - q0)) * D * ES
                            : (char*)p.o + ((int64_t)b * p.o_sb + (int64_t)hd * p.o_sh +
                                                  (int64_t)m * p.o_ss) * ES;
@@ -875,13 +996,26 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p) {
   if (p.lse && c == 0) p.lse[((int64_t)b * p.shp.H + hd) * S + m] = sum > 0.f ? mx + __logf(sum) : -INFINITY;
 }
 
-template <typename T, int D, int MASK, bool CAUSAL, bool QI8 = false, bool ROPE = true>
+template <typename T, int D, int MASK, bool CAUSAL, int QI8 = 0, bool ROPE = true, bool QEXP = false>
 static int launch_fwd_t(const FwdParams& p, void* stream) {
   const int grid = p.split_iters > 0 ? p.split_full + p.split_grid
                    : CAUSAL        ? (p.num_qt + 1) / 2 * p.shp.H * p.shp.B
                                    : p.num_qt * p.shp.H * p.shp.B;
-  hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL, QI8, ROPE>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
-                     (hipStream_t)stream, p);
+  if constexpr (MASK == MASK_BOOL) {
+    // an all-true bool mask runs the unmasked kernel (same schedule, same slots): decided on
+    // the device by the gate word, with no host synchronisation
+    FwdParams pn = p;
+    pn.gate_mode = 1;
+    hipLaunchKernelGGL((fwd_kernel<T, D, MASK_NONE, CAUSAL, QI8, ROPE, QEXP>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
+                       (hipStream_t)stream, pn);
+    FwdParams pb = p;
+    pb.gate_mode = 2;
+    hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL, QI8, ROPE, QEXP>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
+                       (hipStream_t)stream, pb);
+  } else {
+    hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL, QI8, ROPE, QEXP>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
+                       (hipStream_t)stream, p);
+  }
   if (p.split_iters > 0) {
     const int cut = p.num_qt * p.shp.H * p.shp.B - p.split_full;
     hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3(cut * (FwdCfg<T>::BM / 32)), dim3(256), 0,
@@ -913,9 +1047,12 @@ static int launch_fwd_dt(int D, int mask_kind, bool causal, const FwdParams& p, 
 }
 
 template <typename T>
-static int launch_fwd_int8(int D, const FwdParams& p, void* stream) {
-  return D == 64 ? launch_fwd_t<T, 64, MASK_NONE, false, true>(p, stream)
-                 : launch_fwd_t<T, 128, MASK_NONE, false, true>(p, stream);
+static int launch_fwd_int8(int D, int mode, const FwdParams& p, void* stream) {
+  if (mode == 2)
+    return D == 64 ? launch_fwd_t<T, 64, MASK_NONE, false, 2>(p, stream)
+                   : launch_fwd_t<T, 128, MASK_NONE, false, 2>(p, stream);
+  return D == 64 ? launch_fwd_t<T, 64, MASK_NONE, false, 1>(p, stream)
+                 : launch_fwd_t<T, 128, MASK_NONE, false, 1>(p, stream);
 }
 
 

@@ -130,7 +130,9 @@ rs_status validate_args(const rs_args* a, Shape* out) {
     s.Bt = 0;  // no packed tables
   }
 
-  if (a->flags & ~(uint32_t)(RS_FLAG_CAUSAL | RS_FLAG_QUANT_INT8_QK)) return RS_ERR_INVALID;
+  if (a->flags & ~(uint32_t)(RS_FLAG_CAUSAL | RS_FLAG_QUANT_INT8_QK | RS_FLAG_QUANT_INT8_PREPASS))
+    return RS_ERR_INVALID;
+  if ((a->flags & RS_FLAG_QUANT_INT8_PREPASS) && !(a->flags & RS_FLAG_QUANT_INT8_QK)) return RS_ERR_INVALID;
   const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
   if (!(std::isfinite(a->scale)) || a->scale < 0.f) return RS_ERR_INVALID;
   s.scale = a->scale == 0.f ? (float)(1.0 / std::sqrt((double)s.D)) : a->scale;
@@ -184,11 +186,12 @@ rs_status validate_args(const rs_args* a, Shape* out) {
 struct Layout {
   size_t ctrl, table, tiles, delta, qrot, qc, kc, qs, ks, part, cnt, total;
   int64_t nqt, nkt;
-  int64_t sp, nblk;  // int8 variant: padded rows per (b, h) slice and 64-token blocks
+  int64_t sp, nblk;  // pre-quantized int8: padded rows per (b, h) slice and 64-token blocks
   SplitPlan split;   // forward only: work split over the current device's workgroups
 };
 
-Layout layout(const Shape& s, int mask_kind, bool backward, bool int8, bool causal) {
+// int8: 0 none, 1 quantized in the attention kernel, 2 codes from the quantizer pass
+Layout layout(const Shape& s, int mask_kind, bool backward, int int8, bool causal) {
   Layout L{};
   size_t off = 0;
   L.ctrl = off;
@@ -205,15 +208,13 @@ Layout layout(const Shape& s, int mask_kind, bool backward, bool int8, bool caus
   if (backward) off += round_up((size_t)(s.B * s.H * s.S) * sizeof(float), 256);
   L.qrot = off;
   if (backward && s.dtype != F32 && s.D == 128) off += round_up((size_t)(s.B * s.H * s.S * s.D) * 2, 256);
-  if (int8) {
+  if (int8 == 2) {
     L.nblk = (s.S + 63) / 64;
     L.sp = L.nblk * 64;
-    const size_t qcodes = round_up((size_t)(s.B * s.H * L.sp * s.D), 256);
-    const size_t kcodes = round_up((size_t)(s.B * s.Hkv * L.sp * s.D), 256);
     L.qc = off;
-    off += qcodes;
+    off += round_up((size_t)(s.B * s.H * L.sp * s.D), 256);
     L.kc = off;
-    off += kcodes;
+    off += round_up((size_t)(s.B * s.Hkv * L.sp * s.D), 256);
     L.qs = off;
     off += round_up((size_t)(s.B * s.H * L.nblk) * sizeof(float), 256);
     L.ks = off;
@@ -222,7 +223,7 @@ Layout layout(const Shape& s, int mask_kind, bool backward, bool int8, bool caus
   if (!backward) {
     const int64_t bm = fwd_block_m(s.dtype), bn = fwd_block_n(s.dtype);
     const int64_t units = s.B * s.H * ((s.S + bm - 1) / bm);
-    L.split = fwd_split_plan(s.dtype, (int)s.D, int8, causal, mask_kind, units, (int)((s.S + bn - 1) / bn));
+    L.split = fwd_split_plan(s.dtype, (int)s.D, int8 != 0, causal, mask_kind, units, (int)((s.S + bn - 1) / bn));
     if (L.split.iters > 0) {
       L.part = off;
       off += round_up(2 * (size_t)L.split.grid * L.split.slot_bytes, 256);
@@ -328,28 +329,32 @@ Opnd opnd(const rs_tensor* t) {
   return o;
 }
 
-QuantParams quant_params(const rs_args* a, const Shape& s, const Layout& L, char* ws, int8_t* qc,
-                         int8_t* kc, float* qs, float* ks, int64_t rows) {
+int int8_mode(uint32_t flags) {
+  if (!(flags & RS_FLAG_QUANT_INT8_QK)) return 0;
+  return (flags & RS_FLAG_QUANT_INT8_PREPASS) ? 2 : 1;
+}
+
+QuantParams quant_params(const rs_args* a, const Shape& s, const Layout& L, char* ws) {
   QuantParams qp{};
   qp.x[0] = opnd(a->q);
   qp.x[1] = opnd(a->k);
   qp.tab.ptr = (const float*)(ws + L.table);
   qp.tab.sb = s.Bt > 1 ? s.S * s.D : 0;
-  qp.codes[0] = qc;
-  qp.codes[1] = kc;
-  qp.c_sh[0] = qp.c_sh[1] = rows * s.D;
-  qp.c_sb[0] = s.H * rows * s.D;
-  qp.c_sb[1] = s.Hkv * rows * s.D;
-  qp.rows = (int)rows;
-  qp.scales[0] = qs;
-  qp.scales[1] = ks;
+  qp.codes[0] = (int8_t*)(ws + L.qc);
+  qp.codes[1] = (int8_t*)(ws + L.kc);
+  qp.c_sh[0] = qp.c_sh[1] = L.sp * s.D;
+  qp.c_sb[0] = s.H * L.sp * s.D;
+  qp.c_sb[1] = s.Hkv * L.sp * s.D;
+  qp.rows = (int)L.sp;
+  qp.scales[0] = (float*)(ws + L.qs);
+  qp.scales[1] = (float*)(ws + L.ks);
   qp.Hx[0] = (int)s.H;
   qp.Hx[1] = (int)s.Hkv;
   qp.B = (int)s.B;
   qp.H = (int)s.H;
   qp.S = (int)s.S;
   qp.D = (int)s.D;
-  qp.nblk = (int)((s.S + 63) / 64);
+  qp.nblk = (int)L.nblk;
   return qp;
 }
 
@@ -391,7 +396,7 @@ rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* by
   rs_status st = validate_args(args, &s);
   if (st != RS_OK) return fail(st);
   *bytes = s.empty ? 0
-                   : layout(s, args->mask_kind, backward != 0, (args->flags & RS_FLAG_QUANT_INT8_QK) != 0,
+                   : layout(s, args->mask_kind, backward != 0, backward ? 0 : int8_mode(args->flags),
                             (args->flags & RS_FLAG_CAUSAL) != 0)
                          .total;
   return RS_OK;
@@ -415,7 +420,7 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
   if ((st = check_bhsd(o, s.dtype, sz, s.empty)) != RS_OK) return fail(st);
   if (lse && ((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
   if (s.empty) return RS_OK;  // nothing to compute: no workspace or device needed
-  const bool int8 = (a->flags & RS_FLAG_QUANT_INT8_QK) != 0;
+  const int int8 = int8_mode(a->flags);
   const Layout L = layout(s, a->mask_kind, false, int8, (a->flags & RS_FLAG_CAUSAL) != 0);
   if (scratch) {
     if (L.total > kScratchBytes) return fail(RS_ERR_SCRATCH);
@@ -429,11 +434,7 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
   char* w = (char*)ws;
   hipStream_t strm = (hipStream_t)stream;
   if ((st = prepare(a, s, L, w, strm)) != RS_OK) return fail(st);
-  if (int8) {
-    const QuantParams qp = quant_params(a, s, L, w, (int8_t*)(w + L.qc), (int8_t*)(w + L.kc),
-                                        (float*)(w + L.qs), (float*)(w + L.ks), L.sp);
-    if (launch_quant_int8(s.dtype, qp, strm) != 0) return fail(RS_ERR_LAUNCH);
-  }
+  if (int8 == 2 && launch_quant_int8(s.dtype, quant_params(a, s, L, w), strm) != 0) return fail(RS_ERR_LAUNCH);
   FwdParams p{};
   p.q = opnd(a->q);
   p.k = opnd(a->k);
@@ -446,11 +447,12 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
   p.tab.ptr = s.rope ? (const float*)(w + L.table) : nullptr;
   p.tab.sb = s.Bt > 1 ? s.S * s.D : 0;
   p.mask = mask_view(a, s, L, w);
+  p.gate = (const unsigned*)(w + L.ctrl);  // (used by the bool-mask launch only)
   p.shp = attn_shape(s);
   const int bm = fwd_block_m(s.dtype);
   p.num_qt = (int)((s.S + bm - 1) / bm);
   const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
-  if (int8) {
+  if (int8 == 2) {
     p.qc = (const int8_t*)(w + L.qc);
     p.kc = (const int8_t*)(w + L.kc);
     p.qsc = (const float*)(w + L.qs);
@@ -501,14 +503,26 @@ rs_status rope_sdpa_debug_quantize_qk(const rs_args* a, int8_t* q_codes, int8_t*
   if (!q_codes || !k_codes || !q_scales || !k_scales) return fail(RS_ERR_NULL);
   if (((uintptr_t)q_codes) % 8 != 0 || ((uintptr_t)k_codes) % 8 != 0) return fail(RS_ERR_ALIGN);
   if (((uintptr_t)q_scales) % 4 != 0 || ((uintptr_t)k_scales) % 4 != 0) return fail(RS_ERR_ALIGN);
-  const Layout L = layout(s, a->mask_kind, false, true, false);
+  const Layout L = layout(s, a->mask_kind, false, 1, false);
   if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
   if ((st = current_device_ok()) != RS_OK) return fail(st);
   char* w = (char*)ws;
   hipStream_t strm = (hipStream_t)stream;
   if ((st = prepare(a, s, L, w, strm)) != RS_OK) return fail(st);
-  const QuantParams qp = quant_params(a, s, L, w, q_codes, k_codes, q_scales, k_scales, s.S);
-  if (launch_quant_int8(s.dtype, qp, strm) != 0) return fail(RS_ERR_LAUNCH);
+  // the int8 forward itself, in its code export mode: the codes it computes, not a copy
+  FwdParams p{};
+  p.q = opnd(a->q);
+  p.k = opnd(a->k);
+  p.v = opnd(a->v);
+  p.tab.ptr = (const float*)(w + L.table);
+  p.tab.sb = s.Bt > 1 ? s.S * s.D : 0;
+  p.shp = attn_shape(s);
+  p.num_qt = (int)((s.S + fwd_block_m(s.dtype) - 1) / fwd_block_m(s.dtype));
+  p.xq_codes = q_codes;
+  p.xk_codes = k_codes;
+  p.xq_scales = q_scales;
+  p.xk_scales = k_scales;
+  if (launch_fwd_int8_export(s.dtype, (int)s.D, p, strm) != 0) return fail(RS_ERR_LAUNCH);
   return RS_OK;
 }
 

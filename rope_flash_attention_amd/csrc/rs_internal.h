@@ -61,13 +61,26 @@ struct FwdParams {
   MaskView mask;
   AttnShape shp;
   int num_qt;  // query tiles per (b, h)
-  // blockwise int8 variant: codes of the rotated Q and K, [B][H][sp][D] int8 with sp = S
-  // rounded up to 64 (padding rows zero), and their fp32 scales [B][H][sp / 64]
+  // blockwise int8 variant with codes from the quantizer pass: codes of the rotated Q and K,
+  // [B][H|Hkv][sp][D] int8 with sp = S rounded up to 64 (padding rows zero), and their fp32
+  // scales [B][H|Hkv][sp / 64]
   const int8_t* qc;
   const int8_t* kc;
   const float* qsc;
   const float* ksc;
   int sp;
+  // blockwise int8 variant, code export mode only (the test-only export of the codes the
+  // kernel computes): contiguous Q codes [B][H][S][D], K codes [B][Hkv][S][D] and their fp32
+  // scales [B][H][nblk], [B][Hkv][nblk] (nblk = ceil(S / 64))
+  int8_t* xq_codes;
+  int8_t* xk_codes;
+  float* xq_scales;
+  float* xk_scales;
+  // bool masks: the unmasked and the masked kernel are both enqueued; each reads the mask
+  // classifier's word gate[0] (nonzero: some key is excluded) at entry and returns at once
+  // unless gate_mode says it is the one to run (1: gate[0] == 0, 2: gate[0] != 0; 0: always)
+  const unsigned* gate;
+  int gate_mode;
   // split of the work (see the forward kernel): split_iters = 0 for one workgroup per unit
   int split_full;       // units run whole by the first workgroups (a multiple of 8)
   int split_grid;       // further workgroups sharing the remaining units' key tiles
@@ -102,15 +115,16 @@ struct PackParams {
   unsigned* ctrl;                  // control words cleared for the mask classifier
 };
 
-// Rotation + blockwise int8 quantization of Q (x[0]) and K (x[1]).
+// Rotation + blockwise int8 quantization of Q (x[0]) and K (x[1]): the quantizer pass of
+// the pre-quantized int8 mode.
 struct QuantParams {
   Opnd x[2];
   Table tab;
-  int8_t* codes[2];        // [B][Hx][rows][D] with the strides below
+  int8_t* codes[2];          // [B][Hx][rows][D] with the strides below
   int64_t c_sb[2], c_sh[2];  // element strides of the codes over b and h
-  int rows;                // allocated rows per (b, h) slice (>= S); rows past S are written as 0
-  float* scales[2];        // [B][Hx][nblk]
-  int Hx[2];               // heads of Q (H) and of K (Hkv)
+  int rows;                  // allocated rows per (b, h) slice (>= S); rows past S are written as 0
+  float* scales[2];          // [B][Hx][nblk]
+  int Hx[2];                 // heads of Q (H) and of K (Hkv)
   int B, H, S, D, nblk;
 };
 
@@ -146,11 +160,14 @@ struct SplitPlan {
   int64_t cut_units;  // units whose key tiles are shared out
 };
 SplitPlan fwd_split_plan(int dtype, int D, bool int8, bool causal, int mask_kind, int64_t units, int nkt);
-int launch_fwd(int dtype, int D, int mask_kind, bool causal, bool int8, const FwdParams& p, void* stream);
+// int8: 0 = none, 1 = quantized in the attention kernel, 2 = codes from the quantizer pass
+int launch_fwd(int dtype, int D, int mask_kind, bool causal, int int8, const FwdParams& p, void* stream);
+int launch_quant_int8(int dtype, const QuantParams& p, void* stream);
 // The forward without rotation (no tables: plain attention).
 int launch_fwd_plain(int dtype, int D, int mask_kind, bool causal, const FwdParams& p, void* stream);
 int launch_rotate(int dtype, const RotateParams& p, void* stream);
-int launch_quant_int8(int dtype, const QuantParams& p, void* stream);
+// The int8 forward in code export mode (no output written; see FwdParams).
+int launch_fwd_int8_export(int dtype, int D, const FwdParams& p, void* stream);
 int launch_bwd(int dtype, int D, int mask_kind, bool causal, const BwdParams& p, void* stream);
 // Reads (and optionally clears) the device-side count of all-true bool masks.
 int read_all_true_counter(uint64_t* value, bool reset);

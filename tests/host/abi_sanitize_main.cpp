@@ -144,15 +144,18 @@ int main() {
         Case c(dt, 2, 6, 300, 128, 1, Hkv);
         CHECK(run(c, bwd != 0) == RS_OK, "GQA dt=%d Hkv=%d bwd=%d", dt, Hkv, bwd);
         Case ci(dt == RS_F32 ? RS_BF16 : dt, 2, 6, 300, 128, 1, Hkv);
-        ci.a.flags = RS_FLAG_QUANT_INT8_QK;
+        ci.a.flags = RS_FLAG_QUANT_INT8_QK | (bwd ? RS_FLAG_QUANT_INT8_PREPASS : 0u);
         CHECK(run(ci, false) == RS_OK, "GQA int8 Hkv=%d", Hkv);
       }
   for (int dt : {RS_F16, RS_BF16})
-    for (int S : {64, 77, 4608}) {
-      Case c(dt, 1, 4, S, 128);
-      c.a.flags = RS_FLAG_QUANT_INT8_QK;
-      CHECK(run(c, false) == RS_OK, "int8 forward S=%d", S);
-    }
+    for (int S : {64, 77, 4608})
+      for (uint32_t extra : {0u, (uint32_t)RS_FLAG_QUANT_INT8_PREPASS}) {
+        Case c(dt, 1, 4, S, 128);
+        c.a.flags = RS_FLAG_QUANT_INT8_QK | extra;
+        CHECK(run(c, false) == RS_OK, "int8 forward S=%d prepass=%u", S, extra);
+      }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT8_PREPASS;
+    expect_error(c, false, RS_ERR_INVALID, "prepass without int8"); }
   // plain attention (no tables): forward only
   for (int dt : dts)
     for (int variant = 0; variant < 3; ++variant) {

@@ -78,18 +78,20 @@ int launch_classify(const ClassifyParams& p, void*) {
   return 0;
 }
 
-int launch_fwd(int dtype, int D, int, bool, bool int8, const FwdParams& p, void*) {
+int launch_fwd(int dtype, int D, int, bool, int int8, const FwdParams& p, void*) {
   ++stub::launches;
   const int B = p.shp.B, H = p.shp.H, S = p.shp.S;
   stub::need(p.tab.ptr, (size_t)(p.tab.sb ? B : 1) * S * D * sizeof(float), "packed tables");
   if (p.mask.tiles) stub::need(p.mask.tiles, 1, "mask tile states");
   if (p.shp.Hkv <= 0 || H % p.shp.Hkv != 0 || p.shp.group != H / p.shp.Hkv) std::abort();
-  if (int8) {
-    const int Hkv = p.shp.Hkv;
+  if (int8 && (p.xq_codes || p.xk_codes)) std::abort();  // the forward never exports codes
+  if (int8 == 2) {  // codes and scales of the quantizer pass in the workspace
     stub::need(p.qc, (size_t)B * H * p.sp * D, "q codes");
-    stub::need(p.kc, (size_t)B * Hkv * p.sp * D, "k codes");
+    stub::need(p.kc, (size_t)B * p.shp.Hkv * p.sp * D, "k codes");
     stub::need(p.qsc, (size_t)B * H * (p.sp / 64) * sizeof(float), "q scales");
-    stub::need(p.ksc, (size_t)B * Hkv * (p.sp / 64) * sizeof(float), "k scales");
+    stub::need(p.ksc, (size_t)B * p.shp.Hkv * (p.sp / 64) * sizeof(float), "k scales");
+  } else if (p.qc || p.kc) {
+    std::abort();
   }
   if (p.split_iters > 0) {
     const size_t bm = (size_t)fwd_block_m(dtype), es = dtype == F32 ? 4 : 2;
@@ -114,6 +116,17 @@ int launch_rotate(int, const RotateParams& p, void*) {
 int launch_quant_int8(int, const QuantParams& p, void*) {
   ++stub::launches;
   stub::need(p.tab.ptr, (size_t)(p.tab.sb ? p.B : 1) * p.S * p.D * sizeof(float), "packed tables");
+  for (int w = 0; w < 2; ++w) {
+    stub::need(p.codes[w], (size_t)p.B * p.Hx[w] * p.rows * p.D, "codes");
+    stub::need(p.scales[w], (size_t)p.B * p.Hx[w] * p.nblk * sizeof(float), "scales");
+  }
+  return 0;
+}
+
+int launch_fwd_int8_export(int, int, const FwdParams& p, void*) {
+  ++stub::launches;
+  if (!p.xq_codes || !p.xk_codes || !p.xq_scales || !p.xk_scales || p.split_iters != 0) std::abort();
+  stub::need(p.tab.ptr, (size_t)(p.tab.sb ? p.shp.B : 1) * p.shp.S * 4 * 64, "packed tables");
   return 0;
 }
 

@@ -46,7 +46,7 @@ def _check_codes(w, got):
             assert np.all((blk == 127) | (sc[:, :, t] == 0))
 
 
-def _run_int8(w, need_lse=True, q=None, k=None, v=None):
+def _run_int8(w, need_lse=True, q=None, k=None, v=None, mode="int8"):
     d = dev()
     q = w.q.to(d) if q is None else q
     k = w.k.to(d) if k is None else k
@@ -54,13 +54,33 @@ def _run_int8(w, need_lse=True, q=None, k=None, v=None):
     with torch.no_grad():
         if need_lse:
             o, lse = rfa.rope_sdpa_fwd_with_lse(q, k, v, w.cos.to(d), w.sin.to(d), scale=w.scale,
-                                                quantization="int8")
+                                                quantization=mode)
         else:
             o = rfa.rope_scaled_dot_product_attention(q, k, v, w.cos.to(d), w.sin.to(d), scale=w.scale,
-                                                      quantization="int8")
+                                                      quantization=mode)
             lse = None
     torch.cuda.synchronize()
     return o, lse
+
+
+@pytest.mark.parametrize("case", ["small_d64", "small_d128", "split", "gqa", "f16_per_sample"])
+def test_prepass_mode_is_bitwise_the_in_kernel_mode(case):
+    """The pre-quantized mode (a quantizer pass writes the codes, the attention kernel streams
+    them) and the default mode (the attention kernel quantizes in registers) take the same
+    integer decisions and run the same attention arithmetic: O and LSE are equal bit for bit."""
+    if case == "small_d64":
+        w = syn.random_small(2, 3, 77, 64, "bf16", seed=140)
+    elif case == "small_d128":
+        w = syn.random_small(2, 3, 300, 128, "bf16", seed=141)
+    elif case == "split":  # S = 1104: units cut over the last round
+        w = syn.random_small(1, 3, 1104, 128, "bf16", seed=142)
+    elif case == "gqa":
+        w = syn.random_small(2, 6, 200, 128, "bf16", seed=143, kv_heads=2)
+    else:
+        w = syn.random_small(2, 2, 130, 128, "f16", seed=144, per_sample_tables=True)
+    o1, l1 = _run_int8(w, mode="int8")
+    o2, l2 = _run_int8(w, mode="int8_prepass")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -118,8 +138,9 @@ def test_int8_determinism_and_counter():
     rfa.rope_sdpa_reset_stats()
     o1, _ = _run_int8(w, need_lse=False)
     o2, _ = _run_int8(w, need_lse=False)
-    assert torch.equal(o1, o2)
-    assert rfa.rope_sdpa_get_stats()["quant_int8"] == 2
+    o3, _ = _run_int8(w, need_lse=False, mode="int8_prepass")
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+    assert rfa.rope_sdpa_get_stats()["quant_int8"] == 3
 
 
 def test_int8_rejections():
@@ -173,6 +194,14 @@ def test_int8_long_two_full_heads():
     whole."""
     w = syn.flux(batch=1, heads=48, grid=128, dtype="bf16", seed=5000)
     _full_heads(w, (0, 47))
+
+
+def test_int8_prepass_long_is_bitwise_the_in_kernel_mode():
+    """The long shape in both int8 modes: every output and LSE element equal."""
+    w = syn.flux(batch=1, heads=48, grid=128, dtype="bf16", seed=5000)
+    o1, l1 = _run_int8(w, mode="int8")
+    o2, l2 = _run_int8(w, mode="int8_prepass")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def test_int8_split_key_ranges():
