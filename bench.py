@@ -59,7 +59,7 @@ def _source_hash():
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rope_flash_attention_amd", "csrc")
-    for name in ("rs_fwd.hip", "rs_device.hpp", "rs_internal.h"):  # what the forward kernel is built from
+    for name in ("rs_fwd.hip", "rs_fwd_kernel.hpp", "rs_device.hpp", "rs_internal.h"):  # the forward kernel's sources
         if True:
             text = open(os.path.join(csrc, name)).read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -291,8 +291,8 @@ def traffic_from_counters(fetch_db, write_db, command):
 def pmc_legs(reps):
     """Workloads for rocprofv3 --pmc passes, each call run `reps` times: the tiny fp32 forward
     (B=1, H=2, S=128, D=64), the FLUX forward (B=1, no mask), the FLUX forward with the
-    additive 4-D bf16 mask (B=2) and the FLUX backward (B=2), then a 256 MiB device copy
-    whose byte counters scale the others."""
+    additive 4-D bf16 mask (B=2), the FLUX backward (B=2) and the causal backward (B=4, H=16,
+    S=2048), then a 256 MiB device copy whose byte counters scale the others."""
     import torch
 
     import synthetic as syn
@@ -325,12 +325,19 @@ def pmc_legs(reps):
     for _ in range(reps):
         rfa.rope_sdpa_bwd_explicit(*t[:5], o, lse, t[5])
     del o, lse, t
+    w = syn.causal_1axis(batch=4, heads=16, seq=2048, dim=128, dtype="bf16", seed=4200)
+    t = [x.to(dev) for x in (w.q, w.k, w.v, w.cos, w.sin, w.do)]
+    o, lse = rfa.rope_sdpa_fwd_with_lse(*t[:5], is_causal=True)
+    for _ in range(reps):
+        rfa.rope_sdpa_bwd_explicit(*t[:5], o, lse, t[5], is_causal=True)
+    del o, lse, t
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_legs": ["tiny_fp32", "flux_fwd_b1", "flux_fwd_b2_additive_4d", "flux_bwd_b2", "copy_256MiB"],
+    print(json.dumps({"pmc_legs": ["tiny_fp32", "flux_fwd_b1", "flux_fwd_b2_additive_4d", "flux_bwd_b2",
+                                   "causal_bwd_b4", "copy_256MiB"],
                       "reps": reps}))
 
 
