@@ -59,12 +59,12 @@ def _source_hash():
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rope_flash_attention_amd", "csrc")
-    for name in ("rs_fwd.hip", "rs_fwd_kernel.hpp", "rs_device.hpp", "rs_internal.h"):  # the forward kernel's sources
-        if True:
-            text = open(os.path.join(csrc, name)).read()
-            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            text = re.sub(r"//[^\n]*", "", text)
-            h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
+    for name in ("rs_fwd.hip", "rs_fwd_qk.hip", "rs_fwd_kernel.hpp", "rs_device.hpp", "rs_internal.h",
+                 "rs_host.cpp"):  # the forward's sources
+        text = open(os.path.join(csrc, name)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
@@ -173,6 +173,12 @@ def _prepare(dev, extra, train):
                          c.sin.to(dev))
         prep["gqa"] = to_dev(syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=740, kv_heads=6,
                                       per_sample_tables=True), qkvcs)
+        # the autocast layout: fp32 Q/K (to be RMS-normalized in the kernel) beside bf16 V
+        q32 = syn.normal(3000, syn.STREAM_Q, tuple(w.q.shape), "f32", 4.0).to(dev)
+        k32 = syn.normal(3000, syn.STREAM_K, tuple(w.k.shape), "f32", 4.0).to(dev)
+        prep["flux_b2_f32qk"] = (q32, k32) + prep["flux_b2"][2:]
+        prep["flux_b2_f32"] = (prep["flux_b2"][0].float(), prep["flux_b2"][1].float()) + prep["flux_b2"][2:]
+        prep["norm_w"] = tuple(t.to(dev) for t in syn.norm_weights(3000, 128))
     if train:
         prep["train_flux"] = to_dev(syn.flux(batch=2, heads=24, grid=64, dtype="bf16", seed=4100, with_grad=True),
                                     qkvcs + ("do",))
@@ -191,12 +197,12 @@ def _extra_cases(prep, steps, warmup, stream):
     out = {}
     n = max(5, steps // 3)
 
-    def timed(name, w_dev, mask=None, quant=None, note=""):
+    def timed(name, w_dev, mask=None, quant=None, note="", **kw):
         q, k, v, c, s = w_dev
         B, H, S, D = q.shape
 
         def f():
-            rfa.rope_scaled_dot_product_attention(q, k, v, c, s, attn_mask=mask, quantization=quant)
+            rfa.rope_scaled_dot_product_attention(q, k, v, c, s, attn_mask=mask, quantization=quant, **kw)
 
         with torch.no_grad():
             ms = _events_time(f, n, warmup, stream)
@@ -208,6 +214,10 @@ def _extra_cases(prep, steps, warmup, stream):
     timed("long_bf16", prep["long"])  # first: its seconds of work bring the clock to its steady value
     wd, bm = prep["flux_b2"], prep["mask_bool"]
     timed("no_mask_b2", wd, note="reference for the masked B=2 calls")
+    qn, kn = prep["norm_w"]
+    timed("f32qk_rmsnorm_b2", prep["flux_b2_f32qk"], q_norm_weight=qn, k_norm_weight=kn,
+          note="fp32 Q/K RMS-normalized and rotated in the kernel, bf16 V and O (autocast layout)")
+    timed("f32qk_b2", prep["flux_b2_f32"], note="fp32 Q/K (no_mask_b2's values), bf16 V and O")
     timed("mask_bool_key_padding", wd, bm, note="bool [2,1,1,S]; dense flop count")
     timed("mask_all_true", wd, torch.ones_like(bm), note="bool [2,1,1,S] all True (skip path)")
     timed("mask_additive_4d", wd, prep["mask_add"], note="bf16 [2,24,S,S] 0/-inf, 2.04 GB read")
@@ -583,9 +593,10 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": _traffic("fwd_bf16_d128_flux_b1"),
-            "kernel": "fwd_kernel<bf16,128,MASK_NONE>; achieved = algorithmic flops over the event-timed forward "
-                      "call, which is three launches: pack_tables_kernel (table repack), fwd_kernel (attention) and "
-                      "fwd_merge_kernel<bf16,128> (combines the pieces of the units cut over the last round)",
+            "kernel": "fwd_kernel<bf16,128,MASK_NONE,QKM=4>; achieved = algorithmic flops over the event-timed "
+                      "forward call, which is four launches: pack_tables_kernel (table repack), kprep_kernel (K "
+                      "rotated once), fwd_kernel (attention, Q rotated in its prologue) and fwd_merge_kernel "
+                      "(combines the pieces of the units cut over the last round)",
         },
         "train": train,
         "forward_variants": extra,

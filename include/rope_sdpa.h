@@ -86,8 +86,14 @@ typedef struct {
 } rs_tensor;
 
 typedef struct {
-  const rs_tensor* q;    /* [B, H, S, D]  f32 | f16 | bf16 */
-  /* K and V: [B, Hkv, S, D], same dtype as q, with H % Hkv == 0.  Hkv < H is grouped-query
+  /* Q: [B, H, S, D] in the dtype of v (f32, f16 or bf16), or f32 with v in f16/bf16: the
+   * autocast layout of flux-style attention, where RMSNorm hands fp32 Q and K to attention
+   * while V stays bf16 (diffusers issue "Flux-family attention: flash-attn and other backends fail in an autocast
+   * context", section "Root cause, in order").  Such Q and K are read in fp32, rotated in fp32
+   * and rounded to the dtype of v for the matrix products; O is in the dtype of v.
+   * rope_sdpa_fwd only (rope_sdpa_bwd returns RS_ERR_UNSUPPORTED), no additive mask, no int8. */
+  const rs_tensor* q;
+  /* K and V: [B, Hkv, S, D], K in the dtype of q, with H % Hkv == 0.  Hkv < H is grouped-query
    * (Hkv == 1: multi-query) attention: query head h reads K/V head h / (H / Hkv), and K is
    * rotated at its own head count (section "Fused RoPE + SDPA": GQA inputs are rotated at
    * the K/V head count and expanded afterwards); dK and dV of the backward have Hkv heads,
@@ -110,19 +116,32 @@ typedef struct {
   int32_t mask_kind;     /* rs_mask_kind */
   uint32_t flags;        /* RS_FLAG_* */
   float scale;           /* softmax scale; 0 means 1/sqrt(D); otherwise finite and > 0 */
+  /* Optional RMSNorm of Q and K over the head dimension before the rotation, as flux-style
+   * attention applies it (same diffusers issue, "Describe the bug"): x / sqrt(mean_d x_d^2 +
+   * norm_eps) * w_d in fp32, with per-dimension weights w: DEVICE pointers to fp32 [D],
+   * 16-byte aligned.  Both NULL: no normalization; both or neither (else RS_ERR_INVALID).
+   * norm_eps finite and >= 0.  Same restrictions as fp32 Q/K above (forward, no additive
+   * mask, no int8).  Zero-initialized rs_args mean no normalization. */
+  const float* q_norm_weight;
+  const float* k_norm_weight;
+  float norm_eps;
 } rs_args;
 
 /* Bytes of device workspace a call needs (0 only for an empty call, B, H or S = 0; otherwise
- * the rotation tables are repacked into it).  `backward` = 0 for rope_sdpa_fwd, 1 for
- * rope_sdpa_bwd. */
+ * the rotation tables are repacked into it, and a bf16/f16 forward without int8 or additive
+ * mask also holds K' = R(K): B * Hkv * S * D elements of the dtype of v).  `backward` = 0 for
+ * rope_sdpa_fwd, 1 for rope_sdpa_bwd. */
 rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* bytes);
 
 /*
- * Forward.  Writes o (same dtype, sizes as q; any valid strides) and, when lse is not NULL,
+ * Forward.  Writes o (dtype of v, sizes of q; any valid strides) and, when lse is not NULL,
  * the natural-log row normaliser lse[b][h][i] = log(sum_j exp(scale q'_i.k'_j + m_ij)) into a
  * contiguous fp32 [B, H, S] buffer (-inf for a row with no valid key); lse is what
  * rope_sdpa_bwd needs.  An all-true bool mask is detected on the device and then costs no
- * per-element mask reads.
+ * per-element mask reads.  bf16/f16 without int8 or additive mask: K is rotated once (per
+ * batch item and K/V head) into the workspace by a pass of its own and Q inside the attention
+ * kernel, each product and sum in fp32 and the result rounded to the input dtype; the
+ * attention kernel then reads K' with no table in its key loop.
  * RS_FLAG_QUANT_INT8_QK (bf16/f16 inputs, no mask, no causal, lse may be NULL): after the
  * fp32 rotation (each product and sum rounded), Q' and K' are quantized per (b, h, 64-token
  * block) to int8 codes round-half-even(x * fp32(127/amax)) with scale amax/127, QK^T runs on
@@ -144,7 +163,10 @@ rs_status rope_sdpa_fwd(const rs_args* args, const rs_tensor* o, float* lse,
  * workspace: the library keeps a device scratch array of rope_sdpa_noalloc_scratch_bytes()
  * bytes (64 MiB) per device, held from the first call on that device until the process ends,
  * and this call allocates nothing (no hipMalloc, no allocating library routine).  A call whose
- * workspace would exceed that size returns RS_ERR_SCRATCH and launches nothing.  The caller
+ * workspace would exceed that size leaves K' out of the scratch where it can (K is then
+ * rotated inside the attention kernel, with the same arithmetic: the same results bit for
+ * bit); a call that still does not fit, or that needs K' (normalized or fp32 Q/K), returns
+ * RS_ERR_SCRATCH and launches nothing.  The caller
  * still owns and passes inputs, o and lse.  Every call on one device shares that device's
  * scratch: calls that overlap on one device (enqueued on different streams without ordering
  * between them, or from several threads onto unordered streams) race and give undefined

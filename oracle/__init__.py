@@ -35,4 +35,5 @@ from .rope_sdpa_ref import (  # noqa: F401
     rope_sdpa_forward_int8,
     expand_kv,
     reduce_kv,
+    rms_norm,
 )

@@ -8,6 +8,8 @@ and that (batch, head) pairs may be mapped over a thread pool.
 
 Citations name the page and section the step follows:
   [FR]  "Metal Flash Attention" (SimpleTuner docs), section "Fused RoPE + SDPA"
+  [DF]  diffusers issue "Flux-family attention: flash-attn and other backends fail in an
+        autocast context", sections "Describe the bug" and "Root cause, in order"
   [EN]  same page, section "Enable In SimpleTuner"
   [RQ]  same page, section "Requirements"
   [PR]  SimpleTuner pull request "metal-flash-attention: causal training ungated;
@@ -306,12 +308,25 @@ def reduce_kv(g, Hkv):
     return g.reshape(B, Hkv, G, *g.shape[2:]).sum(axis=2) if G > 1 else g
 
 
+def rms_norm(x, w, eps):
+    """RMSNorm over the head dimension, as flux-style attention applies it to Q and K just
+    before the rotation ([DF] root cause): x / sqrt(mean_d x_d^2 + eps) * w_d, in float64."""
+    x = _np64(x)
+    w = _np64(w)
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + float(eps)) * w
+
+
 def rope_sdpa_forward(q, k, v, cos, sin, mask=None, mask_kind="none", causal=False, scale=None,
-                      rows=None, pairs=None, workers=1):
+                      rows=None, pairs=None, workers=1, q_norm_weight=None, k_norm_weight=None, norm_eps=1e-6):
     """Fused RoPE + SDPA forward [FR]: rotate Q and K, then exact attention.  K and V may have
     fewer heads than Q (grouped-query attention): they are rotated at their own head count and
-    expanded afterwards.  Returns (O, LSE)."""
+    expanded afterwards.  With q_norm_weight / k_norm_weight, Q / K are RMS-normalized over
+    the head dimension first (rms_norm).  Returns (O, LSE)."""
     q64, k64, v64 = _np64(q), _np64(k), _np64(v)
+    if q_norm_weight is not None:
+        q64 = rms_norm(q64, q_norm_weight, norm_eps)
+    if k_norm_weight is not None:
+        k64 = rms_norm(k64, k_norm_weight, norm_eps)
     qr = rope_rotate(q64, cos, sin)
     kr = expand_kv(rope_rotate(k64, cos, sin), q64.shape[1])
     v64 = expand_kv(v64, q64.shape[1])

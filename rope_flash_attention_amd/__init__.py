@@ -16,6 +16,10 @@ rotated at its own head count); rope_cos/rope_sin are pair-duplicated
 tables of shape [S, D], [1, S, D] or [B, S, D] in any float dtype (normalised to fp32),
 masks are bool (True = attend) or additive float, broadcastable, up to 4-D.  Gradients
 flow to query, key (pre-rotation) and value.
+
+Forward only: query and key may be fp32 beside an fp16/bf16 value (the autocast layout of
+flux-style attention; the output takes value's dtype), and q_norm_weight/k_norm_weight apply
+RMSNorm over the head dimension to query and key before the rotation, inside the kernel.
 """
 from __future__ import annotations
 
@@ -106,7 +110,7 @@ def _mask4(mask: torch.Tensor | None, qdtype):
 class _Call:
     """Holds the ctypes descriptors of one call (kept alive for the duration of the call)."""
 
-    def __init__(self, q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant=None):
+    def __init__(self, q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant=None, norm=None):
         self.tq, self.tk, self.tv = _desc(q), _desc(k), _desc(v)
         self.tc = _desc(cos4) if cos4 is not None else None  # no tables: plain attention
         self.ts = _desc(sin4) if sin4 is not None else None
@@ -119,6 +123,10 @@ class _Call:
         a.mask_kind = mask_kind
         a.flags = (RS_FLAG_CAUSAL if causal else 0) | _QUANT_FLAGS[quant]
         a.scale = 0.0 if scale is None else float(scale)
+        if norm is not None:  # (q weights, k weights, eps): fp32 [D] device tensors
+            self.norm = norm
+            a.q_norm_weight, a.k_norm_weight = norm[0].data_ptr(), norm[1].data_ptr()
+            a.norm_eps = float(norm[2])
         self.args = a
 
     def workspace(self, backward: bool, device) -> torch.Tensor:
@@ -131,11 +139,11 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _forward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, need_lse, quant=None):
+def _forward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, need_lse, quant=None, norm=None):
     lib = _abi.load()
-    call = _Call(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant)
+    call = _Call(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant, norm)
     B, H, S, D = q.shape
-    o = torch.empty((B, H, S, D), dtype=q.dtype, device=q.device)
+    o = torch.empty((B, H, S, D), dtype=v.dtype, device=q.device)  # the compute dtype
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if need_lse else None
     ws = call.workspace(False, q.device)
     to = _desc(o)
@@ -179,39 +187,70 @@ class _RopeSdpaFn(torch.autograd.Function):
         return dq, dk, dv, None, None, None, None, None, None
 
 
+def _norm_args(query, q_norm_weight, k_norm_weight, norm_eps):
+    """(q weights, k weights, eps) as fp32 [D] device tensors, or None without normalization."""
+    if q_norm_weight is None and k_norm_weight is None:
+        return None
+    if q_norm_weight is None or k_norm_weight is None:
+        raise ValueError("q_norm_weight and k_norm_weight go together")
+    D = query.shape[-1]
+    w = [t.to(device=query.device, dtype=torch.float32).contiguous() for t in (q_norm_weight, k_norm_weight)]
+    if any(t.shape != (D,) for t in w):
+        raise ValueError(f"norm weights must have shape [{D}]")
+    return w[0], w[1], float(norm_eps)
+
+
+def _check_dtypes(query, key, value):
+    """Q and K share a dtype; V the same, or 16-bit beside fp32 Q/K (forward only)."""
+    if query.dtype != key.dtype:
+        raise RopeSdpaError(-2)
+    if query.dtype != value.dtype and not (query.dtype == torch.float32 and value.dtype in (torch.float16,
+                                                                                           torch.bfloat16)):
+        raise RopeSdpaError(-2)
+
+
 def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, attn_mask=None, is_causal=False,
-                                      scale=None, quantization=None):
+                                      scale=None, quantization=None, q_norm_weight=None, k_norm_weight=None,
+                                      norm_eps=1e-6):
     """softmax(scale * R(Q) R(K)^T + mask) V with R the interleaved-pair rotation of the tables.
 
     quantization: None, "int8" for the blockwise int8 Q'/K' forward quantized in the attention
     kernel, or "int8_prepass" for the same forward with the codes written by a quantizer pass
     first (bit-identical results, faster); no gradient.
+
+    q_norm_weight, k_norm_weight ([D] each, together or not at all): RMSNorm of query and key
+    over the head dimension, x / sqrt(mean(x^2) + norm_eps) * w in fp32, before the rotation.
+    fp32 query/key with fp16/bf16 value are read in fp32 and rounded to value's dtype after the
+    rotation; the output has value's dtype.  Both are forward only (no gradient).
     """
     if not (query.is_cuda and key.is_cuda and value.is_cuda):
         raise ValueError("query, key and value must be device tensors")
-    if query.dtype != key.dtype or query.dtype != value.dtype:
-        raise RopeSdpaError(-2)
+    _check_dtypes(query, key, value)
     cos4 = _tables4(rope_cos, query.device)
     sin4 = _tables4(rope_sin, query.device)
-    mask, kind = _mask4(attn_mask, query.dtype)
+    mask, kind = _mask4(attn_mask, value.dtype)
     if quantization not in _QUANT_FLAGS:
         raise ValueError("quantization must be None, 'int8' or 'int8_prepass'")
+    norm = _norm_args(query, q_norm_weight, k_norm_weight, norm_eps)
     needs_grad = torch.is_grad_enabled() and (query.requires_grad or key.requires_grad or value.requires_grad)
-    if quantization is not None:
+    if quantization is not None or norm is not None or query.dtype != value.dtype:
         if needs_grad:
             raise RopeSdpaError(-6)
-        return _forward(query, key, value, cos4, sin4, mask, kind, is_causal, scale, False, quant=quantization)[0]
+        return _forward(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale, False,
+                        quant=quantization, norm=norm)[0]
     if needs_grad:
         return _RopeSdpaFn.apply(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale)
     return _forward(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale, need_lse=False)[0]
 
 
 def rope_sdpa_fwd_with_lse(query, key, value, rope_cos, rope_sin, attn_mask=None, is_causal=False, scale=None,
-                           quantization=None):
+                           quantization=None, q_norm_weight=None, k_norm_weight=None, norm_eps=1e-6):
     """Forward returning (O, LSE) without autograd (LSE is fp32 [B, H, S], natural log)."""
-    mask, kind = _mask4(attn_mask, query.dtype)
+    _check_dtypes(query, key, value)
+    mask, kind = _mask4(attn_mask, value.dtype)
     return _forward(query, key, value, _tables4(rope_cos, query.device), _tables4(rope_sin, query.device),
-                    mask, kind, bool(is_causal), scale, need_lse=True, quant=quantization)
+                    mask, kind, bool(is_causal), scale, need_lse=True, quant=quantization,
+                    norm=_norm_args(query, q_norm_weight, k_norm_weight, norm_eps))
 
 
 def rope_rotate(x, rope_cos, rope_sin, out=None):

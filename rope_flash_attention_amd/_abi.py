@@ -46,6 +46,9 @@ class RsArgs(ctypes.Structure):
         ("mask_kind", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
         ("scale", ctypes.c_float),
+        ("q_norm_weight", ctypes.c_void_p),
+        ("k_norm_weight", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
     ]
 
 

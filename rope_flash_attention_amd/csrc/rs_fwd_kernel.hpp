@@ -88,11 +88,20 @@ constexpr int PV_AHEAD = 3;  // V^T fragments (two reads each) in flight ahead o
 // QEXP (with QI8 = 1): code export mode for tests, which writes the codes and scales
 // instead of the output.
 // ROPE = false: plain attention, Q and K used as given (no tables read, no rotation).
-template <typename T, int D, int MASK, bool CAUSAL, int QI8 = 0, bool ROPE = true, bool QEXP = false>
+// QKM: the Q/K prologue.  Bit 0: Q is RMS-normalized over the head dimension (weights
+// p.qnw) before its rotation; bit 1: Q is stored in fp32 while V, O and the matrix products
+// are in T (the autocast layout of flux-style attention); bit 2: K arrives already
+// normalized and rotated, in T (kprep_kernel's output), so the key loop reads no tables.
+template <typename T, int D, int MASK, bool CAUSAL, int QI8 = 0, bool ROPE = true, bool QEXP = false, int QKM = 0>
 __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   static_assert(!QI8 || (sizeof(T) == 2 && MASK == MASK_NONE && !CAUSAL), "int8 variant: 16-bit, unmasked");
   static_assert(ROPE || !QI8, "the int8 variant rotates");
   static_assert(!QEXP || QI8 == 1, "code export is the in-kernel int8 mode");
+  static_assert(QKM == 0 || (ROPE && !QI8 && (QKM & 4)), "Q/K prologue: rotating path, K prepared");
+  constexpr bool NORM = (QKM & 1) != 0;
+  using TQ = typename std::conditional<(QKM & 2) != 0, float, T>::type;  // Q storage type
+  static_assert((QKM & 2) == 0 || sizeof(T) == 2, "fp32 Q/K with 16-bit V");
+  constexpr bool KROT = ROPE && (QKM & 4) == 0;  // K rotated in the key loop
   using M = Mf<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = 2 * KPL;
@@ -106,8 +115,8 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   constexpr int KBYTES = BN * KP;
   constexpr int VRB = D * ES;      // V row bytes in LDS (row-major, unpadded)
   constexpr int VBYTES = BN * VRB;
-  constexpr int CPR = D / EPC;     // 16-byte chunks per K (and V) row
-  constexpr int KCPT = BN * CPR / NT;
+  constexpr int CPR = D / EPC;     // 16-byte chunks per V row
+  constexpr int KCPT = BN * CPR / NT;  // 16-byte K chunks per thread and tile
   static_assert(KCPT * NT == BN * CPR, "K tile split");
   constexpr int NW = NT / 64;
   constexpr int VLD = VBYTES / 1024 / NW;  // direct-to-LDS V loads per wave (1 KB each)
@@ -177,7 +186,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   const int mc = m < S ? m : S - 1;
 
   const int hk = hd / p.shp.group;  // K/V head (grouped-query attention)
-  const T* qbase = (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh;
+  const TQ* qbase = (const TQ*)p.q.ptr + b * p.q.sb + hd * p.q.sh;
   const T* kbase = (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh;
   const T* vbase = (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh;
   const float* tab = p.tab.ptr + b * p.tab.sb;  // float2 pairs, row stride D/2 pairs = D floats
@@ -253,17 +262,49 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         p.xq_scales[((int64_t)b * p.shp.H + hd) * nblk + row0 / 64] = qsc;
     }
   } else {
-    const T* qrow = qbase + (int64_t)mc * p.q.ss;
+    const TQ* qrow = qbase + (int64_t)mc * p.q.ss;
     const float* trow = tab + (int64_t)mc * D;
     if constexpr (KPL == 8) {
+      // this lane holds elements t * 16 + hh * 8 + e of its row, the partner lane (the other
+      // half of the wave) the rest
+      float xq[NQK][8];
 #pragma unroll
       for (int t = 0; t < NQK; ++t) {
         const int d0 = t * 16 + hh * 8;
-        typedef T v8 __attribute__((ext_vector_type(8)));
-        v8 x = *(const v8*)(qrow + d0);
+        if constexpr (sizeof(TQ) == 4) {
+          const float4 a = *(const float4*)(qrow + d0), c = *(const float4*)(qrow + d0 + 4);
+          xq[t][0] = a.x; xq[t][1] = a.y; xq[t][2] = a.z; xq[t][3] = a.w;
+          xq[t][4] = c.x; xq[t][5] = c.y; xq[t][6] = c.z; xq[t][7] = c.w;
+        } else {
+          typedef T v8 __attribute__((ext_vector_type(8)));
+          const v8 x = *(const v8*)(qrow + d0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xq[t][e] = to_f(x[e]);
+        }
+      }
+      if constexpr (NORM) {  // x / sqrt(mean x^2 + eps) * w over the whole row
+        float ssq = 0.f;
+#pragma unroll
+        for (int t = 0; t < NQK; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ssq = fmaf(xq[t][e], xq[t][e], ssq);
+        ssq = xhalf_sum(ssq);
+        const float inv = 1.f / __builtin_sqrtf(ssq * (1.f / D) + p.norm_eps);
+#pragma unroll
+        for (int t = 0; t < NQK; ++t) {
+          const int d0 = t * 16 + hh * 8;
+          const float4 wa = *(const float4*)(p.qnw + d0), wb = *(const float4*)(p.qnw + d0 + 4);
+          const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xq[t][e] = xq[t][e] * inv * wv[e];
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NQK; ++t) {
+        const int d0 = t * 16 + hh * 8;
         if constexpr (!ROPE) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qf[t][e] = from_f<T>(to_f(x[e]) * c2);
+          for (int e = 0; e < 8; ++e) qf[t][e] = from_f<T>(xq[t][e] * c2);
           continue;
         }
         const float4 cs0 = *(const float4*)(trow + d0);      // pairs d0/2, d0/2+1
@@ -272,15 +313,31 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         const float ss[4] = {cs0.y, cs0.w, cs1.y, cs1.w};
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-          float2 rr = rot_pair_fma(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), cc[pp], ss[pp]);
+          float2 rr = rot_pair_fma(xq[t][2 * pp], xq[t][2 * pp + 1], cc[pp], ss[pp]);
           qf[t][2 * pp] = from_f<T>(rr.x * c2);
           qf[t][2 * pp + 1] = from_f<T>(rr.y * c2);
         }
       }
     } else {
+      // fp32: every lane reads its whole row (element d = 2t + hh of pair t is its own)
+      float inv = 1.f;
+      if constexpr (NORM) {
+        float ssq = 0.f;
+#pragma unroll
+        for (int t = 0; t < NQK; ++t) {
+          const float2 x = *(const float2*)(qrow + 2 * t);
+          ssq = fmaf(x.x, x.x, fmaf(x.y, x.y, ssq));
+        }
+        inv = 1.f / __builtin_sqrtf(ssq * (1.f / D) + p.norm_eps);
+      }
 #pragma unroll
       for (int t = 0; t < NQK; ++t) {  // element d = 2t + hh of pair t
-        const float2 x = *(const float2*)(qrow + 2 * t);
+        float2 x = *(const float2*)(qrow + 2 * t);
+        if constexpr (NORM) {
+          const float2 wq = *(const float2*)(p.qnw + 2 * t);
+          x.x = x.x * inv * wq.x;
+          x.y = x.y * inv * wq.y;
+        }
         if constexpr (!ROPE) {
           qf[t] = (hh ? x.y : x.x) * c2;
           continue;
@@ -396,7 +453,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
                                              krs, (uint32_t)((k_off + it * KROWS_PER_IT * (int)p.k.ss) * ES), 0, 0));
   };
   auto load_k_tab = [&](int kt) __attribute__((always_inline)) {
-    if constexpr (!ROPE || QI8 == 2) return;
+    if constexpr (!KROT || QI8 == 2) return;
     const __amdgpu_buffer_rsrc_t trs = rows_rsrc(tab, kt * BN, S, D * 4, D * 4);
 #pragma unroll
     for (int it = 0; it < KCPT; ++it)
@@ -499,7 +556,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     for (int it = 0; it < KCPT; ++it) {
       const float* tf = (const float*)&kt4[it][0];  // (c, s) per pair
       uint4 outw;
-      if constexpr (!ROPE) {
+      if constexpr (!KROT) {
         outw = kx[it];
       } else if constexpr (ES == 2) {
         typedef T v8 __attribute__((ext_vector_type(8)));
@@ -996,7 +1053,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p) {
   if (p.lse && c == 0) p.lse[((int64_t)b * p.shp.H + hd) * S + m] = sum > 0.f ? mx + __logf(sum) : -INFINITY;
 }
 
-template <typename T, int D, int MASK, bool CAUSAL, int QI8 = 0, bool ROPE = true, bool QEXP = false>
+template <typename T, int D, int MASK, bool CAUSAL, int QI8 = 0, bool ROPE = true, bool QEXP = false, int QKM = 0>
 static int launch_fwd_t(const FwdParams& p, void* stream) {
   const int grid = p.split_iters > 0 ? p.split_full + p.split_grid
                    : CAUSAL        ? (p.num_qt + 1) / 2 * p.shp.H * p.shp.B
@@ -1006,14 +1063,14 @@ static int launch_fwd_t(const FwdParams& p, void* stream) {
     // the device by the gate word, with no host synchronisation
     FwdParams pn = p;
     pn.gate_mode = 1;
-    hipLaunchKernelGGL((fwd_kernel<T, D, MASK_NONE, CAUSAL, QI8, ROPE, QEXP>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
+    hipLaunchKernelGGL((fwd_kernel<T, D, MASK_NONE, CAUSAL, QI8, ROPE, QEXP, QKM>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
                        (hipStream_t)stream, pn);
     FwdParams pb = p;
     pb.gate_mode = 2;
-    hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL, QI8, ROPE, QEXP>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
+    hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL, QI8, ROPE, QEXP, QKM>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
                        (hipStream_t)stream, pb);
   } else {
-    hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL, QI8, ROPE, QEXP>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
+    hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL, QI8, ROPE, QEXP, QKM>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
                        (hipStream_t)stream, p);
   }
   if (p.split_iters > 0) {

@@ -64,6 +64,9 @@ rs_status check_bhsd(const rs_tensor* t, int dtype, const int64_t* size, bool em
 
 struct Shape {
   int64_t B, H, S, D;
+  int qdtype;   // dtype of Q and K (that of V, or f32 with 16-bit V)
+  int qkm;      // Q/K prologue: bit 0 RMSNorm, bit 1 fp32 Q/K with 16-bit V
+  bool kprep;   // forward: K rotated (and normalized) once into the workspace by kprep_kernel
   bool rope;    // rotation tables given (both NULL: plain attention, forward only)
   int64_t Hkv;  // heads of K and V (grouped-query attention: H % Hkv == 0)
   bool empty;  // B, H or S is 0: a valid call with nothing to compute
@@ -93,9 +96,13 @@ rs_status validate_args(const rs_args* a, Shape* out) {
   if (!a || !a->q || !a->k || !a->v) return RS_ERR_NULL;
   if ((a->cos == nullptr) != (a->sin == nullptr)) return RS_ERR_NULL;  // both or neither
   const rs_tensor* q = a->q;
-  const int dt = q->dtype;
+  const int dt = a->v->dtype;  // the compute dtype: V, O and the matrix products
   if (dt != RS_F32 && dt != RS_F16 && dt != RS_BF16) return RS_ERR_DTYPE;
+  const int qdt = q->dtype;
+  if (qdt != dt && !(qdt == RS_F32 && dt != RS_F32)) return RS_ERR_DTYPE;
   Shape s{};
+  s.qdtype = qdt;
+  s.qkm = qdt != dt ? 2 : 0;
   s.B = q->size[0];
   s.H = q->size[1];
   s.S = q->size[2];
@@ -110,15 +117,22 @@ rs_status validate_args(const rs_args* a, Shape* out) {
   if (s.B * s.H * nqt >= ((int64_t)1 << 31) || s.B * s.H * s.S >= ((int64_t)1 << 31)) return RS_ERR_SHAPE;
   const int64_t sz[4] = {s.B, s.H, s.S, s.D};
   rs_status st;
-  if ((st = check_bhsd(q, dt, sz, s.empty)) != RS_OK) return st;
-  // K and V: same dtype as Q (mixed dtypes, e.g. fp32 Q/K with bf16 V, are rejected), and
-  // Hkv heads with H % Hkv == 0 (grouped-query attention when Hkv < H)
-  if (a->k->dtype != dt || a->v->dtype != dt) return RS_ERR_DTYPE;
+  if ((st = check_bhsd(q, qdt, sz, s.empty)) != RS_OK) return st;
+  // K in Q's dtype, V in the compute dtype, Hkv heads with H % Hkv == 0 (grouped-query
+  // attention when Hkv < H)
+  if (a->k->dtype != qdt) return RS_ERR_DTYPE;
   s.Hkv = a->k->size[1];
   if (s.H == 0 ? s.Hkv != 0 : (s.Hkv <= 0 || s.H % s.Hkv != 0)) return RS_ERR_SHAPE;
   const int64_t szkv[4] = {s.B, s.Hkv, s.S, s.D};
-  if ((st = check_bhsd(a->k, dt, szkv, s.empty)) != RS_OK) return st;
+  if ((st = check_bhsd(a->k, qdt, szkv, s.empty)) != RS_OK) return st;
   if ((st = check_bhsd(a->v, dt, szkv, s.empty)) != RS_OK) return st;
+  // optional Q/K RMSNorm: both weights or neither
+  if ((a->q_norm_weight == nullptr) != (a->k_norm_weight == nullptr)) return RS_ERR_INVALID;
+  if (a->q_norm_weight) {
+    if (!std::isfinite(a->norm_eps) || a->norm_eps < 0.f) return RS_ERR_INVALID;
+    if (((uintptr_t)a->q_norm_weight) % 16 != 0 || ((uintptr_t)a->k_norm_weight) % 16 != 0) return RS_ERR_ALIGN;
+    s.qkm |= 1;
+  }
   s.rope = a->cos != nullptr;
   if (s.rope) {
     int64_t bt_c = 0, bt_s = 0;
@@ -170,8 +184,9 @@ rs_status validate_args(const rs_args* a, Shape* out) {
   } else {
     return RS_ERR_INVALID;
   }
+  if (s.qkm != 0 && (!s.rope || a->mask_kind == RS_MASK_ADDITIVE)) return RS_ERR_UNSUPPORTED;
   if (a->flags & RS_FLAG_QUANT_INT8_QK) {
-    if (dt == RS_F32 || !s.rope) return RS_ERR_UNSUPPORTED;
+    if (dt == RS_F32 || !s.rope || s.qkm != 0) return RS_ERR_UNSUPPORTED;
     if (a->mask_kind != RS_MASK_NONE || causal) return RS_ERR_UNSUPPORTED;
   }
   if (a->mask_kind == RS_MASK_BOOL) {
@@ -179,12 +194,16 @@ rs_status validate_args(const rs_args* a, Shape* out) {
     // grid limits of the tile classifier (y: query tiles, z: mask batch x heads)
     if ((s.mQ + kMaskTile - 1) / kMaskTile > 65535 || s.mB * s.mH > 65535) return RS_ERR_SHAPE;
   }
+  // The 16-bit rotating forward (no int8, no additive mask) rotates K once into the
+  // workspace and keeps tables out of its key loop; the Q/K prologue always does.
+  s.kprep = s.qkm != 0 || (s.rope && dt != RS_F32 && !(a->flags & RS_FLAG_QUANT_INT8_QK) &&
+                           a->mask_kind != RS_MASK_ADDITIVE);
   *out = s;
   return RS_OK;
 }
 
 struct Layout {
-  size_t ctrl, table, tiles, delta, qrot, qc, kc, qs, ks, part, cnt, total;
+  size_t ctrl, table, tiles, delta, qrot, qc, kc, qs, ks, kprep, part, cnt, total;
   int64_t nqt, nkt;
   int64_t sp, nblk;  // pre-quantized int8: padded rows per (b, h) slice and 64-token blocks
   SplitPlan split;   // forward only: work split over the current device's workgroups
@@ -220,6 +239,8 @@ Layout layout(const Shape& s, int mask_kind, bool backward, int int8, bool causa
     L.ks = off;
     off += round_up((size_t)(s.B * s.Hkv * L.nblk) * sizeof(float), 256);
   }
+  L.kprep = off;  // K' of the Q/K prologue: [B][Hkv][S][D] in the compute dtype
+  if (!backward && s.kprep) off += round_up((size_t)(s.B * s.Hkv * s.S * s.D) * elem_size(s.dtype), 256);
   if (!backward) {
     const int64_t bm = fwd_block_m(s.dtype), bn = fwd_block_n(s.dtype);
     const int64_t units = s.B * s.H * ((s.S + bm - 1) / bm);
@@ -421,7 +442,12 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
   if (lse && ((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
   if (s.empty) return RS_OK;  // nothing to compute: no workspace or device needed
   const int int8 = int8_mode(a->flags);
-  const Layout L = layout(s, a->mask_kind, false, int8, (a->flags & RS_FLAG_CAUSAL) != 0);
+  const bool causal_flag = (a->flags & RS_FLAG_CAUSAL) != 0;
+  Layout L = layout(s, a->mask_kind, false, int8, causal_flag);
+  if (scratch && L.total > kScratchBytes && s.kprep && s.qkm == 0) {
+    s.kprep = false;  // the fixed scratch cannot hold K': rotate K in the key loop instead
+    L = layout(s, a->mask_kind, false, int8, causal_flag);
+  }
   if (scratch) {
     if (L.total > kScratchBytes) return fail(RS_ERR_SCRATCH);
     if ((st = current_device_ok()) != RS_OK) return fail(st);
@@ -466,8 +492,29 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
     p.part_o = w + L.part;
     p.part_lse = (float*)(w + L.cnt);
   }
-  const int lerr = s.rope ? launch_fwd(s.dtype, (int)s.D, a->mask_kind, causal, int8, p, strm)
-                         : launch_fwd_plain(s.dtype, (int)s.D, a->mask_kind, causal, p, strm);
+  p.qnw = a->q_norm_weight;
+  p.knw = a->k_norm_weight;
+  p.norm_eps = a->norm_eps;
+  if (s.kprep) {  // K prepared once into the workspace, then read as K' by the attention kernel
+    KPrepParams kp{};
+    kp.x = p.k;
+    kp.out = w + L.kprep;
+    kp.tab = p.tab;
+    kp.w = a->k_norm_weight;
+    kp.eps = a->norm_eps;
+    kp.B = (int)s.B;
+    kp.H = (int)s.Hkv;
+    kp.S = (int)s.S;
+    kp.D = (int)s.D;
+    if (launch_kprep(s.dtype, s.qkm, kp, strm) != 0) return fail(RS_ERR_LAUNCH);
+    p.k.ptr = w + L.kprep;
+    p.k.sb = s.Hkv * s.S * s.D;
+    p.k.sh = s.S * s.D;
+    p.k.ss = s.D;
+  }
+  const int lerr = !s.rope        ? launch_fwd_plain(s.dtype, (int)s.D, a->mask_kind, causal, p, strm)
+                   : s.kprep    ? launch_fwd_qk(s.dtype, (int)s.D, a->mask_kind, causal, s.qkm | 4, p, strm)
+                                : launch_fwd(s.dtype, (int)s.D, a->mask_kind, causal, int8, p, strm);
   if (lerr != 0) return fail(RS_ERR_LAUNCH);
 
   (lse ? g_ctr.fwd_autograd : g_ctr.fwd_instream).fetch_add(1, std::memory_order_relaxed);
@@ -534,6 +581,7 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   if (st != RS_OK) return fail(st);
   if (a->flags & RS_FLAG_QUANT_INT8_QK) return fail(RS_ERR_UNSUPPORTED);
   if (!s.rope) return fail(RS_ERR_UNSUPPORTED);  // the backward is the fused one: tables required
+  if (s.qkm != 0) return fail(RS_ERR_UNSUPPORTED);  // no backward through the Q/K prologue
   const int64_t sz[4] = {s.B, s.H, s.S, s.D};
   const int64_t szkv[4] = {s.B, s.Hkv, s.S, s.D};
   if (!o || !dout || !dq || !dk || !dv || (!lse && !s.empty)) return fail(RS_ERR_NULL);

@@ -76,6 +76,10 @@ struct FwdParams {
   int8_t* xk_codes;
   float* xq_scales;
   float* xk_scales;
+  // Q/K RMSNorm weights (fp32 [D], device; used when the launch asks for the normalization)
+  const float* qnw;
+  const float* knw;
+  float norm_eps;
   // bool masks: the unmasked and the masked kernel are both enqueued; each reads the mask
   // classifier's word gate[0] (nonzero: some key is excluded) at entry and returns at once
   // unless gate_mode says it is the one to run (1: gate[0] == 0, 2: gate[0] != 0; 0: always)
@@ -163,6 +167,22 @@ SplitPlan fwd_split_plan(int dtype, int D, bool int8, bool causal, int mask_kind
 // int8: 0 = none, 1 = quantized in the attention kernel, 2 = codes from the quantizer pass
 int launch_fwd(int dtype, int D, int mask_kind, bool causal, int int8, const FwdParams& p, void* stream);
 int launch_quant_int8(int dtype, const QuantParams& p, void* stream);
+// K of the Q/K prologue, prepared once: RMS-normalized (optional), rotated with the packed
+// tables and rounded to the compute dtype, into a contiguous [B][H][S][D] buffer (H = the
+// K/V head count).  Input in the compute dtype, or fp32 beside 16-bit V.
+struct KPrepParams {
+  Opnd x;
+  void* out;
+  Table tab;
+  const float* w;  // RMSNorm weights [D] (normalizing launches only)
+  float eps;
+  int B, H, S, D;
+};
+// qkm: bit 0 normalize, bit 1 fp32 input
+int launch_kprep(int dtype, int qkm, const KPrepParams& p, void* stream);
+// The forward with the Q/K prologue (qkm: bit 0 Q normalized, bit 1 Q in fp32 beside 16-bit V,
+// bit 2 set: K prepared by launch_kprep); no mask, bool mask or causal.
+int launch_fwd_qk(int dtype, int D, int mask_kind, bool causal, int qkm, const FwdParams& p, void* stream);
 // The forward without rotation (no tables: plain attention).
 int launch_fwd_plain(int dtype, int D, int mask_kind, bool causal, const FwdParams& p, void* stream);
 int launch_rotate(int dtype, const RotateParams& p, void* stream);

@@ -33,7 +33,7 @@ import torch
 
 # Independent random streams per tensor role, so that changing one tensor's shape
 # never changes another tensor's values.
-STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_LEN, STREAM_TAB = 1, 2, 3, 4, 5, 6
+STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_LEN, STREAM_TAB, STREAM_NORM = 1, 2, 3, 4, 5, 6, 7
 STREAM_LAYER = 100  # + 2 * layer (K) and + 2 * layer + 1 (V) of a chain
 
 _TORCH_DTYPES = {
@@ -53,6 +53,14 @@ def normal(seed: int, stream: int, shape, dtype: str = "bf16", std: float = 1.0)
     if std != 1.0:
         x = x * np.float32(std)
     return torch.from_numpy(x).to(_TORCH_DTYPES[dtype])
+
+
+def norm_weights(seed: int, dim: int):
+    """Per-dimension RMSNorm weights for Q and K: fp32 [dim] each, 1 + 0.25 N(0, 1) (learned
+    weights stay near their initial value of one)."""
+    x = rng(seed, STREAM_NORM).standard_normal(size=(2, dim), dtype=np.float32)
+    w = torch.from_numpy(np.float32(1.0) + np.float32(0.25) * x)
+    return w[0].clone(), w[1].clone()
 
 
 def rope_angles(positions: np.ndarray, dim: int, theta: float) -> np.ndarray:

@@ -168,6 +168,40 @@ int main() {
       c.a.cos = c.a.sin = nullptr;
       expect_error(c, true, RS_ERR_UNSUPPORTED, "plain backward");
     }
+  // fp32 Q/K beside 16-bit V, and the Q/K RMSNorm prologue: forward only
+  for (int dt : dts)
+    for (int mixed = 0; mixed < 2; ++mixed)
+      for (int norm = 0; norm < 2; ++norm)
+        for (int variant = 0; variant < 4; ++variant) {
+          if (!mixed && !norm) continue;
+          if (mixed && dt == RS_F32) continue;
+          Case c(dt, 2, 6, 300, variant == 3 ? 64 : 128, variant == 3 ? 2 : 1, variant == 3 ? 2 : 6);
+          if (mixed) c.q.dtype = c.k.dtype = RS_F32;
+          if (norm) {
+            c.a.q_norm_weight = (const float*)fake_ptr();
+            c.a.k_norm_weight = (const float*)fake_ptr();
+            c.a.norm_eps = 1e-6f;
+          }
+          if (variant == 1) c.a.flags = RS_FLAG_CAUSAL;
+          if (variant == 2) c.set_mask(RS_MASK_BOOL, RS_BOOL, 2, 1, 1, 300);
+          CHECK(run(c, false) == RS_OK, "Q/K prologue dt=%d mixed=%d norm=%d variant=%d", dt, mixed, norm, variant);
+          expect_error(c, true, RS_ERR_UNSUPPORTED, "Q/K prologue backward");
+          c.set_mask(RS_MASK_ADDITIVE, RS_F32, 1, 1, 1, 300);
+          c.a.flags = 0;
+          expect_error(c, false, RS_ERR_UNSUPPORTED, "Q/K prologue with an additive mask");
+        }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.q.dtype = c.k.dtype = RS_F32; c.a.cos = c.a.sin = nullptr;
+    expect_error(c, false, RS_ERR_UNSUPPORTED, "fp32 Q/K without tables"); }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.q.dtype = c.k.dtype = RS_F32; c.a.flags = RS_FLAG_QUANT_INT8_QK;
+    expect_error(c, false, RS_ERR_UNSUPPORTED, "fp32 Q/K with int8"); }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.a.q_norm_weight = (const float*)fake_ptr();
+    expect_error(c, false, RS_ERR_INVALID, "one norm weight"); }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.a.q_norm_weight = (const float*)fake_ptr();
+    c.a.k_norm_weight = (const float*)fake_ptr(); c.a.norm_eps = -1.f;
+    expect_error(c, false, RS_ERR_INVALID, "negative norm eps"); }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.a.q_norm_weight = (const float*)fake_ptr();
+    c.a.k_norm_weight = (const float*)((uintptr_t)fake_ptr() + 4);
+    expect_error(c, false, RS_ERR_ALIGN, "misaligned norm weight"); }
   { Case c(RS_BF16, 1, 2, 128, 64); c.a.sin = nullptr; expect_error(c, false, RS_ERR_NULL, "one table missing"); }
   { Case c(RS_BF16, 1, 2, 128, 64); c.a.cos = c.a.sin = nullptr; c.a.flags = RS_FLAG_QUANT_INT8_QK;
     expect_error(c, false, RS_ERR_UNSUPPORTED, "int8 without tables"); }
@@ -205,7 +239,9 @@ int main() {
   }
   { Case c(RS_BF16, 1, 2, 128, 64); c.a.q = nullptr; expect_error(c, false, RS_ERR_NULL, "null q"); }
   { Case c(RS_BF16, 1, 2, 128, 64); c.q.data = nullptr; expect_error(c, false, RS_ERR_NULL, "null q data"); }
-  { Case c(RS_BF16, 1, 2, 128, 64); c.q.dtype = c.k.dtype = RS_F32; expect_error(c, false, RS_ERR_DTYPE, "fp32 Q/K with bf16 V"); }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.q.dtype = RS_F16; c.k.dtype = RS_F16; expect_error(c, false, RS_ERR_DTYPE, "f16 Q/K with bf16 V"); }
+  { Case c(RS_F32, 1, 2, 128, 64); c.q.dtype = c.k.dtype = RS_BF16; expect_error(c, false, RS_ERR_DTYPE, "bf16 Q/K with f32 V"); }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.q.dtype = RS_F32; expect_error(c, false, RS_ERR_DTYPE, "fp32 Q with bf16 K"); }
   { Case c(RS_BF16, 1, 2, 128, 64); c.o.dtype = RS_F16; expect_error(c, false, RS_ERR_DTYPE, "output dtype"); }
   { Case c(RS_BOOL, 1, 2, 128, 64); expect_error(c, false, RS_ERR_DTYPE, "bool q"); }
   { Case c(RS_BF16, 1, 2, 128, 96); expect_error(c, false, RS_ERR_SHAPE, "D = 96"); }

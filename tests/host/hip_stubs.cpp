@@ -107,6 +107,37 @@ int launch_fwd_plain(int, int, int, bool, const FwdParams& p, void*) {
   return 0;
 }
 
+int launch_kprep(int dtype, int qkm, const KPrepParams& p, void*) {
+  ++stub::launches;
+  const size_t es = dtype == F32 ? 4 : 2;
+  stub::need(p.out, (size_t)p.B * p.H * p.S * p.D * es, "prepared K");
+  stub::need(p.tab.ptr, (size_t)(p.tab.sb ? p.B : 1) * p.S * p.D * sizeof(float), "packed tables");
+  if ((qkm & 1) != (p.w != nullptr)) std::abort();
+  if ((qkm & 2) && dtype == F32) std::abort();
+  if (p.D != 64 && p.D != 128) std::abort();
+  return 0;
+}
+
+int launch_fwd_qk(int dtype, int D, int, bool, int qkm, const FwdParams& p, void*) {
+  ++stub::launches;
+  const int B = p.shp.B, S = p.shp.S;
+  stub::need(p.tab.ptr, (size_t)(p.tab.sb ? B : 1) * S * D * sizeof(float), "packed tables");
+  if (qkm < 4 || qkm > 7) std::abort();
+  // K is the prepared, contiguous K' in the workspace
+  const size_t es = dtype == F32 ? 4 : 2;
+  stub::need(p.k.ptr, (size_t)B * p.shp.Hkv * S * D * es, "prepared K");
+  if (p.k.ss != D || p.k.sh != (int64_t)S * D || p.k.sb != (int64_t)p.shp.Hkv * S * D) std::abort();
+  if ((qkm & 1) != (p.qnw != nullptr) || (p.qnw == nullptr) != (p.knw == nullptr)) std::abort();
+  if ((qkm & 2) && dtype == F32) std::abort();  // fp32 Q/K only beside 16-bit V
+  if (p.qc || p.kc || p.xq_codes || p.xk_codes) std::abort();
+  if (p.split_iters > 0) {
+    const size_t bm = (size_t)fwd_block_m(dtype), es = dtype == F32 ? 4 : 2;
+    stub::need(p.part_o, 2 * (size_t)p.split_grid * bm * D * es, "pieces' outputs");
+    stub::need(p.part_lse, 2 * (size_t)p.split_grid * bm * sizeof(float), "pieces' LSE");
+  }
+  return 0;
+}
+
 int launch_rotate(int, const RotateParams& p, void*) {
   ++stub::launches;
   if (!p.cos || !p.sin || !p.out || p.B <= 0 || p.H <= 0 || p.S <= 0 || (p.D != 64 && p.D != 128)) std::abort();

@@ -172,13 +172,15 @@ def test_int8_flag_limits():
 
 def test_int8_workspace_holds_no_codes():
     """The int8 forward quantizes Q' and K' inside the attention kernel: its workspace is the
-    16-bit forward's (no codes or scales in memory)."""
+    16-bit forward's without the rotated K' the 16-bit forward prepares (no codes or scales in
+    memory)."""
     c = Call(B=2, H=3, S=100, D=128)
     st, n = c.ws_size(0)
     c.flags = RS_FLAG_QUANT_INT8_QK
     st8, n8 = c.ws_size(0)
     assert st == 0 and st8 == 0
-    assert n8 == n
+    kprime = -(-(2 * 3 * 100 * 128 * 2) // 256) * 256
+    assert n8 == n - kprime
 
 
 def test_debug_quantize_validation():
@@ -218,10 +220,11 @@ def test_workspace_size_layout():
     st, n = c.ws_size(0)
     assert st == 0
     table = 100 * 128 * 4  # (cos, sin) pairs: D/2 float2 per position
-    assert n == 256 + -(-table // 256) * 256
+    kprime = -(-(2 * 3 * 100 * 128 * 2) // 256) * 256  # 16-bit forward: K' = R(K), rotated once
+    assert n == 256 + -(-table // 256) * 256 + kprime
     st, nb = c.ws_size(1)
-    # backward: + delta (fp32 per row) + Q' = R(Q) in the input dtype (16-bit, D = 128)
-    assert st == 0 and nb == n + -(-(2 * 3 * 100 * 4) // 256) * 256 + -(-(2 * 3 * 100 * 128 * 2) // 256) * 256
+    # backward: + delta (fp32 per row) + Q' = R(Q) in the input dtype (16-bit, D = 128), no K'
+    assert st == 0 and nb == n - kprime + -(-(2 * 3 * 100 * 4) // 256) * 256 + -(-(2 * 3 * 100 * 128 * 2) // 256) * 256
     f = Call(B=2, H=3, S=100, D=128, dt=RS_F32, es=4)
     st, nf = f.ws_size(0)
     st2, nfb = f.ws_size(1)
@@ -233,7 +236,7 @@ def test_workspace_size_layout():
     c.sin.size[0] = 2
     c.mask, c.kind = None, RS_MASK_NONE
     st, n2 = c.ws_size(0)
-    assert st == 0 and n2 == 256 + -(-(2 * table) // 256) * 256
+    assert st == 0 and n2 == 256 + -(-(2 * table) // 256) * 256 + kprime
 
 
 def test_backward_validation_and_error_counter():

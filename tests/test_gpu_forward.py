@@ -191,10 +191,15 @@ def test_dispatch_counters_split_instream_and_autograd():
 
 
 def test_rejects_mixed_dtypes_without_launching():
+    """fp32 Q/K beside bf16 V is accepted (forward only); Q and K of different dtypes, or
+    16-bit Q/K of another dtype than V, are not."""
     w = syn.random_small(1, 1, 64, 64, "bf16", seed=29)
     d = dev()
     with pytest.raises(rfa.RopeSdpaError):
-        rfa.rope_scaled_dot_product_attention(w.q.float().to(d), w.k.float().to(d), w.v.to(d),
+        rfa.rope_scaled_dot_product_attention(w.q.float().to(d), w.k.to(d), w.v.to(d),
+                                              w.cos.to(d), w.sin.to(d))
+    with pytest.raises(rfa.RopeSdpaError):
+        rfa.rope_scaled_dot_product_attention(w.q.half().to(d), w.k.half().to(d), w.v.to(d),
                                               w.cos.to(d), w.sin.to(d))
 
 

@@ -24,10 +24,12 @@ def _desc(t):
     return make_tensor(t.data_ptr(), _DT[t.dtype], t.shape, t.stride())
 
 
-def _run(w, noalloc, int8=False):
-    """One forward through the C ABI on device copies of workload w: returns (O, LSE)."""
+def _run(w, noalloc, int8=False, qk=None, norm=None):
+    """One forward through the C ABI on device copies of workload w (Q and K replaced by `qk`
+    when given; `norm` = (q weights, k weights, eps) for the RMSNorm prologue): returns
+    (O, LSE)."""
     d = torch.device("cuda:0")
-    q, k, v = (t.to(d) for t in (w.q, w.k, w.v))
+    q, k, v = (t.to(d) for t in ((w.q, w.k) if qk is None else qk) + (w.v,))
     cos = w.cos.to(d).unsqueeze(1)
     sin = w.sin.to(d).unsqueeze(1)
     mask = None
@@ -41,7 +43,10 @@ def _run(w, noalloc, int8=False):
     a.mask_kind = {"none": _abi.RS_MASK_NONE, "bool": _abi.RS_MASK_BOOL, "additive": _abi.RS_MASK_ADDITIVE}[w.mask_kind]
     a.flags = RS_FLAG_QUANT_INT8_QK if int8 else 0
     a.scale = 0.0
-    o = torch.empty_like(q)
+    if norm is not None:
+        wq, wk = norm[0].to(d), norm[1].to(d)
+        a.q_norm_weight, a.k_norm_weight, a.norm_eps = wq.data_ptr(), wk.data_ptr(), norm[2]
+    o = torch.empty(q.shape, dtype=v.dtype, device=d)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=d)
     to = _desc(o)
     lib = _abi.load()
@@ -61,6 +66,8 @@ def _run(w, noalloc, int8=False):
 def _case(name):
     if name == "flux":  # 432 units: the last round's units are cut into pieces
         return syn.flux(batch=1, heads=24, grid=64, dtype="bf16", seed=2000)
+    if name == "flux_b3":  # K' (81 MiB) does not fit the scratch: K is rotated in the key loop
+        return syn.flux(batch=3, heads=24, grid=64, dtype="bf16", seed=2001)
     if name == "flux_bool":
         w = syn.flux(batch=2, heads=8, grid=64, dtype="bf16", seed=3000)
         w.mask = syn.key_padding_mask(syn.key_padding_lengths(3000, 2), 512, w.q.shape[2])
@@ -76,7 +83,7 @@ def _case(name):
 
 
 @pytest.mark.parametrize("first,second", [("flux", "small_split"), ("flux_bool", "small_fp32_mask"),
-                                          ("small_split", "tiny")])
+                                          ("small_split", "tiny"), ("flux_b3", "flux")])
 def test_noalloc_matches_workspace_forward_on_two_calls(first, second):
     for name in (first, second):
         w = _case(name)
@@ -84,6 +91,18 @@ def test_noalloc_matches_workspace_forward_on_two_calls(first, second):
         o, l = _run(w, noalloc=True)
         assert torch.equal(o, o_ref), name
         assert torch.equal(l, l_ref), name
+
+
+def test_noalloc_qk_prologue_two_calls():
+    """fp32 Q/K with RMSNorm beside bf16 V (K' prepared in the scratch), then a smaller call."""
+    for B, H, grid, seed in ((1, 8, 64, 140), (1, 2, 16, 141)):
+        w = syn.flux(batch=B, heads=H, grid=grid, dtype="bf16", seed=seed)
+        qk = (syn.normal(seed, syn.STREAM_Q, tuple(w.q.shape), "f32", 4.0),
+              syn.normal(seed, syn.STREAM_K, tuple(w.k.shape), "f32", 4.0))
+        norm = (*syn.norm_weights(seed, 128), 1e-6)
+        o_ref, l_ref = _run(w, noalloc=False, qk=qk, norm=norm)
+        o, l = _run(w, noalloc=True, qk=qk, norm=norm)
+        assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
 
 
 def test_noalloc_int8_and_rejection():
