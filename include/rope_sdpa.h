@@ -74,7 +74,8 @@ typedef enum { RS_MASK_NONE = 0, RS_MASK_BOOL = 1, RS_MASK_ADDITIVE = 2 } rs_mas
 enum {
   RS_FLAG_CAUSAL = 1u << 0,          /* exclude key j > query i; cannot be combined with a mask */
   RS_FLAG_QUANT_INT8_QK = 1u << 1,   /* forward only: blockwise int8 Q'/K' (see rope_sdpa_fwd) */
-  RS_FLAG_QUANT_INT8_PREPASS = 1u << 2 /* with RS_FLAG_QUANT_INT8_QK: codes from a quantizer pass */
+  RS_FLAG_QUANT_INT8_PREPASS = 1u << 2, /* with either QUANT flag: codes from a quantizer pass */
+  RS_FLAG_QUANT_INT4_QK = 1u << 3    /* as RS_FLAG_QUANT_INT8_QK with int4 codes (not both flags) */
 };
 
 typedef struct {
@@ -152,6 +153,11 @@ rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* by
  * scales of Q' and K' to the workspace first (one byte per element) and the attention kernel
  * streams them: the same codes and the same results bit for bit, faster, because each K
  * block is quantized once instead of once per query tile.
+ * RS_FLAG_QUANT_INT4_QK: the same with int4 codes, round-half-even(x * fp32(7/amax)) in
+ * [-7, 7] with scale amax/7 (pages: the "-int4" alias sets QUANT_INT4 with blockwise
+ * quantization).  CDNA4 has no int4 matrix instruction: the codes, exact as int8 values,
+ * take the int8 MFMA (the same speed as int8) and are stored one per byte in the pre-pass
+ * mode.
  */
 rs_status rope_sdpa_fwd(const rs_args* args, const rs_tensor* o, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);
@@ -181,7 +187,7 @@ size_t rope_sdpa_noalloc_scratch_bytes(void);
  * pre-rotation Q and K).  Inputs: the same args as the forward, its o and lse, and the
  * upstream gradient dout (sizes and dtype of o).  Writes dq (sizes of q), dk and dv (sizes of k),
  * all in the dtype of q.
- * The mask (if any) is a constant: no mask gradient.  Not available with RS_FLAG_QUANT_INT8_QK.
+ * The mask (if any) is a constant: no mask gradient.  Not available with the QUANT flags.
  */
 rs_status rope_sdpa_bwd(const rs_args* args, const rs_tensor* o, const float* lse,
                         const rs_tensor* dout, const rs_tensor* dq, const rs_tensor* dk,
@@ -189,12 +195,13 @@ rs_status rope_sdpa_bwd(const rs_args* args, const rs_tensor* o, const float* ls
                         void* stream);
 
 /*
- * Test-only export of the int8 quantization that rope_sdpa_fwd performs under
- * RS_FLAG_QUANT_INT8_QK (same reading, same kernel): writes the int8 codes of the rotated Q and
+ * Test-only export of the quantization that rope_sdpa_fwd performs under
+ * RS_FLAG_QUANT_INT8_QK or RS_FLAG_QUANT_INT4_QK (same reading, same kernel): writes the codes
+ * (int8 storage; int4 codes lie in [-7, 7]) of the rotated Q and
  * K into q_codes / k_codes, contiguous [B, H, S, D] / [B, Hkv, S, D] DEVICE buffers (8-byte
  * aligned), and their fp32 scales into q_scales / k_scales, contiguous [B, H, ceil(S / 64)] /
  * [B, Hkv, ceil(S / 64)] DEVICE buffers.  args
- * must carry RS_FLAG_QUANT_INT8_QK (else RS_ERR_INVALID) and pass the same validation as the
+ * must carry one of the QUANT flags (else RS_ERR_INVALID) and pass the same validation as the
  * forward; the workspace is the forward's (rope_sdpa_workspace_size(args, 0, ...)).  It lets a
  * test compare the integer decisions bit for bit and run a reference from exactly these
  * values.  Asynchronous on `stream`; nothing is launched on error.

@@ -13,9 +13,10 @@ with R the interleaved-pair rotation driven by caller-supplied cos/sin tables, m
 as in the section "Enable In SimpleTuner" (bool True = attend, additive float,
 broadcast up to 4-D), a causal mode, grouped-query attention (K/V with fewer heads,
 rotated at their own head count and expanded), and gradients with respect to the
-unrotated Q and K (the inverse rotation applied to dQ/dK).  The blockwise int8 variant follows
-the quantizer step by step and then applies the same definition to the dequantized
-rotated Q and K.
+unrotated Q and K (the inverse rotation applied to dQ/dK).  The blockwise int8 and int4
+variants follow the quantizer step by step and then apply the same definition to the
+dequantized rotated Q and K; their backward passes the gradient straight through the
+quantizer (the reading stated at rope_sdpa_backward_quant).
 
 Pins: every function here is checked in tests/test_oracle_*.py against something
 other than itself (naive textbook softmax, torch float64 SDPA as a library routine,
@@ -31,8 +32,13 @@ from .rope_sdpa_ref import (  # noqa: F401
     rope_sdpa_forward,
     rope_sdpa_backward,
     rope_rotate_f32,
+    quantize_blockwise,
     quantize_blockwise_int8,
+    quantize_blockwise_int4,
+    quantized_qk,
     rope_sdpa_forward_int8,
+    rope_sdpa_forward_quant,
+    rope_sdpa_backward_quant,
     expand_kv,
     reduce_kv,
     rms_norm,

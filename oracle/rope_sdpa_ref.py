@@ -380,6 +380,8 @@ def rope_sdpa_backward(q, k, v, cos, sin, do, mask=None, mask_kind="none", causa
 # sum/difference rounded (no fused multiply-add); inv = fp32(127 / amax); code =
 # round-half-even(fp32(x * inv)) clipped to [-127, 127]; the dequantization scale is
 # fp32(amax / 127); an all-zero block gets code 0 and scale 0.
+# The int4 alias ([EN]: "-int4" sets QUANT_INT4 with QUANT_BLOCK_WISE) takes the same
+# reading with qmax = 7: codes in [-7, 7], inv = fp32(7 / amax), scale = fp32(amax / 7).
 # --------------------------------------------------------------------------------------
 def rope_rotate_f32(x, cos, sin) -> np.ndarray:
     """Rotation evaluated in fp32 with every product and sum rounded to fp32 (no FMA)."""
@@ -397,8 +399,8 @@ def rope_rotate_f32(x, cos, sin) -> np.ndarray:
     return out
 
 
-def quantize_blockwise_int8(xr32: np.ndarray, block: int = 64):
-    """Symmetric int8 codes and fp32 scales per (b, h, block of `block` tokens).
+def quantize_blockwise(xr32: np.ndarray, block: int = 64, qmax: int = 127):
+    """Symmetric codes in [-qmax, qmax] and fp32 scales per (b, h, block of `block` tokens).
 
     Returns (codes int8 [B,H,S,D], scales float32 [B,H,ceil(S/block)]).  A final
     partial block uses only its valid rows.
@@ -406,19 +408,30 @@ def quantize_blockwise_int8(xr32: np.ndarray, block: int = 64):
     xr32 = np.asarray(xr32, dtype=np.float32)
     B, H, S, D = xr32.shape
     nb = (S + block - 1) // block
+    qm = np.float32(qmax)
     codes = np.zeros((B, H, S, D), dtype=np.int8)
     scales = np.zeros((B, H, nb), dtype=np.float32)
     for t in range(nb):
         blk = xr32[:, :, t * block:(t + 1) * block, :]
         amax = np.abs(blk).max(axis=(2, 3)).astype(np.float32)  # [B,H]
-        sc = (amax / np.float32(127.0)).astype(np.float32)
-        inv = (np.float32(127.0) / np.where(amax > 0, amax, np.float32(1.0))).astype(np.float32)
+        sc = (amax / qm).astype(np.float32)
+        inv = (qm / np.where(amax > 0, amax, np.float32(1.0))).astype(np.float32)
         qv = np.rint(blk * inv[:, :, None, None])  # fp32 product, round half to even
-        qv = np.clip(qv, -127, 127)
+        qv = np.clip(qv, -qmax, qmax)
         qv = np.where((amax > 0)[:, :, None, None], qv, 0)
         codes[:, :, t * block:(t + 1) * block, :] = qv.astype(np.int8)
         scales[:, :, t] = np.where(amax > 0, sc, np.float32(0.0))
     return codes, scales
+
+
+def quantize_blockwise_int8(xr32: np.ndarray, block: int = 64):
+    """int8 codes ([-127, 127]) and scales: quantize_blockwise with qmax = 127."""
+    return quantize_blockwise(xr32, block, 127)
+
+
+def quantize_blockwise_int4(xr32: np.ndarray, block: int = 64):
+    """int4 codes ([-7, 7], held in int8) and scales: quantize_blockwise with qmax = 7."""
+    return quantize_blockwise(xr32, block, 7)
 
 
 def dequantize_blockwise(codes: np.ndarray, scales: np.ndarray, block: int = 64) -> np.ndarray:
@@ -428,24 +441,59 @@ def dequantize_blockwise(codes: np.ndarray, scales: np.ndarray, block: int = 64)
     return codes.astype(np.float64) * sc[..., None]
 
 
-def rope_sdpa_forward_int8(q, k, v, cos, sin, scale=None, rows=None, pairs=None, block=64, workers=1,
-                           codes=None):
-    """int8 variant: rotate in fp32, quantize Q' and K' blockwise, attend on the dequantized values.
+def _qmax(bits: int) -> int:
+    return {8: 127, 4: 7}[bits]
+
+
+def quantized_qk(q, k, cos, sin, bits=8, block=64):
+    """The dequantized rotated Q and K the quantized variant attends with (float64), at
+    their own head counts."""
+    qc, qs = quantize_blockwise(rope_rotate_f32(q, cos, sin), block, _qmax(bits))
+    kc, ks = quantize_blockwise(rope_rotate_f32(k, cos, sin), block, _qmax(bits))
+    return dequantize_blockwise(qc, qs, block), dequantize_blockwise(kc, ks, block)
+
+
+def rope_sdpa_forward_quant(q, k, v, cos, sin, bits=8, scale=None, rows=None, pairs=None, block=64, workers=1,
+                            codes=None):
+    """Quantized variant (bits = 8 or 4): rotate in fp32, quantize Q' and K' blockwise,
+    attend on the dequantized values.
 
     `codes` may carry externally supplied ((q_codes, q_scales), (k_codes, k_scales)) so the
     attention part can be checked on exactly those quantized values.
     Returns (O, LSE).
     """
     if codes is None:
-        qc, qs = quantize_blockwise_int8(rope_rotate_f32(q, cos, sin), block)
-        kc, ks = quantize_blockwise_int8(rope_rotate_f32(k, cos, sin), block)
+        qh, kh = quantized_qk(q, k, cos, sin, bits, block)
     else:
         (qc, qs), (kc, ks) = codes
-    qh = dequantize_blockwise(qc, qs, block)
-    kh = expand_kv(dequantize_blockwise(kc, ks, block), qh.shape[1])  # K quantized at its own head count
+        qh, kh = dequantize_blockwise(qc, qs, block), dequantize_blockwise(kc, ks, block)
+    kh = expand_kv(kh, qh.shape[1])  # K quantized at its own head count
     v64 = expand_kv(_np64(v), qh.shape[1])
     return attention_forward(qh, kh, v64, _resolve_scale(scale, qh.shape[-1]), None, False,
                              rows=rows, pairs=pairs, workers=workers)
+
+
+def rope_sdpa_forward_int8(q, k, v, cos, sin, scale=None, rows=None, pairs=None, block=64, workers=1,
+                           codes=None):
+    """int8 variant: rope_sdpa_forward_quant with bits = 8."""
+    return rope_sdpa_forward_quant(q, k, v, cos, sin, 8, scale, rows, pairs, block, workers, codes)
+
+
+def rope_sdpa_backward_quant(q, k, v, cos, sin, do, bits=8, scale=None, block=64, workers=1):
+    """Gradients of the quantized variant w.r.t. the unrotated Q, K and V ([EN]: quantized
+    training goes through a quantized autograd entry point; [RQ] names it).  The pages do
+    not say how a gradient passes the quantizer.  Reading taken (straight-through): the
+    quantize-dequantize step counts as the identity in the backward, so the attention
+    backward runs at the values the forward attended with (the dequantized Q', K' and V),
+    and its dQ', dK' go unchanged into the inverse rotation.  Returns (dQ, dK, dV); dK and
+    dV at the K/V head count (summed over each group)."""
+    do64 = _np64(do)
+    qh, kh = quantized_qk(q, k, cos, sin, bits, block)
+    H, Hkv = qh.shape[1], kh.shape[1]
+    dqh, dkh, dv = attention_backward(qh, expand_kv(kh, H), expand_kv(_np64(v), H), do64,
+                                      _resolve_scale(scale, qh.shape[-1]), None, False, workers=workers)
+    dkh, dv = reduce_kv(dkh, Hkv), reduce_kv(dv, Hkv)
+    return rope_rotate_vjp(dqh, cos, sin), rope_rotate_vjp(dkh, cos, sin), dv
 
 
 def default_workers() -> int:

@@ -28,13 +28,14 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import (RS_BF16, RS_BOOL, RS_F16, RS_F32, RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT8_PREPASS,
-                   RS_FLAG_QUANT_INT8_QK, RS_MASK_ADDITIVE, RS_MASK_BOOL, RS_MASK_NONE, RsArgs, RsStats,
-                   make_tensor)
+from ._abi import (RS_BF16, RS_BOOL, RS_F16, RS_F32, RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT4_QK,
+                   RS_FLAG_QUANT_INT8_PREPASS, RS_FLAG_QUANT_INT8_QK, RS_MASK_ADDITIVE, RS_MASK_BOOL, RS_MASK_NONE,
+                   RsArgs, RsStats, make_tensor)
 
-# quantization= values -> flags: "int8" quantizes in the attention kernel (no codes in memory),
-# "int8_prepass" has a quantizer pass write the codes first (same results, faster)
-_QUANT_FLAGS = {None: 0, "int8": RS_FLAG_QUANT_INT8_QK, "int8_prepass": RS_FLAG_QUANT_INT8_QK | RS_FLAG_QUANT_INT8_PREPASS}
+# quantization= values -> flags: "int8" / "int4" quantize in the attention kernel (no codes
+# in memory), "..._prepass" has a quantizer pass write the codes first (same results, faster)
+_QUANT_FLAGS = {None: 0, "int8": RS_FLAG_QUANT_INT8_QK, "int8_prepass": RS_FLAG_QUANT_INT8_QK | RS_FLAG_QUANT_INT8_PREPASS,
+                "int4": RS_FLAG_QUANT_INT4_QK, "int4_prepass": RS_FLAG_QUANT_INT4_QK | RS_FLAG_QUANT_INT8_PREPASS}
 
 __all__ = [
     "rope_scaled_dot_product_attention", "rope_sdpa_fwd", "rope_sdpa_bwd", "rope_sdpa_workspace_size",
@@ -216,7 +217,8 @@ def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, att
 
     quantization: None, "int8" for the blockwise int8 Q'/K' forward quantized in the attention
     kernel, or "int8_prepass" for the same forward with the codes written by a quantizer pass
-    first (bit-identical results, faster); no gradient.
+    first (bit-identical results, faster); "int4" / "int4_prepass" the same with codes in
+    [-7, 7]; no gradient.
 
     q_norm_weight, k_norm_weight ([D] each, together or not at all): RMSNorm of query and key
     over the head dimension, x / sqrt(mean(x^2) + norm_eps) * w in fp32, before the rotation.
@@ -230,7 +232,7 @@ def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, att
     sin4 = _tables4(rope_sin, query.device)
     mask, kind = _mask4(attn_mask, value.dtype)
     if quantization not in _QUANT_FLAGS:
-        raise ValueError("quantization must be None, 'int8' or 'int8_prepass'")
+        raise ValueError("quantization must be None, 'int8', 'int8_prepass', 'int4' or 'int4_prepass'")
     norm = _norm_args(query, q_norm_weight, k_norm_weight, norm_eps)
     needs_grad = torch.is_grad_enabled() and (query.requires_grad or key.requires_grad or value.requires_grad)
     if quantization is not None or norm is not None or query.dtype != value.dtype:
@@ -275,14 +277,14 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, is_causal=Fa
     return _forward(query, key, value, None, None, mask, kind, bool(is_causal), scale, need_lse=False)[0]
 
 
-def debug_quantize_qk(query, key, rope_cos, rope_sin):
-    """The int8 codes and scales the int8 forward computes, for tests.
+def debug_quantize_qk(query, key, rope_cos, rope_sin, bits=8):
+    """The int8 (bits=8) or int4 (bits=4) codes and scales the quantized forward computes, for tests.
 
     Returns (q_codes, q_scales, k_codes, k_scales): int8 [B, H|Hkv, S, D] and fp32 [B, H|Hkv, ceil(S/64)].
     """
     lib = _abi.load()
     cos4, sin4 = _tables4(rope_cos, query.device), _tables4(rope_sin, query.device)
-    call = _Call(query, key, key, cos4, sin4, None, 0, False, None, quant="int8")
+    call = _Call(query, key, key, cos4, sin4, None, 0, False, None, quant={8: "int8", 4: "int4"}[bits])
     B, H, S, D = query.shape
     nb = -(-S // 64)
     Hkv = key.shape[1]

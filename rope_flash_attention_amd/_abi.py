@@ -15,7 +15,7 @@ STATUS_NAMES = {
 }
 RS_F32, RS_F16, RS_BF16, RS_BOOL = 0, 1, 2, 3
 RS_MASK_NONE, RS_MASK_BOOL, RS_MASK_ADDITIVE = 0, 1, 2
-RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT8_QK, RS_FLAG_QUANT_INT8_PREPASS = 1, 2, 4
+RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT8_QK, RS_FLAG_QUANT_INT8_PREPASS, RS_FLAG_QUANT_INT4_QK = 1, 2, 4, 8
 
 # Every symbol include/rope_sdpa.h declares.
 EXPORTED = (

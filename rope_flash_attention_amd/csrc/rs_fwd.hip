@@ -17,16 +17,20 @@ int launch_fwd(int dtype, int D, int mask_kind, bool causal, int int8, const Fwd
   }
 }
 
-// The int8 forward in code export mode (tests): one workgroup per unit, no split, no output.
-template <typename T>
+// The quantized forward in code export mode (tests): one workgroup per unit, no split, no
+// output.  QI8 = 1 (int8) or 5 (int4).
+template <typename T, int QI8>
 static int launch_fwd_int8_export_t(int D, const FwdParams& p, void* stream) {
-  return D == 64 ? launch_fwd_t<T, 64, MASK_NONE, false, 1, true, true>(p, stream)
-                 : launch_fwd_t<T, 128, MASK_NONE, false, 1, true, true>(p, stream);
+  return D == 64 ? launch_fwd_t<T, 64, MASK_NONE, false, QI8, true, true>(p, stream)
+                 : launch_fwd_t<T, 128, MASK_NONE, false, QI8, true, true>(p, stream);
 }
 
-int launch_fwd_int8_export(int dtype, int D, const FwdParams& p, void* stream) {
-  return dtype == F16 ? launch_fwd_int8_export_t<_Float16>(D, p, stream)
-                      : launch_fwd_int8_export_t<__bf16>(D, p, stream);
+int launch_fwd_int8_export(int dtype, int D, bool int4, const FwdParams& p, void* stream) {
+  if (int4)
+    return dtype == F16 ? launch_fwd_int8_export_t<_Float16, 5>(D, p, stream)
+                        : launch_fwd_int8_export_t<__bf16, 5>(D, p, stream);
+  return dtype == F16 ? launch_fwd_int8_export_t<_Float16, 1>(D, p, stream)
+                      : launch_fwd_int8_export_t<__bf16, 1>(D, p, stream);
 }
 
 int fwd_block_m(int dtype) { return dtype == F32 ? FwdCfg<float>::BM : FwdCfg<__bf16>::BM; }

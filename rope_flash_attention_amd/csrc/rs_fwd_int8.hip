@@ -1,17 +1,20 @@
-// Blockwise int8 quantization of the rotated Q and K (forward with RS_FLAG_QUANT_INT8_QK).
+// Blockwise int8 / int4 quantization of the rotated Q and K (forward with
+// RS_FLAG_QUANT_INT8_QK or RS_FLAG_QUANT_INT4_QK, and the quantizer pass).
 //
 // The pages (page "Metal Flash Attention", SimpleTuner docs, sections "Requirements" and
-// "Enable In SimpleTuner") name an int8 mode with blockwise quantization but not what is
-// quantized.  Reading implemented here and in the int8 attention kernel: Q' = R(Q) and
-// K' = R(K) are evaluated in fp32 (each product and each sum rounded, no fused multiply-add),
-// then each (b, h, block of 64 tokens) spanning all of D gets
+// "Enable In SimpleTuner") name int8 and int4 modes with blockwise quantization but not what
+// is quantized.  Reading implemented here and in the quantized attention kernel: Q' = R(Q)
+// and K' = R(K) are evaluated in fp32 (each product and each sum rounded, no fused
+// multiply-add), then each (b, h, block of 64 tokens) spanning all of D gets, with
+// qmax = 127 (int8) or 7 (int4),
 //     amax  = max |x'|                   over the block's valid rows
-//     inv   = fp32(127 / amax)           (correctly rounded division)
-//     code  = round-half-even(fp32(x' * inv)), clamped to [-127, 127]
-//     scale = fp32(amax / 127)
+//     inv   = fp32(qmax / amax)          (correctly rounded division)
+//     code  = round-half-even(fp32(x' * inv)), clamped to [-qmax, qmax]
+//     scale = fp32(amax / qmax)
 // and an all-zero block gets codes 0 and scale 0.  Scores are then
 //     s = softmax_scale * scale_q * scale_k * (codes_q . codes_k),
-// the integer product being exact on int8 MFMA (|sum| <= 128 * 127^2 < 2^31).
+// the integer product being exact on int8 MFMA (|sum| <= 128 * 127^2 < 2^31); int4 codes
+// are stored one per byte and take the same instruction.
 //
 // One workgroup of 256 threads per (block, head, sample, tensor): it holds the block's
 // rotated values in registers (64 rows x D / 256 threads), reduces the block maximum through
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantParams p) {
   if (lane == 0) red[wave] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float inv = amax > 0.f ? 127.f / amax : 0.f;
+  const float inv = amax > 0.f ? p.qmax / amax : 0.f;
 
   int8_t* cb = p.codes[which] + b * p.c_sb[which] + h * p.c_sh[which];
 #pragma unroll
@@ -78,12 +81,12 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float c = __builtin_rintf(v[i][j] * inv);  // round half to even
-      c = fminf(fmaxf(c, -127.f), 127.f);
+      c = fminf(fmaxf(c, -p.qmax), p.qmax);
       w[j >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (j & 3));
     }
     *(uint2*)(cb + (int64_t)s * D + ch * 8) = make_uint2(w[0], w[1]);
   }
-  if (tid == 0) p.scales[which][((int64_t)b * p.Hx[which] + h) * p.nblk + blk] = amax > 0.f ? amax / 127.f : 0.f;
+  if (tid == 0) p.scales[which][((int64_t)b * p.Hx[which] + h) * p.nblk + blk] = amax > 0.f ? amax / p.qmax : 0.f;
 }
 
 template <typename T>

@@ -79,13 +79,15 @@ constexpr int kMaxStateTiles = kMaxBoolMaskSeq / 32;  // key tiles (32 keys or m
 constexpr int QK_AHEAD = 4;  // K' fragment reads kept in flight ahead of the QK^T products
 constexpr int PV_AHEAD = 3;  // V^T fragments (two reads each) in flight ahead of the P.V products
 
-// QI8: blockwise int8 variant; Q'K'^T runs on int8 MFMA with exact int32 sums, scaled into
-// the fp32 scores once per tile.  QI8 = 1: the rotated Q' and K' are quantized here, per
-// (b, h, 64-token block), to int8 codes with one fp32 scale: Q once per workgroup from its
-// own four 64-row blocks, K per 64-key tile (one tile is one block) with the tile's amax
-// reduced over the workgroup through LDS; no code reaches memory.  QI8 = 2: the codes and
-// scales come from the quantizer pass (quant_kernel) and K code tiles go straight into LDS.
-// QEXP (with QI8 = 1): code export mode for tests, which writes the codes and scales
+// QI8: blockwise quantized variant; Q'K'^T runs on int8 MFMA with exact int32 sums, scaled
+// into the fp32 scores once per tile.  QI8 & 3 = 1: the rotated Q' and K' are quantized
+// here, per (b, h, 64-token block), to codes with one fp32 scale: Q once per workgroup from
+// its own four 64-row blocks, K per 64-key tile (one tile is one block) with the tile's amax
+// reduced over the workgroup through LDS; no code reaches memory.  QI8 & 3 = 2: the codes
+// and scales come from the quantizer pass (quant_kernel) and K code tiles go straight into
+// LDS.  QI8 & 4: int4 codes (range [-7, 7], one per byte; CDNA4 has no int4 matrix
+// instruction, and such codes are exact int8 operands), else int8 codes ([-127, 127]).
+// QEXP (with QI8 & 3 = 1): code export mode for tests, which writes the codes and scales
 // instead of the output.
 // ROPE = false: plain attention, Q and K used as given (no tables read, no rotation).
 // QKM: the Q/K prologue.  Bit 0: Q is RMS-normalized over the head dimension (weights
@@ -96,7 +98,9 @@ template <typename T, int D, int MASK, bool CAUSAL, int QI8 = 0, bool ROPE = tru
 __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   static_assert(!QI8 || (sizeof(T) == 2 && MASK == MASK_NONE && !CAUSAL), "int8 variant: 16-bit, unmasked");
   static_assert(ROPE || !QI8, "the int8 variant rotates");
-  static_assert(!QEXP || QI8 == 1, "code export is the in-kernel int8 mode");
+  constexpr int QM = QI8 & 3;                     // 1: quantized here, 2: codes from the quantizer pass
+  constexpr float QMAX = (QI8 & 4) ? 7.f : 127.f;  // code range: int4 or int8
+  static_assert(!QEXP || QM == 1, "code export is the in-kernel quantization mode");
   static_assert(QKM == 0 || (ROPE && !QI8 && (QKM & 4)), "Q/K prologue: rotating path, K prepared");
   constexpr bool NORM = (QKM & 1) != 0;
   using TQ = typename std::conditional<(QKM & 2) != 0, float, T>::type;  // Q storage type
@@ -198,13 +202,13 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   QF qf;
   float q8scale = 0.f;
   const int nblk = (S + 63) / 64;  // int8 quantization blocks of a (b, h) slice
-  if constexpr (QI8 == 2) {
+  if constexpr (QM == 2) {
     const int slice = b * p.shp.H + hd;  // (b, h) index into the codes and scales
     const int8_t* qrow = p.qc + ((int64_t)slice * p.sp + mc) * D;
 #pragma unroll
     for (int t = 0; t < NQ8; ++t) qf[t] = *(const i32x4*)(qrow + 32 * t + 16 * hh);
     q8scale = p.qsc[(int64_t)slice * (p.sp / 64) + mc / 64] * c2;  // mc < S: always a valid block
-  } else if constexpr (QI8 == 1) {
+  } else if constexpr (QM == 1) {
     // this lane holds elements 32t + 16hh + e (e < 16) of row mc, rotated with every product
     // and sum rounded to fp32 (the quantizer's integer decisions are then reproducible)
     const T* qrow = qbase + (int64_t)mc * p.q.ss;
@@ -238,14 +242,14 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     if (lane == 0) s_qamax[wave] = amx;
     __syncthreads();
     const float am = fmaxf(s_qamax[wave & ~1], s_qamax[wave | 1]);
-    const float inv = am > 0.f ? 127.f / am : 0.f;
-    const float qsc = am > 0.f ? am / 127.f : 0.f;
+    const float inv = am > 0.f ? QMAX / am : 0.f;
+    const float qsc = am > 0.f ? am / QMAX : 0.f;
 #pragma unroll
     for (int t = 0; t < NQ8; ++t) {
       uint32_t wv[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float c = fminf(fmaxf(__builtin_rintf(qv[t][e] * inv), -127.f), 127.f);  // half to even
+        const float c = fminf(fmaxf(__builtin_rintf(qv[t][e] * inv), -QMAX), QMAX);  // half to even
         wv[e >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (e & 3));
       }
       qf[t] = i32x4{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
@@ -445,7 +449,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // past S read as zeros, and every call issues the same loads (so the wait for them can
   // let later loads stay in flight)
   auto load_k_rows = [&](int kt) __attribute__((always_inline)) {
-    if constexpr (QI8 == 2) return;
+    if constexpr (QM == 2) return;
     const __amdgpu_buffer_rsrc_t krs = rows_rsrc(kbase, kt * BN, S, (int)p.k.ss * ES, D * ES);
 #pragma unroll
     for (int it = 0; it < KCPT; ++it)
@@ -453,7 +457,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
                                              krs, (uint32_t)((k_off + it * KROWS_PER_IT * (int)p.k.ss) * ES), 0, 0));
   };
   auto load_k_tab = [&](int kt) __attribute__((always_inline)) {
-    if constexpr (!KROT || QI8 == 2) return;
+    if constexpr (!KROT || QM == 2) return;
     const __amdgpu_buffer_rsrc_t trs = rows_rsrc(tab, kt * BN, S, D * 4, D * 4);
 #pragma unroll
     for (int it = 0; it < KCPT; ++it)
@@ -486,15 +490,15 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // codes from the quantizer pass: this wave's 1 KB share of a code tile straight into LDS
   // (code rows past the padded sequence read as zero)
   const int slice_k = b * p.shp.Hkv + hk;  // (b, K/V head) index into the K codes and scales
-  const int8_t* kcodes = QI8 == 2 ? p.kc + (int64_t)slice_k * p.sp * D : nullptr;
+  const int8_t* kcodes = QM == 2 ? p.kc + (int64_t)slice_k * p.sp * D : nullptr;
   uint32_t k8_voff = 0;
-  if constexpr (QI8 == 2) {
+  if constexpr (QM == 2) {
     const int byte = wave * 1024 + lane * 16;
     const int row = byte / D, pch = (byte % D) / 16;
     k8_voff = (uint32_t)(perm_row(row) * D + ((pch ^ k8sw(row)) << 4));
   }
   auto dma_k = [&](int kt, char* sK) __attribute__((always_inline)) {
-    if constexpr (QI8 == 2) {
+    if constexpr (QM == 2) {
       if (wave < K8LD)
         buffer_load_lds16(tile_rsrc(kcodes, (int64_t)kt * BN * D, (int64_t)p.sp * D), sK + wave * 1024, k8_voff, 0);
     }
@@ -504,8 +508,8 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // variant: rotate (fp32, rounded products), reduce the tile's amax over the workgroup,
   // quantize, store codes; returns the tile's scale (other variants: 0).
   auto store_tile = [&](char* sK, int kt) __attribute__((always_inline)) -> float {
-    if constexpr (QI8 == 2) return kt < nkt_all ? p.ksc[(int64_t)slice_k * (p.sp / 64) + kt] : 0.f;
-    if constexpr (QI8 == 1) {
+    if constexpr (QM == 2) return kt < nkt_all ? p.ksc[(int64_t)slice_k * (p.sp / 64) + kt] : 0.f;
+    if constexpr (QM == 1) {
       float kv[KCPT][8];
       float amx = 0.f;
 #pragma unroll
@@ -529,13 +533,13 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
       float am = s_kamax[slot][0];
 #pragma unroll
       for (int w2 = 1; w2 < NW; ++w2) am = fmaxf(am, s_kamax[slot][w2]);
-      const float inv = am > 0.f ? 127.f / am : 0.f;
+      const float inv = am > 0.f ? QMAX / am : 0.f;
 #pragma unroll
       for (int it = 0; it < KCPT; ++it) {
         uint32_t wv[2] = {0u, 0u};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float c = fminf(fmaxf(__builtin_rintf(kv[it][e] * inv), -127.f), 127.f);
+          const float c = fminf(fmaxf(__builtin_rintf(kv[it][e] * inv), -QMAX), QMAX);
           wv[e >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (e & 3));
         }
         const int key = k_key0 + it * KROWS_PER_IT, lrow = perm_row(key);
@@ -546,7 +550,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
             *(uint2*)(p.xk_codes + (((int64_t)b * p.shp.Hkv + hk) * S + j) * D + k_cc * 8) = make_uint2(wv[0], wv[1]);
         }
       }
-      const float ksc = am > 0.f ? am / 127.f : 0.f;
+      const float ksc = am > 0.f ? am / QMAX : 0.f;
       if constexpr (QEXP) {
         if (hk_export && kt < nkt_all && tid == 0) p.xk_scales[((int64_t)b * p.shp.Hkv + hk) * nblk + kt] = ksc;
       }
@@ -867,9 +871,9 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     qk(sKr, s_nxt, ks_t1);
     probs(s_cur, pt);
     if constexpr (KPL == 8) {
-      if constexpr (QI8 == 2) {
+      if constexpr (QM == 2) {
         sched_mfma_interleave<NKB * NQ8, 1, NKB * NQ8, 8, 0>();
-      } else if constexpr (QI8 == 1) {
+      } else if constexpr (QM == 1) {
         sched_mfma_interleave_loads<NKB * NQ8, 1, NKB * NQ8, 8, 4, 0>();
       } else {
         sched_mfma_interleave_loads<NKB * NQK, 1, QK_AHEAD, 4, kMaskTileLds ? 6 : 2, 0>();
@@ -1103,13 +1107,23 @@ static int launch_fwd_dt(int D, int mask_kind, bool causal, const FwdParams& p, 
                  : launch_fwd_d<T, 128, ROPE>(mask_kind, causal, p, stream);
 }
 
+template <typename T, int QI8>
+static int launch_fwd_q_d(int D, const FwdParams& p, void* stream) {
+  return D == 64 ? launch_fwd_t<T, 64, MASK_NONE, false, QI8>(p, stream)
+                 : launch_fwd_t<T, 128, MASK_NONE, false, QI8>(p, stream);
+}
+
+// mode: 1 / 2 int8 quantized in the kernel / codes from the quantizer pass; 5 / 6 the same
+// with int4 codes
 template <typename T>
 static int launch_fwd_int8(int D, int mode, const FwdParams& p, void* stream) {
-  if (mode == 2)
-    return D == 64 ? launch_fwd_t<T, 64, MASK_NONE, false, 2>(p, stream)
-                   : launch_fwd_t<T, 128, MASK_NONE, false, 2>(p, stream);
-  return D == 64 ? launch_fwd_t<T, 64, MASK_NONE, false, 1>(p, stream)
-                 : launch_fwd_t<T, 128, MASK_NONE, false, 1>(p, stream);
+  switch (mode) {
+    case 1: return launch_fwd_q_d<T, 1>(D, p, stream);
+    case 2: return launch_fwd_q_d<T, 2>(D, p, stream);
+    case 5: return launch_fwd_q_d<T, 5>(D, p, stream);
+    case 6: return launch_fwd_q_d<T, 6>(D, p, stream);
+    default: return -1;
+  }
 }
 
 

@@ -12,6 +12,10 @@
 #include "rs_internal.h"
 
 namespace {
+constexpr uint32_t kQuantFlags = RS_FLAG_QUANT_INT8_QK | RS_FLAG_QUANT_INT4_QK;
+}  // namespace
+
+namespace {
 
 using namespace rs;
 
@@ -144,9 +148,9 @@ rs_status validate_args(const rs_args* a, Shape* out) {
     s.Bt = 0;  // no packed tables
   }
 
-  if (a->flags & ~(uint32_t)(RS_FLAG_CAUSAL | RS_FLAG_QUANT_INT8_QK | RS_FLAG_QUANT_INT8_PREPASS))
-    return RS_ERR_INVALID;
-  if ((a->flags & RS_FLAG_QUANT_INT8_PREPASS) && !(a->flags & RS_FLAG_QUANT_INT8_QK)) return RS_ERR_INVALID;
+  if (a->flags & ~(uint32_t)(RS_FLAG_CAUSAL | kQuantFlags | RS_FLAG_QUANT_INT8_PREPASS)) return RS_ERR_INVALID;
+  if ((a->flags & kQuantFlags) == kQuantFlags) return RS_ERR_INVALID;  // int8 or int4, not both
+  if ((a->flags & RS_FLAG_QUANT_INT8_PREPASS) && !(a->flags & kQuantFlags)) return RS_ERR_INVALID;
   const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
   if (!(std::isfinite(a->scale)) || a->scale < 0.f) return RS_ERR_INVALID;
   s.scale = a->scale == 0.f ? (float)(1.0 / std::sqrt((double)s.D)) : a->scale;
@@ -185,7 +189,7 @@ rs_status validate_args(const rs_args* a, Shape* out) {
     return RS_ERR_INVALID;
   }
   if (s.qkm != 0 && (!s.rope || a->mask_kind == RS_MASK_ADDITIVE)) return RS_ERR_UNSUPPORTED;
-  if (a->flags & RS_FLAG_QUANT_INT8_QK) {
+  if (a->flags & kQuantFlags) {
     if (dt == RS_F32 || !s.rope || s.qkm != 0) return RS_ERR_UNSUPPORTED;
     if (a->mask_kind != RS_MASK_NONE || causal) return RS_ERR_UNSUPPORTED;
   }
@@ -196,7 +200,7 @@ rs_status validate_args(const rs_args* a, Shape* out) {
   }
   // The 16-bit rotating forward (no int8, no additive mask) rotates K once into the
   // workspace and keeps tables out of its key loop; the Q/K prologue always does.
-  s.kprep = s.qkm != 0 || (s.rope && dt != RS_F32 && !(a->flags & RS_FLAG_QUANT_INT8_QK) &&
+  s.kprep = s.qkm != 0 || (s.rope && dt != RS_F32 && !(a->flags & kQuantFlags) &&
                            a->mask_kind != RS_MASK_ADDITIVE);
   *out = s;
   return RS_OK;
@@ -209,7 +213,8 @@ struct Layout {
   SplitPlan split;   // forward only: work split over the current device's workgroups
 };
 
-// int8: 0 none, 1 quantized in the attention kernel, 2 codes from the quantizer pass
+// int8: quantization mode (quant_mode): 0 none, 1 quantized in the attention kernel, 2 codes
+// from the quantizer pass, + 4 for int4 codes
 Layout layout(const Shape& s, int mask_kind, bool backward, int int8, bool causal) {
   Layout L{};
   size_t off = 0;
@@ -227,7 +232,7 @@ Layout layout(const Shape& s, int mask_kind, bool backward, int int8, bool causa
   if (backward) off += round_up((size_t)(s.B * s.H * s.S) * sizeof(float), 256);
   L.qrot = off;
   if (backward && s.dtype != F32 && s.D == 128) off += round_up((size_t)(s.B * s.H * s.S * s.D) * 2, 256);
-  if (int8 == 2) {
+  if ((int8 & 3) == 2) {
     L.nblk = (s.S + 63) / 64;
     L.sp = L.nblk * 64;
     L.qc = off;
@@ -350,9 +355,10 @@ Opnd opnd(const rs_tensor* t) {
   return o;
 }
 
+// 0 none; 1 quantized in the attention kernel, 2 codes from the quantizer pass; + 4 for int4
 int int8_mode(uint32_t flags) {
-  if (!(flags & RS_FLAG_QUANT_INT8_QK)) return 0;
-  return (flags & RS_FLAG_QUANT_INT8_PREPASS) ? 2 : 1;
+  if (!(flags & kQuantFlags)) return 0;
+  return ((flags & RS_FLAG_QUANT_INT8_PREPASS) ? 2 : 1) | ((flags & RS_FLAG_QUANT_INT4_QK) ? 4 : 0);
 }
 
 QuantParams quant_params(const rs_args* a, const Shape& s, const Layout& L, char* ws) {
@@ -369,6 +375,7 @@ QuantParams quant_params(const rs_args* a, const Shape& s, const Layout& L, char
   qp.rows = (int)L.sp;
   qp.scales[0] = (float*)(ws + L.qs);
   qp.scales[1] = (float*)(ws + L.ks);
+  qp.qmax = (a->flags & RS_FLAG_QUANT_INT4_QK) ? 7.f : 127.f;
   qp.Hx[0] = (int)s.H;
   qp.Hx[1] = (int)s.Hkv;
   qp.B = (int)s.B;
@@ -460,7 +467,7 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
   char* w = (char*)ws;
   hipStream_t strm = (hipStream_t)stream;
   if ((st = prepare(a, s, L, w, strm)) != RS_OK) return fail(st);
-  if (int8 == 2 && launch_quant_int8(s.dtype, quant_params(a, s, L, w), strm) != 0) return fail(RS_ERR_LAUNCH);
+  if ((int8 & 3) == 2 && launch_quant_int8(s.dtype, quant_params(a, s, L, w), strm) != 0) return fail(RS_ERR_LAUNCH);
   FwdParams p{};
   p.q = opnd(a->q);
   p.k = opnd(a->k);
@@ -478,7 +485,7 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
   const int bm = fwd_block_m(s.dtype);
   p.num_qt = (int)((s.S + bm - 1) / bm);
   const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
-  if (int8 == 2) {
+  if ((int8 & 3) == 2) {
     p.qc = (const int8_t*)(w + L.qc);
     p.kc = (const int8_t*)(w + L.kc);
     p.qsc = (const float*)(w + L.qs);
@@ -545,7 +552,7 @@ rs_status rope_sdpa_debug_quantize_qk(const rs_args* a, int8_t* q_codes, int8_t*
   Shape s;
   rs_status st = validate_args(a, &s);
   if (st != RS_OK) return fail(st);
-  if (!(a->flags & RS_FLAG_QUANT_INT8_QK)) return fail(RS_ERR_INVALID);
+  if (!(a->flags & kQuantFlags)) return fail(RS_ERR_INVALID);
   if (s.empty) return RS_OK;
   if (!q_codes || !k_codes || !q_scales || !k_scales) return fail(RS_ERR_NULL);
   if (((uintptr_t)q_codes) % 8 != 0 || ((uintptr_t)k_codes) % 8 != 0) return fail(RS_ERR_ALIGN);
@@ -569,7 +576,8 @@ rs_status rope_sdpa_debug_quantize_qk(const rs_args* a, int8_t* q_codes, int8_t*
   p.xk_codes = k_codes;
   p.xq_scales = q_scales;
   p.xk_scales = k_scales;
-  if (launch_fwd_int8_export(s.dtype, (int)s.D, p, strm) != 0) return fail(RS_ERR_LAUNCH);
+  if (launch_fwd_int8_export(s.dtype, (int)s.D, (a->flags & RS_FLAG_QUANT_INT4_QK) != 0, p, strm) != 0)
+    return fail(RS_ERR_LAUNCH);
   return RS_OK;
 }
 
@@ -579,7 +587,7 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   Shape s;
   rs_status st = validate_args(a, &s);
   if (st != RS_OK) return fail(st);
-  if (a->flags & RS_FLAG_QUANT_INT8_QK) return fail(RS_ERR_UNSUPPORTED);
+  if (a->flags & kQuantFlags) return fail(RS_ERR_UNSUPPORTED);
   if (!s.rope) return fail(RS_ERR_UNSUPPORTED);  // the backward is the fused one: tables required
   if (s.qkm != 0) return fail(RS_ERR_UNSUPPORTED);  // no backward through the Q/K prologue
   const int64_t sz[4] = {s.B, s.H, s.S, s.D};

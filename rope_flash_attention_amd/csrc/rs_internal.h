@@ -130,6 +130,7 @@ struct QuantParams {
   float* scales[2];          // [B][Hx][nblk]
   int Hx[2];                 // heads of Q (H) and of K (Hkv)
   int B, H, S, D, nblk;
+  float qmax;                // code range [-qmax, qmax]: 127 (int8) or 7 (int4)
 };
 
 // The eager rotation pass (rope_sdpa_rotate): out = R(x) for a [B, H, S, D] operand.
@@ -187,7 +188,7 @@ int launch_fwd_qk(int dtype, int D, int mask_kind, bool causal, int qkm, const F
 int launch_fwd_plain(int dtype, int D, int mask_kind, bool causal, const FwdParams& p, void* stream);
 int launch_rotate(int dtype, const RotateParams& p, void* stream);
 // The int8 forward in code export mode (no output written; see FwdParams).
-int launch_fwd_int8_export(int dtype, int D, const FwdParams& p, void* stream);
+int launch_fwd_int8_export(int dtype, int D, bool int4, const FwdParams& p, void* stream);
 int launch_bwd(int dtype, int D, int mask_kind, bool causal, const BwdParams& p, void* stream);
 // Reads (and optionally clears) the device-side count of all-true bool masks.
 int read_all_true_counter(uint64_t* value, bool reset);

@@ -149,11 +149,16 @@ int main() {
       }
   for (int dt : {RS_F16, RS_BF16})
     for (int S : {64, 77, 4608})
-      for (uint32_t extra : {0u, (uint32_t)RS_FLAG_QUANT_INT8_PREPASS}) {
-        Case c(dt, 1, 4, S, 128);
-        c.a.flags = RS_FLAG_QUANT_INT8_QK | extra;
-        CHECK(run(c, false) == RS_OK, "int8 forward S=%d prepass=%u", S, extra);
-      }
+      for (uint32_t bits : {(uint32_t)RS_FLAG_QUANT_INT8_QK, (uint32_t)RS_FLAG_QUANT_INT4_QK})
+        for (uint32_t extra : {0u, (uint32_t)RS_FLAG_QUANT_INT8_PREPASS}) {
+          Case c(dt, 1, 4, S, 128);
+          c.a.flags = bits | extra;
+          CHECK(run(c, false) == RS_OK, "quantized forward S=%d flags=%u", S, bits | extra);
+        }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT8_QK | RS_FLAG_QUANT_INT4_QK;
+    expect_error(c, false, RS_ERR_INVALID, "int8 and int4"); }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT4_QK | RS_FLAG_CAUSAL;
+    expect_error(c, false, RS_ERR_UNSUPPORTED, "int4 causal"); }
   { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT8_PREPASS;
     expect_error(c, false, RS_ERR_INVALID, "prepass without int8"); }
   // plain attention (no tables): forward only

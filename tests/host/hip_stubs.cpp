@@ -85,7 +85,8 @@ int launch_fwd(int dtype, int D, int, bool, int int8, const FwdParams& p, void*)
   if (p.mask.tiles) stub::need(p.mask.tiles, 1, "mask tile states");
   if (p.shp.Hkv <= 0 || H % p.shp.Hkv != 0 || p.shp.group != H / p.shp.Hkv) std::abort();
   if (int8 && (p.xq_codes || p.xk_codes)) std::abort();  // the forward never exports codes
-  if (int8 == 2) {  // codes and scales of the quantizer pass in the workspace
+  if (int8 != 0 && int8 != 1 && int8 != 2 && int8 != 5 && int8 != 6) std::abort();
+  if ((int8 & 3) == 2) {  // codes and scales of the quantizer pass in the workspace
     stub::need(p.qc, (size_t)B * H * p.sp * D, "q codes");
     stub::need(p.kc, (size_t)B * p.shp.Hkv * p.sp * D, "k codes");
     stub::need(p.qsc, (size_t)B * H * (p.sp / 64) * sizeof(float), "q scales");
@@ -146,6 +147,7 @@ int launch_rotate(int, const RotateParams& p, void*) {
 
 int launch_quant_int8(int, const QuantParams& p, void*) {
   ++stub::launches;
+  if (p.qmax != 127.f && p.qmax != 7.f) std::abort();
   stub::need(p.tab.ptr, (size_t)(p.tab.sb ? p.B : 1) * p.S * p.D * sizeof(float), "packed tables");
   for (int w = 0; w < 2; ++w) {
     stub::need(p.codes[w], (size_t)p.B * p.Hx[w] * p.rows * p.D, "codes");
@@ -154,7 +156,7 @@ int launch_quant_int8(int, const QuantParams& p, void*) {
   return 0;
 }
 
-int launch_fwd_int8_export(int, int, const FwdParams& p, void*) {
+int launch_fwd_int8_export(int, int, bool, const FwdParams& p, void*) {
   ++stub::launches;
   if (!p.xq_codes || !p.xk_codes || !p.xq_scales || !p.xk_scales || p.split_iters != 0) std::abort();
   stub::need(p.tab.ptr, (size_t)(p.tab.sb ? p.shp.B : 1) * p.shp.S * 4 * 64, "packed tables");
