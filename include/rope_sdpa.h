@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ROPE_SDPA_ABI_VERSION 2
+#define ROPE_SDPA_ABI_VERSION 3
 
 typedef enum {
   RS_OK = 0,
@@ -236,9 +236,10 @@ typedef struct {
   uint64_t masked_bool;        /* calls (fwd or bwd) with a bool mask */
   uint64_t masked_additive;
   uint64_t causal;
-  uint64_t quant_int8;
+  uint64_t quant_int8;         /* quantized forward calls (int8 or int4) */
   uint64_t mask_all_true_skipped; /* bool masks found all-true on the device */
   uint64_t errors;             /* calls rejected with a negative status */
+  uint64_t quant_bwd;          /* quantized backward calls (the quantized autograd path) */
 } rs_stats;
 
 void rope_sdpa_get_stats(rs_stats* out);

@@ -154,9 +154,9 @@ def _forward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, need_lse, quan
     return o, lse
 
 
-def _backward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, o, lse, do):
+def _backward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, o, lse, do, quant=None):
     lib = _abi.load()
-    call = _Call(q, k, v, cos4, sin4, mask, mask_kind, causal, scale)
+    call = _Call(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant)
     dq = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     dk = torch.empty(k.shape, dtype=q.dtype, device=q.device)  # K/V heads (grouped-query attention)
     dv = torch.empty(v.shape, dtype=q.dtype, device=q.device)
@@ -170,11 +170,11 @@ def _backward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, o, lse, do):
 
 class _RopeSdpaFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, cos4, sin4, mask, mask_kind, causal, scale):
-        o, lse = _forward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, need_lse=True)
+    def forward(ctx, q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant=None):
+        o, lse = _forward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, need_lse=True, quant=quant)
         ctx.save_for_backward(q, k, v, cos4, sin4, o, lse, mask if mask is not None else torch.empty(0))
         ctx.has_mask = mask is not None
-        ctx.mask_kind, ctx.causal, ctx.scale = mask_kind, causal, scale
+        ctx.mask_kind, ctx.causal, ctx.scale, ctx.quant = mask_kind, causal, scale, quant
         return o
 
     @staticmethod
@@ -184,8 +184,8 @@ class _RopeSdpaFn(torch.autograd.Function):
                 (s * do.element_size()) % 16 for s, n in zip(do.stride()[:3], do.shape[:3]) if n > 1):
             do = do.contiguous()
         dq, dk, dv = _backward(q, k, v, cos4, sin4, mask if ctx.has_mask else None, ctx.mask_kind, ctx.causal,
-                               ctx.scale, o, lse, do)
-        return dq, dk, dv, None, None, None, None, None, None
+                               ctx.scale, o, lse, do, ctx.quant)
+        return dq, dk, dv, None, None, None, None, None, None, None
 
 
 def _norm_args(query, q_norm_weight, k_norm_weight, norm_eps):
@@ -218,7 +218,8 @@ def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, att
     quantization: None, "int8" for the blockwise int8 Q'/K' forward quantized in the attention
     kernel, or "int8_prepass" for the same forward with the codes written by a quantizer pass
     first (bit-identical results, faster); "int4" / "int4_prepass" the same with codes in
-    [-7, 7]; no gradient.
+    [-7, 7].  Gradients (D = 128) pass the quantizer straight through: the backward runs at
+    the dequantized rotated Q and K the forward attended with.
 
     q_norm_weight, k_norm_weight ([D] each, together or not at all): RMSNorm of query and key
     over the head dimension, x / sqrt(mean(x^2) + norm_eps) * w in fp32, before the rotation.
@@ -235,6 +236,10 @@ def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, att
         raise ValueError("quantization must be None, 'int8', 'int8_prepass', 'int4' or 'int4_prepass'")
     norm = _norm_args(query, q_norm_weight, k_norm_weight, norm_eps)
     needs_grad = torch.is_grad_enabled() and (query.requires_grad or key.requires_grad or value.requires_grad)
+    if quantization is not None and needs_grad and norm is None and query.dtype == value.dtype:
+        if query.shape[-1] != 128:
+            raise RopeSdpaError(-6)  # the quantized backward runs at D = 128
+        return _RopeSdpaFn.apply(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale, quantization)
     if quantization is not None or norm is not None or query.dtype != value.dtype:
         if needs_grad:
             raise RopeSdpaError(-6)
@@ -369,6 +374,7 @@ def get_dispatch_stats() -> dict:
         "masked_additive": s["masked_additive"],
         "causal": s["causal"],
         "quantized_int8": s["quant_int8"],
+        "quantized_autograd": s["quant_bwd"],
         "mask_all_true_skipped": s["mask_all_true_skipped"],
         "errors": s["errors"],
         "pytorch_fallback": 0,

@@ -55,10 +55,11 @@ class RsArgs(ctypes.Structure):
 class RsStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "fwd_instream", "fwd_autograd", "bwd_calls", "masked_bool", "masked_additive", "causal",
-        "quant_int8", "mask_all_true_skipped", "errors")]
+        "quant_int8", "mask_all_true_skipped", "errors", "quant_bwd")]
 
 
 _lib = None
+ABI_VERSION = 3  # ROPE_SDPA_ABI_VERSION of include/rope_sdpa.h that these structures mirror
 
 
 def load(path: str = LIB_PATH):
@@ -70,6 +71,10 @@ def load(path: str = LIB_PATH):
         raise RuntimeError(
             f"{path} is missing: build the HIP library first (python -c 'import __graft_entry__ as g; g.build()')")
     lib = ctypes.CDLL(path)
+    lib.rope_sdpa_abi_version.restype = ctypes.c_int
+    if lib.rope_sdpa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.rope_sdpa_abi_version()}, this binding needs "
+                           f"{ABI_VERSION}: rebuild the HIP library")
     P = ctypes.POINTER
     lib.rope_sdpa_workspace_size.argtypes = [P(RsArgs), ctypes.c_int, P(ctypes.c_size_t)]
     lib.rope_sdpa_workspace_size.restype = ctypes.c_int

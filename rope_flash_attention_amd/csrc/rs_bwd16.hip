@@ -106,16 +106,22 @@ __device__ inline float2 rot_fma(float x0, float x1, float c, float s) {
   return r;
 }
 
-// B fragments of one row (D = 128): element e of fragment t = row[32t + 8g + e], rotated
-// with the packed table row and multiplied by `mul` when ROT.
-template <typename T, bool ROT>
+// B fragments of one row (D = 128): element e of fragment t = row[32t + 8g + e]; kRowRot:
+// rotated with the packed table row and multiplied by `mul`; kRowMul: multiplied by `mul`
+// (a row rotated already); kRowRaw: as stored.
+constexpr int kRowRaw = 0, kRowRot = 1, kRowMul = 2;
+template <typename T, int MODE>
 __device__ inline void row_frags(typename Mf<T>::frag* f, const T* row, const float* trow, int g, float mul) {
   typedef T v8 __attribute__((ext_vector_type(8)));
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int d0 = 32 * t + 8 * g;
     v8 x = *(const v8*)(row + d0);
-    if constexpr (ROT) {
+    if constexpr (MODE == kRowMul) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = from_f<T>(to_f(x[e]) * mul);
+    }
+    if constexpr (MODE == kRowRot) {
       const float4 a = *(const float4*)(trow + d0), b = *(const float4*)(trow + d0 + 4);
       const float cc[4] = {a.x, a.z, b.x, b.z}, ss[4] = {a.y, a.w, b.y, b.w};
 #pragma unroll
@@ -237,7 +243,11 @@ struct DmaTile {
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
-template <typename T, int MASK, bool CAUSAL>
+// PRE bit 0: K arrives rotated (K' in the workspace, contiguous): its tiles go straight from
+// memory into LDS like V's, with no table in the key loop.  PRE bit 1: Q arrives rotated too
+// (Q' in the workspace, e.g. the dequantized values of the quantized forward): it is only
+// scaled, and not written back.
+template <typename T, int MASK, bool CAUSAL, int PRE>
 __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
   using frag = typename Mf<T>::frag;
   using M = M16<T>;
@@ -274,10 +284,14 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
   const float* tab = p.tab.ptr + b * p.tab.sb;
 
   frag qf[4], gf[4];
-  row_frags_qrot<T>(qf, m < S ? (T*)p.qrot + ((int64_t)bh * S + m) * D : nullptr,
-                    (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh + (int64_t)mc * p.q.ss, tab + (int64_t)mc * D, g,
-                    p.shp.scale_log2);
-  row_frags<T, false>(gf, (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh + (int64_t)mc * p.dout.ss, nullptr,
+  if constexpr ((PRE & 2) != 0) {
+    row_frags<T, kRowMul>(qf, (const T*)p.qrot + ((int64_t)bh * S + mc) * D, nullptr, g, p.shp.scale_log2);
+  } else {
+    row_frags_qrot<T>(qf, m < S ? (T*)p.qrot + ((int64_t)bh * S + m) * D : nullptr,
+                      (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh + (int64_t)mc * p.q.ss, tab + (int64_t)mc * D, g,
+                      p.shp.scale_log2);
+  }
+  row_frags<T, kRowRaw>(gf, (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh + (int64_t)mc * p.dout.ss, nullptr,
                       g, 1.f);
   const int64_t rowid = ((int64_t)b * p.shp.H + hd) * S + mc;
   const float lse_v = p.lse[rowid];
@@ -322,16 +336,26 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
   LaneOffsets lo;
   lo.init(c, g);
   RotStager<T> sk;
-  sk.init(tid);
+  DmaTile dkt;  // PRE & 1: K' tiles
+  if constexpr ((PRE & 1) != 0) {
+    dkt.init(kbase, p.k.ss, S, wave, lane);
+  } else {
+    sk.init(tid);
+  }
   DmaTile dv;
   dv.init(vbase, p.v.ss, S, wave, lane);
   const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
 
   int kt = next_tile(0);
   if (kt < kt_end) {
-    sk.load(kbase, p.k.ss, tab, kt * BN, S);
-    dv.issue(sv0, kt * BN, wave);
-    sk.store(sk0);
+    if constexpr ((PRE & 1) != 0) {
+      dkt.issue(sk0, kt * BN, wave);
+      dv.issue(sv0, kt * BN, wave);
+    } else {
+      sk.load(kbase, p.k.ss, tab, kt * BN, S);
+      dv.issue(sv0, kt * BN, wave);
+      sk.store(sk0);
+    }
   }
   wait_vmem_and_sync();
 
@@ -343,7 +367,11 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
     char* sVn = stage ? sv0 : sv1;
     const int ktn = next_tile(kt + 1);
     if (ktn < kt_end) {
-      sk.load(kbase, p.k.ss, tab, ktn * BN, S);
+      if constexpr ((PRE & 1) != 0) {
+        dkt.issue(sKn, ktn * BN, wave);
+      } else {
+        sk.load(kbase, p.k.ss, tab, ktn * BN, S);
+      }
       dv.issue(sVn, ktn * BN, wave);
     }
     const int kv0 = kt * BN;
@@ -412,7 +440,9 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
       for (int ks = 0; ks < 2; ++ks) dq[db] = M::mma(tr_frag<frag>(sK, lo, ks, db), dsf[ks], dq[db]);
     sched_reads_ahead<16, 2, 3, 1>();
 
-    if (ktn < kt_end) sk.store(sKn);
+    if constexpr ((PRE & 1) == 0) {
+      if (ktn < kt_end) sk.store(sKn);
+    }
     wait_vmem_and_sync();
     kt = ktn;
   };
@@ -446,7 +476,8 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-template <typename T, int MASK, bool CAUSAL>
+// PRE bit 0: K arrives rotated (K' in the workspace): its rows are only scaled.
+template <typename T, int MASK, bool CAUSAL, int PRE>
 __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   using frag = typename Mf<T>::frag;
   using M = M16<T>;
@@ -480,9 +511,9 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
 
   // K' (times scale log2 e) and V of this lane's key as B fragments
   frag kf[4], vf[4];
-  row_frags<T, true>(kf, (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh + (int64_t)jc * p.k.ss, tab + (int64_t)jc * D,
-                     g, p.shp.scale_log2);
-  row_frags<T, false>(vf, (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh + (int64_t)jc * p.v.ss, nullptr, g, 1.f);
+  row_frags<T, (PRE & 1) ? kRowMul : kRowRot>(kf, (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh + (int64_t)jc * p.k.ss,
+                                              tab + (int64_t)jc * D, g, p.shp.scale_log2);
+  row_frags<T, kRowRaw>(vf, (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh + (int64_t)jc * p.v.ss, nullptr, g, 1.f);
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 dv[8], dk[8];
 #pragma unroll
@@ -744,35 +775,47 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-template <typename T, int MASK, bool CAUSAL>
+template <typename T, int MASK, bool CAUSAL, int PRE>
 static int launch_bwd16_t(const BwdParams& p, void* stream) {
   const int S = p.shp.S, BH = p.shp.B * p.shp.H;
   // dQ first: it also writes Q' for the dK/dV kernel.  Causal: two query tiles of one head
   // per workgroup (see the kernel)
   const int grid_q = CAUSAL ? ((S + 127) / 128 + 1) / 2 * BH : ((S + 127) / 128) * BH;
-  hipLaunchKernelGGL((dq16_kernel<T, MASK, CAUSAL>), dim3(grid_q), dim3(512), 0,
+  hipLaunchKernelGGL((dq16_kernel<T, MASK, CAUSAL, PRE>), dim3(grid_q), dim3(512), 0,
                      (hipStream_t)stream, p);
   int e = (int)hipGetLastError();
   if (e) return e;
-  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL>), dim3(((S + 127) / 128) * p.shp.B * p.shp.Hkv), dim3(512), 0,
-                     (hipStream_t)stream, p);
+  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL, PRE & 1>), dim3(((S + 127) / 128) * p.shp.B * p.shp.Hkv),
+                     dim3(512), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int PRE>
 static int launch_bwd16_dt(int mask_kind, bool causal, const BwdParams& p, void* stream) {
-  if (causal) return launch_bwd16_t<T, MASK_NONE, true>(p, stream);
+  if (causal) return launch_bwd16_t<T, MASK_NONE, true, PRE>(p, stream);
   switch (mask_kind) {
-    case MASK_BOOL: return launch_bwd16_t<T, MASK_BOOL, false>(p, stream);
-    case MASK_ADD: return launch_bwd16_t<T, MASK_ADD, false>(p, stream);
-    default: return launch_bwd16_t<T, MASK_NONE, false>(p, stream);
+    case MASK_BOOL: return launch_bwd16_t<T, MASK_BOOL, false, PRE>(p, stream);
+    case MASK_ADD: return launch_bwd16_t<T, MASK_ADD, false, PRE>(p, stream);
+    default: return launch_bwd16_t<T, MASK_NONE, false, PRE>(p, stream);
   }
 }
 
-// dK/dV and dQ for 16-bit inputs at D = 128 (after the delta pre-pass).
-int launch_bwd16(int dtype, int mask_kind, bool causal, const BwdParams& p, void* stream) {
-  return dtype == F16 ? launch_bwd16_dt<_Float16>(mask_kind, causal, p, stream)
-                      : launch_bwd16_dt<__bf16>(mask_kind, causal, p, stream);
+template <typename T>
+static int launch_bwd16_pre(int mask_kind, bool causal, int pre, const BwdParams& p, void* stream) {
+  switch (pre) {
+    case 0: return launch_bwd16_dt<T, 0>(mask_kind, causal, p, stream);
+    case 1: return launch_bwd16_dt<T, 1>(mask_kind, causal, p, stream);
+    case 3:  // (the quantized backward: no mask, not causal)
+      return launch_bwd16_t<T, MASK_NONE, false, 3>(p, stream);
+    default: return -1;
+  }
+}
+
+// dK/dV and dQ for 16-bit inputs at D = 128 (after the delta pre-pass).  pre: 0 Q and K
+// rotated here; 1 K' prepared in p.k; 3 Q' (p.qrot) and K' (p.k) both prepared.
+int launch_bwd16(int dtype, int mask_kind, bool causal, int pre, const BwdParams& p, void* stream) {
+  return dtype == F16 ? launch_bwd16_pre<_Float16>(mask_kind, causal, pre, p, stream)
+                      : launch_bwd16_pre<__bf16>(mask_kind, causal, pre, p, stream);
 }
 
 }  // namespace rs

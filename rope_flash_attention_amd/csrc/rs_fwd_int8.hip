@@ -26,7 +26,7 @@ namespace rs {
 
 constexpr int kQuantBlock = 64;
 
-template <typename T, int D>
+template <typename T, int D, bool DEQ>
 __global__ __launch_bounds__(256) void quant_kernel(QuantParams p) {
   constexpr int UPR = D / 8;                 // 8-element units per row
   constexpr int UPT = kQuantBlock * UPR / 256;  // units per thread
@@ -70,6 +70,27 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantParams p) {
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float inv = amax > 0.f ? p.qmax / amax : 0.f;
+  const float scale = amax > 0.f ? amax / p.qmax : 0.f;
+
+  if constexpr (DEQ) {  // the dequantized values, code * scale, in the input dtype
+    T* db = (T*)p.deq[which] + ((int64_t)b * p.Hx[which] + h) * p.S * D;
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + 256 * i, row = u / UPR, ch = u % UPR;
+      const int s = blk * kQuantBlock + row;
+      if (s >= p.S) continue;
+      typedef T v8 __attribute__((ext_vector_type(8)));
+      v8 y;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float c = __builtin_rintf(v[i][j] * inv);  // round half to even
+        c = fminf(fmaxf(c, -p.qmax), p.qmax);
+        y[j] = from_f<T>(c * scale);
+      }
+      *(v8*)(db + (int64_t)s * D + ch * 8) = y;
+    }
+    return;
+  }
 
   int8_t* cb = p.codes[which] + b * p.c_sb[which] + h * p.c_sh[which];
 #pragma unroll
@@ -86,17 +107,22 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantParams p) {
     }
     *(uint2*)(cb + (int64_t)s * D + ch * 8) = make_uint2(w[0], w[1]);
   }
-  if (tid == 0) p.scales[which][((int64_t)b * p.Hx[which] + h) * p.nblk + blk] = amax > 0.f ? amax / p.qmax : 0.f;
+  if (tid == 0) p.scales[which][((int64_t)b * p.Hx[which] + h) * p.nblk + blk] = scale;
+}
+
+template <typename T, bool DEQ>
+static int launch_quant_td(const QuantParams& p, void* stream) {
+  const dim3 grid(p.nblk, p.H, 2 * p.B);
+  if (p.D == 64)
+    hipLaunchKernelGGL((quant_kernel<T, 64, DEQ>), grid, dim3(256), 0, (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL((quant_kernel<T, 128, DEQ>), grid, dim3(256), 0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
 }
 
 template <typename T>
 static int launch_quant_t(const QuantParams& p, void* stream) {
-  const dim3 grid(p.nblk, p.H, 2 * p.B);
-  if (p.D == 64)
-    hipLaunchKernelGGL((quant_kernel<T, 64>), grid, dim3(256), 0, (hipStream_t)stream, p);
-  else
-    hipLaunchKernelGGL((quant_kernel<T, 128>), grid, dim3(256), 0, (hipStream_t)stream, p);
-  return (int)hipGetLastError();
+  return p.deq[0] ? launch_quant_td<T, true>(p, stream) : launch_quant_td<T, false>(p, stream);
 }
 
 int launch_quant_int8(int dtype, const QuantParams& p, void* stream) {

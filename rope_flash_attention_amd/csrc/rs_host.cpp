@@ -21,7 +21,7 @@ using namespace rs;
 
 struct Counters {
   std::atomic<uint64_t> fwd_instream{0}, fwd_autograd{0}, bwd_calls{0}, masked_bool{0},
-      masked_additive{0}, causal{0}, quant_int8{0}, errors{0};
+      masked_additive{0}, causal{0}, quant_int8{0}, quant_bwd{0}, errors{0};
 };
 Counters g_ctr;
 
@@ -244,8 +244,9 @@ Layout layout(const Shape& s, int mask_kind, bool backward, int int8, bool causa
     L.ks = off;
     off += round_up((size_t)(s.B * s.Hkv * L.nblk) * sizeof(float), 256);
   }
-  L.kprep = off;  // K' of the Q/K prologue: [B][Hkv][S][D] in the compute dtype
-  if (!backward && s.kprep) off += round_up((size_t)(s.B * s.Hkv * s.S * s.D) * elem_size(s.dtype), 256);
+  L.kprep = off;  // K' = R(K) rotated once: [B][Hkv][S][D] in the compute dtype
+  if ((!backward && s.kprep) || (backward && s.dtype != F32 && s.D == 128))
+    off += round_up((size_t)(s.B * s.Hkv * s.S * s.D) * elem_size(s.dtype), 256);
   if (!backward) {
     const int64_t bm = fwd_block_m(s.dtype), bn = fwd_block_n(s.dtype);
     const int64_t units = s.B * s.H * ((s.S + bm - 1) / bm);
@@ -587,7 +588,8 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   Shape s;
   rs_status st = validate_args(a, &s);
   if (st != RS_OK) return fail(st);
-  if (a->flags & kQuantFlags) return fail(RS_ERR_UNSUPPORTED);
+  const bool quant = (a->flags & kQuantFlags) != 0;
+  if (quant && s.D != 128) return fail(RS_ERR_UNSUPPORTED);  // quantized backward: D = 128
   if (!s.rope) return fail(RS_ERR_UNSUPPORTED);  // the backward is the fused one: tables required
   if (s.qkm != 0) return fail(RS_ERR_UNSUPPORTED);  // no backward through the Q/K prologue
   const int64_t sz[4] = {s.B, s.H, s.S, s.D};
@@ -633,9 +635,38 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   p.mask = mask_view(a, s, L, w);
   p.shp = attn_shape(s);
   const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
-  if (launch_bwd(s.dtype, (int)s.D, a->mask_kind, causal, p, strm) != 0) return fail(RS_ERR_LAUNCH);
+  int pre = 0;
+  if (s.dtype != F32 && s.D == 128) {
+    // K' = R(K) once into the workspace (the dQ kernel then streams K' tiles with no table);
+    // quantized: the dequantized Q' and K' the forward attended with, by the quantizer pass
+    if (quant) {
+      QuantParams qp = quant_params(a, s, L, w);
+      qp.nblk = (int)((s.S + 63) / 64);
+      qp.deq[0] = w + L.qrot;
+      qp.deq[1] = w + L.kprep;
+      if (launch_quant_int8(s.dtype, qp, strm) != 0) return fail(RS_ERR_LAUNCH);
+      pre = 3;
+    } else {
+      KPrepParams kp{};
+      kp.x = p.k;
+      kp.out = w + L.kprep;
+      kp.tab = p.tab;
+      kp.B = (int)s.B;
+      kp.H = (int)s.Hkv;
+      kp.S = (int)s.S;
+      kp.D = (int)s.D;
+      if (launch_kprep(s.dtype, 0, kp, strm) != 0) return fail(RS_ERR_LAUNCH);
+      pre = 1;
+    }
+    p.k.ptr = w + L.kprep;
+    p.k.sb = s.Hkv * s.S * s.D;
+    p.k.sh = s.S * s.D;
+    p.k.ss = s.D;
+  }
+  if (launch_bwd(s.dtype, (int)s.D, a->mask_kind, causal, pre, p, strm) != 0) return fail(RS_ERR_LAUNCH);
 
   g_ctr.bwd_calls.fetch_add(1, std::memory_order_relaxed);
+  if (quant) g_ctr.quant_bwd.fetch_add(1, std::memory_order_relaxed);
   if (a->mask_kind == RS_MASK_BOOL) g_ctr.masked_bool.fetch_add(1, std::memory_order_relaxed);
   if (a->mask_kind == RS_MASK_ADDITIVE) g_ctr.masked_additive.fetch_add(1, std::memory_order_relaxed);
   if (causal) g_ctr.causal.fetch_add(1, std::memory_order_relaxed);
@@ -699,6 +730,7 @@ void rope_sdpa_get_stats(rs_stats* out) {
   out->causal = g_ctr.causal.load();
   out->quant_int8 = g_ctr.quant_int8.load();
   out->errors = g_ctr.errors.load();
+  out->quant_bwd = g_ctr.quant_bwd.load();
   if (current_device_ok() == RS_OK) {
     uint64_t v = 0;
     if (hipDeviceSynchronize() == hipSuccess && read_all_true_counter(&v, false) == 0) out->mask_all_true_skipped = v;
@@ -713,6 +745,7 @@ void rope_sdpa_reset_stats(void) {
   g_ctr.masked_additive = 0;
   g_ctr.causal = 0;
   g_ctr.quant_int8 = 0;
+  g_ctr.quant_bwd = 0;
   g_ctr.errors = 0;
   if (current_device_ok() == RS_OK) {
     uint64_t v = 0;

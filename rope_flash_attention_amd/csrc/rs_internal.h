@@ -131,6 +131,10 @@ struct QuantParams {
   int Hx[2];                 // heads of Q (H) and of K (Hkv)
   int B, H, S, D, nblk;
   float qmax;                // code range [-qmax, qmax]: 127 (int8) or 7 (int4)
+  // dequantizing mode (the quantized backward): when deq[0] is set, the pass writes
+  // code * scale rounded to the input dtype, contiguous [B][Hx][S][D], instead of codes and
+  // scales
+  void* deq[2];
 };
 
 // The eager rotation pass (rope_sdpa_rotate): out = R(x) for a [B, H, S, D] operand.
@@ -189,7 +193,10 @@ int launch_fwd_plain(int dtype, int D, int mask_kind, bool causal, const FwdPara
 int launch_rotate(int dtype, const RotateParams& p, void* stream);
 // The int8 forward in code export mode (no output written; see FwdParams).
 int launch_fwd_int8_export(int dtype, int D, bool int4, const FwdParams& p, void* stream);
-int launch_bwd(int dtype, int D, int mask_kind, bool causal, const BwdParams& p, void* stream);
+// pre (16-bit inputs at D = 128 only, else 0): 0 Q and K rotated in the backward kernels; 1 K'
+// prepared in p.k (contiguous); 3 Q' in p.qrot and K' in p.k both prepared (the quantized
+// backward's dequantized values)
+int launch_bwd(int dtype, int D, int mask_kind, bool causal, int pre, const BwdParams& p, void* stream);
 // Reads (and optionally clears) the device-side count of all-true bool masks.
 int read_all_true_counter(uint64_t* value, bool reset);
 

@@ -148,6 +148,11 @@ int launch_rotate(int, const RotateParams& p, void*) {
 int launch_quant_int8(int, const QuantParams& p, void*) {
   ++stub::launches;
   if (p.qmax != 127.f && p.qmax != 7.f) std::abort();
+  if (p.nblk != (p.S + 63) / 64) std::abort();
+  if (p.deq[0]) {  // dequantizing mode (the quantized backward): T values, no codes
+    for (int w = 0; w < 2; ++w) stub::need(p.deq[w], (size_t)p.B * p.Hx[w] * p.S * p.D * 2, "dequantized values");
+    return 0;
+  }
   stub::need(p.tab.ptr, (size_t)(p.tab.sb ? p.B : 1) * p.S * p.D * sizeof(float), "packed tables");
   for (int w = 0; w < 2; ++w) {
     stub::need(p.codes[w], (size_t)p.B * p.Hx[w] * p.rows * p.D, "codes");
@@ -163,13 +168,20 @@ int launch_fwd_int8_export(int, int, bool, const FwdParams& p, void*) {
   return 0;
 }
 
-int launch_bwd(int dtype, int D, int, bool, const BwdParams& p, void*) {
+int launch_bwd(int dtype, int D, int, bool, int pre, const BwdParams& p, void*) {
   ++stub::launches;
   const int B = p.shp.B, H = p.shp.H, S = p.shp.S;
   if (p.shp.Hkv <= 0 || H % p.shp.Hkv != 0 || p.shp.group != H / p.shp.Hkv) std::abort();
   stub::need(p.tab.ptr, (size_t)(p.tab.sb ? B : 1) * S * D * sizeof(float), "packed tables");
   stub::need(p.delta, (size_t)B * H * S * sizeof(float), "delta");
-  if (dtype != F32 && D == 128) stub::need(p.qrot, (size_t)B * H * S * D * 2, "rotated Q");
+  if (dtype != F32 && D == 128) {
+    stub::need(p.qrot, (size_t)B * H * S * D * 2, "rotated Q");
+    if (pre != 1 && pre != 3) std::abort();  // K' prepared in the workspace
+    stub::need(p.k.ptr, (size_t)B * p.shp.Hkv * S * D * 2, "prepared K");
+    if (p.k.ss != D || p.k.sh != (int64_t)S * D || p.k.sb != (int64_t)p.shp.Hkv * S * D) std::abort();
+  } else if (pre != 0) {
+    std::abort();
+  }
   return 0;
 }
 

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = lib()
-    assert L.rope_sdpa_abi_version() == 2
+    assert L.rope_sdpa_abi_version() == 3
     for code, name in _abi.STATUS_NAMES.items():
         assert _abi.status_string(code).startswith(name)
     assert "unknown" in _abi.status_string(-99)
@@ -223,8 +223,8 @@ def test_workspace_size_layout():
     kprime = -(-(2 * 3 * 100 * 128 * 2) // 256) * 256  # 16-bit forward: K' = R(K), rotated once
     assert n == 256 + -(-table // 256) * 256 + kprime
     st, nb = c.ws_size(1)
-    # backward: + delta (fp32 per row) + Q' = R(Q) in the input dtype (16-bit, D = 128), no K'
-    assert st == 0 and nb == n - kprime + -(-(2 * 3 * 100 * 4) // 256) * 256 + -(-(2 * 3 * 100 * 128 * 2) // 256) * 256
+    # backward: + delta (fp32 per row) + Q' = R(Q) in the input dtype (16-bit, D = 128); K' too
+    assert st == 0 and nb == n + -(-(2 * 3 * 100 * 4) // 256) * 256 + -(-(2 * 3 * 100 * 128 * 2) // 256) * 256
     f = Call(B=2, H=3, S=100, D=128, dt=RS_F32, es=4)
     st, nf = f.ws_size(0)
     st2, nfb = f.ws_size(1)
@@ -256,15 +256,20 @@ def test_backward_validation_and_error_counter():
     st = L.rope_sdpa_bwd(ctypes.byref(a), ctypes.byref(c.o), c.lse, ctypes.byref(do), ctypes.byref(dq),
                          ctypes.byref(dk), ctypes.byref(dv), c.ws, c.ws_bytes, None)
     assert st == ERR["RS_ERR_DTYPE"]
-    c.flags = RS_FLAG_QUANT_INT8_QK
+    c.flags = RS_FLAG_QUANT_INT8_QK  # the quantized backward (D = 128) is accepted: no device here
     a = c.args()
     dv.dtype = RS_BF16
+    st = L.rope_sdpa_bwd(ctypes.byref(a), ctypes.byref(c.o), c.lse, ctypes.byref(do), ctypes.byref(dq),
+                         ctypes.byref(dk), ctypes.byref(dv), c.ws, c.ws_bytes, None)
+    assert st == ERR["RS_ERR_NO_DEVICE"]
+    c.flags = RS_FLAG_QUANT_INT8_QK | RS_FLAG_CAUSAL
+    a = c.args()
     st = L.rope_sdpa_bwd(ctypes.byref(a), ctypes.byref(c.o), c.lse, ctypes.byref(do), ctypes.byref(dq),
                          ctypes.byref(dk), ctypes.byref(dv), c.ws, c.ws_bytes, None)
     assert st == ERR["RS_ERR_UNSUPPORTED"]
     s = RsStats()
     L.rope_sdpa_get_stats(ctypes.byref(s))
-    assert s.errors == 4 and s.bwd_calls == 0 and s.fwd_instream == 0
+    assert s.errors == 5 and s.bwd_calls == 0 and s.fwd_instream == 0 and s.quant_bwd == 0
 
 
 @pytest.mark.parametrize("dims", [dict(B=0), dict(H=0), dict(S=0)])
