@@ -10,12 +10,16 @@
  *
  * with M from a bool mask (True = attend) or an additive float mask, broadcast over up to
  * four dimensions (same page, section "Enable In SimpleTuner"), or a causal (top-left,
- * key j > query i excluded) pattern.  The forward rotates Q and K inside the attention
- * kernel, in registers: it writes no rotated copy of Q or K to memory.  The backward rotates
- * each Q row once, in its dQ kernel, and leaves Q' = R(Q), rounded to the input dtype, in the
- * caller's workspace ([B, H, S, D], 16-bit inputs at D = 128) for its dK/dV kernel; K' is
- * never written.  The backward returns gradients with respect to the unrotated Q and K (the
- * inverse rotation, i.e. the same rotation with sin negated, applied to dQ' and dK'), and V.
+ * key j > query i excluded) pattern.  The forward rotates Q inside the attention kernel, in
+ * registers, and never writes Q'.  K is rotated once per (batch, K/V head) into the caller's
+ * workspace (K' = R(K) rounded to the input dtype, [B, Hkv, S, D]) for bf16/f16 without
+ * quantization or additive mask, so that the attention kernel's key loop reads no table;
+ * otherwise (fp32, additive masks, the quantized forward) K is rotated in the key loop and
+ * no rotated copy is written (the quantized pre-pass mode writes codes instead).  The backward
+ * (16-bit inputs at D = 128) leaves Q' (written by its dQ kernel) and K' (by a rotation pass)
+ * in the workspace; at D = 64 and in fp32 it rotates both inside its kernels.  The backward
+ * returns gradients with respect to the unrotated Q and K (the inverse rotation, i.e. the
+ * same rotation with sin negated, applied to dQ' and dK'), and V.
  *
  * Conventions for every entry point
  *  - All tensors are described by rs_tensor: a DEVICE pointer, a dtype and four sizes and
@@ -143,7 +147,7 @@ rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* by
  * batch item and K/V head) into the workspace by a pass of its own and Q inside the attention
  * kernel, each product and sum in fp32 and the result rounded to the input dtype; the
  * attention kernel then reads K' with no table in its key loop.
- * RS_FLAG_QUANT_INT8_QK (bf16/f16 inputs, no mask, no causal, lse may be NULL): after the
+ * RS_FLAG_QUANT_INT8_QK (bf16/f16 inputs; any mask kind or causal; lse may be NULL): after the
  * fp32 rotation (each product and sum rounded), Q' and K' are quantized per (b, h, 64-token
  * block) to int8 codes round-half-even(x * fp32(127/amax)) with scale amax/127, QK^T runs on
  * int8 MFMA with exact int32 accumulation, and P.V stays in the input precision (pages:
@@ -187,7 +191,14 @@ size_t rope_sdpa_noalloc_scratch_bytes(void);
  * pre-rotation Q and K).  Inputs: the same args as the forward, its o and lse, and the
  * upstream gradient dout (sizes and dtype of o).  Writes dq (sizes of q), dk and dv (sizes of k),
  * all in the dtype of q.
- * The mask (if any) is a constant: no mask gradient.  Not available with the QUANT flags.
+ * The mask (if any) is a constant: no mask gradient.
+ * With RS_FLAG_QUANT_INT8_QK or RS_FLAG_QUANT_INT4_QK (16-bit inputs at D = 128; D = 64 returns
+ * RS_ERR_UNSUPPORTED): the gradients of the quantized forward with the gradient passed
+ * straight through the quantizer (the pages name a quantized autograd entry point without
+ * saying how gradients cross the quantizer; this is the reading taken).  The quantizer pass
+ * writes the dequantized values code * scale of Q' and K', rounded to the input dtype, to the
+ * workspace, and the backward runs at those values: dV = P^T dO, dQ' = scale dS K^, dK' =
+ * scale dS^T Q^, then the inverse rotation.  RS_FLAG_QUANT_INT8_PREPASS changes nothing here.
  */
 rs_status rope_sdpa_bwd(const rs_args* args, const rs_tensor* o, const float* lse,
                         const rs_tensor* dout, const rs_tensor* dq, const rs_tensor* dk,

@@ -454,9 +454,10 @@ def quantized_qk(q, k, cos, sin, bits=8, block=64):
 
 
 def rope_sdpa_forward_quant(q, k, v, cos, sin, bits=8, scale=None, rows=None, pairs=None, block=64, workers=1,
-                            codes=None):
+                            codes=None, mask=None, mask_kind="none", causal=False):
     """Quantized variant (bits = 8 or 4): rotate in fp32, quantize Q' and K' blockwise,
-    attend on the dequantized values.
+    attend on the dequantized values (with masks and causal as the unquantized forward:
+    [EN] the quantized dispatchers take the same masks).
 
     `codes` may carry externally supplied ((q_codes, q_scales), (k_codes, k_scales)) so the
     attention part can be checked on exactly those quantized values.
@@ -469,8 +470,8 @@ def rope_sdpa_forward_quant(q, k, v, cos, sin, bits=8, scale=None, rows=None, pa
         qh, kh = dequantize_blockwise(qc, qs, block), dequantize_blockwise(kc, ks, block)
     kh = expand_kv(kh, qh.shape[1])  # K quantized at its own head count
     v64 = expand_kv(_np64(v), qh.shape[1])
-    return attention_forward(qh, kh, v64, _resolve_scale(scale, qh.shape[-1]), None, False,
-                             rows=rows, pairs=pairs, workers=workers)
+    return attention_forward(qh, kh, v64, _resolve_scale(scale, qh.shape[-1]), mask_to_additive(mask, mask_kind),
+                             causal, rows=rows, pairs=pairs, workers=workers)
 
 
 def rope_sdpa_forward_int8(q, k, v, cos, sin, scale=None, rows=None, pairs=None, block=64, workers=1,
@@ -479,7 +480,8 @@ def rope_sdpa_forward_int8(q, k, v, cos, sin, scale=None, rows=None, pairs=None,
     return rope_sdpa_forward_quant(q, k, v, cos, sin, 8, scale, rows, pairs, block, workers, codes)
 
 
-def rope_sdpa_backward_quant(q, k, v, cos, sin, do, bits=8, scale=None, block=64, workers=1):
+def rope_sdpa_backward_quant(q, k, v, cos, sin, do, bits=8, scale=None, block=64, workers=1, mask=None,
+                             mask_kind="none", causal=False):
     """Gradients of the quantized variant w.r.t. the unrotated Q, K and V ([EN]: quantized
     training goes through a quantized autograd entry point; [RQ] names it).  The pages do
     not say how a gradient passes the quantizer.  Reading taken (straight-through): the
@@ -491,7 +493,8 @@ def rope_sdpa_backward_quant(q, k, v, cos, sin, do, bits=8, scale=None, block=64
     qh, kh = quantized_qk(q, k, cos, sin, bits, block)
     H, Hkv = qh.shape[1], kh.shape[1]
     dqh, dkh, dv = attention_backward(qh, expand_kv(kh, H), expand_kv(_np64(v), H), do64,
-                                      _resolve_scale(scale, qh.shape[-1]), None, False, workers=workers)
+                                      _resolve_scale(scale, qh.shape[-1]), mask_to_additive(mask, mask_kind),
+                                      causal, workers=workers)
     dkh, dv = reduce_kv(dkh, Hkv), reduce_kv(dv, Hkv)
     return rope_rotate_vjp(dqh, cos, sin), rope_rotate_vjp(dkh, cos, sin), dv
 

@@ -805,8 +805,7 @@ static int launch_bwd16_pre(int mask_kind, bool causal, int pre, const BwdParams
   switch (pre) {
     case 0: return launch_bwd16_dt<T, 0>(mask_kind, causal, p, stream);
     case 1: return launch_bwd16_dt<T, 1>(mask_kind, causal, p, stream);
-    case 3:  // (the quantized backward: no mask, not causal)
-      return launch_bwd16_t<T, MASK_NONE, false, 3>(p, stream);
+    case 3: return launch_bwd16_dt<T, 3>(mask_kind, causal, p, stream);
     default: return -1;
   }
 }

@@ -7,9 +7,13 @@
 
 namespace rs {
 
+// the quantized forward's instantiations, one translation unit per code width
+int launch_fwd_q8(int dtype, int D, int mask_kind, bool causal, int mode, const FwdParams& p, void* stream);
+int launch_fwd_q4(int dtype, int D, int mask_kind, bool causal, int mode, const FwdParams& p, void* stream);
+
 int launch_fwd(int dtype, int D, int mask_kind, bool causal, int int8, const FwdParams& p, void* stream) {
-  if (int8)
-    return dtype == F16 ? launch_fwd_int8<_Float16>(D, int8, p, stream) : launch_fwd_int8<__bf16>(D, int8, p, stream);
+  if (int8 & 4) return launch_fwd_q4(dtype, D, mask_kind, causal, int8, p, stream);
+  if (int8) return launch_fwd_q8(dtype, D, mask_kind, causal, int8, p, stream);
   switch (dtype) {
     case F32: return launch_fwd_dt<float, true>(D, mask_kind, causal, p, stream);
     case F16: return launch_fwd_dt<_Float16, true>(D, mask_kind, causal, p, stream);

@@ -96,7 +96,7 @@ constexpr int PV_AHEAD = 3;  // V^T fragments (two reads each) in flight ahead o
 // normalized and rotated, in T (kprep_kernel's output), so the key loop reads no tables.
 template <typename T, int D, int MASK, bool CAUSAL, int QI8 = 0, bool ROPE = true, bool QEXP = false, int QKM = 0>
 __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
-  static_assert(!QI8 || (sizeof(T) == 2 && MASK == MASK_NONE && !CAUSAL), "int8 variant: 16-bit, unmasked");
+  static_assert(!QI8 || sizeof(T) == 2, "quantized variant: 16-bit inputs");
   static_assert(ROPE || !QI8, "the int8 variant rotates");
   constexpr int QM = QI8 & 3;                     // 1: quantized here, 2: codes from the quantizer pass
   constexpr float QMAX = (QI8 & 4) ? 7.f : 127.f;  // code range: int4 or int8
@@ -631,7 +631,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int t = 0; t < NQ8; ++t) ia = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[t], qf[t], ia, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = fmaf((float)ia[i], f, -m_base);
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = kAddMask ? (float)ia[i] * f : fmaf((float)ia[i], f, -m_base);
       }
     } else {
 #pragma unroll
@@ -1085,19 +1085,19 @@ static int launch_fwd_t(const FwdParams& p, void* stream) {
   return (int)hipGetLastError();
 }
 
-template <typename T, int D, bool ROPE>
+template <typename T, int D, bool ROPE, int QI8 = 0>
 static int launch_fwd_d(int mask_kind, bool causal, const FwdParams& p, void* stream) {
-  if (causal) return launch_fwd_t<T, D, MASK_NONE, true, false, ROPE>(p, stream);
+  if (causal) return launch_fwd_t<T, D, MASK_NONE, true, QI8, ROPE>(p, stream);
   switch (mask_kind) {
-    case MASK_BOOL: return launch_fwd_t<T, D, MASK_BOOL, false, false, ROPE>(p, stream);
+    case MASK_BOOL: return launch_fwd_t<T, D, MASK_BOOL, false, QI8, ROPE>(p, stream);
     case MASK_ADD:
       if constexpr (sizeof(T) == 2) {
         if (p.mask.dtype != F32 && !p.mask.key_bcast && p.mask.sq != 0 && p.shp.S % 8 == 0 &&
             p.mask.sq * 2 * FwdCfg<T>::BM < ((int64_t)1 << 31))
-          return launch_fwd_t<T, D, MASK_ADD_TILE, false, false, ROPE>(p, stream);
+          return launch_fwd_t<T, D, MASK_ADD_TILE, false, QI8, ROPE>(p, stream);
       }
-      return launch_fwd_t<T, D, MASK_ADD, false, false, ROPE>(p, stream);
-    default: return launch_fwd_t<T, D, MASK_NONE, false, false, ROPE>(p, stream);
+      return launch_fwd_t<T, D, MASK_ADD, false, QI8, ROPE>(p, stream);
+    default: return launch_fwd_t<T, D, MASK_NONE, false, QI8, ROPE>(p, stream);
   }
 }
 
@@ -1108,22 +1108,9 @@ static int launch_fwd_dt(int D, int mask_kind, bool causal, const FwdParams& p, 
 }
 
 template <typename T, int QI8>
-static int launch_fwd_q_d(int D, const FwdParams& p, void* stream) {
-  return D == 64 ? launch_fwd_t<T, 64, MASK_NONE, false, QI8>(p, stream)
-                 : launch_fwd_t<T, 128, MASK_NONE, false, QI8>(p, stream);
-}
-
-// mode: 1 / 2 int8 quantized in the kernel / codes from the quantizer pass; 5 / 6 the same
-// with int4 codes
-template <typename T>
-static int launch_fwd_int8(int D, int mode, const FwdParams& p, void* stream) {
-  switch (mode) {
-    case 1: return launch_fwd_q_d<T, 1>(D, p, stream);
-    case 2: return launch_fwd_q_d<T, 2>(D, p, stream);
-    case 5: return launch_fwd_q_d<T, 5>(D, p, stream);
-    case 6: return launch_fwd_q_d<T, 6>(D, p, stream);
-    default: return -1;
-  }
+static int launch_fwd_q_d(int D, int mask_kind, bool causal, const FwdParams& p, void* stream) {
+  return D == 64 ? launch_fwd_d<T, 64, true, QI8>(mask_kind, causal, p, stream)
+                 : launch_fwd_d<T, 128, true, QI8>(mask_kind, causal, p, stream);
 }
 
 

@@ -191,7 +191,6 @@ rs_status validate_args(const rs_args* a, Shape* out) {
   if (s.qkm != 0 && (!s.rope || a->mask_kind == RS_MASK_ADDITIVE)) return RS_ERR_UNSUPPORTED;
   if (a->flags & kQuantFlags) {
     if (dt == RS_F32 || !s.rope || s.qkm != 0) return RS_ERR_UNSUPPORTED;
-    if (a->mask_kind != RS_MASK_NONE || causal) return RS_ERR_UNSUPPORTED;
   }
   if (a->mask_kind == RS_MASK_BOOL) {
     if (s.S > kMaxBoolMaskSeq) return RS_ERR_SHAPE;

@@ -157,8 +157,17 @@ int main() {
         }
   { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT8_QK | RS_FLAG_QUANT_INT4_QK;
     expect_error(c, false, RS_ERR_INVALID, "int8 and int4"); }
-  { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT4_QK | RS_FLAG_CAUSAL;
-    expect_error(c, false, RS_ERR_UNSUPPORTED, "int4 causal"); }
+  // the quantized forward and backward take every mask kind and causal
+  for (uint32_t bits : {(uint32_t)RS_FLAG_QUANT_INT8_QK, (uint32_t)RS_FLAG_QUANT_INT4_QK})
+    for (int variant = 0; variant < 4; ++variant)
+      for (int bwd = 0; bwd < 2; ++bwd) {
+        Case c(RS_BF16, 2, 3, 300, 128);
+        c.a.flags = bits;
+        if (variant == 1) c.a.flags |= RS_FLAG_CAUSAL;
+        if (variant == 2) c.set_mask(RS_MASK_BOOL, RS_BOOL, 2, 1, 1, 300);
+        if (variant == 3) c.set_mask(RS_MASK_ADDITIVE, RS_BF16, 1, 3, 300, 300);
+        CHECK(run(c, bwd != 0) == RS_OK, "quantized flags=%u variant=%d bwd=%d", bits, variant, bwd);
+      }
   { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT8_PREPASS;
     expect_error(c, false, RS_ERR_INVALID, "prepass without int8"); }
   // plain attention (no tables): forward only
@@ -277,7 +286,6 @@ int main() {
   { Case c(RS_BF16, 1, 2, 128, 64); c.cos.dtype = RS_F16; expect_error(c, false, RS_ERR_DTYPE, "table dtype"); }
   { Case c(RS_BF16, 2, 2, 128, 64, 2); c.sin.size[0] = 1; c.sin.stride[0] = 0; expect_error(c, false, RS_ERR_SHAPE, "table batch mismatch"); }
   { Case c(RS_F32, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT8_QK; expect_error(c, false, RS_ERR_UNSUPPORTED, "int8 fp32"); }
-  { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT8_QK | RS_FLAG_CAUSAL; expect_error(c, false, RS_ERR_UNSUPPORTED, "int8 causal"); }
   { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT8_QK; expect_error(c, true, RS_ERR_UNSUPPORTED, "int8 backward D=64"); }
   // the quantized backward (D = 128): int8 and int4, grouped-query included
   for (uint32_t bits : {(uint32_t)RS_FLAG_QUANT_INT8_QK, (uint32_t)RS_FLAG_QUANT_INT4_QK})

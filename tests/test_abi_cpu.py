@@ -13,7 +13,7 @@ import pytest
 
 from rope_flash_attention_amd import _abi
 from rope_flash_attention_amd._abi import (RS_BF16, RS_BOOL, RS_F16, RS_F32, RS_FLAG_CAUSAL,
-                                           RS_FLAG_QUANT_INT8_QK, RS_MASK_ADDITIVE, RS_MASK_BOOL,
+                                           RS_FLAG_QUANT_INT8_QK, RS_FLAG_QUANT_INT4_QK, RS_MASK_ADDITIVE, RS_MASK_BOOL,
                                            RS_MASK_NONE, RsArgs, RsStats, make_tensor)
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "rope_sdpa.h")
@@ -158,13 +158,13 @@ def test_int8_flag_limits():
     c = Call(dt=RS_F32, es=4)
     c.flags = RS_FLAG_QUANT_INT8_QK
     assert c.fwd() == ERR["RS_ERR_UNSUPPORTED"]
-    c = Call()
+    c = Call()  # causal and masks are valid with quantization: only the missing device stops them
     c.flags = RS_FLAG_QUANT_INT8_QK | RS_FLAG_CAUSAL
-    assert c.fwd() == ERR["RS_ERR_UNSUPPORTED"]
+    assert c.fwd() == ERR["RS_ERR_NO_DEVICE"]
     c = Call()
     _bool_mask(c, (2, 1, 1, 100), (112, 0, 0, 1))
     c.flags = RS_FLAG_QUANT_INT8_QK
-    assert c.fwd() == ERR["RS_ERR_UNSUPPORTED"]
+    assert c.fwd() == ERR["RS_ERR_NO_DEVICE"]
     c = Call()
     c.flags = RS_FLAG_QUANT_INT8_QK  # a valid int8 request: only the missing device stops it
     assert c.fwd() == ERR["RS_ERR_NO_DEVICE"]
@@ -262,11 +262,11 @@ def test_backward_validation_and_error_counter():
     st = L.rope_sdpa_bwd(ctypes.byref(a), ctypes.byref(c.o), c.lse, ctypes.byref(do), ctypes.byref(dq),
                          ctypes.byref(dk), ctypes.byref(dv), c.ws, c.ws_bytes, None)
     assert st == ERR["RS_ERR_NO_DEVICE"]
-    c.flags = RS_FLAG_QUANT_INT8_QK | RS_FLAG_CAUSAL
+    c.flags = RS_FLAG_QUANT_INT8_QK | RS_FLAG_QUANT_INT4_QK
     a = c.args()
     st = L.rope_sdpa_bwd(ctypes.byref(a), ctypes.byref(c.o), c.lse, ctypes.byref(do), ctypes.byref(dq),
                          ctypes.byref(dk), ctypes.byref(dv), c.ws, c.ws_bytes, None)
-    assert st == ERR["RS_ERR_UNSUPPORTED"]
+    assert st == ERR["RS_ERR_INVALID"]
     s = RsStats()
     L.rope_sdpa_get_stats(ctypes.byref(s))
     assert s.errors == 5 and s.bwd_calls == 0 and s.fwd_instream == 0 and s.quant_bwd == 0
