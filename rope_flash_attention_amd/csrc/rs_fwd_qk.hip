@@ -14,79 +14,129 @@
 
 namespace rs {
 
-// One row of K per D/8 consecutive threads, 8 elements (4 rotation pairs) per thread.
-template <typename TI, typename TO, bool NORM>
+// One position s per D/8 consecutive threads (8 elements, 4 rotation pairs, per thread), for a
+// group of up to kKprepHeads heads of one sample: the table row is read once for all of them
+// (one group's rows of K span all heads; re-reading the caller's pair-duplicated tables per
+// head would move more bytes than K itself), and every head's row is loaded before the first
+// is rotated.  With PACK the first head group also writes the packed (cos, sin) rows that the
+// attention kernel's Q prologue reads, and workgroup 0 clears the control words (the work of
+// pack_tables_kernel, in the same launch).  Grid: (row blocks) x (head groups) x (samples),
+// flattened; no thread divides by S or H.
+constexpr int kKprepHeads = 8;
+
+template <typename TI, typename TO, bool NORM, bool PACK, bool VEC>
 __global__ __launch_bounds__(256) void kprep_kernel(KPrepParams p) {
-  const int tpr = p.D / 8;  // threads per row (8 or 16: a row never straddles a wave)
-  const int64_t rows = (int64_t)p.B * p.H * p.S;
-  const int64_t n = rows * tpr;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    // n and the stride are multiples of tpr: the threads of a row stay in the loop together
-    const int ch = (int)(i % tpr);
-    const int64_t row = i / tpr;
-    const int s = (int)(row % p.S);
-    const int64_t bh = row / p.S;
-    const int h = (int)(bh % p.H), b = (int)(bh / p.H);
-    const TI* src = (const TI*)p.x.ptr + b * p.x.sb + h * p.x.sh + (int64_t)s * p.x.ss + ch * 8;
-    float x[8];
+  constexpr int HG = kKprepHeads;
+  const int tpr = p.D / 8, rpw = 256 / tpr;  // threads per row (8 or 16: within a wave), rows per workgroup
+  const int tid = threadIdx.x, ch = tid % tpr, r0 = tid / tpr;
+  const int nbs = (p.S + rpw - 1) / rpw, ngr = (p.H + HG - 1) / HG;
+  const int blk = blockIdx.x % nbs, t = blockIdx.x / nbs;
+  const int g = t % ngr, b = t / ngr;
+  if (PACK && blockIdx.x == 0 && tid < 2) p.pk.ctrl[tid] = 0u;
+  const int srow = blk * rpw + r0;
+  const int sc = min(srow, p.S - 1);  // rows past S: loads of a valid row, no store
+  const int h0 = g * HG, nh = min(HG, p.H - h0);
+
+  // the rows of every head of the group
+  float x[HG][8];
+  const TI* xs = (const TI*)p.x.ptr + b * p.x.sb + (int64_t)sc * p.x.ss + ch * 8;
+#pragma unroll
+  for (int j = 0; j < HG; ++j) {
+    if (j >= nh) break;
+    const TI* src = xs + (h0 + j) * p.x.sh;
     if constexpr (sizeof(TI) == 4) {
       const float4 a = *(const float4*)src, c = *(const float4*)(src + 4);
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-      x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+      x[j][0] = a.x; x[j][1] = a.y; x[j][2] = a.z; x[j][3] = a.w;
+      x[j][4] = c.x; x[j][5] = c.y; x[j][6] = c.z; x[j][7] = c.w;
     } else {
       typedef TI v8 __attribute__((ext_vector_type(8)));
       const v8 v = *(const v8*)src;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = to_f(v[e]);
+      for (int e = 0; e < 8; ++e) x[j][e] = to_f(v[e]);
     }
-    if constexpr (NORM) {
+  }
+  // the table row, once: the caller's pair-duplicated rows, even entries
+  const int tb = p.pk.Bt > 1 ? b : 0;
+  const float* cr = p.pk.cos + tb * p.pk.c_sb + (int64_t)sc * p.pk.c_ss + ch * 8;
+  const float* sr = p.pk.sin + tb * p.pk.s_sb + (int64_t)sc * p.pk.s_ss + ch * 8;
+  float cc[4], ss[4];
+  if constexpr (VEC) {  // 16-byte aligned table rows
+    const float4 c0 = *(const float4*)cr, c1 = *(const float4*)(cr + 4);
+    const float4 s0 = *(const float4*)sr, s1 = *(const float4*)(sr + 4);
+    cc[0] = c0.x; cc[1] = c0.z; cc[2] = c1.x; cc[3] = c1.z;
+    ss[0] = s0.x; ss[1] = s0.z; ss[2] = s1.x; ss[3] = s1.z;
+  } else {
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      cc[pp] = cr[2 * pp];
+      ss[pp] = sr[2 * pp];
+    }
+  }
+  if (PACK && g == 0 && b < p.pk.Bt && srow < p.S) {
+    float* pr = p.pk.out + ((int64_t)b * p.S + srow) * p.D + ch * 8;
+    *(float4*)pr = make_float4(cc[0], ss[0], cc[1], ss[1]);
+    *(float4*)(pr + 4) = make_float4(cc[2], ss[2], cc[3], ss[3]);
+  }
+
+  TO* out = (TO*)p.out + (((int64_t)b * p.H + h0) * p.S + srow) * p.D + ch * 8;
+#pragma unroll
+  for (int j = 0; j < HG; ++j) {
+    if (j >= nh) break;
+    if constexpr (NORM) {  // the tpr threads of a row share its sum of squares
       float ssq = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ssq = fmaf(x[e], x[e], ssq);
+      for (int e = 0; e < 8; ++e) ssq = fmaf(x[j][e], x[j][e], ssq);
       for (int off = tpr / 2; off >= 1; off >>= 1) ssq += __shfl_xor(ssq, off, tpr);
       const float inv = 1.f / __builtin_sqrtf(ssq * (1.f / (float)p.D) + p.eps);
       const float4 wa = *(const float4*)(p.w + ch * 8), wb = *(const float4*)(p.w + ch * 8 + 4);
       const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = x[e] * inv * wv[e];
+      for (int e = 0; e < 8; ++e) x[j][e] = x[j][e] * inv * wv[e];
     }
-    // packed table row: (cos, sin) of pair i at floats 2i, 2i + 1
-    const float* tr = p.tab.ptr + b * p.tab.sb + (int64_t)s * p.D + ch * 8;
-    const float4 t0 = *(const float4*)tr, t1 = *(const float4*)(tr + 4);
-    const float cc[4] = {t0.x, t0.z, t1.x, t1.z}, ss[4] = {t0.y, t0.w, t1.y, t1.w};
     typedef TO vo __attribute__((ext_vector_type(8)));
     vo y;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      const float2 rr = rot_pair_fma(x[2 * pp], x[2 * pp + 1], cc[pp], ss[pp]);
+      const float2 rr = rot_pair_fma(x[j][2 * pp], x[j][2 * pp + 1], cc[pp], ss[pp]);
       y[2 * pp] = from_f<TO>(rr.x);
       y[2 * pp + 1] = from_f<TO>(rr.y);
     }
-    *(vo*)((TO*)p.out + row * p.D + ch * 8) = y;
+    if (srow < p.S) *(vo*)(out + (int64_t)j * p.S * p.D) = y;
   }
 }
 
-template <typename TI, typename TO>
+template <typename TI, typename TO, bool PACK, bool VEC>
 static int launch_kprep_t(bool norm, const KPrepParams& p, void* stream) {
-  const int64_t n = (int64_t)p.B * p.H * p.S * (p.D / 8);
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 16384) blocks = 16384;
-  if (blocks < 1) blocks = 1;
+  const int rpw = 256 / (p.D / 8);
+  const int64_t blocks = (int64_t)((p.S + rpw - 1) / rpw) * ((p.H + kKprepHeads - 1) / kKprepHeads) * p.B;
+  if (blocks < 1 || blocks > 0x7fffffff) return -1;
   if (norm)
-    hipLaunchKernelGGL((kprep_kernel<TI, TO, true>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p);
+    hipLaunchKernelGGL((kprep_kernel<TI, TO, true, PACK, VEC>), dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, p);
   else
-    hipLaunchKernelGGL((kprep_kernel<TI, TO, false>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p);
+    hipLaunchKernelGGL((kprep_kernel<TI, TO, false, PACK, VEC>), dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, p);
   return (int)hipGetLastError();
+}
+
+template <typename TI, typename TO>
+static int launch_kprep_p(bool norm, const KPrepParams& p, void* stream) {
+  const PackParams& t = p.pk;
+  const bool vec = ((uintptr_t)t.cos % 16 == 0) && ((uintptr_t)t.sin % 16 == 0) && t.c_ss % 4 == 0 &&
+                   t.s_ss % 4 == 0 && t.c_sb % 4 == 0 && t.s_sb % 4 == 0;
+  if (p.pk.out)
+    return vec ? launch_kprep_t<TI, TO, true, true>(norm, p, stream) : launch_kprep_t<TI, TO, true, false>(norm, p, stream);
+  return vec ? launch_kprep_t<TI, TO, false, true>(norm, p, stream) : launch_kprep_t<TI, TO, false, false>(norm, p, stream);
 }
 
 int launch_kprep(int dtype, int qkm, const KPrepParams& p, void* stream) {
   const bool norm = (qkm & 1) != 0, f32in = (qkm & 2) != 0;
   switch (dtype) {
-    case F32: return launch_kprep_t<float, float>(norm, p, stream);
-    case F16: return f32in ? launch_kprep_t<float, _Float16>(norm, p, stream)
-                           : launch_kprep_t<_Float16, _Float16>(norm, p, stream);
-    default: return f32in ? launch_kprep_t<float, __bf16>(norm, p, stream)
-                          : launch_kprep_t<__bf16, __bf16>(norm, p, stream);
+    case F32: return launch_kprep_p<float, float>(norm, p, stream);
+    case F16: return f32in ? launch_kprep_p<float, _Float16>(norm, p, stream)
+                           : launch_kprep_p<_Float16, _Float16>(norm, p, stream);
+    default: return f32in ? launch_kprep_p<float, __bf16>(norm, p, stream)
+                          : launch_kprep_p<__bf16, __bf16>(norm, p, stream);
   }
 }
 

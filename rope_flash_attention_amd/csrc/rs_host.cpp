@@ -315,7 +315,16 @@ AttnShape attn_shape(const Shape& s) {
 }
 
 // Enqueues the preparation kernels shared by both directions.
-rs_status prepare(const rs_args* a, const Shape& s, const Layout& L, char* ws, hipStream_t stream) {
+Opnd opnd(const rs_tensor* t) {
+  Opnd o;
+  o.ptr = t->data;
+  o.sb = t->stride[0];
+  o.sh = t->stride[1];
+  o.ss = t->stride[2];
+  return o;
+}
+
+PackParams pack_params(const rs_args* a, const Shape& s, const Layout& L, char* ws) {
   PackParams pp{};  // (no tables, Bt = 0: the launch only clears the control words)
   if (s.rope) {
     pp.cos = (const float*)a->cos->data;
@@ -330,7 +339,29 @@ rs_status prepare(const rs_args* a, const Shape& s, const Layout& L, char* ws, h
   pp.S = (int)s.S;
   pp.D = (int)s.D;
   pp.ctrl = (unsigned*)(ws + L.ctrl);
-  if (launch_pack_tables(pp, stream) != 0) return RS_ERR_LAUNCH;
+  return pp;
+}
+
+// K' = R(K) (RMS-normalized first when the Q/K prologue asks for it) into the workspace, in
+// the same launch as the table packing and the clearing of the control words.
+rs_status launch_kprep_packed(const rs_args* a, const Shape& s, const Layout& L, char* ws, hipStream_t stream) {
+  KPrepParams kp{};
+  kp.x = opnd(a->k);
+  kp.out = ws + L.kprep;
+  kp.pk = pack_params(a, s, L, ws);
+  kp.w = a->k_norm_weight;
+  kp.eps = a->norm_eps;
+  kp.B = (int)s.B;
+  kp.H = (int)s.Hkv;
+  kp.S = (int)s.S;
+  kp.D = (int)s.D;
+  return launch_kprep(s.dtype, s.qkm, kp, stream) != 0 ? RS_ERR_LAUNCH : RS_OK;
+}
+
+// Table packing (unless a K preparation launch already did it) and bool-mask classification.
+rs_status prepare(const rs_args* a, const Shape& s, const Layout& L, char* ws, hipStream_t stream,
+                  bool pack = true) {
+  if (pack && launch_pack_tables(pack_params(a, s, L, ws), stream) != 0) return RS_ERR_LAUNCH;
   if (a->mask_kind == RS_MASK_BOOL) {
     ClassifyParams cp{};
     cp.mask = mask_view(a, s, L, ws);
@@ -346,14 +377,6 @@ rs_status prepare(const rs_args* a, const Shape& s, const Layout& L, char* ws, h
   return RS_OK;
 }
 
-Opnd opnd(const rs_tensor* t) {
-  Opnd o;
-  o.ptr = t->data;
-  o.sb = t->stride[0];
-  o.sh = t->stride[1];
-  o.ss = t->stride[2];
-  return o;
-}
 
 // 0 none; 1 quantized in the attention kernel, 2 codes from the quantizer pass; + 4 for int4
 int int8_mode(uint32_t flags) {
@@ -466,7 +489,10 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
 
   char* w = (char*)ws;
   hipStream_t strm = (hipStream_t)stream;
-  if ((st = prepare(a, s, L, w, strm)) != RS_OK) return fail(st);
+  // K prepared once into the workspace (with the tables packed in the same launch), then read
+  // as K' by the attention kernel
+  if (s.kprep && (st = launch_kprep_packed(a, s, L, w, strm)) != RS_OK) return fail(st);
+  if ((st = prepare(a, s, L, w, strm, !s.kprep)) != RS_OK) return fail(st);
   if ((int8 & 3) == 2 && launch_quant_int8(s.dtype, quant_params(a, s, L, w), strm) != 0) return fail(RS_ERR_LAUNCH);
   FwdParams p{};
   p.q = opnd(a->q);
@@ -502,18 +528,7 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
   p.qnw = a->q_norm_weight;
   p.knw = a->k_norm_weight;
   p.norm_eps = a->norm_eps;
-  if (s.kprep) {  // K prepared once into the workspace, then read as K' by the attention kernel
-    KPrepParams kp{};
-    kp.x = p.k;
-    kp.out = w + L.kprep;
-    kp.tab = p.tab;
-    kp.w = a->k_norm_weight;
-    kp.eps = a->norm_eps;
-    kp.B = (int)s.B;
-    kp.H = (int)s.Hkv;
-    kp.S = (int)s.S;
-    kp.D = (int)s.D;
-    if (launch_kprep(s.dtype, s.qkm, kp, strm) != 0) return fail(RS_ERR_LAUNCH);
+  if (s.kprep) {
     p.k.ptr = w + L.kprep;
     p.k.sb = s.Hkv * s.S * s.D;
     p.k.sh = s.S * s.D;
@@ -607,7 +622,12 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
 
   char* w = (char*)ws;
   hipStream_t strm = (hipStream_t)stream;
-  if ((st = prepare(a, s, L, w, strm)) != RS_OK) return fail(st);
+  // 16-bit at D = 128: K' = R(K) once into the workspace (the dQ kernel then streams K' tiles
+  // with no table), in the launch that packs the tables; quantized: the dequantized Q' and K'
+  // the forward attended with, by the quantizer pass (after the table packing)
+  const bool kprep = s.dtype != F32 && s.D == 128 && !quant;
+  if (kprep && (st = launch_kprep_packed(a, s, L, w, strm)) != RS_OK) return fail(st);
+  if ((st = prepare(a, s, L, w, strm, !kprep)) != RS_OK) return fail(st);
   BwdParams p{};
   p.q = opnd(a->q);
   p.k = opnd(a->k);
@@ -636,8 +656,6 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
   int pre = 0;
   if (s.dtype != F32 && s.D == 128) {
-    // K' = R(K) once into the workspace (the dQ kernel then streams K' tiles with no table);
-    // quantized: the dequantized Q' and K' the forward attended with, by the quantizer pass
     if (quant) {
       QuantParams qp = quant_params(a, s, L, w);
       qp.nblk = (int)((s.S + 63) / 64);
@@ -646,15 +664,6 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
       if (launch_quant_int8(s.dtype, qp, strm) != 0) return fail(RS_ERR_LAUNCH);
       pre = 3;
     } else {
-      KPrepParams kp{};
-      kp.x = p.k;
-      kp.out = w + L.kprep;
-      kp.tab = p.tab;
-      kp.B = (int)s.B;
-      kp.H = (int)s.Hkv;
-      kp.S = (int)s.S;
-      kp.D = (int)s.D;
-      if (launch_kprep(s.dtype, 0, kp, strm) != 0) return fail(RS_ERR_LAUNCH);
       pre = 1;
     }
     p.k.ptr = w + L.kprep;

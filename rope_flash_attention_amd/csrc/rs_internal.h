@@ -178,7 +178,9 @@ int launch_quant_int8(int dtype, const QuantParams& p, void* stream);
 struct KPrepParams {
   Opnd x;
   void* out;
-  Table tab;
+  // the caller's tables (cos, sin, strides, Bt: always read); out and ctrl set: the launch
+  // also writes the packed tables and clears the control words (pack_tables_kernel's work)
+  PackParams pk;
   const float* w;  // RMSNorm weights [D] (normalizing launches only)
   float eps;
   int B, H, S, D;

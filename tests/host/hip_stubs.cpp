@@ -112,7 +112,11 @@ int launch_kprep(int dtype, int qkm, const KPrepParams& p, void*) {
   ++stub::launches;
   const size_t es = dtype == F32 ? 4 : 2;
   stub::need(p.out, (size_t)p.B * p.H * p.S * p.D * es, "prepared K");
-  stub::need(p.tab.ptr, (size_t)(p.tab.sb ? p.B : 1) * p.S * p.D * sizeof(float), "packed tables");
+  if (!p.pk.cos || !p.pk.sin || p.pk.Bt < 1 || p.pk.S != p.S || p.pk.D != p.D) std::abort();
+  if (p.pk.out) {  // with the table packing
+    stub::need(p.pk.out, (size_t)p.pk.Bt * p.S * p.D * sizeof(float), "packed tables");
+    stub::need(p.pk.ctrl, 2 * sizeof(unsigned), "control words");
+  }
   if ((qkm & 1) != (p.w != nullptr)) std::abort();
   if ((qkm & 2) && dtype == F32) std::abort();
   if (p.D != 64 && p.D != 128) std::abort();
