@@ -10,14 +10,14 @@
  *
  * with M from a bool mask (True = attend) or an additive float mask, broadcast over up to
  * four dimensions (same page, section "Enable In SimpleTuner"), or a causal (top-left,
- * key j > query i excluded) pattern.  The forward rotates Q inside the attention kernel, in
- * registers, and never writes Q'.  K is rotated once per (batch, K/V head) into the caller's
- * workspace (K' = R(K) rounded to the input dtype, [B, Hkv, S, D]) for bf16/f16 without
- * quantization or additive mask, so that the attention kernel's key loop reads no table;
- * otherwise (fp32, additive masks, the quantized forward) K is rotated in the key loop and
- * no rotated copy is written (the quantized pre-pass mode writes codes instead).  The backward
- * (16-bit inputs at D = 128) leaves Q' (written by its dQ kernel) and K' (by a rotation pass)
- * in the workspace; at D = 64 and in fp32 it rotates both inside its kernels.  The backward
+ * key j > query i excluded) pattern.  The forward rotates Q and K inside the attention kernel,
+ * in registers, on their way from HBM: by default it writes no rotated copy of Q or K to
+ * memory.  Two exceptions, both opt-in or forced by the inputs: RS_FLAG_K_PREPASS and the Q/K
+ * prologue (RMS-normalized or fp32 Q/K) rotate K once per (batch, K/V head) into the caller's
+ * workspace (K' = R(K) rounded to the input dtype, [B, Hkv, S, D]), and the quantized
+ * pre-pass mode writes codes.  The backward (16-bit inputs at D = 128) leaves Q' (written by
+ * its dQ kernel) and K' (by a rotation pass) in the workspace; at D = 64 and in fp32 it
+ * rotates both inside its kernels.  The backward
  * returns gradients with respect to the unrotated Q and K (the inverse rotation, i.e. the
  * same rotation with sin negated, applied to dQ' and dK'), and V.
  *
@@ -79,7 +79,8 @@ enum {
   RS_FLAG_CAUSAL = 1u << 0,          /* exclude key j > query i; cannot be combined with a mask */
   RS_FLAG_QUANT_INT8_QK = 1u << 1,   /* forward only: blockwise int8 Q'/K' (see rope_sdpa_fwd) */
   RS_FLAG_QUANT_INT8_PREPASS = 1u << 2, /* with either QUANT flag: codes from a quantizer pass */
-  RS_FLAG_QUANT_INT4_QK = 1u << 3    /* as RS_FLAG_QUANT_INT8_QK with int4 codes (not both flags) */
+  RS_FLAG_QUANT_INT4_QK = 1u << 3,   /* as RS_FLAG_QUANT_INT8_QK with int4 codes (not both flags) */
+  RS_FLAG_K_PREPASS = 1u << 4        /* forward: K rotated by a pass of its own (see rope_sdpa_fwd) */
 };
 
 typedef struct {
@@ -133,9 +134,9 @@ typedef struct {
 } rs_args;
 
 /* Bytes of device workspace a call needs (0 only for an empty call, B, H or S = 0; otherwise
- * the rotation tables are repacked into it, and a bf16/f16 forward without int8 or additive
- * mask also holds K' = R(K): B * Hkv * S * D elements of the dtype of v).  `backward` = 0 for
- * rope_sdpa_fwd, 1 for rope_sdpa_bwd. */
+ * the rotation tables are repacked into it, and a forward with RS_FLAG_K_PREPASS or the Q/K
+ * prologue, and the 16-bit backward at D = 128, also hold K' = R(K): B * Hkv * S * D elements
+ * of the dtype of v).  `backward` = 0 for rope_sdpa_fwd, 1 for rope_sdpa_bwd. */
 rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* bytes);
 
 /*
@@ -143,10 +144,12 @@ rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* by
  * the natural-log row normaliser lse[b][h][i] = log(sum_j exp(scale q'_i.k'_j + m_ij)) into a
  * contiguous fp32 [B, H, S] buffer (-inf for a row with no valid key); lse is what
  * rope_sdpa_bwd needs.  An all-true bool mask is detected on the device and then costs no
- * per-element mask reads.  bf16/f16 without int8 or additive mask: K is rotated once (per
- * batch item and K/V head) into the workspace by a pass of its own and Q inside the attention
- * kernel, each product and sum in fp32 and the result rounded to the input dtype; the
- * attention kernel then reads K' with no table in its key loop.
+ * per-element mask reads.
+ * RS_FLAG_K_PREPASS (bf16/f16, rotating, no quantization, no additive mask; else
+ * RS_ERR_UNSUPPORTED): K is rotated once per (batch, K/V head) into the workspace by a pass of
+ * its own, with the arithmetic of the in-kernel rotation, and the attention kernel reads K'
+ * with no table in its key loop: the same results bit for bit, faster at long sequences,
+ * for 2 * B * Hkv * S * D elements more HBM traffic (K' written and read back).
  * RS_FLAG_QUANT_INT8_QK (bf16/f16 inputs; any mask kind or causal; lse may be NULL): after the
  * fp32 rotation (each product and sum rounded), Q' and K' are quantized per (b, h, 64-token
  * block) to int8 codes round-half-even(x * fp32(127/amax)) with scale amax/127, QK^T runs on
@@ -173,10 +176,10 @@ rs_status rope_sdpa_fwd(const rs_args* args, const rs_tensor* o, float* lse,
  * workspace: the library keeps a device scratch array of rope_sdpa_noalloc_scratch_bytes()
  * bytes (64 MiB) per device, held from the first call on that device until the process ends,
  * and this call allocates nothing (no hipMalloc, no allocating library routine).  A call whose
- * workspace would exceed that size leaves K' out of the scratch where it can (K is then
- * rotated inside the attention kernel, with the same arithmetic: the same results bit for
- * bit); a call that still does not fit, or that needs K' (normalized or fp32 Q/K), returns
- * RS_ERR_SCRATCH and launches nothing.  The caller
+ * workspace would exceed that size leaves K' out of the scratch where it can
+ * (RS_FLAG_K_PREPASS is then ignored: the same results bit for bit); a call that still does
+ * not fit, or that needs K' (normalized or fp32 Q/K), returns RS_ERR_SCRATCH and launches
+ * nothing.  The caller
  * still owns and passes inputs, o and lse.  Every call on one device shares that device's
  * scratch: calls that overlap on one device (enqueued on different streams without ordering
  * between them, or from several threads onto unordered streams) race and give undefined
@@ -252,6 +255,15 @@ typedef struct {
   uint64_t errors;             /* calls rejected with a negative status */
   uint64_t quant_bwd;          /* quantized backward calls (the quantized autograd path) */
 } rs_stats;
+
+/* Measurement support (single device): while enabled, every rope_sdpa_fwd call records a pair
+ * of HIP events on its stream right before its attention kernel and right after it (not
+ * around the K preparation or merge launches), so that a benchmark can time that kernel
+ * alone on the stream it runs on.  Enabling (or disabling) forgets the pairs recorded so far.
+ * rope_sdpa_debug_kernel_time waits for the recorded pairs and returns the sum of their
+ * elapsed times in milliseconds and their number.  rope_sdpa_fwd_noalloc records nothing. */
+rs_status rope_sdpa_debug_kernel_timing(int enable);
+rs_status rope_sdpa_debug_kernel_time(double* total_ms, uint64_t* launches);
 
 void rope_sdpa_get_stats(rs_stats* out);
 void rope_sdpa_reset_stats(void);

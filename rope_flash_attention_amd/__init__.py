@@ -28,7 +28,7 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import (RS_BF16, RS_BOOL, RS_F16, RS_F32, RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT4_QK,
+from ._abi import (RS_BF16, RS_BOOL, RS_F16, RS_F32, RS_FLAG_CAUSAL, RS_FLAG_K_PREPASS, RS_FLAG_QUANT_INT4_QK,
                    RS_FLAG_QUANT_INT8_PREPASS, RS_FLAG_QUANT_INT8_QK, RS_MASK_ADDITIVE, RS_MASK_BOOL, RS_MASK_NONE,
                    RsArgs, RsStats, make_tensor)
 
@@ -42,7 +42,7 @@ __all__ = [
     "rope_sdpa_get_stats", "rope_sdpa_reset_stats", "rope_sdpa_abi_version", "rope_sdpa_status_string",
     "get_dispatch_stats", "RopeSdpaError", "library_path", "rope_sdpa_debug_quantize_qk", "debug_quantize_qk",
     "rope_sdpa_fwd_noalloc", "rope_sdpa_noalloc_scratch_bytes", "rope_sdpa_rotate", "rope_rotate",
-    "scaled_dot_product_attention",
+    "scaled_dot_product_attention", "rope_sdpa_debug_kernel_timing", "rope_sdpa_debug_kernel_time",
 ]
 
 _DT = {torch.float32: RS_F32, torch.float16: RS_F16, torch.bfloat16: RS_BF16, torch.bool: RS_BOOL}
@@ -111,7 +111,7 @@ def _mask4(mask: torch.Tensor | None, qdtype):
 class _Call:
     """Holds the ctypes descriptors of one call (kept alive for the duration of the call)."""
 
-    def __init__(self, q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant=None, norm=None):
+    def __init__(self, q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant=None, norm=None, k_prepass=False):
         self.tq, self.tk, self.tv = _desc(q), _desc(k), _desc(v)
         self.tc = _desc(cos4) if cos4 is not None else None  # no tables: plain attention
         self.ts = _desc(sin4) if sin4 is not None else None
@@ -122,7 +122,7 @@ class _Call:
         a.sin = ctypes.pointer(self.ts) if self.ts is not None else None
         a.mask = ctypes.pointer(self.tm) if self.tm is not None else None
         a.mask_kind = mask_kind
-        a.flags = (RS_FLAG_CAUSAL if causal else 0) | _QUANT_FLAGS[quant]
+        a.flags = (RS_FLAG_CAUSAL if causal else 0) | _QUANT_FLAGS[quant] | (RS_FLAG_K_PREPASS if k_prepass else 0)
         a.scale = 0.0 if scale is None else float(scale)
         if norm is not None:  # (q weights, k weights, eps): fp32 [D] device tensors
             self.norm = norm
@@ -140,9 +140,9 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _forward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, need_lse, quant=None, norm=None):
+def _forward(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, need_lse, quant=None, norm=None, k_prepass=False):
     lib = _abi.load()
-    call = _Call(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant, norm)
+    call = _Call(q, k, v, cos4, sin4, mask, mask_kind, causal, scale, quant, norm, k_prepass)
     B, H, S, D = q.shape
     o = torch.empty((B, H, S, D), dtype=v.dtype, device=q.device)  # the compute dtype
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if need_lse else None
@@ -212,7 +212,7 @@ def _check_dtypes(query, key, value):
 
 def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, attn_mask=None, is_causal=False,
                                       scale=None, quantization=None, q_norm_weight=None, k_norm_weight=None,
-                                      norm_eps=1e-6):
+                                      norm_eps=1e-6, k_prepass=False):
     """softmax(scale * R(Q) R(K)^T + mask) V with R the interleaved-pair rotation of the tables.
 
     quantization: None, "int8" for the blockwise int8 Q'/K' forward quantized in the attention
@@ -225,6 +225,9 @@ def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, att
     over the head dimension, x / sqrt(mean(x^2) + norm_eps) * w in fp32, before the rotation.
     fp32 query/key with fp16/bf16 value are read in fp32 and rounded to value's dtype after the
     rotation; the output has value's dtype.  Both are forward only (no gradient).
+
+    k_prepass: rotate K once per (batch, K/V head) by a pass of its own instead of in the
+    attention kernel's key loop (RS_FLAG_K_PREPASS: bit-identical results, K' goes through HBM).
     """
     if not (query.is_cuda and key.is_cuda and value.is_cuda):
         raise ValueError("query, key and value must be device tensors")
@@ -247,17 +250,19 @@ def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, att
                         quant=quantization, norm=norm)[0]
     if needs_grad:
         return _RopeSdpaFn.apply(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale)
-    return _forward(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale, need_lse=False)[0]
+    return _forward(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale, need_lse=False,
+                    k_prepass=k_prepass)[0]
 
 
 def rope_sdpa_fwd_with_lse(query, key, value, rope_cos, rope_sin, attn_mask=None, is_causal=False, scale=None,
-                           quantization=None, q_norm_weight=None, k_norm_weight=None, norm_eps=1e-6):
+                           quantization=None, q_norm_weight=None, k_norm_weight=None, norm_eps=1e-6,
+                           k_prepass=False):
     """Forward returning (O, LSE) without autograd (LSE is fp32 [B, H, S], natural log)."""
     _check_dtypes(query, key, value)
     mask, kind = _mask4(attn_mask, value.dtype)
     return _forward(query, key, value, _tables4(rope_cos, query.device), _tables4(rope_sin, query.device),
                     mask, kind, bool(is_causal), scale, need_lse=True, quant=quantization,
-                    norm=_norm_args(query, q_norm_weight, k_norm_weight, norm_eps))
+                    norm=_norm_args(query, q_norm_weight, k_norm_weight, norm_eps), k_prepass=k_prepass)
 
 
 def rope_rotate(x, rope_cos, rope_sin, out=None):
@@ -356,6 +361,18 @@ def rope_sdpa_get_stats() -> dict:
 
 def rope_sdpa_reset_stats() -> None:
     _abi.load().rope_sdpa_reset_stats()
+
+
+def rope_sdpa_debug_kernel_timing(enable: bool) -> None:
+    """Measurement: record HIP events around each forward's attention kernel (see the header)."""
+    _check(_abi.load().rope_sdpa_debug_kernel_timing(int(bool(enable))))
+
+
+def rope_sdpa_debug_kernel_time():
+    """(total milliseconds, launches) of the attention kernels timed since timing was enabled."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_uint64(0)
+    _check(_abi.load().rope_sdpa_debug_kernel_time(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def rope_sdpa_abi_version() -> int:

@@ -16,11 +16,13 @@ STATUS_NAMES = {
 RS_F32, RS_F16, RS_BF16, RS_BOOL = 0, 1, 2, 3
 RS_MASK_NONE, RS_MASK_BOOL, RS_MASK_ADDITIVE = 0, 1, 2
 RS_FLAG_CAUSAL, RS_FLAG_QUANT_INT8_QK, RS_FLAG_QUANT_INT8_PREPASS, RS_FLAG_QUANT_INT4_QK = 1, 2, 4, 8
+RS_FLAG_K_PREPASS = 16
 
 # Every symbol include/rope_sdpa.h declares.
 EXPORTED = (
     "rope_sdpa_workspace_size", "rope_sdpa_fwd", "rope_sdpa_bwd", "rope_sdpa_status_string",
     "rope_sdpa_get_stats", "rope_sdpa_reset_stats", "rope_sdpa_abi_version", "rope_sdpa_debug_quantize_qk",
+    "rope_sdpa_debug_kernel_timing", "rope_sdpa_debug_kernel_time",
     "rope_sdpa_fwd_noalloc", "rope_sdpa_noalloc_scratch_bytes", "rope_sdpa_rotate",
 )
 
@@ -99,6 +101,10 @@ def load(path: str = LIB_PATH):
     lib.rope_sdpa_debug_quantize_qk.argtypes = [P(RsArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.rope_sdpa_debug_quantize_qk.restype = ctypes.c_int
+    lib.rope_sdpa_debug_kernel_timing.argtypes = [ctypes.c_int]
+    lib.rope_sdpa_debug_kernel_timing.restype = ctypes.c_int
+    lib.rope_sdpa_debug_kernel_time.argtypes = [P(ctypes.c_double), P(ctypes.c_uint64)]
+    lib.rope_sdpa_debug_kernel_time.restype = ctypes.c_int
     lib.rope_sdpa_abi_version.argtypes = []
     lib.rope_sdpa_abi_version.restype = ctypes.c_int
     _lib = lib

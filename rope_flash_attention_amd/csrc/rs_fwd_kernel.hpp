@@ -1062,6 +1062,7 @@ static int launch_fwd_t(const FwdParams& p, void* stream) {
   const int grid = p.split_iters > 0 ? p.split_full + p.split_grid
                    : CAUSAL        ? (p.num_qt + 1) / 2 * p.shp.H * p.shp.B
                                    : p.num_qt * p.shp.H * p.shp.B;
+  if (p.ev_start) (void)hipEventRecord((hipEvent_t)p.ev_start, (hipStream_t)stream);
   if constexpr (MASK == MASK_BOOL) {
     // an all-true bool mask runs the unmasked kernel (same schedule, same slots): decided on
     // the device by the gate word, with no host synchronisation
@@ -1077,6 +1078,7 @@ static int launch_fwd_t(const FwdParams& p, void* stream) {
     hipLaunchKernelGGL((fwd_kernel<T, D, MASK, CAUSAL, QI8, ROPE, QEXP, QKM>), dim3(grid), dim3(FwdCfg<T>::NT), 0,
                        (hipStream_t)stream, p);
   }
+  if (p.ev_stop) (void)hipEventRecord((hipEvent_t)p.ev_stop, (hipStream_t)stream);
   if (p.split_iters > 0) {
     const int cut = p.num_qt * p.shp.H * p.shp.B - p.split_full;
     hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3(cut * (FwdCfg<T>::BM / 32)), dim3(256), 0,

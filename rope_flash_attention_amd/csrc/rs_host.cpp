@@ -7,6 +7,8 @@
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "../../include/rope_sdpa.h"
 #include "rs_internal.h"
@@ -24,6 +26,34 @@ struct Counters {
       masked_additive{0}, causal{0}, quant_int8{0}, quant_bwd{0}, errors{0};
 };
 Counters g_ctr;
+
+// Kernel timing for measurement (rope_sdpa_debug_kernel_timing): one pair of HIP events per
+// timed forward call, recorded around its attention kernel.
+struct KernelTiming {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  size_t used = 0;
+} g_timing;
+
+// The next event pair for a forward call (null when timing is off or events cannot be made).
+bool timing_events(void** start, void** stop) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (!g_timing.on) return false;
+  if (g_timing.used == g_timing.ev.size()) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipEventCreate(&a) != hipSuccess) return false;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return false;
+    }
+    g_timing.ev.emplace_back(a, b);
+  }
+  *start = g_timing.ev[g_timing.used].first;
+  *stop = g_timing.ev[g_timing.used].second;
+  ++g_timing.used;
+  return true;
+}
 
 rs_status fail(rs_status s) {
   g_ctr.errors.fetch_add(1, std::memory_order_relaxed);
@@ -148,7 +178,8 @@ rs_status validate_args(const rs_args* a, Shape* out) {
     s.Bt = 0;  // no packed tables
   }
 
-  if (a->flags & ~(uint32_t)(RS_FLAG_CAUSAL | kQuantFlags | RS_FLAG_QUANT_INT8_PREPASS)) return RS_ERR_INVALID;
+  if (a->flags & ~(uint32_t)(RS_FLAG_CAUSAL | kQuantFlags | RS_FLAG_QUANT_INT8_PREPASS | RS_FLAG_K_PREPASS))
+    return RS_ERR_INVALID;
   if ((a->flags & kQuantFlags) == kQuantFlags) return RS_ERR_INVALID;  // int8 or int4, not both
   if ((a->flags & RS_FLAG_QUANT_INT8_PREPASS) && !(a->flags & kQuantFlags)) return RS_ERR_INVALID;
   const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
@@ -197,10 +228,14 @@ rs_status validate_args(const rs_args* a, Shape* out) {
     // grid limits of the tile classifier (y: query tiles, z: mask batch x heads)
     if ((s.mQ + kMaskTile - 1) / kMaskTile > 65535 || s.mB * s.mH > 65535) return RS_ERR_SHAPE;
   }
-  // The 16-bit rotating forward (no int8, no additive mask) rotates K once into the
-  // workspace and keeps tables out of its key loop; the Q/K prologue always does.
-  s.kprep = s.qkm != 0 || (s.rope && dt != RS_F32 && !(a->flags & kQuantFlags) &&
-                           a->mask_kind != RS_MASK_ADDITIVE);
+  // K rotated once into the workspace by a pass of its own (kprep_kernel) instead of in the
+  // attention kernel's key loop: on request (RS_FLAG_K_PREPASS: the 16-bit rotating forward
+  // without quantization or additive mask), and always for the Q/K prologue
+  if (a->flags & RS_FLAG_K_PREPASS) {
+    if (!s.rope || dt == RS_F32 || (a->flags & kQuantFlags) || a->mask_kind == RS_MASK_ADDITIVE)
+      return RS_ERR_UNSUPPORTED;
+  }
+  s.kprep = s.qkm != 0 || (a->flags & RS_FLAG_K_PREPASS) != 0;
   *out = s;
   return RS_OK;
 }
@@ -421,6 +456,29 @@ extern "C" {
 
 int rope_sdpa_abi_version(void) { return ROPE_SDPA_ABI_VERSION; }
 
+rs_status rope_sdpa_debug_kernel_timing(int enable) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = enable != 0;
+  g_timing.used = 0;
+  return RS_OK;
+}
+
+rs_status rope_sdpa_debug_kernel_time(double* total_ms, uint64_t* launches) {
+  if (!total_ms || !launches) return fail(RS_ERR_NULL);
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  double t = 0.0;
+  for (size_t i = 0; i < g_timing.used; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_timing.ev[i].second) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timing.ev[i].first, g_timing.ev[i].second) != hipSuccess)
+      return fail(RS_ERR_LAUNCH);
+    t += ms;
+  }
+  *total_ms = t;
+  *launches = g_timing.used;
+  return RS_OK;
+}
+
 const char* rope_sdpa_status_string(rs_status st) {
   switch (st) {
     case RS_OK: return "RS_OK: success";
@@ -528,6 +586,7 @@ rs_status fwd_impl(const rs_args* a, const rs_tensor* o, float* lse, void* ws, s
   p.qnw = a->q_norm_weight;
   p.knw = a->k_norm_weight;
   p.norm_eps = a->norm_eps;
+  if (!scratch) timing_events(&p.ev_start, &p.ev_stop);
   if (s.kprep) {
     p.k.ptr = w + L.kprep;
     p.k.sb = s.Hkv * s.S * s.D;

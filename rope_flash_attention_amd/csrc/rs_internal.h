@@ -76,6 +76,10 @@ struct FwdParams {
   int8_t* xk_codes;
   float* xq_scales;
   float* xk_scales;
+  // measurement only: HIP events recorded on the launch stream right before the attention
+  // kernel and right after it (before the merge launch); null: none
+  void* ev_start;
+  void* ev_stop;
   // Q/K RMSNorm weights (fp32 [D], device; used when the launch asks for the normalization)
   const float* qnw;
   const float* knw;

@@ -233,6 +233,40 @@ int main() {
     CHECK(rope_sdpa_rotate(&e.q, &e.cos, &e.sin, &e.o, nullptr) == RS_ERR_SHAPE, "rotate D = 96");
     CHECK(stub::launches == before + 2, "rotate launched on error");
   }
+  // K rotated by a pass of its own (RS_FLAG_K_PREPASS): 16-bit, rotating, no quantization, no
+  // additive mask
+  for (int dt : {RS_F16, RS_BF16})
+    for (int variant = 0; variant < 4; ++variant) {
+      Case c(dt, 2, 6, 300, variant == 3 ? 64 : 128, variant == 3 ? 2 : 1, variant == 3 ? 3 : 6);
+      c.a.flags = RS_FLAG_K_PREPASS;
+      if (variant == 1) c.a.flags |= RS_FLAG_CAUSAL;
+      if (variant == 2) c.set_mask(RS_MASK_BOOL, RS_BOOL, 2, 1, 1, 300);
+      CHECK(run(c, false) == RS_OK, "K pre-pass dt=%d variant=%d", dt, variant);
+    }
+  { Case c(RS_F32, 1, 2, 128, 64); c.a.flags = RS_FLAG_K_PREPASS; expect_error(c, false, RS_ERR_UNSUPPORTED, "K pre-pass fp32"); }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_K_PREPASS | RS_FLAG_QUANT_INT8_QK;
+    expect_error(c, false, RS_ERR_UNSUPPORTED, "K pre-pass int8"); }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_K_PREPASS; c.set_mask(RS_MASK_ADDITIVE, RS_F32, 1, 1, 1, 128);
+    expect_error(c, false, RS_ERR_UNSUPPORTED, "K pre-pass additive"); }
+  { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_K_PREPASS; c.a.cos = c.a.sin = nullptr;
+    expect_error(c, false, RS_ERR_UNSUPPORTED, "K pre-pass without tables"); }
+  // kernel timing for measurement: one event pair per timed forward call
+  {
+    CHECK(rope_sdpa_debug_kernel_timing(1) == RS_OK, "timing on");
+    for (int i = 0; i < 3; ++i) {
+      Case c(RS_BF16, 1, 2, 300, 128);
+      CHECK(run(c, false) == RS_OK, "timed forward");
+    }
+    double ms = -1.0;
+    uint64_t n = 0;
+    CHECK(rope_sdpa_debug_kernel_time(&ms, &n) == RS_OK && n == 3 && ms == 0.75, "timing read: %llu calls, %g ms",
+          (unsigned long long)n, ms);
+    CHECK(rope_sdpa_debug_kernel_time(nullptr, &n) == RS_ERR_NULL, "timing read NULL");
+    CHECK(rope_sdpa_debug_kernel_timing(0) == RS_OK, "timing off");
+    Case c(RS_BF16, 1, 2, 300, 128);
+    CHECK(run(c, false) == RS_OK, "untimed forward");
+    CHECK(rope_sdpa_debug_kernel_time(&ms, &n) == RS_OK && n == 0, "timing off: no pairs");
+  }
   // empty calls: no workspace, nothing launched, data pointers may be NULL
   for (int e = 0; e < 3; ++e) {
     Case c(RS_BF16, e == 0 ? 0 : 2, e == 1 ? 0 : 3, e == 2 ? 0 : 64, 64);

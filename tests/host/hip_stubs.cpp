@@ -41,6 +41,20 @@ hipError_t hipGetDevicePropertiesR0600(hipDeviceProp_tR0600* prop, int) {
   return hipSuccess;
 }
 hipError_t hipDeviceSynchronize(void) { return hipSuccess; }
+// events: fake handles, never dereferenced by the host code
+hipError_t hipEventCreate(hipEvent_t* e) {
+  static uintptr_t next = 0x1000;
+  next += 16;
+  *e = (hipEvent_t)next;
+  return hipSuccess;
+}
+hipError_t hipEventDestroy(hipEvent_t) { return hipSuccess; }
+hipError_t hipEventSynchronize(hipEvent_t e) { return e ? hipSuccess : hipErrorInvalidValue; }
+hipError_t hipEventElapsedTime(float* ms, hipEvent_t a, hipEvent_t b) {
+  if (!a || !b || a == b) return hipErrorInvalidValue;
+  *ms = 0.25f;
+  return hipSuccess;
+}
 }
 
 namespace rs {

@@ -13,7 +13,7 @@ import pytest
 
 from rope_flash_attention_amd import _abi
 from rope_flash_attention_amd._abi import (RS_BF16, RS_BOOL, RS_F16, RS_F32, RS_FLAG_CAUSAL,
-                                           RS_FLAG_QUANT_INT8_QK, RS_FLAG_QUANT_INT4_QK, RS_MASK_ADDITIVE, RS_MASK_BOOL,
+                                           RS_FLAG_QUANT_INT8_QK, RS_FLAG_QUANT_INT4_QK, RS_FLAG_K_PREPASS, RS_MASK_ADDITIVE, RS_MASK_BOOL,
                                            RS_MASK_NONE, RsArgs, RsStats, make_tensor)
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "rope_sdpa.h")
@@ -172,15 +172,16 @@ def test_int8_flag_limits():
 
 def test_int8_workspace_holds_no_codes():
     """The int8 forward quantizes Q' and K' inside the attention kernel: its workspace is the
-    16-bit forward's without the rotated K' the 16-bit forward prepares (no codes or scales in
-    memory)."""
+    16-bit forward's (no codes or scales in memory)."""
     c = Call(B=2, H=3, S=100, D=128)
     st, n = c.ws_size(0)
     c.flags = RS_FLAG_QUANT_INT8_QK
     st8, n8 = c.ws_size(0)
     assert st == 0 and st8 == 0
-    kprime = -(-(2 * 3 * 100 * 128 * 2) // 256) * 256
-    assert n8 == n - kprime
+    assert n8 == n
+    c.flags = RS_FLAG_K_PREPASS  # K rotated by a pass of its own: + K' in the workspace
+    st, nk = c.ws_size(0)
+    assert st == 0 and nk == n + -(-(2 * 3 * 100 * 128 * 2) // 256) * 256
 
 
 def test_debug_quantize_validation():
@@ -220,11 +221,11 @@ def test_workspace_size_layout():
     st, n = c.ws_size(0)
     assert st == 0
     table = 100 * 128 * 4  # (cos, sin) pairs: D/2 float2 per position
-    kprime = -(-(2 * 3 * 100 * 128 * 2) // 256) * 256  # 16-bit forward: K' = R(K), rotated once
-    assert n == 256 + -(-table // 256) * 256 + kprime
+    kprime = -(-(2 * 3 * 100 * 128 * 2) // 256) * 256  # K' = R(K) or Q' = R(Q), 16-bit
+    assert n == 256 + -(-table // 256) * 256
     st, nb = c.ws_size(1)
-    # backward: + delta (fp32 per row) + Q' = R(Q) in the input dtype (16-bit, D = 128); K' too
-    assert st == 0 and nb == n + -(-(2 * 3 * 100 * 4) // 256) * 256 + -(-(2 * 3 * 100 * 128 * 2) // 256) * 256
+    # backward (16-bit, D = 128): + delta (fp32 per row) + Q' + K', both in the input dtype
+    assert st == 0 and nb == n + -(-(2 * 3 * 100 * 4) // 256) * 256 + 2 * kprime
     f = Call(B=2, H=3, S=100, D=128, dt=RS_F32, es=4)
     st, nf = f.ws_size(0)
     st2, nfb = f.ws_size(1)
@@ -236,7 +237,7 @@ def test_workspace_size_layout():
     c.sin.size[0] = 2
     c.mask, c.kind = None, RS_MASK_NONE
     st, n2 = c.ws_size(0)
-    assert st == 0 and n2 == 256 + -(-(2 * table) // 256) * 256 + kprime
+    assert st == 0 and n2 == 256 + -(-(2 * table) // 256) * 256
 
 
 def test_backward_validation_and_error_counter():

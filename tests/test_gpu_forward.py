@@ -154,6 +154,32 @@ def test_causal_matches_explicit_tril_mask(dtype):
     assert torch.allclose(oc.float(), ot.float(), atol=1e-6, rtol=0)
 
 
+@pytest.mark.parametrize("case", ["flux_b1", "flux_b2_bool", "causal", "gqa_per_sample", "d64_f16", "ragged"])
+def test_k_prepass_is_bitwise_the_in_kernel_rotation(case):
+    """RS_FLAG_K_PREPASS rotates K once into the workspace with the in-kernel rotation's
+    arithmetic: O and LSE equal the default call's bit for bit."""
+    if case == "flux_b1":
+        w = syn.flux(batch=1, heads=24, grid=64, dtype="bf16", seed=2000)
+    elif case == "flux_b2_bool":
+        w = syn.flux(batch=2, heads=8, grid=64, dtype="bf16", seed=3000)
+        w.mask, w.mask_kind = syn.key_padding_mask(syn.key_padding_lengths(3000, 2), 512, w.q.shape[2]), "bool"
+    elif case == "causal":
+        w = syn.causal_1axis(batch=2, heads=4, seq=1000, dim=128, dtype="bf16", seed=61)
+    elif case == "gqa_per_sample":
+        w = syn.flux(batch=2, heads=12, grid=32, dtype="bf16", seed=62, kv_heads=3, per_sample_tables=True)
+    elif case == "d64_f16":
+        w = syn.random_small(2, 3, 700, 64, "f16", seed=63)
+    else:
+        w = syn.random_small(1, 2, 77, 128, "bf16", seed=64)
+    d = dev()
+    args = [t.to(d) for t in (w.q, w.k, w.v, w.cos, w.sin)]
+    m = w.mask.to(d) if w.mask is not None else None
+    with torch.no_grad():
+        o0, l0 = rfa.rope_sdpa_fwd_with_lse(*args, attn_mask=m, is_causal=w.causal)
+        o1, l1 = rfa.rope_sdpa_fwd_with_lse(*args, attn_mask=m, is_causal=w.causal, k_prepass=True)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
 def test_forward_is_deterministic():
     w = syn.flux(batch=1, heads=4, grid=16)  # S = 512 + 256
     o1, l1 = gpu_forward(w)

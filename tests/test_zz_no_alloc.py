@@ -24,7 +24,7 @@ def _desc(t):
     return make_tensor(t.data_ptr(), _DT[t.dtype], t.shape, t.stride())
 
 
-def _run(w, noalloc, int8=False, qk=None, norm=None):
+def _run(w, noalloc, int8=False, qk=None, norm=None, k_prepass=False):
     """One forward through the C ABI on device copies of workload w (Q and K replaced by `qk`
     when given; `norm` = (q weights, k weights, eps) for the RMSNorm prologue): returns
     (O, LSE)."""
@@ -41,7 +41,7 @@ def _run(w, noalloc, int8=False, qk=None, norm=None):
     a.q, a.k, a.v, a.cos, a.sin = (ctypes.pointer(t) for t in keep)
     a.mask = ctypes.pointer(tm) if tm is not None else None
     a.mask_kind = {"none": _abi.RS_MASK_NONE, "bool": _abi.RS_MASK_BOOL, "additive": _abi.RS_MASK_ADDITIVE}[w.mask_kind]
-    a.flags = RS_FLAG_QUANT_INT8_QK if int8 else 0
+    a.flags = (RS_FLAG_QUANT_INT8_QK if int8 else 0) | (_abi.RS_FLAG_K_PREPASS if k_prepass else 0)
     a.scale = 0.0
     if norm is not None:
         wq, wk = norm[0].to(d), norm[1].to(d)
@@ -66,7 +66,7 @@ def _run(w, noalloc, int8=False, qk=None, norm=None):
 def _case(name):
     if name == "flux":  # 432 units: the last round's units are cut into pieces
         return syn.flux(batch=1, heads=24, grid=64, dtype="bf16", seed=2000)
-    if name == "flux_b3":  # K' (81 MiB) does not fit the scratch: K is rotated in the key loop
+    if name == "flux_b3":  # K' (81 MiB) would not fit the scratch
         return syn.flux(batch=3, heads=24, grid=64, dtype="bf16", seed=2001)
     if name == "flux_bool":
         w = syn.flux(batch=2, heads=8, grid=64, dtype="bf16", seed=3000)
@@ -83,12 +83,16 @@ def _case(name):
 
 
 @pytest.mark.parametrize("first,second", [("flux", "small_split"), ("flux_bool", "small_fp32_mask"),
-                                          ("small_split", "tiny"), ("flux_b3", "flux")])
+                                          ("small_split", "tiny"), ("flux_b3", "flux"),
+                                          ("flux_b3_k_prepass", "flux_k_prepass")])
 def test_noalloc_matches_workspace_forward_on_two_calls(first, second):
+    """(with RS_FLAG_K_PREPASS: the B=3 call cannot hold K' in the scratch and rotates K in the
+    key loop instead, the B=1 call prepares K' in the scratch; both equal the workspace call)"""
     for name in (first, second):
-        w = _case(name)
-        o_ref, l_ref = _run(w, noalloc=False)
-        o, l = _run(w, noalloc=True)
+        kp = name.endswith("_k_prepass")
+        w = _case(name.removesuffix("_k_prepass"))
+        o_ref, l_ref = _run(w, noalloc=False, k_prepass=kp)
+        o, l = _run(w, noalloc=True, k_prepass=kp)
         assert torch.equal(o, o_ref), name
         assert torch.equal(l, l_ref), name
 
