@@ -496,9 +496,17 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   // workgroup = one key tile of one (b, K/V head); with grouped-query attention it runs the
   // query tiles of every query head of the group, dK and dV accumulating across them
   const int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = item % nkt;
-  const int bh = item / nkt;
+  // causal: workgroup runs key tiles ip and nkt - 1 - ip of one slice (nqt - 2 ip and
+  // 2 ip + 2 query tiles: the same total in every workgroup)
+  const int npairs = (nkt + 1) / 2;
+  const int bh = CAUSAL ? item / npairs : item / nkt;
+  const int ip = CAUSAL ? item % npairs : item % nkt;
   const int hk = bh % p.shp.Hkv, b = bh / p.shp.Hkv;
+#pragma unroll 1
+  for (int pu = 0; pu < (CAUSAL ? 2 : 1); ++pu) {
+  if (CAUSAL && pu == 1 && ip == nkt - 1 - ip) break;
+  if (pu > 0) __syncthreads();  // LDS of the first key tile
+  const int kt = CAUSAL && pu == 1 ? nkt - 1 - ip : ip;
   const int k0 = kt * BNK;
   const int j = k0 + 16 * wave + c;  // this lane's key
   const int jc = j < S ? j : S - 1;
@@ -772,6 +780,7 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
       *(v4*)(krow + d0 * 2) = w;
     }
   }
+  }  // key tiles of the workgroup
 }
 
 // ---------------------------------------------------------------------------------------
@@ -785,8 +794,9 @@ static int launch_bwd16_t(const BwdParams& p, void* stream) {
                      (hipStream_t)stream, p);
   int e = (int)hipGetLastError();
   if (e) return e;
-  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL, PRE & 1>), dim3(((S + 127) / 128) * p.shp.B * p.shp.Hkv),
-                     dim3(512), 0, (hipStream_t)stream, p);
+  const int nkt = (S + 127) / 128;
+  const int grid_k = (CAUSAL ? (nkt + 1) / 2 : nkt) * p.shp.B * p.shp.Hkv;
+  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL, PRE & 1>), dim3(grid_k), dim3(512), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
