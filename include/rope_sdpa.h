@@ -17,7 +17,8 @@
  * workspace (K' = R(K) rounded to the input dtype, [B, Hkv, S, D]), and the quantized
  * pre-pass mode writes codes.  The backward (16-bit inputs at D = 128) leaves Q' (written by
  * its dQ kernel) and K' (by a rotation pass) in the workspace; at D = 64 and in fp32 it
- * rotates both inside its kernels.  The backward
+ * rotates both inside its kernels (the quantized backward: the dequantized Q' and K' in the
+ * workspace at either D).  The backward
  * returns gradients with respect to the unrotated Q and K (the inverse rotation, i.e. the
  * same rotation with sin negated, applied to dQ' and dK'), and V.
  *
@@ -195,8 +196,8 @@ size_t rope_sdpa_noalloc_scratch_bytes(void);
  * upstream gradient dout (sizes and dtype of o).  Writes dq (sizes of q), dk and dv (sizes of k),
  * all in the dtype of q.
  * The mask (if any) is a constant: no mask gradient.
- * With RS_FLAG_QUANT_INT8_QK or RS_FLAG_QUANT_INT4_QK (16-bit inputs at D = 128; D = 64 returns
- * RS_ERR_UNSUPPORTED): the gradients of the quantized forward with the gradient passed
+ * With RS_FLAG_QUANT_INT8_QK or RS_FLAG_QUANT_INT4_QK (16-bit inputs): the gradients of the
+ * quantized forward with the gradient passed
  * straight through the quantizer (the pages name a quantized autograd entry point without
  * saying how gradients cross the quantizer; this is the reading taken).  The quantizer pass
  * writes the dequantized values code * scale of Q' and K', rounded to the input dtype, to the

@@ -218,8 +218,8 @@ def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, att
     quantization: None, "int8" for the blockwise int8 Q'/K' forward quantized in the attention
     kernel, or "int8_prepass" for the same forward with the codes written by a quantizer pass
     first (bit-identical results, faster); "int4" / "int4_prepass" the same with codes in
-    [-7, 7].  Gradients (D = 128) pass the quantizer straight through: the backward runs at
-    the dequantized rotated Q and K the forward attended with.
+    [-7, 7].  Gradients pass the quantizer straight through: the backward runs at the
+    dequantized rotated Q and K the forward attended with.
 
     q_norm_weight, k_norm_weight ([D] each, together or not at all): RMSNorm of query and key
     over the head dimension, x / sqrt(mean(x^2) + norm_eps) * w in fp32, before the rotation.
@@ -240,8 +240,6 @@ def rope_scaled_dot_product_attention(query, key, value, rope_cos, rope_sin, att
     norm = _norm_args(query, q_norm_weight, k_norm_weight, norm_eps)
     needs_grad = torch.is_grad_enabled() and (query.requires_grad or key.requires_grad or value.requires_grad)
     if quantization is not None and needs_grad and norm is None and query.dtype == value.dtype:
-        if query.shape[-1] != 128:
-            raise RopeSdpaError(-6)  # the quantized backward runs at D = 128
         return _RopeSdpaFn.apply(query, key, value, cos4, sin4, mask, kind, bool(is_causal), scale, quantization)
     if quantization is not None or norm is not None or query.dtype != value.dtype:
         if needs_grad:

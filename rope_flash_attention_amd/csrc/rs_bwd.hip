@@ -250,14 +250,17 @@ struct DkdvCfg {
   static constexpr int BMQ = sizeof(T) == 4 ? 32 : 64;  // queries per LDS tile
 };
 
-template <typename T, int D, int MASK, bool CAUSAL>
+// PRE: Q and K arrive rotated (p.q, p.k point at Q' and K' in the workspace, e.g. the
+// dequantized values of the quantized forward): no rotation on load; the epilogues still
+// apply the inverse rotation.
+template <typename T, int D, int MASK, bool CAUSAL, bool PRE>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   using M = Mf<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = 2 * KPL, NQK = D / KSTEP, NDB = D / 32;
   constexpr int ES = (int)sizeof(T);
   constexpr int BNK = DkdvCfg<T>::BNK, BMQ = DkdvCfg<T>::BMQ, NMB = BMQ / 32;
-  using St = Stager<T, D, BMQ, true>;
+  using St = Stager<T, D, BMQ, !PRE>;
   using Sd = Stager<T, D, BMQ, false>;
   constexpr int RB = BMQ * St::RP, TB = D * St::TROW;
   constexpr int OFF_Q = 0, OFF_QT = RB, OFF_DO = RB + TB, OFF_DOT = 2 * RB + TB, OFF_L = 2 * RB + 2 * TB;
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   // K' and V of this lane's key as B fragments (column = key)
   frag kf[NQK], vf[NQK];
   if (j < S) {
-    load_row_frags<T, D, true>(kf, (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh + (int64_t)j * p.k.ss,
+    load_row_frags<T, D, !PRE>(kf, (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh + (int64_t)j * p.k.ss,
                                tab + (int64_t)j * D, hh);
     load_row_frags<T, D, false>(vf, (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh + (int64_t)j * p.v.ss,
                                 nullptr, hh);
@@ -531,14 +534,14 @@ struct DqCfg {
   static constexpr int BN = sizeof(T) == 4 ? 32 : 64;
 };
 
-template <typename T, int D, int MASK, bool CAUSAL>
+template <typename T, int D, int MASK, bool CAUSAL, bool PRE>
 __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
   using M = Mf<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = 2 * KPL, NQK = D / KSTEP, NDB = D / 32;
   constexpr int ES = (int)sizeof(T);
   constexpr int BM = DqCfg<T>::BM, BN = DqCfg<T>::BN, NKB = BN / 32;
-  using Sk = Stager<T, D, BN, true>;
+  using Sk = Stager<T, D, BN, !PRE>;
   using Sv = Stager<T, D, BN, false>;
   constexpr int RB = BN * Sk::RP, TB = D * Sk::TROW;
   constexpr int OFF_K = 0, OFF_KT = RB, OFF_V = RB + TB;
@@ -564,7 +567,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
   const float* tab = p.tab.ptr + b * p.tab.sb;
 
   frag qf[NQK], gf[NQK];
-  load_row_frags<T, D, true>(qf, (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh + (int64_t)mc * p.q.ss,
+  load_row_frags<T, D, !PRE>(qf, (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh + (int64_t)mc * p.q.ss,
                              tab + (int64_t)mc * D, hh);
   load_row_frags<T, D, false>(gf, (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh + (int64_t)mc * p.dout.ss,
                               nullptr, hh);
@@ -741,7 +744,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-template <typename T, int D, int MASK, bool CAUSAL>
+template <typename T, int D, int MASK, bool CAUSAL, bool PRE = false>
 static int launch_bwd_t(const BwdParams& p, hipStream_t s) {
   constexpr int LPR = D * (int)sizeof(T) / 16, RPB = 256 / LPR;
   const int64_t nrows = (int64_t)p.shp.B * p.shp.H * p.shp.S;
@@ -749,21 +752,21 @@ static int launch_bwd_t(const BwdParams& p, hipStream_t s) {
   int e = (int)hipGetLastError();
   if (e) return e;
   const int nk = (p.shp.S + DkdvCfg<T>::BNK - 1) / DkdvCfg<T>::BNK;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, MASK, CAUSAL>), dim3(nk * p.shp.Hkv * p.shp.B), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((dkdv_kernel<T, D, MASK, CAUSAL, PRE>), dim3(nk * p.shp.Hkv * p.shp.B), dim3(256), 0, s, p);
   e = (int)hipGetLastError();
   if (e) return e;
   const int nq = (p.shp.S + DqCfg<T>::BM - 1) / DqCfg<T>::BM;
-  hipLaunchKernelGGL((dq_kernel<T, D, MASK, CAUSAL>), dim3(nq * p.shp.H * p.shp.B), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((dq_kernel<T, D, MASK, CAUSAL, PRE>), dim3(nq * p.shp.H * p.shp.B), dim3(256), 0, s, p);
   return (int)hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PRE = false>
 static int launch_bwd_d(int mask_kind, bool causal, const BwdParams& p, hipStream_t s) {
-  if (causal) return launch_bwd_t<T, D, MASK_NONE, true>(p, s);
+  if (causal) return launch_bwd_t<T, D, MASK_NONE, true, PRE>(p, s);
   switch (mask_kind) {
-    case MASK_BOOL: return launch_bwd_t<T, D, MASK_BOOL, false>(p, s);
-    case MASK_ADD: return launch_bwd_t<T, D, MASK_ADD, false>(p, s);
-    default: return launch_bwd_t<T, D, MASK_NONE, false>(p, s);
+    case MASK_BOOL: return launch_bwd_t<T, D, MASK_BOOL, false, PRE>(p, s);
+    case MASK_ADD: return launch_bwd_t<T, D, MASK_ADD, false, PRE>(p, s);
+    default: return launch_bwd_t<T, D, MASK_NONE, false, PRE>(p, s);
   }
 }
 
@@ -778,7 +781,10 @@ int launch_bwd16(int dtype, int mask_kind, bool causal, int pre, const BwdParams
 template <typename T>
 static int launch_bwd_16bit(int dtype, int D, int mask_kind, bool causal, int pre, const BwdParams& p,
                             hipStream_t s) {
-  if (D == 64) return pre == 0 ? launch_bwd_d<T, 64>(mask_kind, causal, p, s) : -1;
+  if (D == 64) {  // (pre: 0, or 3 for the quantized backward's Q' and K')
+    if (pre == 3) return launch_bwd_d<T, 64, true>(mask_kind, causal, p, s);
+    return pre == 0 ? launch_bwd_d<T, 64>(mask_kind, causal, p, s) : -1;
+  }
   constexpr int LPR = 128 * 2 / 16, RPB = 256 / LPR;
   const int64_t nrows = (int64_t)p.shp.B * p.shp.H * p.shp.S;
   hipLaunchKernelGGL((bwd_pre_kernel<T, 128>), dim3((unsigned)((nrows + RPB - 1) / RPB)), dim3(256), 0, s, p);

@@ -264,9 +264,11 @@ Layout layout(const Shape& s, int mask_kind, bool backward, int int8, bool causa
   }
   L.delta = off;
   if (backward) off += round_up((size_t)(s.B * s.H * s.S) * sizeof(float), 256);
+  // (backward, 16-bit: Q' at D = 128, and at D = 64 for the quantized backward's Q^')
+  const bool bwd_prep = backward && s.dtype != F32 && (s.D == 128 || int8 != 0);
   L.qrot = off;
-  if (backward && s.dtype != F32 && s.D == 128) off += round_up((size_t)(s.B * s.H * s.S * s.D) * 2, 256);
-  if ((int8 & 3) == 2) {
+  if (bwd_prep) off += round_up((size_t)(s.B * s.H * s.S * s.D) * 2, 256);
+  if (!backward && (int8 & 3) == 2) {
     L.nblk = (s.S + 63) / 64;
     L.sp = L.nblk * 64;
     L.qc = off;
@@ -279,7 +281,7 @@ Layout layout(const Shape& s, int mask_kind, bool backward, int int8, bool causa
     off += round_up((size_t)(s.B * s.Hkv * L.nblk) * sizeof(float), 256);
   }
   L.kprep = off;  // K' = R(K) rotated once: [B][Hkv][S][D] in the compute dtype
-  if ((!backward && s.kprep) || (backward && s.dtype != F32 && s.D == 128))
+  if ((!backward && s.kprep) || bwd_prep)
     off += round_up((size_t)(s.B * s.Hkv * s.S * s.D) * elem_size(s.dtype), 256);
   if (!backward) {
     const int64_t bm = fwd_block_m(s.dtype), bn = fwd_block_n(s.dtype);
@@ -505,7 +507,7 @@ rs_status rope_sdpa_workspace_size(const rs_args* args, int backward, size_t* by
   rs_status st = validate_args(args, &s);
   if (st != RS_OK) return fail(st);
   *bytes = s.empty ? 0
-                   : layout(s, args->mask_kind, backward != 0, backward ? 0 : int8_mode(args->flags),
+                   : layout(s, args->mask_kind, backward != 0, int8_mode(args->flags),
                             (args->flags & RS_FLAG_CAUSAL) != 0)
                          .total;
   return RS_OK;
@@ -662,7 +664,6 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   rs_status st = validate_args(a, &s);
   if (st != RS_OK) return fail(st);
   const bool quant = (a->flags & kQuantFlags) != 0;
-  if (quant && s.D != 128) return fail(RS_ERR_UNSUPPORTED);  // quantized backward: D = 128
   if (!s.rope) return fail(RS_ERR_UNSUPPORTED);  // the backward is the fused one: tables required
   if (s.qkm != 0) return fail(RS_ERR_UNSUPPORTED);  // no backward through the Q/K prologue
   const int64_t sz[4] = {s.B, s.H, s.S, s.D};
@@ -675,7 +676,7 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   }
   if (((uintptr_t)lse) % 4 != 0) return fail(RS_ERR_ALIGN);
   if (s.empty) return RS_OK;
-  const Layout L = layout(s, a->mask_kind, true, false, (a->flags & RS_FLAG_CAUSAL) != 0);
+  const Layout L = layout(s, a->mask_kind, true, int8_mode(a->flags), (a->flags & RS_FLAG_CAUSAL) != 0);
   if ((st = check_ws(ws, ws_bytes, L)) != RS_OK) return fail(st);
   if ((st = current_device_ok()) != RS_OK) return fail(st);
 
@@ -714,7 +715,7 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
   p.shp = attn_shape(s);
   const bool causal = (a->flags & RS_FLAG_CAUSAL) != 0;
   int pre = 0;
-  if (s.dtype != F32 && s.D == 128) {
+  if (s.dtype != F32 && (s.D == 128 || quant)) {
     if (quant) {
       QuantParams qp = quant_params(a, s, L, w);
       qp.nblk = (int)((s.S + 63) / 64);
@@ -722,6 +723,12 @@ rs_status rope_sdpa_bwd(const rs_args* a, const rs_tensor* o, const float* lse, 
       qp.deq[1] = w + L.kprep;
       if (launch_quant_int8(s.dtype, qp, strm) != 0) return fail(RS_ERR_LAUNCH);
       pre = 3;
+      if (s.D != 128) {  // the 32x32 kernels read Q^' as Q
+        p.q.ptr = w + L.qrot;
+        p.q.sb = s.H * s.S * s.D;
+        p.q.sh = s.S * s.D;
+        p.q.ss = s.D;
+      }
     } else {
       pre = 1;
     }

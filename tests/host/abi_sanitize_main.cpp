@@ -320,14 +320,14 @@ int main() {
   { Case c(RS_BF16, 1, 2, 128, 64); c.cos.dtype = RS_F16; expect_error(c, false, RS_ERR_DTYPE, "table dtype"); }
   { Case c(RS_BF16, 2, 2, 128, 64, 2); c.sin.size[0] = 1; c.sin.stride[0] = 0; expect_error(c, false, RS_ERR_SHAPE, "table batch mismatch"); }
   { Case c(RS_F32, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT8_QK; expect_error(c, false, RS_ERR_UNSUPPORTED, "int8 fp32"); }
-  { Case c(RS_BF16, 1, 2, 128, 64); c.a.flags = RS_FLAG_QUANT_INT8_QK; expect_error(c, true, RS_ERR_UNSUPPORTED, "int8 backward D=64"); }
-  // the quantized backward (D = 128): int8 and int4, grouped-query included
+  // the quantized backward: int8 and int4, D = 64 and 128, grouped-query included
   for (uint32_t bits : {(uint32_t)RS_FLAG_QUANT_INT8_QK, (uint32_t)RS_FLAG_QUANT_INT4_QK})
-    for (int Hkv : {4, 2}) {
-      Case c(RS_BF16, 2, 4, 300, 128, 1, Hkv);
-      c.a.flags = bits;
-      CHECK(run(c, true) == RS_OK, "quantized backward flags=%u Hkv=%d", bits, Hkv);
-    }
+    for (int D : {64, 128})
+      for (int Hkv : {4, 2}) {
+        Case c(RS_BF16, 2, 4, 300, D, 1, Hkv);
+        c.a.flags = bits;
+        CHECK(run(c, true) == RS_OK, "quantized backward flags=%u D=%d Hkv=%d", bits, D, Hkv);
+      }
   { Case c(RS_BF16, 1, 2, 128, 64);
     const int before = stub::launches;
     std::vector<char> buf(1 << 20);

@@ -192,11 +192,12 @@ int launch_bwd(int dtype, int D, int, bool, int pre, const BwdParams& p, void*) 
   if (p.shp.Hkv <= 0 || H % p.shp.Hkv != 0 || p.shp.group != H / p.shp.Hkv) std::abort();
   stub::need(p.tab.ptr, (size_t)(p.tab.sb ? B : 1) * S * D * sizeof(float), "packed tables");
   stub::need(p.delta, (size_t)B * H * S * sizeof(float), "delta");
-  if (dtype != F32 && D == 128) {
+  if (dtype != F32 && (D == 128 || pre == 3)) {
     stub::need(p.qrot, (size_t)B * H * S * D * 2, "rotated Q");
     if (pre != 1 && pre != 3) std::abort();  // K' prepared in the workspace
     stub::need(p.k.ptr, (size_t)B * p.shp.Hkv * S * D * 2, "prepared K");
     if (p.k.ss != D || p.k.sh != (int64_t)S * D || p.k.sb != (int64_t)p.shp.Hkv * S * D) std::abort();
+    if (D != 128 && p.q.ptr != p.qrot) std::abort();  // the 32x32 kernels read Q^' as Q
   } else if (pre != 0) {
     std::abort();
   }

@@ -63,12 +63,32 @@ def test_quant_backward_flux_shape(mode):
     _compare(w, mode)
 
 
-def test_quant_backward_counter_and_d64_rejected():
+def test_quant_backward_counter():
     w = syn.random_small(1, 2, 64, 128, "bf16", seed=311, with_grad=True)
     rfa.rope_sdpa_reset_stats()
     _gpu(w, "int8")
     s = rfa.get_dispatch_stats()
     assert s["quantized_autograd"] == 1 and s["backward"] == 1 and s["quantized_int8"] == 1
-    w64 = syn.random_small(1, 2, 64, 64, "bf16", seed=312, with_grad=True)
-    with pytest.raises(rfa.RopeSdpaError):
-        _gpu(w64, "int8")
+
+
+@pytest.mark.parametrize("mode", ["int8", "int4"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("variant", ["none", "causal", "gqa"])
+def test_quant_backward_d64(mode, dtype, variant):
+    """D = 64 (the 32x32 backward kernels reading the dequantized Q' and K')."""
+    H, Hkv = (4, 2) if variant == "gqa" else (2, 2)
+    w = syn.random_small(2, H, 300, 64, dtype, seed=312 + H, kv_heads=Hkv, with_grad=True,
+                         causal=(variant == "causal"))
+    bits = 4 if mode == "int4" else 8
+    d = dev()
+    q, k, v = (t.to(d).detach().requires_grad_() for t in (w.q, w.k, w.v))
+    o = rfa.rope_scaled_dot_product_attention(q, k, v, w.cos.to(d), w.sin.to(d), is_causal=w.causal,
+                                              quantization=mode)
+    o.backward(w.do.to(d))
+    torch.cuda.synchronize()
+    kw = dict(causal=w.causal, workers=8)
+    O_ref, _ = rope_sdpa_forward_quant(w.q, w.k, w.v, w.cos, w.sin, bits=bits, **kw)
+    check_out("O", to64(o), O_ref, dtype)
+    refs = rope_sdpa_backward_quant(w.q, w.k, w.v, w.cos, w.sin, w.do, bits=bits, **kw)
+    for name, g, r in zip(("dQ", "dK", "dV"), (q.grad, k.grad, v.grad), refs):
+        check_grad(name, to64(g), r, dtype)
