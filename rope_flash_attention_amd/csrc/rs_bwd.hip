@@ -777,7 +777,8 @@ static int launch_bwd_dt(int D, int mask_kind, bool causal, const BwdParams& p, 
 
 int launch_bwd16(int dtype, int mask_kind, bool causal, int pre, const BwdParams& p, void* stream);
 
-// 16-bit inputs at D = 128 use the 16x16 kernels of rs_bwd16.hip after the delta pre-pass.
+// 16-bit inputs at D = 128 use the 16x16 kernels of rs_bwd16.hip (whose dQ kernel computes
+// delta on the way; no pre-pass).
 template <typename T>
 static int launch_bwd_16bit(int dtype, int D, int mask_kind, bool causal, int pre, const BwdParams& p,
                             hipStream_t s) {
@@ -785,11 +786,6 @@ static int launch_bwd_16bit(int dtype, int D, int mask_kind, bool causal, int pr
     if (pre == 3) return launch_bwd_d<T, 64, true>(mask_kind, causal, p, s);
     return pre == 0 ? launch_bwd_d<T, 64>(mask_kind, causal, p, s) : -1;
   }
-  constexpr int LPR = 128 * 2 / 16, RPB = 256 / LPR;
-  const int64_t nrows = (int64_t)p.shp.B * p.shp.H * p.shp.S;
-  hipLaunchKernelGGL((bwd_pre_kernel<T, 128>), dim3((unsigned)((nrows + RPB - 1) / RPB)), dim3(256), 0, s, p);
-  const int e = (int)hipGetLastError();
-  if (e) return e;
   return launch_bwd16(dtype, mask_kind, causal, pre, p, s);
 }
 

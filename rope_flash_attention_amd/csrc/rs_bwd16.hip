@@ -11,8 +11,8 @@
 //            scale log2 e) and dO stay in registers as B operands; K' is rotated on its way
 //            into LDS and V goes straight from memory into LDS; per 64-key tile
 //            S'^T = K' Q'^T, dP^T = V dO^T (row reads), dQ'^T += K'^T dS^T (transposed reads).
-//            Launched first: it also writes its rows of Q' (unscaled, in the input dtype) to
-//            the workspace for dkdv16.
+//            Launched first: it also writes its rows of Q' (unscaled, in the input dtype) and
+//            their delta = sum_d dO O to the workspace for dkdv16.
 //  * dkdv16: workgroup = 128 keys (16 per wave); K' (times scale log2 e) and V stay in
 //            registers; Q' (from dq16) and dO tiles of 64 queries go straight from memory
 //            into LDS; per tile S' = Q' K'^T, dP = dO V^T, dV^T += dO^T P, dK'^T += Q'^T dS;
@@ -296,7 +296,22 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
   const int64_t rowid = ((int64_t)b * p.shp.H + hd) * S + mc;
   const float lse_v = p.lse[rowid];
   const float l2 = (m >= S || lse_v == -INFINITY) ? INFINITY : lse_v * kL2e;
-  const float dlt = p.delta[rowid];
+  // delta = sum_d dO O of the row in fp32: this lane's 32 elements, then the four lanes of the
+  // row (c, c + 16, c + 32, c + 48); written to the workspace for the dK/dV kernel
+  float dlt = 0.f;
+  {
+    typedef T v8 __attribute__((ext_vector_type(8)));
+    const T* orow = (const T*)p.o.ptr + b * p.o.sb + hd * p.o.sh + (int64_t)mc * p.o.ss;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v8 ov = *(const v8*)(orow + 32 * t + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dlt = fmaf(to_f(ov[e]), to_f(gf[t][e]), dlt);
+    }
+    dlt += __shfl_xor(dlt, 16, 64);
+    dlt += __shfl_xor(dlt, 32, 64);
+    if (g == 0 && m < S) p.delta[rowid] = dlt;
+  }
   const f32x4 cinit = {-l2, -l2, -l2, -l2};  // S'^T - LSE log2 e through the accumulator
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -820,7 +835,7 @@ static int launch_bwd16_pre(int mask_kind, bool causal, int pre, const BwdParams
   }
 }
 
-// dK/dV and dQ for 16-bit inputs at D = 128 (after the delta pre-pass).  pre: 0 Q and K
+// dK/dV and dQ for 16-bit inputs at D = 128 (the dQ kernel computes delta).  pre: 0 Q and K
 // rotated here; 1 K' prepared in p.k; 3 Q' (p.qrot) and K' (p.k) both prepared.
 int launch_bwd16(int dtype, int mask_kind, bool causal, int pre, const BwdParams& p, void* stream) {
   return dtype == F16 ? launch_bwd16_pre<_Float16>(mask_kind, causal, pre, p, stream)
