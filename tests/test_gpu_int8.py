@@ -144,13 +144,19 @@ def test_int8_determinism_and_counter():
 
 
 def test_int8_rejections():
-    """fp32 inputs have no quantized path; gradients of the quantized path need D = 128."""
+    """fp32 inputs have no quantized path, and the quantized path takes no Q/K RMSNorm
+    prologue (forward or with gradients)."""
     w = syn.random_small(1, 2, 64, 64, dtype="bf16", seed=94)
     d = dev()
     q, k, v = (t.to(d) for t in (w.q, w.k, w.v))
+    nw = torch.ones(64, device=d, dtype=torch.float32)
+    with torch.no_grad(), pytest.raises(rfa.RopeSdpaError):
+        rfa.rope_scaled_dot_product_attention(q, k, v, w.cos.to(d), w.sin.to(d), quantization="int8",
+                                              q_norm_weight=nw, k_norm_weight=nw)
     qg = q.clone().requires_grad_(True)
     with pytest.raises(rfa.RopeSdpaError):
-        rfa.rope_scaled_dot_product_attention(qg, k, v, w.cos.to(d), w.sin.to(d), quantization="int8")
+        rfa.rope_scaled_dot_product_attention(qg, k, v, w.cos.to(d), w.sin.to(d), quantization="int8",
+                                              q_norm_weight=nw, k_norm_weight=nw)
     w32 = syn.random_small(1, 2, 64, 64, dtype="f32", seed=94)
     with pytest.raises(rfa.RopeSdpaError):
         rfa.rope_scaled_dot_product_attention(*(t.to(d) for t in (w32.q, w32.k, w32.v)), w32.cos.to(d),
