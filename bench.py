@@ -605,14 +605,15 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": _traffic("fwd_bf16_d128_flux_b1"),
-            "kernel": "fwd_kernel<bf16,128,MASK_NONE,QKM=4> (attention, Q rotated in its prologue, K' read as "
-                      "prepared)",
+            "kernel": "fwd_kernel<bf16,128,MASK_NONE,ROPE> (attention; Q rotated in its prologue, K rotated "
+                      "in the key loop on its way into LDS)",
             "kernel_ms": round(k_ms, 5),
             "kernel_launches": k_launches,
             "note": "achieved = 4*B*H*S^2*D algorithmic flops over the attention kernel's average duration, "
                     "from HIP events the library records on the call's stream around that kernel during "
-                    "the timed calls; a timed call (value) is three launches: kprep_kernel (K rotated once, "
-                    "tables packed), the attention kernel and fwd_merge_kernel (the cut units' pieces)",
+                    "the timed calls; a timed call (value) is three launches: pack_tables_kernel (the "
+                    "caller's cos/sin repacked into (cos, sin) pairs), the attention kernel and "
+                    "fwd_merge_kernel (the cut units' pieces)",
             "call_tflops": round(tflops, 2),
         },
         "train": train,
