@@ -7,13 +7,16 @@
 //    P = exp(scale S - LSE),  dV = P^T dO,  dP = dO V^T,  delta_i = sum_d dO_id O_id,
 //    dS = P o (dP - delta),   dQ' = scale dS K',  dK' = scale dS^T Q',
 //    dQ = R^T dQ',  dK = R^T dK'.
-// Three launches, no atomics (results are deterministic):
+// These 32x32 kernels serve fp32 inputs and D = 64 (16-bit inputs at D = 128 take the
+// kernels of rs_bwd16.hip).  Three launches, no atomics (results are deterministic):
 //   bwd_pre : delta per row;
 //   dkdv    : one workgroup per 128 keys (32 per wave), looping over query tiles; K' and V
 //             stay in registers, Q' and dO stream through LDS in row and transposed forms;
 //   dq      : one workgroup per 128 queries, looping over key tiles; Q' and dO stay in
 //             registers, K' (row and transposed) and V stream through LDS.
 // Q and K are rotated in registers wherever they are loaded; no rotated copy is stored.
+// PRE (the quantized backward at D = 64): Q' and K' arrive already rotated (the dequantized
+// values the quantized forward attended with, in the workspace) and are only scaled.
 #include "rs_device.hpp"
 
 namespace rs {
