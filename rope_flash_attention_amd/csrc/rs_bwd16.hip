@@ -8,11 +8,12 @@
 // The 16x16 products keep a wave's accumulators small (a 16 x 128 block is 32 registers
 // instead of 64 for 32 rows), so eight waves of one workgroup fit two per SIMD:
 //  * dq16:   workgroup = 128 queries (16 per wave, one per lane column); Q' (times
-//            scale log2 e) and dO stay in registers as B operands; K' is rotated on its way
-//            into LDS and V goes straight from memory into LDS; per 64-key tile
-//            S'^T = K' Q'^T, dP^T = V dO^T (row reads), dQ'^T += K'^T dS^T (transposed reads).
-//            Launched first: it also writes its rows of Q' (unscaled, in the input dtype) and
-//            their delta = sum_d dO O to the workspace for dkdv16.
+//            scale log2 e) and dO stay in registers as B operands; K' (rotated once by
+//            kprep_kernel) and V tiles go straight from memory into LDS, two 64-key tiles per
+//            barrier; per 64-key tile S'^T = K' Q'^T, dP^T = V dO^T (row reads),
+//            dQ'^T += K'^T dS^T (transposed reads).  Launched first: it also writes its rows
+//            of Q' (unscaled, in the input dtype) and their delta = sum_d dO O to the
+//            workspace for dkdv16.
 //  * dkdv16: workgroup = 128 keys (16 per wave); K' (times scale log2 e) and V stay in
 //            registers; Q' (from dq16) and dO tiles of 64 queries go straight from memory
 //            into LDS; per tile S' = Q' K'^T, dP = dO V^T, dV^T += dO^T P, dK'^T += Q'^T dS;
@@ -106,12 +107,11 @@ __device__ inline float2 rot_fma(float x0, float x1, float c, float s) {
   return r;
 }
 
-// B fragments of one row (D = 128): element e of fragment t = row[32t + 8g + e]; kRowRot:
-// rotated with the packed table row and multiplied by `mul`; kRowMul: multiplied by `mul`
-// (a row rotated already); kRowRaw: as stored.
-constexpr int kRowRaw = 0, kRowRot = 1, kRowMul = 2;
+// B fragments of one row (D = 128): element e of fragment t = row[32t + 8g + e]; kRowMul:
+// multiplied by `mul` (a row rotated already); kRowRaw: as stored.
+constexpr int kRowRaw = 0, kRowMul = 2;
 template <typename T, int MODE>
-__device__ inline void row_frags(typename Mf<T>::frag* f, const T* row, const float* trow, int g, float mul) {
+__device__ inline void row_frags(typename Mf<T>::frag* f, const T* row, int g, float mul) {
   typedef T v8 __attribute__((ext_vector_type(8)));
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -121,68 +121,13 @@ __device__ inline void row_frags(typename Mf<T>::frag* f, const T* row, const fl
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = from_f<T>(to_f(x[e]) * mul);
     }
-    if constexpr (MODE == kRowRot) {
-      const float4 a = *(const float4*)(trow + d0), b = *(const float4*)(trow + d0 + 4);
-      const float cc[4] = {a.x, a.z, b.x, b.z}, ss[4] = {a.y, a.w, b.y, b.w};
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const float2 r = rot_fma(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), cc[pp], ss[pp]);
-        x[2 * pp] = from_f<T>(r.x * mul);
-        x[2 * pp + 1] = from_f<T>(r.y * mul);
-      }
-    }
     f[t] = x;
   }
 }
 
-// Staging of a 64-row tile that needs rotation (K for dq16): each of the 512
-// threads loads two 16-byte chunks and their table pairs into registers, rotates them and
-// writes them swizzled.
-template <typename T>
-struct RotStager {
-  uint4 x[2];
-  float4 t[2][2];
-  int row, ch;
-  __device__ void init(int tid) {
-    row = tid >> 4;
-    ch = tid & 15;
-  }
-  __device__ void load(const T* base, int64_t ss, const float* tab, int row0, int S) {
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int j = row0 + row + 32 * it;
-      if (row0 + 64 <= S || j < S) {
-        x[it] = *(const uint4*)(base + (int64_t)j * ss + 8 * ch);
-        const float* tr = tab + (int64_t)j * 128 + 8 * ch;
-        t[it][0] = *(const float4*)tr;
-        t[it][1] = *(const float4*)(tr + 4);
-      } else {
-        x[it] = make_uint4(0, 0, 0, 0);
-        t[it][0] = make_float4(0.f, 0.f, 0.f, 0.f);
-        t[it][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-  }
-  __device__ void store(char* tile) {
-    typedef T v8 __attribute__((ext_vector_type(8)));
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const float* tf = (const float*)&t[it][0];
-      v8 v = *(const v8*)&x[it];
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const float2 r = rot_fma(to_f(v[2 * pp]), to_f(v[2 * pp + 1]), tf[2 * pp], tf[2 * pp + 1]);
-        v[2 * pp] = from_f<T>(r.x);
-        v[2 * pp + 1] = from_f<T>(r.y);
-      }
-      *(uint4*)(tile + lds_off(row + 32 * it, 16 * ch)) = *(const uint4*)&v;
-    }
-  }
-};
-
-// row_frags<T, true> for a Q row that also writes Q' = R(Q) (unscaled, in the input dtype,
-// rounded as RotStager rounds it) to `dst` unless it is null: the dQ kernel writes these rows
-// for the dK/dV kernel, whose tiles then hold exactly the values it would rotate itself.
+// B fragments of a Q row rotated with its packed table row and multiplied by `mul`, which
+// also writes Q' = R(Q) (unscaled, rounded once to the input dtype) to `dst` unless it is
+// null: the dQ kernel writes these rows for the dK/dV kernel.
 // Every load is issued before the first store (a store in between would make the compiler
 // issue the later loads again, one round trip each).
 template <typename T>
@@ -243,19 +188,23 @@ struct DmaTile {
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
-// PRE bit 0: K arrives rotated (K' in the workspace, contiguous): its tiles go straight from
-// memory into LDS like V's, with no table in the key loop.  PRE bit 1: Q arrives rotated too
-// (Q' in the workspace, e.g. the dequantized values of the quantized forward): it is only
-// scaled, and not written back.
-template <typename T, int MASK, bool CAUSAL, int PRE>
+// K arrives rotated (K' in the workspace, contiguous): its tiles go straight from memory
+// into LDS like V's, with no table in the key loop.  QROT: Q arrives rotated too (Q' in the
+// workspace, the dequantized values of the quantized forward): it is only scaled, and not
+// written back.
+// Without causal masking a step runs two 64-key tiles (NT) between barriers: the LDS buffers
+// hold both, and the next step's pair streams into the other buffers meanwhile (FLUX B=2
+// backward 1.3% faster; the causal kernel's short key ranges run one tile per step, which
+// measured faster there).
+template <typename T, int MASK, bool CAUSAL, bool QROT>
 __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
   using frag = typename Mf<T>::frag;
   using M = M16<T>;
-  constexpr int D = 128, BM = 128, BN = 64, TILE = BN * 256;
-  __shared__ __attribute__((aligned(16))) char sk0[TILE];
-  __shared__ __attribute__((aligned(16))) char sk1[TILE];
-  __shared__ __attribute__((aligned(16))) char sv0[TILE];
-  __shared__ __attribute__((aligned(16))) char sv1[TILE];
+  constexpr int D = 128, BM = 128, BN = 64, TILE = BN * 256, NT = CAUSAL ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) char sk0[NT * TILE];
+  __shared__ __attribute__((aligned(16))) char sk1[NT * TILE];
+  __shared__ __attribute__((aligned(16))) char sv0[NT * TILE];
+  __shared__ __attribute__((aligned(16))) char sv1[NT * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -284,15 +233,15 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
   const float* tab = p.tab.ptr + b * p.tab.sb;
 
   frag qf[4], gf[4];
-  if constexpr ((PRE & 2) != 0) {
-    row_frags<T, kRowMul>(qf, (const T*)p.qrot + ((int64_t)bh * S + mc) * D, nullptr, g, p.shp.scale_log2);
+  if constexpr (QROT) {
+    row_frags<T, kRowMul>(qf, (const T*)p.qrot + ((int64_t)bh * S + mc) * D, g, p.shp.scale_log2);
   } else {
     row_frags_qrot<T>(qf, m < S ? (T*)p.qrot + ((int64_t)bh * S + m) * D : nullptr,
                       (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh + (int64_t)mc * p.q.ss, tab + (int64_t)mc * D, g,
                       p.shp.scale_log2);
   }
-  row_frags<T, kRowRaw>(gf, (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh + (int64_t)mc * p.dout.ss, nullptr,
-                      g, 1.f);
+  row_frags<T, kRowRaw>(gf, (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh + (int64_t)mc * p.dout.ss, g,
+                        1.f);
   const int64_t rowid = ((int64_t)b * p.shp.H + hd) * S + mc;
   const float lse_v = p.lse[rowid];
   const float l2 = (m >= S || lse_v == -INFINITY) ? INFINITY : lse_v * kL2e;
@@ -350,45 +299,24 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
 
   LaneOffsets lo;
   lo.init(c, g);
-  RotStager<T> sk;
-  DmaTile dkt;  // PRE & 1: K' tiles
-  if constexpr ((PRE & 1) != 0) {
-    dkt.init(kbase, p.k.ss, S, wave, lane);
-  } else {
-    sk.init(tid);
-  }
-  DmaTile dv;
+  DmaTile dkt, dv;  // K' and V tiles
+  dkt.init(kbase, p.k.ss, S, wave, lane);
   dv.init(vbase, p.v.ss, S, wave, lane);
   const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
-
-  int kt = next_tile(0);
-  if (kt < kt_end) {
-    if constexpr ((PRE & 1) != 0) {
-      dkt.issue(sk0, kt * BN, wave);
-      dv.issue(sv0, kt * BN, wave);
-    } else {
-      sk.load(kbase, p.k.ss, tab, kt * BN, S);
-      dv.issue(sv0, kt * BN, wave);
-      sk.store(sk0);
+  // the tiles of one step (kt_end where the step has fewer) into buffers sK, sV
+  auto issue = [&](int ka, int kb2, char* sKd, char* sVd) {
+    if (ka < kt_end) {
+      dkt.issue(sKd, ka * BN, wave);
+      dv.issue(sVd, ka * BN, wave);
     }
-  }
-  wait_vmem_and_sync();
-
-  auto body = [&](auto stage_c) {
-    constexpr int stage = decltype(stage_c)::value;
-    const char* sK = stage ? sk1 : sk0;
-    const char* sV = stage ? sv1 : sv0;
-    char* sKn = stage ? sk0 : sk1;
-    char* sVn = stage ? sv0 : sv1;
-    const int ktn = next_tile(kt + 1);
-    if (ktn < kt_end) {
-      if constexpr ((PRE & 1) != 0) {
-        dkt.issue(sKn, ktn * BN, wave);
-      } else {
-        sk.load(kbase, p.k.ss, tab, ktn * BN, S);
-      }
-      dv.issue(sVn, ktn * BN, wave);
+    if (NT == 2 && kb2 < kt_end) {
+      dkt.issue(sKd + TILE, kb2 * BN, wave);
+      dv.issue(sVd + TILE, kb2 * BN, wave);
     }
+  };
+
+  // one 64-key tile kt from LDS tiles sK, sV
+  auto tile = [&](int kt, const char* sK, const char* sV) __attribute__((always_inline)) {
     const int kv0 = kt * BN;
 
     // S'^T - l2 and dP^T: rows = keys (permuted order), column = this lane's query
@@ -454,12 +382,26 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) dq[db] = M::mma(tr_frag<frag>(sK, lo, ks, db), dsf[ks], dq[db]);
     sched_reads_ahead<16, 2, 3, 1>();
+  };
 
-    if constexpr ((PRE & 1) == 0) {
-      if (ktn < kt_end) sk.store(sKn);
-    }
+  // step: tiles kt and kt2 (kt2 = kt_end when the step has one)
+  int kt = next_tile(0);
+  int kt2 = NT == 2 && kt < kt_end ? next_tile(kt + 1) : kt_end;
+  issue(kt, kt2, sk0, sv0);
+  wait_vmem_and_sync();
+
+  auto body = [&](auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
+    const char* sK = stage ? sk1 : sk0;
+    const char* sV = stage ? sv1 : sv0;
+    const int ktn = next_tile((kt2 < kt_end ? kt2 : kt) + 1);
+    const int ktn2 = NT == 2 && ktn < kt_end ? next_tile(ktn + 1) : kt_end;
+    issue(ktn, ktn2, stage ? sk0 : sk1, stage ? sv0 : sv1);
+    tile(kt, sK, sV);
+    if (NT == 2 && kt2 < kt_end) tile(kt2, sK + TILE, sV + TILE);
     wait_vmem_and_sync();
     kt = ktn;
+    kt2 = ktn2;
   };
   while (kt < kt_end) {
     body(std::integral_constant<int, 0>{});
@@ -491,8 +433,8 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// PRE bit 0: K arrives rotated (K' in the workspace): its rows are only scaled.
-template <typename T, int MASK, bool CAUSAL, int PRE>
+// K arrives rotated (K' in the workspace): its rows are only scaled.
+template <typename T, int MASK, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   using frag = typename Mf<T>::frag;
   using M = M16<T>;
@@ -534,9 +476,8 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
 
   // K' (times scale log2 e) and V of this lane's key as B fragments
   frag kf[4], vf[4];
-  row_frags<T, (PRE & 1) ? kRowMul : kRowRot>(kf, (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh + (int64_t)jc * p.k.ss,
-                                              tab + (int64_t)jc * D, g, p.shp.scale_log2);
-  row_frags<T, kRowRaw>(vf, (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh + (int64_t)jc * p.v.ss, nullptr, g, 1.f);
+  row_frags<T, kRowMul>(kf, (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh + (int64_t)jc * p.k.ss, g, p.shp.scale_log2);
+  row_frags<T, kRowRaw>(vf, (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh + (int64_t)jc * p.v.ss, g, 1.f);
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 dv[8], dk[8];
 #pragma unroll
@@ -799,44 +740,43 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-template <typename T, int MASK, bool CAUSAL, int PRE>
+template <typename T, int MASK, bool CAUSAL, bool QROT>
 static int launch_bwd16_t(const BwdParams& p, void* stream) {
   const int S = p.shp.S, BH = p.shp.B * p.shp.H;
-  // dQ first: it also writes Q' for the dK/dV kernel.  Causal: two query tiles of one head
-  // per workgroup (see the kernel)
+  // dQ first: it also writes Q' and delta for the dK/dV kernel.  Causal: two query tiles of
+  // one head per workgroup (see the kernel)
   const int grid_q = CAUSAL ? ((S + 127) / 128 + 1) / 2 * BH : ((S + 127) / 128) * BH;
-  hipLaunchKernelGGL((dq16_kernel<T, MASK, CAUSAL, PRE>), dim3(grid_q), dim3(512), 0,
-                     (hipStream_t)stream, p);
+  hipLaunchKernelGGL((dq16_kernel<T, MASK, CAUSAL, QROT>), dim3(grid_q), dim3(512), 0, (hipStream_t)stream, p);
   int e = (int)hipGetLastError();
   if (e) return e;
   const int nkt = (S + 127) / 128;
   const int grid_k = (CAUSAL ? (nkt + 1) / 2 : nkt) * p.shp.B * p.shp.Hkv;
-  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL, PRE & 1>), dim3(grid_k), dim3(512), 0, (hipStream_t)stream, p);
+  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL>), dim3(grid_k), dim3(512), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
-template <typename T, int PRE>
+template <typename T, bool QROT>
 static int launch_bwd16_dt(int mask_kind, bool causal, const BwdParams& p, void* stream) {
-  if (causal) return launch_bwd16_t<T, MASK_NONE, true, PRE>(p, stream);
+  if (causal) return launch_bwd16_t<T, MASK_NONE, true, QROT>(p, stream);
   switch (mask_kind) {
-    case MASK_BOOL: return launch_bwd16_t<T, MASK_BOOL, false, PRE>(p, stream);
-    case MASK_ADD: return launch_bwd16_t<T, MASK_ADD, false, PRE>(p, stream);
-    default: return launch_bwd16_t<T, MASK_NONE, false, PRE>(p, stream);
+    case MASK_BOOL: return launch_bwd16_t<T, MASK_BOOL, false, QROT>(p, stream);
+    case MASK_ADD: return launch_bwd16_t<T, MASK_ADD, false, QROT>(p, stream);
+    default: return launch_bwd16_t<T, MASK_NONE, false, QROT>(p, stream);
   }
 }
 
 template <typename T>
 static int launch_bwd16_pre(int mask_kind, bool causal, int pre, const BwdParams& p, void* stream) {
   switch (pre) {
-    case 0: return launch_bwd16_dt<T, 0>(mask_kind, causal, p, stream);
-    case 1: return launch_bwd16_dt<T, 1>(mask_kind, causal, p, stream);
-    case 3: return launch_bwd16_dt<T, 3>(mask_kind, causal, p, stream);
+    case 1: return launch_bwd16_dt<T, false>(mask_kind, causal, p, stream);
+    case 3: return launch_bwd16_dt<T, true>(mask_kind, causal, p, stream);
     default: return -1;
   }
 }
 
-// dK/dV and dQ for 16-bit inputs at D = 128 (the dQ kernel computes delta).  pre: 0 Q and K
-// rotated here; 1 K' prepared in p.k; 3 Q' (p.qrot) and K' (p.k) both prepared.
+// dK/dV and dQ for 16-bit inputs at D = 128 (the dQ kernel computes delta).  pre: 1 K'
+// prepared in p.k (kprep_kernel); 3 Q' (p.qrot) and K' (p.k) both prepared (the dequantized
+// values of the quantized forward).
 int launch_bwd16(int dtype, int mask_kind, bool causal, int pre, const BwdParams& p, void* stream) {
   return dtype == F16 ? launch_bwd16_pre<_Float16>(mask_kind, causal, pre, p, stream)
                       : launch_bwd16_pre<__bf16>(mask_kind, causal, pre, p, stream);
