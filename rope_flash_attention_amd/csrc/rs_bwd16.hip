@@ -17,7 +17,8 @@
 //  * dkdv16: workgroup = 128 keys (16 per wave); K' (times scale log2 e) and V stay in
 //            registers; Q' (from dq16) and dO tiles of 64 queries go straight from memory
 //            into LDS; per tile S' = Q' K'^T, dP = dO V^T, dV^T += dO^T P, dK'^T += Q'^T dS;
-//            waves 0-3 and 4-7 work half a tile apart (two barriers per tile, see the kernel).
+//            waves 0-3 and 4-7 work half a tile apart (three LDS buffers per operand, one
+//            barrier per tile, see the kernel).
 // The score rows are read in a permuted order so that the four accumulator rows a lane holds
 // in two consecutive 16-row blocks are eight consecutive contraction indices of the next
 // product: P and dS go from accumulators to B operands without leaving registers.
@@ -439,12 +440,16 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   using frag = typename Mf<T>::frag;
   using M = M16<T>;
   constexpr int D = 128, BNK = 128, BMQ = 64, TILE = BMQ * 256;
+  // three buffers of each: tile i uses buffer i % 3 (see the step loop)
   __shared__ __attribute__((aligned(16))) char sq0[TILE];
   __shared__ __attribute__((aligned(16))) char sq1[TILE];
+  __shared__ __attribute__((aligned(16))) char sq2[TILE];
   __shared__ __attribute__((aligned(16))) char sd0[TILE];
   __shared__ __attribute__((aligned(16))) char sd1[TILE];
+  __shared__ __attribute__((aligned(16))) char sd2[TILE];
   __shared__ __attribute__((aligned(16))) float sl0[2 * BMQ];  // l2 then delta per query
   __shared__ __attribute__((aligned(16))) float sl1[2 * BMQ];
+  __shared__ __attribute__((aligned(16))) float sl2[2 * BMQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -624,15 +629,15 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
     sched_reads_ahead<32, 2, 3, 1>();
   };
 
-  // The two waves of a SIMD work half a tile apart.  A step has two halves separated by a
-  // barrier: waves 0-3 take the tile's scores (row reads) and then its gradient products
-  // (transposed reads); waves 4-7 first finish the previous tile's gradient products, then
-  // take this tile's scores, whose P and dS stay in registers across the barrier.  Each half
-  // then has one wave per SIMD on each kind of product, and the LDS serves both kinds of
-  // reads at once.  The previous tile's buffer is free after the first half: the next tile
-  // is loaded into it during the second.  The two wave groups run separate loops (one
-  // branch outside), so that neither carries the other's registers; both pass the same
-  // barriers: two per tile.
+  // The two waves of a SIMD work half a tile apart: in the step of tile i, waves 0-3 take the
+  // tile's scores (row reads) and then its gradient products (transposed reads); waves 4-7
+  // first finish the previous tile's gradient products (its P and dS kept in registers),
+  // then take this tile's scores.  Each half of a step then has one wave per SIMD on each
+  // kind of product, and the LDS serves both kinds of reads at once.  Tile i sits in buffer
+  // i % 3: the step of tile i reads buffers i % 3 and (waves 4-7) (i - 1) % 3, and loads tile
+  // i + 1 into buffer (i + 1) % 3 from its start, the buffer of tile i - 2, which the previous
+  // step finished with: one barrier per step.  The two wave groups run separate loops (one
+  // branch outside), so that neither carries the other's registers.
 #pragma unroll 1
   for (int gq = 0; gq < p.shp.group; ++gq) {
   hd = hk * p.shp.group + gq;
@@ -654,23 +659,22 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   }
   wait_vmem_and_sync();
   frag pf[2], sf[2];
+  auto bufq = [&](int k) -> char* { return k == 0 ? sq0 : (k == 1 ? sq1 : sq2); };
+  auto bufd = [&](int k) -> char* { return k == 0 ? sd0 : (k == 1 ? sd1 : sd2); };
+  auto bufl = [&](int k) -> float* { return k == 0 ? sl0 : (k == 1 ? sl1 : sl2); };
   if (__builtin_amdgcn_readfirstlane(wave) < 4) {
     auto body = [&](auto stage_c) __attribute__((always_inline)) {
-      constexpr int stage = decltype(stage_c)::value;
-      char* sQ = stage ? sq1 : sq0;
-      char* sD = stage ? sd1 : sd0;
-      float* sL = stage ? sl1 : sl0;
-      char* sQn = stage ? sq0 : sq1;
-      char* sDn = stage ? sd0 : sd1;
-      float* sLn = stage ? sl0 : sl1;
+      constexpr int st = decltype(stage_c)::value;
+      char* sQ = bufq(st);
+      char* sD = bufd(st);
+      float* sL = bufl(st);
+      const int qtn = next_tile(qt + 1);
       f32x4 sacc[4], dpacc[4];
       rows(sQ, sD, sacc, dpacc);
       softmax(qt, sL, sacc, dpacc, pf, sf);
-      __syncthreads();
-      const int qtn = next_tile(qt + 1);
-      if (qtn < nqt) load_tile(qtn, sQn, sDn);
+      if (qtn < nqt) load_tile(qtn, bufq((st + 1) % 3), bufd((st + 1) % 3));
       cols(sQ, sD, pf, sf);
-      if (qtn < nqt) store_tile(sLn);
+      if (qtn < nqt) store_tile(bufl((st + 1) % 3));
       wait_vmem_and_sync();
       qt = qtn;
     };
@@ -678,25 +682,23 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
       body(std::integral_constant<int, 0>{});
       if (qt >= nqt) break;
       body(std::integral_constant<int, 1>{});
+      if (qt >= nqt) break;
+      body(std::integral_constant<int, 2>{});
     }
   } else {
     bool has_prev = false;
     auto body = [&](auto stage_c) __attribute__((always_inline)) {
-      constexpr int stage = decltype(stage_c)::value;
-      char* sQ = stage ? sq1 : sq0;
-      char* sD = stage ? sd1 : sd0;
-      float* sL = stage ? sl1 : sl0;
-      char* sQp = stage ? sq0 : sq1;  // the previous tile, then the next one
-      char* sDp = stage ? sd0 : sd1;
-      float* sLp = stage ? sl0 : sl1;
-      if (has_prev) cols(sQp, sDp, pf, sf);
-      __syncthreads();
+      constexpr int st = decltype(stage_c)::value;
+      char* sQ = bufq(st);
+      char* sD = bufd(st);
+      float* sL = bufl(st);
       const int qtn = next_tile(qt + 1);
-      if (qtn < nqt) load_tile(qtn, sQp, sDp);
+      if (has_prev) cols(bufq((st + 2) % 3), bufd((st + 2) % 3), pf, sf);  // the previous tile
+      if (qtn < nqt) load_tile(qtn, bufq((st + 1) % 3), bufd((st + 1) % 3));
       f32x4 sacc[4], dpacc[4];
       rows(sQ, sD, sacc, dpacc);
       softmax(qt, sL, sacc, dpacc, pf, sf);
-      if (qtn < nqt) store_tile(sLp);
+      if (qtn < nqt) store_tile(bufl((st + 1) % 3));
       wait_vmem_and_sync();
       has_prev = true;
       qt = qtn;
@@ -708,8 +710,11 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
       if (qt >= nqt) break;
       body(std::integral_constant<int, 1>{});
       last = 1;
+      if (qt >= nqt) break;
+      body(std::integral_constant<int, 2>{});
+      last = 2;
     }
-    if (has_prev) cols(last ? sq1 : sq0, last ? sd1 : sd0, pf, sf);
+    if (has_prev) cols(bufq(last), bufd(last), pf, sf);
   }
   }  // query heads of the group
 
