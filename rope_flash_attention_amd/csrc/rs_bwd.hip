@@ -5,6 +5,7 @@
 // (the same pairwise rotation with sin negated) to dQ' and dK'.  With P recomputed from the
 // saved row normaliser LSE:
 //    P = exp(scale S - LSE),  dV = P^T dO,  dP = dO V^T,  delta_i = sum_d dO_id O_id,
+// (the scores recomputed from the forward's rounded operands: Q' scale log2 e and K')
 //    dS = P o (dP - delta),   dQ' = scale dS K',  dK' = scale dS^T Q',
 //    dQ = R^T dQ',  dK = R^T dK'.
 // These 32x32 kernels serve fp32 inputs and D = 64 (16-bit inputs at D = 128 take the
@@ -96,29 +97,33 @@ struct Stager {
       }
     }
   }
-  __device__ void rotate() {
-    if constexpr (ROT) {
+  // rotated (ROT) as the forward rotates, multiplied by `mul` and rounded once
+  __device__ void rotate(float mul) {
+    if constexpr (!ROT) {
+      if (mul == 1.f) return;
+    }
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float* tf = (const float*)&t[rr][0];
-        if constexpr (ES == 2) {
-          typedef T v8 __attribute__((ext_vector_type(8)));
-          v8 v = *(const v8*)&x[rr];
+    for (int rr = 0; rr < 4; ++rr) {
+      const float* tf = (const float*)&t[rr][0];
+      if constexpr (ES == 2) {
+        typedef T v8 __attribute__((ext_vector_type(8)));
+        v8 v = *(const v8*)&x[rr];
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
-            float2 q = rot_pair(to_f(v[2 * pp]), to_f(v[2 * pp + 1]), tf[2 * pp], tf[2 * pp + 1]);
-            v[2 * pp] = from_f<T>(q.x);
-            v[2 * pp + 1] = from_f<T>(q.y);
-          }
-          x[rr] = *(const uint4*)&v;
-        } else {
-          float* v = (float*)&x[rr];
+        for (int pp = 0; pp < 4; ++pp) {
+          float2 q = make_float2(to_f(v[2 * pp]), to_f(v[2 * pp + 1]));
+          if constexpr (ROT) q = rot_pair_fma(q.x, q.y, tf[2 * pp], tf[2 * pp + 1]);
+          v[2 * pp] = from_f<T>(q.x * mul);
+          v[2 * pp + 1] = from_f<T>(q.y * mul);
+        }
+        x[rr] = *(const uint4*)&v;
+      } else {
+        float* v = (float*)&x[rr];
 #pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-            float2 q = rot_pair(v[2 * pp], v[2 * pp + 1], tf[2 * pp], tf[2 * pp + 1]);
-            v[2 * pp] = q.x;
-            v[2 * pp + 1] = q.y;
-          }
+        for (int pp = 0; pp < 2; ++pp) {
+          float2 q = make_float2(v[2 * pp], v[2 * pp + 1]);
+          if constexpr (ROT) q = rot_pair_fma(q.x, q.y, tf[2 * pp], tf[2 * pp + 1]);
+          v[2 * pp] = q.x * mul;
+          v[2 * pp + 1] = q.y * mul;
         }
       }
     }
@@ -158,9 +163,11 @@ struct Stager {
 };
 
 // B fragments of one lane: row `row` of a [*, D] operand, contraction element
-// t*KSTEP + hh*KPL + e, optionally rotated (fp32 math) and rounded to T.
+// t*KSTEP + hh*KPL + e, optionally rotated (fp32 math, as the forward rotates), multiplied
+// by `mul` and rounded once to T.
 template <typename T, int D, bool ROT>
-__device__ inline void load_row_frags(typename Mf<T>::frag* f, const T* rowp, const float* trow, int hh) {
+__device__ inline void load_row_frags(typename Mf<T>::frag* f, const T* rowp, const float* trow, int hh,
+                                      float mul = 1.f) {
   constexpr int KPL = Mf<T>::KPL, KSTEP = 2 * KPL, NQK = D / KSTEP;
   if constexpr (KPL == 8) {
 #pragma unroll
@@ -175,10 +182,13 @@ __device__ inline void load_row_frags(typename Mf<T>::frag* f, const T* rowp, co
         const float ss[4] = {cs0.y, cs0.w, cs1.y, cs1.w};
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-          float2 rr = rot_pair(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), cc[pp], ss[pp]);
-          x[2 * pp] = from_f<T>(rr.x);
-          x[2 * pp + 1] = from_f<T>(rr.y);
+          float2 rr = rot_pair_fma(to_f(x[2 * pp]), to_f(x[2 * pp + 1]), cc[pp], ss[pp]);
+          x[2 * pp] = from_f<T>(rr.x * mul);
+          x[2 * pp + 1] = from_f<T>(rr.y * mul);
         }
+      } else if (mul != 1.f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = from_f<T>(to_f(x[e]) * mul);
       }
       f[t] = x;
     }
@@ -188,10 +198,10 @@ __device__ inline void load_row_frags(typename Mf<T>::frag* f, const T* rowp, co
       const float2 x = *(const float2*)(rowp + 2 * t);
       if constexpr (ROT) {
         const float2 cs = *(const float2*)(trow + 2 * t);
-        const float2 rr = rot_pair(x.x, x.y, cs.x, cs.y);
-        f[t] = hh ? rr.y : rr.x;
+        const float2 rr = rot_pair_fma(x.x, x.y, cs.x, cs.y);
+        f[t] = (hh ? rr.y : rr.x) * mul;
       } else {
-        f[t] = hh ? x.y : x.x;
+        f[t] = (hh ? x.y : x.x) * mul;
       }
     }
   }
@@ -360,7 +370,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   };
   auto store_tile = [&](int stage) {
     char* base = smem + stage * STAGE;
-    sq.rotate();
+    sq.rotate(p.shp.scale_log2);  // Q' scale log2 e: the forward's score operand
     sq.store_rows(base + OFF_Q);
     sq.store_t(base + OFF_QT);
     sdo.store_rows(base + OFF_DO);
@@ -371,7 +381,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     }
   };
 
-  const float c2 = p.shp.scale_log2;
 #pragma unroll 1
   for (int g = 0; g < p.shp.group; ++g) {
   set_head(hk * p.shp.group + g);
@@ -405,7 +414,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       }
     }
 
-    // P = exp2(S c2 - LSE log2 e) on attended entries, 0 elsewhere; dS = P (dP - delta)
+    // P = exp2(S - LSE log2 e) on attended entries (S from the forward's operands Q' scale
+    // log2 e and K', in log2 units), 0 elsewhere; dS = P (dP - delta)
     const float* sl = (const float*)(base + OFF_L);
     const bool tail = q0 + BMQ > S || k0 + BNK > S;
     const bool diag = CAUSAL && (q0 < k0 + BNK - 1);
@@ -423,7 +433,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
           for (int i = 0; i < 16; ++i) {
             const int qi = min(q0 + 32 * mb + c_idx_sig(i, hh), S - 1);
             const float* mrow = (const float*)mask_row_ptr(p.mask, bm, hm, p.mask.sq ? qi : 0, 4);
-            sacc[mb][i] = fmaf(mrow[jj], p.shp.inv_scale, sacc[mb][i]);
+            sacc[mb][i] = fmaf(mrow[jj], kLog2eF, sacc[mb][i]);
           }
       } else {
 #pragma unroll
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
           for (int i = 0; i < 16; ++i) {
             const int qi = min(q0 + 32 * mb + c_idx_sig(i, hh), S - 1);
             const T* mrow = (const T*)mask_row_ptr(p.mask, bm, hm, p.mask.sq ? qi : 0, ES);
-            sacc[mb][i] = fmaf(to_f(mrow[jj]), p.shp.inv_scale, sacc[mb][i]);
+            sacc[mb][i] = fmaf(to_f(mrow[jj]), kLog2eF, sacc[mb][i]);
           }
       }
     }
@@ -460,7 +470,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
               }
             }
           }
-          const float pv = ok ? fast_exp2(fmaf(s, c2, -lv[e])) : 0.f;
+          const float pv = ok ? fast_exp2(s - lv[e]) : 0.f;
           sacc[mb][8 * c + e] = pv;
           dpacc[mb][8 * c + e] = pv * (dpacc[mb][8 * c + e] - dv[e]);
         }
@@ -525,7 +535,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     char* dvrow = (char*)p.dv + ((int64_t)b * p.dv_sb + (int64_t)hk * p.dv_sh + (int64_t)j * p.dv_ss) * ES;
     store_acc_row<T, D, false>(dvrow, dv_acc, 1.f, nullptr, hh);
     char* dkrow = (char*)p.dk + ((int64_t)b * p.dk_sb + (int64_t)hk * p.dk_sh + (int64_t)j * p.dk_ss) * ES;
-    store_acc_row<T, D, true>(dkrow, dk_acc, p.shp.scale, tab + (int64_t)j * D, hh);
+    store_acc_row<T, D, true>(dkrow, dk_acc, kLn2F, tab + (int64_t)j * D, hh);  // (Q' carried log2 e)
   }
 }
 
@@ -571,7 +581,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
 
   frag qf[NQK], gf[NQK];
   load_row_frags<T, D, !PRE>(qf, (const T*)p.q.ptr + b * p.q.sb + hd * p.q.sh + (int64_t)mc * p.q.ss,
-                             tab + (int64_t)mc * D, hh);
+                             tab + (int64_t)mc * D, hh, p.shp.scale_log2);  // the forward's Q' scale log2 e
   load_row_frags<T, D, false>(gf, (const T*)p.dout.ptr + b * p.dout.sb + hd * p.dout.sh + (int64_t)mc * p.dout.ss,
                               nullptr, hh);
   const int64_t rowid = ((int64_t)b * p.shp.H + hd) * S + mc;
@@ -614,13 +624,12 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
   };
   auto store_tile = [&](int stage) {
     char* base = smem + stage * STAGE;
-    sk.rotate();
+    sk.rotate(1.f);
     sk.store_rows(base + OFF_K);
     sk.store_t(base + OFF_KT);
     sv.store_rows(base + OFF_V);
   };
 
-  const float c2 = p.shp.scale_log2;
   int kt = next_tile(0);
   if (kt < kt_end) {
     load_tile(kt);
@@ -664,7 +673,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
           float mv[8];
           mask_add8<T>(p.mask, mrow, kv0 + 32 * kb + 16 * c + 8 * hh, S, mv);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(mv[e], p.shp.inv_scale, sacc[kb][8 * c + e]);
+          for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(mv[e], kLog2eF, sacc[kb][8 * c + e]);
         }
     }
     const bool check = tail || diag || (MASK == MASK_BOOL && st != TILE_ALL_TRUE);
@@ -689,7 +698,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
             ok = jj < S && m < S && ((bits >> e) & 1u);
             if (CAUSAL) ok = ok && jj <= m;
           }
-          const float pv = ok ? fast_exp2(fmaf(sacc[kb][8 * c + e], c2, -l2)) : 0.f;
+          const float pv = ok ? fast_exp2(sacc[kb][8 * c + e] - l2) : 0.f;
           sacc[kb][8 * c + e] = pv * (dpacc[kb][8 * c + e] - dlt);  // dS^T
         }
       }

@@ -12,10 +12,12 @@
 //            kprep_kernel) and V tiles go straight from memory into LDS, two 64-key tiles per
 //            barrier; per 64-key tile S'^T = K' Q'^T, dP^T = V dO^T (row reads),
 //            dQ'^T += K'^T dS^T (transposed reads).  Launched first: it also writes its rows
-//            of Q' (unscaled, in the input dtype) and their delta = sum_d dO O to the
-//            workspace for dkdv16.
-//  * dkdv16: workgroup = 128 keys (16 per wave); K' (times scale log2 e) and V stay in
-//            registers; Q' (from dq16) and dO tiles of 64 queries go straight from memory
+//            of Q' (times scale log2 e, rounded to the input dtype as the forward rounds them)
+//            and their delta = sum_d dO O to the workspace for dkdv16.
+// Both recompute the scores from the forward's rounded operands (Q' scale log2 e, K'), so
+// that P matches the forward's row log-sum-exp.
+//  * dkdv16: workgroup = 128 keys (16 per wave); K' and V stay in registers; Q' (times
+//            scale log2 e, from dq16) and dO tiles of 64 queries go straight from memory
 //            into LDS; per tile S' = Q' K'^T, dP = dO V^T, dV^T += dO^T P, dK'^T += Q'^T dS;
 //            waves 0-3 and 4-7 work half a tile apart (three LDS buffers per operand, one
 //            barrier per tile, see the kernel).
@@ -100,14 +102,6 @@ __device__ inline F tr_frag(const char* tile, const LaneOffsets& lo_, int s, int
   return f;
 }
 
-// Rotation of one pair with fused multiply-adds (the forward's form for Q and K).
-__device__ inline float2 rot_fma(float x0, float x1, float c, float s) {
-  float2 r;
-  r.x = fmaf(x0, c, -x1 * s);
-  r.y = fmaf(x0, s, x1 * c);
-  return r;
-}
-
 // B fragments of one row (D = 128): element e of fragment t = row[32t + 8g + e]; kRowMul:
 // multiplied by `mul` (a row rotated already); kRowRaw: as stored.
 constexpr int kRowRaw = 0, kRowMul = 2;
@@ -126,9 +120,10 @@ __device__ inline void row_frags(typename Mf<T>::frag* f, const T* row, int g, f
   }
 }
 
-// B fragments of a Q row rotated with its packed table row and multiplied by `mul`, which
-// also writes Q' = R(Q) (unscaled, rounded once to the input dtype) to `dst` unless it is
-// null: the dQ kernel writes these rows for the dK/dV kernel.
+// B fragments of a Q row rotated with its packed table row and multiplied by `mul` (the
+// forward's Q' scale log2 e, rounded once to the input dtype as the forward rounds it), also
+// written to `dst` unless it is null: the dQ kernel writes these rows for the dK/dV kernel,
+// whose scores then use the forward's rounded operands too.
 // Every load is issued before the first store (a store in between would make the compiler
 // issue the later loads again, one round trip each).
 template <typename T>
@@ -147,17 +142,15 @@ __device__ inline void row_frags_qrot(typename Mf<T>::frag* f, T* dst, const T* 
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const float cc[4] = {ta[t].x, ta[t].z, tb[t].x, tb[t].z}, ss[4] = {ta[t].y, ta[t].w, tb[t].y, tb[t].w};
-    v8 y, z;
+    v8 y;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      const float2 r = rot_fma(to_f(x[t][2 * pp]), to_f(x[t][2 * pp + 1]), cc[pp], ss[pp]);
+      const float2 r = rot_pair_fma(to_f(x[t][2 * pp]), to_f(x[t][2 * pp + 1]), cc[pp], ss[pp]);
       y[2 * pp] = from_f<T>(r.x * mul);
       y[2 * pp + 1] = from_f<T>(r.y * mul);
-      z[2 * pp] = from_f<T>(r.x);
-      z[2 * pp + 1] = from_f<T>(r.y);
     }
     f[t] = y;
-    if (dst) *(v8*)(dst + 32 * t + 8 * g) = z;
+    if (dst) *(v8*)(dst + 32 * t + 8 * g) = y;
   }
 }
 
@@ -434,8 +427,11 @@ __global__ __launch_bounds__(512, 1) void dq16_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// K arrives rotated (K' in the workspace): its rows are only scaled.
-template <typename T, int MASK, bool CAUSAL>
+// K arrives rotated (K' in the workspace).  QS: the Q' tiles (from the dQ kernel) carry the
+// forward's factor scale log2 e, so the scores are the forward's products of its rounded
+// operands and K' is used as it is; dK' then carries log2 e, taken out with ln 2 at the end.
+// Otherwise (the quantized backward's dequantized Q') K' is scaled here.
+template <typename T, int MASK, bool CAUSAL, bool QS>
 __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   using frag = typename Mf<T>::frag;
   using M = M16<T>;
@@ -479,9 +475,10 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
   const float* lse = nullptr;
   const float* dlt = nullptr;
 
-  // K' (times scale log2 e) and V of this lane's key as B fragments
+  // K' (times scale log2 e unless the Q' tiles carry it) and V of this lane's key as B fragments
   frag kf[4], vf[4];
-  row_frags<T, kRowMul>(kf, (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh + (int64_t)jc * p.k.ss, g, p.shp.scale_log2);
+  row_frags<T, QS ? kRowRaw : kRowMul>(kf, (const T*)p.k.ptr + b * p.k.sb + hk * p.k.sh + (int64_t)jc * p.k.ss, g,
+                                       p.shp.scale_log2);
   row_frags<T, kRowRaw>(vf, (const T*)p.v.ptr + b * p.v.sb + hk * p.v.sh + (int64_t)jc * p.v.ss, g, 1.f);
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 dv[8], dk[8];
@@ -731,7 +728,7 @@ __global__ __launch_bounds__(512, 1) void dkdv16_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i) w[i] = from_f<T>(dv[db][i]);
       *(v4*)(vrow + d0 * 2) = w;
       const float4 cs = *(const float4*)(trow + d0);
-      const float sc = p.shp.scale;
+      const float sc = QS ? kLn2F : p.shp.scale;
       const float2 a = rot_pair_t(dk[db][0] * sc, dk[db][1] * sc, cs.x, cs.y);
       const float2 e = rot_pair_t(dk[db][2] * sc, dk[db][3] * sc, cs.z, cs.w);
       w[0] = from_f<T>(a.x);
@@ -756,7 +753,7 @@ static int launch_bwd16_t(const BwdParams& p, void* stream) {
   if (e) return e;
   const int nkt = (S + 127) / 128;
   const int grid_k = (CAUSAL ? (nkt + 1) / 2 : nkt) * p.shp.B * p.shp.Hkv;
-  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL>), dim3(grid_k), dim3(512), 0, (hipStream_t)stream, p);
+  hipLaunchKernelGGL((dkdv16_kernel<T, MASK, CAUSAL, !QROT>), dim3(grid_k), dim3(512), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 

@@ -185,6 +185,19 @@ __device__ inline float2 rot_pair(float x0, float x1, float c, float s) {
   return r;
 }
 
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kLn2F = 0.6931471805599453f;
+
+// Rotation of one pair with fused multiply-adds: the form the forward uses for Q and K (the
+// quantized variants use rot_pair), and the backward with it, so that both round the same
+// rotated values.
+__device__ inline float2 rot_pair_fma(float x0, float x1, float c, float s) {
+  float2 r;
+  r.x = fmaf(x0, c, -x1 * s);
+  r.y = fmaf(x0, s, x1 * c);
+  return r;
+}
+
 // Inverse (transposed) rotation of a gradient pair: (g0 c + g1 s, -g0 s + g1 c).
 __device__ inline float2 rot_pair_t(float g0, float g1, float c, float s) {
 #pragma clang fp contract(off)

@@ -41,8 +41,6 @@ struct FwdCfg {
   static constexpr int NT = 2 * BM;                      // threads: one wave per 32 rows
 };
 
-constexpr float kLog2eF = 1.4426950408889634f;
-constexpr float kLn2F = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.f;  // rescale when a row max grows by more than 2^8
 
 // Row-sum of eight rounded probabilities (one fragment) into acc.
@@ -65,14 +63,6 @@ __device__ inline float frag_sum(f16x8 f, float acc) {
     acc = __builtin_amdgcn_fdot2(x, one, acc, false);
   }
   return acc;
-}
-
-// Rotation of one pair with fused multiply-adds (the int8 variant uses rot_pair instead).
-__device__ inline float2 rot_pair_fma(float x0, float x1, float c, float s) {
-  float2 r;
-  r.x = fmaf(x0, c, -x1 * s);
-  r.y = fmaf(x0, s, x1 * c);
-  return r;
 }
 
 constexpr int kMaxStateTiles = kMaxBoolMaskSeq / 32;  // key tiles (32 keys or more) of a bool-masked call

@@ -347,7 +347,6 @@ AttnShape attn_shape(const Shape& s) {
   a.group = s.Hkv > 0 ? (int)(s.H / s.Hkv) : 1;
   a.scale = s.scale;
   a.scale_log2 = (float)((double)s.scale * 1.4426950408889634);
-  a.inv_scale = (float)(1.0 / (double)s.scale);
   return a;
 }
 

@@ -43,7 +43,6 @@ struct AttnShape {
                      // query head h reads K/V head h / group); Hkv == H, group == 1 otherwise
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
-  float inv_scale;   // 1 / scale
 };
 
 // Packed rotation table: per (sample, position) D/2 pairs of (cos, sin) as float2.
