@@ -89,3 +89,85 @@ def test_random_case(case):
         torch.cuda.synchronize()
         check_out("O", to64(o), O_ref, c["dtype"])
         check_lse(to64(lse), L_ref, c["dtype"])
+
+
+# ---- forward-only variants ----------------------------------------------------------------
+# K rotated by its own pass, the Q/K RMSNorm prologue, fp32 Q/K beside 16-bit V, and the
+# blockwise int8 / int4 forwards in both quantization modes, each under the mask kinds it
+# takes, on random shapes.
+
+N_VARIANT_CASES = 32
+MODES = ["k_prepass", "rmsnorm", "f32qk", "f32qk_rmsnorm", "int8", "int4", "int8_prepass", "int4_prepass"]
+
+
+def _variant_cases():
+    r = np.random.default_rng(20261204)
+    out = []
+    for i in range(N_VARIANT_CASES):
+        mode = MODES[i % len(MODES)]
+        B = int(r.choice([1, 2]))
+        H = int(r.choice([1, 2, 4, 6]))
+        Hkv = int(r.choice([d for d in range(1, H + 1) if H % d == 0]))
+        S = int(r.integers(1, 520))
+        D = int(r.choice([64, 128]))
+        vdtype = str(r.choice(["bf16", "f16"]))
+        kinds = ["none", "causal", "bool"] + (["additive"] if mode.startswith("int") else [])
+        variant = str(r.choice(kinds))
+        shape = None
+        if variant in ("bool", "additive"):
+            shape = tuple(int(full) if r.random() < 0.5 else 1 for full in (B, H, S))
+            shape = shape + (S if r.random() < 0.8 else 1,)
+        scale = None if r.random() < 0.6 else float(r.uniform(0.05, 0.3))
+        out.append(dict(i=i, mode=mode, B=B, H=H, Hkv=Hkv, S=S, D=D, vdtype=vdtype, variant=variant,
+                        shape=shape, scale=scale, per_sample=bool(r.random() < 0.3)))
+    return out
+
+
+VARIANT_CASES = _variant_cases()
+
+
+@pytest.mark.parametrize("case", VARIANT_CASES, ids=lambda c: f"v{c['i']}_{c['mode']}_b{c['B']}h{c['H']}kv{c['Hkv']}"
+                         f"s{c['S']}d{c['D']}_{c['vdtype']}_{c['variant']}")
+def test_random_forward_variant(case):
+    from oracle import rope_sdpa_forward_quant
+
+    c = case
+    kw = {}
+    if c["variant"] == "causal":
+        kw = dict(causal=True)
+    elif c["variant"] != "none":
+        kw = dict(mask_kind=c["variant"], mask_shape=c["shape"])
+    seed = 1900 + c["i"]
+    w = syn.random_small(c["B"], c["H"], c["S"], c["D"], c["vdtype"], seed=seed, per_sample_tables=c["per_sample"],
+                         kv_heads=c["Hkv"] if c["Hkv"] < c["H"] else None, **kw)
+    q, k = w.q, w.k
+    mode = c["mode"]
+    if mode.startswith("f32qk"):  # fp32 Q and K with values off the 16-bit grid
+        q = syn.normal(seed, syn.STREAM_Q, tuple(w.q.shape), "f32")
+        k = syn.normal(seed, syn.STREAM_K, tuple(w.k.shape), "f32")
+    norm = None
+    if mode.endswith("rmsnorm"):
+        g = np.random.default_rng(seed)
+        norm = (torch.from_numpy(g.uniform(0.5, 1.5, c["D"]).astype(np.float32)),
+                torch.from_numpy(g.uniform(0.5, 1.5, c["D"]).astype(np.float32)), 1e-6)
+    d = dev()
+    m = w.mask.to(d) if w.mask is not None else None
+    gkw = dict(attn_mask=m, is_causal=w.causal, scale=c["scale"])
+    okw = dict(mask=w.mask, mask_kind=w.mask_kind, causal=w.causal, scale=c["scale"], workers=8)
+    if mode.startswith("int"):
+        gkw["quantization"] = mode
+        O_ref, L_ref = rope_sdpa_forward_quant(q, k, w.v, w.cos, w.sin, bits=4 if mode.startswith("int4") else 8,
+                                               **okw)
+    else:
+        if mode == "k_prepass":
+            gkw["k_prepass"] = True
+        if norm is not None:
+            gkw.update(q_norm_weight=norm[0].to(d), k_norm_weight=norm[1].to(d), norm_eps=norm[2])
+            okw.update(q_norm_weight=norm[0], k_norm_weight=norm[1], norm_eps=norm[2])
+        O_ref, L_ref = rope_sdpa_forward(q, k, w.v, w.cos, w.sin, **okw)
+    with torch.no_grad():
+        o, lse = rfa.rope_sdpa_fwd_with_lse(q.to(d), k.to(d), w.v.to(d), w.cos.to(d), w.sin.to(d), **gkw)
+    torch.cuda.synchronize()
+    assert o.dtype == w.v.dtype
+    check_out("O", to64(o), O_ref, c["vdtype"])
+    check_lse(to64(lse), L_ref, c["vdtype"])
