@@ -18,7 +18,7 @@ from parity_util import check_grad, check_lse, check_out, dev, to64
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = 100
 
 
 def _cases():
@@ -96,7 +96,7 @@ def test_random_case(case):
 # blockwise int8 / int4 forwards in both quantization modes, each under the mask kinds it
 # takes, on random shapes.
 
-N_VARIANT_CASES = 32
+N_VARIANT_CASES = 64
 MODES = ["k_prepass", "rmsnorm", "f32qk", "f32qk_rmsnorm", "int8", "int4", "int8_prepass", "int4_prepass"]
 
 
