@@ -61,7 +61,7 @@ typedef enum {
   RS_ERR_SHAPE = -3,       /* sizes inconsistent or not supported (e.g. D not 64/128) */
   RS_ERR_STRIDE = -4,      /* stride[3] != 1 or a stride not a multiple of 16 bytes */
   RS_ERR_ALIGN = -5,       /* base pointer not 16-byte aligned (workspace: 256-byte) */
-  RS_ERR_UNSUPPORTED = -6, /* valid request this build does not implement */
+  RS_ERR_UNSUPPORTED = -6, /* valid request the library does not implement */
   RS_ERR_WORKSPACE = -7,   /* workspace NULL or smaller than rope_sdpa_workspace_size() */
   RS_ERR_INVALID = -8,     /* bad flag, mask kind, scale, or causal together with a mask */
   RS_ERR_NO_DEVICE = -9,   /* no usable gfx950 device is current */
