@@ -171,3 +171,58 @@ def test_random_forward_variant(case):
     assert o.dtype == w.v.dtype
     check_out("O", to64(o), O_ref, c["vdtype"])
     check_lse(to64(lse), L_ref, c["vdtype"])
+
+
+# ---- forwards whose units are cut into key ranges -----------------------------------------
+# With at least 16 key tiles and fewer units than resident workgroups, the forward cuts the
+# units' key ranges into pieces on separate workgroups and merges them (no causal masking);
+# these cases reach that path with random lengths, heads, masks and dtypes.
+
+N_SPLIT_CASES = 24
+
+
+def _split_cases():
+    r = np.random.default_rng(20261205)
+    out = []
+    for i in range(N_SPLIT_CASES):
+        B = int(r.choice([1, 2]))
+        H = int(r.choice([1, 2, 3]))
+        Hkv = int(r.choice([d for d in range(1, H + 1) if H % d == 0]))
+        S = int(r.integers(1024, 2600))
+        D = int(r.choice([64, 128]))
+        dtype = str(r.choice(["bf16", "f16", "f32"]))
+        variant = str(r.choice(["none", "bool", "additive"]))
+        shape = None
+        if variant != "none":
+            shape = (int(r.choice([1, B])), int(r.choice([1, H])), int(r.choice([1, S])), S)
+        out.append(dict(i=i, B=B, H=H, Hkv=Hkv, S=S, D=D, dtype=dtype, variant=variant, shape=shape,
+                        scale=None if r.random() < 0.6 else float(r.uniform(0.05, 0.3)),
+                        lse=bool(r.random() < 0.7)))
+    return out
+
+
+SPLIT_CASES = _split_cases()
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: f"s{c['i']}_b{c['B']}h{c['H']}kv{c['Hkv']}s{c['S']}"
+                         f"d{c['D']}_{c['dtype']}_{c['variant']}{'_lse' if c['lse'] else ''}")
+def test_random_split_forward(case):
+    c = case
+    kw = {} if c["variant"] == "none" else dict(mask_kind=c["variant"], mask_shape=c["shape"])
+    w = syn.random_small(c["B"], c["H"], c["S"], c["D"], c["dtype"], seed=2900 + c["i"],
+                         kv_heads=c["Hkv"] if c["Hkv"] < c["H"] else None, **kw)
+    d = dev()
+    m = w.mask.to(d) if w.mask is not None else None
+    gkw = dict(attn_mask=m, scale=c["scale"])
+    with torch.no_grad():
+        if c["lse"]:
+            o, lse = rfa.rope_sdpa_fwd_with_lse(w.q.to(d), w.k.to(d), w.v.to(d), w.cos.to(d), w.sin.to(d), **gkw)
+        else:
+            o = rfa.rope_scaled_dot_product_attention(w.q.to(d), w.k.to(d), w.v.to(d), w.cos.to(d), w.sin.to(d),
+                                                      **gkw)
+    torch.cuda.synchronize()
+    O_ref, L_ref = rope_sdpa_forward(w.q, w.k, w.v, w.cos, w.sin, mask=w.mask, mask_kind=w.mask_kind,
+                                     scale=c["scale"], workers=8)
+    check_out("O", to64(o), O_ref, c["dtype"])
+    if c["lse"]:
+        check_lse(to64(lse), L_ref, c["dtype"])
