@@ -7,6 +7,8 @@ tables, explicit or default scale, and contiguous or [B, S, H, D]-strided inputs
 combinations the fixed grids do not list are covered too.  The case list is fixed by the
 seed below; a failure names its case.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,7 +20,10 @@ from parity_util import check_grad, check_lse, check_out, dev, to64
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 100
+# RS_SWEEP_SCALE multiplies the case counts (a longer sweep on request; the seeds stay fixed,
+# so the default cases are always the first ones)
+_SCALE = max(1, int(os.environ.get("RS_SWEEP_SCALE", "1")))
+N_CASES = 100 * _SCALE
 
 
 def _cases():
@@ -96,7 +101,7 @@ def test_random_case(case):
 # blockwise int8 / int4 forwards in both quantization modes, each under the mask kinds it
 # takes, on random shapes.
 
-N_VARIANT_CASES = 64
+N_VARIANT_CASES = 64 * _SCALE
 MODES = ["k_prepass", "rmsnorm", "f32qk", "f32qk_rmsnorm", "int8", "int4", "int8_prepass", "int4_prepass"]
 
 
@@ -178,7 +183,7 @@ def test_random_forward_variant(case):
 # units' key ranges into pieces on separate workgroups and merges them (no causal masking);
 # these cases reach that path with random lengths, heads, masks and dtypes.
 
-N_SPLIT_CASES = 24
+N_SPLIT_CASES = 24 * _SCALE
 
 
 def _split_cases():
