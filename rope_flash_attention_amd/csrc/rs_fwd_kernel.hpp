@@ -417,21 +417,31 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     const int bm = p.mask.sb ? b : 0, hm = p.mask.sh ? hd : 0;
     mbase = mask_row_ptr(p.mask, bm, hm, 0, 2);
   }
+  // The 1 KB load i of wave w covers tile rows 32w + 8i + lane/8, 16-byte chunk lane % 8 of
+  // each: the swizzled chunk is (lane % 8) ^ (lane / 8) ^ (i & 1), so a lane's offset is one
+  // of two values (even or odd i) plus 8i rows (added to the per-lane offset, which the
+  // descriptor's range check covers: rows at or past S read as zero).
+  constexpr int ML = BM * MROW / 1024 / NW;
+  static_assert(!kMaskTileLds || (MROW == 128 && ML * 1024 == 32 * MROW), "mask tile: 32 rows of 128 bytes per wave");
+  uint32_t m_voff[2] = {0u, 0u};
+  uint32_t m_lds = 0u;  // byte of this lane's 16-byte chunk 0 of its row, XOR-able with 16 (4kb + 2c)
+  if constexpr (kMaskTileLds) {
+    const int row = 32 * wave + (lane >> 3);
+    const int rstride = (int)p.mask.sq * 2;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      m_voff[par] = (uint32_t)(row * rstride + ((((lane & 7) ^ (lane >> 3)) ^ par) << 4));
+    const int rl = 32 * wave + r;
+    m_lds = (uint32_t)(rl * MROW + ((hh ^ msw(rl)) << 4));
+  }
   auto dma_mask = [&](int kt, char* sM) __attribute__((always_inline)) {
     if constexpr (kMaskTileLds) {
-      constexpr int ML = BM * MROW / 1024 / NW;
+      const int rstride = (int)p.mask.sq * 2;
       const __amdgpu_buffer_rsrc_t rs =
-          rows_rsrc((const char*)mbase + kt * BN * 2, q0, S, (int)p.mask.sq * 2, (S - kt * BN) * 2);
-      // per-lane offsets recomputed here (cheap) rather than held in registers throughout
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
+          rows_rsrc((const char*)mbase + kt * BN * 2, q0, S, rstride, (S - kt * BN) * 2);
 #pragma unroll
-      for (int i = 0; i < ML; ++i) {
-        const int byte = (wave * ML + i) * 1024 + ln * 16;
-        const int row = byte / MROW, pch = (byte % MROW) / 16;
-        const uint32_t off = (uint32_t)(row * (int)p.mask.sq * 2 + ((pch ^ msw(row)) << 4));
-        buffer_load_lds16(rs, sM + (wave * ML + i) * 1024, off, 0);
-      }
+      for (int i = 0; i < ML; ++i)
+        buffer_load_lds16(rs, sM + (wave * ML + i) * 1024, m_voff[i & 1] + (uint32_t)(8 * i * rstride), 0);
     }
   };
 
@@ -644,16 +654,14 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     if constexpr (MASK == MASK_BOOL) st = tile_state(kt);
     if constexpr (MASK == MASK_ADD || MASK == MASK_ADD_TILE) {
       if constexpr (kMaskTileLds) {
-        // row 32 wave + r of the tile, keys 32kb + 16c + 8hh .. +7 = logical chunk 4kb + 2c + hh
-        // (addresses recomputed per tile, not held in registers across the loop)
-        int rl = 32 * wave + r;
-        asm volatile("" : "+v"(rl));
+        // row 32 wave + r of the tile, keys 32kb + 16c + 8hh .. +7 = logical chunk 4kb + 2c + hh,
+        // stored at chunk (4kb + 2c + hh) ^ msw(row): m_lds ^ 16 (4kb + 2c)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             typedef T v8 __attribute__((ext_vector_type(8)));
-            const v8 mv = *(const v8*)(sM + rl * MROW + (((4 * kb + 2 * c + hh) ^ msw(rl)) << 4));
+            const v8 mv = *(const v8*)(sM + (m_lds ^ (uint32_t)(16 * (4 * kb + 2 * c))));
 #pragma unroll
             for (int e = 0; e < 8; ++e) sacc[kb][8 * c + e] = fmaf(to_f(mv[e]), kLog2eF, sacc[kb][8 * c + e]) - m_base;
           }
