@@ -226,6 +226,34 @@ __device__ inline float xhalf_sum(float x) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum over the 64 lanes of a wave of non-negative, non-NaN floats (whose bit patterns
+// order like unsigned integers): four DPP steps within each row of 16 lanes (neighbour pairs,
+// pairs of pairs, half-row mirror, row mirror), then the four rows' first lanes through
+// scalar registers.  Exact, so the same as any other reduction order.  All lanes active.
+__device__ inline float wave_max_nonneg(float v) {
+  uint32_t x = __float_as_uint(v);
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));  // row_mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return __uint_as_float(max(max(r0, r1), max(r2, r3)));
+}
+
+// Blockwise quantizer code of x: round half to even of the fp32 product x * inv, returned in
+// the low byte (two's complement) of the result.  Adding 1.5 * 2^23 to the product, with the
+// sum rounded to fp32, rounds it to an integer (ties to even) kept in the low mantissa bits;
+// valid for |x * inv| < 2^22.  The two operations stay separate (no fused multiply-add):
+// the product is rounded first, as the definition says.  Callers have |x| <= amax and
+// inv = fp32(QMAX / amax), so the product never leaves [-QMAX, QMAX] after rounding and
+// no clamp is needed.
+__device__ inline uint32_t quant_bits(float x, float inv) {
+#pragma clang fp contract(off)
+  const float y = x * inv + 12582912.0f;
+  return __float_as_uint(y);
+}
+
 // Work-item order for a 1-D grid: consecutive workgroups land on different XCDs (round
 // robin over 8), so renumber such that each XCD receives a contiguous range of items and
 // neighbouring query tiles of one head share that XCD's L2.

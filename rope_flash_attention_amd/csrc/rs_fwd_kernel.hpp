@@ -225,8 +225,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
       }
     }
     if (m >= S) amx = 0.f;  // a block's amax is over its valid rows
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amx = fmaxf(amx, __shfl_xor(amx, off, 64));
+    amx = wave_max_nonneg(amx);
     // a 64-row block is the 32 rows of waves 2j and 2j + 1
     __shared__ float s_qamax[NW];
     if (lane == 0) s_qamax[wave] = amx;
@@ -238,10 +237,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     for (int t = 0; t < NQ8; ++t) {
       uint32_t wv[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float c = fminf(fmaxf(__builtin_rintf(qv[t][e] * inv), -QMAX), QMAX);  // half to even
-        wv[e >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (e & 3));
-      }
+      for (int e = 0; e < 16; ++e) wv[e >> 2] |= (quant_bits(qv[t][e], inv) & 0xffu) << (8 * (e & 3));
       qf[t] = i32x4{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
     }
     q8scale = qsc * c2;
@@ -525,8 +521,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
           amx = fmaxf(amx, fmaxf(fabsf(rr.x), fabsf(rr.y)));  // rows past S were read as zeros
         }
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) amx = fmaxf(amx, __shfl_xor(amx, off, 64));
+      amx = wave_max_nonneg(amx);
       const int slot = sK == sk0 ? 0 : 1;
       if (lane == 0) s_kamax[slot][wave] = amx;
       __syncthreads();
@@ -538,10 +533,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
       for (int it = 0; it < KCPT; ++it) {
         uint32_t wv[2] = {0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float c = fminf(fmaxf(__builtin_rintf(kv[it][e] * inv), -QMAX), QMAX);
-          wv[e >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (e & 3));
-        }
+        for (int e = 0; e < 8; ++e) wv[e >> 2] |= (quant_bits(kv[it][e], inv) & 0xffu) << (8 * (e & 3));
         const int key = k_key0 + it * KROWS_PER_IT, lrow = perm_row(key);
         *(uint2*)(sK + lrow * D + (((k_cc >> 1) ^ k8sw(lrow)) << 4) + (k_cc & 1) * 8) = make_uint2(wv[0], wv[1]);
         if constexpr (QEXP) {
