@@ -405,6 +405,54 @@ def summarize_counters(mfma_db, fetch_db, write_db, command):
     return "\n".join(out)
 
 
+STALL_PASSES = (
+    ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES",
+     "GRBM_GUI_ACTIVE"),
+    ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"),
+)
+
+
+def summarize_stalls(a_db, b_db, command):
+    """Per kernel launch: how the matrix cores and the waves spend their cycles, from two
+    rocprofv3 --pmc runs of `bench.py --pmc-legs` with the counters of STALL_PASSES.
+    Fractions of the dispatch's cycles per SIMD (1024 SIMDs; GRBM_GUI_ACTIVE / 8 cycles):
+    matrix core busy (SQ_VALU_MFMA_BUSY_CYCLES) and busy while a plain vector instruction
+    issues (SQ_VALU_MFMA_COEXEC_CYCLES).  Fractions of the waves' cycles (SQ_WAVE_CYCLES;
+    all three in units of 4 cycles): waiting for anything (s_waitcnt, barriers:
+    SQ_WAIT_ANY), waiting for an instruction to issue (SQ_WAIT_INST_ANY) and for an LDS
+    instruction to issue (SQ_WAIT_INST_LDS).  Instruction mix per matrix instruction:
+    SQ_INSTS_VALU (which counts the matrix instructions too) and SQ_INSTS_LDS over
+    SQ_INSTS_MFMA."""
+    import sqlite3
+
+    data = {}
+    for db, counters in zip((a_db, b_db), STALL_PASSES):
+        con = sqlite3.connect(db)
+        q = ("select kernel_name, grid_size, counter_name, avg(value), avg(duration) from counters_collection "
+             "where counter_name in (%s) group by kernel_name, grid_size, counter_name" % ",".join("?" * len(counters)))
+        for name, grid, cname, val, dur in con.execute(q, counters).fetchall():
+            e = data.setdefault((name, grid), {})
+            e[cname if cname not in e else cname + "_b"] = val
+            e.setdefault("dur_ns", dur)
+    out = [f"command: {command}", "",
+           f"{'kernel':58s} {'grid':>8s} {'us':>8s} {'MFMA':>6s} {'co-iss':>6s} {'wait':>6s} {'issue':>6s} "
+           f"{'LDSiss':>6s} {'VALU/MF':>7s} {'LDS/MF':>7s}"]
+    for (name, grid), e in sorted(data.items(), key=lambda kv: -kv[1].get("dur_ns", 0)):
+        if not (name.startswith("_ZN2rs") or "rs::" in name) or e.get("dur_ns", 0) < 50e3:
+            continue
+        if not all(c in e for c in ("GRBM_GUI_ACTIVE", "SQ_WAVE_CYCLES", "SQ_INSTS_MFMA")) or not e["SQ_INSTS_MFMA"]:
+            continue
+        cyc = e["GRBM_GUI_ACTIVE"] / 8 * 1024
+        wave = e["SQ_WAVE_CYCLES"]
+        wave_b = e.get("SQ_WAVE_CYCLES_b", wave)
+        f = lambda v: f"{100 * v:5.1f}%"
+        out.append(f"{name[:58]:58s} {grid:8d} {e['dur_ns'] / 1000:8.1f} {f(e['SQ_VALU_MFMA_BUSY_CYCLES'] / cyc)} "
+                   f"{f(e['SQ_VALU_MFMA_COEXEC_CYCLES'] / cyc)} {f(e['SQ_WAIT_ANY'] / wave)} "
+                   f"{f(e['SQ_WAIT_INST_ANY'] / wave)} {f(e['SQ_WAIT_INST_LDS'] / wave_b)} "
+                   f"{e['SQ_INSTS_VALU'] / e['SQ_INSTS_MFMA']:7.2f} {e['SQ_INSTS_LDS'] / e['SQ_INSTS_MFMA']:7.2f}")
+    return "\n".join(out)
+
+
 def summarize_rocpd(db_path, command):
     """Text summary of a rocprofv3 kernel trace: per kernel and grid size, calls and durations."""
     import sqlite3
@@ -484,6 +532,9 @@ def main():
                     help="run the counter workloads (tiny fp32, FLUX, FLUX additive 4-D, copy probe) and exit")
     ap.add_argument("--counters", nargs=3, metavar=("MFMA_DB", "FETCH_DB", "WRITE_DB"),
                     help="print matrix-core busy fraction and HBM bytes per forward launch and exit")
+    ap.add_argument("--stalls", nargs=2, metavar=("A_DB", "B_DB"),
+                    help="print matrix-core, issue and wait fractions per kernel launch from two "
+                         "rocprofv3 --pmc runs (the counters of STALL_PASSES) and exit")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="print HBM bytes per forward launch from two rocprofv3 --pmc results databases and exit")
     args = ap.parse_args()
@@ -495,6 +546,9 @@ def main():
         return
     if args.counters:
         print(summarize_counters(*args.counters, args.command))
+        return
+    if args.stalls:
+        print(summarize_stalls(*args.stalls, args.command))
         return
     if args.pmc_legs:
         pmc_legs(args.pmc_legs)
