@@ -363,8 +363,26 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // would make every wait for them also wait for all outstanding LDS reads)
   // (the host limits bool-masked sequences to kMaxStateTiles key tiles)
   __shared__ uint8_t s_tstate[MASK == MASK_BOOL ? kMaxStateTiles : 1];
+  // and s_next[kt] = the first tile at or after kt that is not all-false (kt_end if none):
+  // the key loop then finds its next tile with one LDS read instead of a scan.  Wave 0 fills
+  // it in chunks of 64 tiles from the end: a ballot of the chunk's non-skipped tiles gives
+  // each lane the next one at or after it, and the chunk's first one carries to the chunk
+  // before.
+  __shared__ uint16_t s_next[MASK == MASK_BOOL ? kMaxStateTiles : 1];
   if constexpr (MASK == MASK_BOOL) {
     for (int i = tid; i < kt_end; i += NT) s_tstate[i] = (uint8_t)tile_state_mem(i);
+    __syncthreads();
+    if (wave == 0) {
+      int carry = kt_end;
+      for (int c0 = kt_end > 0 ? ((kt_end - 1) / 64) * 64 : -64; c0 >= 0; c0 -= 64) {
+        const int i = c0 + lane;
+        const bool keep = i < kt_end && s_tstate[i] != TILE_ALL_FALSE;
+        const uint64_t vm = __builtin_amdgcn_ballot_w64(keep);
+        const uint64_t rest = vm >> lane;
+        if (i < kt_end) s_next[i] = (uint16_t)(rest ? i + (int)__builtin_ctzll(rest) : carry);
+        carry = vm ? c0 + (int)__builtin_ctzll(vm) : carry;
+      }
+    }
     __syncthreads();
   }
   auto tile_state = [&](int kt) __attribute__((always_inline)) -> uint32_t {
@@ -378,8 +396,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // result, the same in every lane, is read from the first lane to keep it scalar)
   auto next_tile = [&](int kt) __attribute__((always_inline)) -> int {
     if constexpr (MASK == MASK_BOOL) {
-      while (kt < kt_end && tile_state(kt) == TILE_ALL_FALSE) ++kt;
-      kt = __builtin_amdgcn_readfirstlane(kt);
+      if (kt < kt_end) kt = __builtin_amdgcn_readfirstlane((int)s_next[kt]);
     }
     return kt;
   };
