@@ -363,11 +363,11 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   // would make every wait for them also wait for all outstanding LDS reads)
   // (the host limits bool-masked sequences to kMaxStateTiles key tiles)
   __shared__ uint8_t s_tstate[MASK == MASK_BOOL ? kMaxStateTiles : 1];
-  // and s_next[kt] = the first tile at or after kt that is not all-false (kt_end if none):
-  // the key loop then finds its next tile with one LDS read instead of a scan.  Wave 0 fills
-  // it in chunks of 64 tiles from the end: a ballot of the chunk's non-skipped tiles gives
-  // each lane the next one at or after it, and the chunk's first one carries to the chunk
-  // before.
+  // and s_next[kt] = the first tile at or after kt that is not all-false (kt_end if none) in
+  // bits 0-13, with that tile's state in bits 14-15: the key loop then finds its next tile and
+  // its state with one LDS read instead of a scan.  Wave 0 fills it in chunks of 64 tiles from
+  // the end: a ballot of the chunk's non-skipped tiles gives each lane the next one at or
+  // after it, and the chunk's first one carries to the chunk before.
   __shared__ uint16_t s_next[MASK == MASK_BOOL ? kMaxStateTiles : 1];
   if constexpr (MASK == MASK_BOOL) {
     for (int i = tid; i < kt_end; i += NT) s_tstate[i] = (uint8_t)tile_state_mem(i);
@@ -379,27 +379,26 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
         const bool keep = i < kt_end && s_tstate[i] != TILE_ALL_FALSE;
         const uint64_t vm = __builtin_amdgcn_ballot_w64(keep);
         const uint64_t rest = vm >> lane;
-        if (i < kt_end) s_next[i] = (uint16_t)(rest ? i + (int)__builtin_ctzll(rest) : carry);
+        const int nx = rest ? i + (int)__builtin_ctzll(rest) : carry;
+        if (i < kt_end) s_next[i] = (uint16_t)(nx | (nx < kt_end ? (int)s_tstate[nx] << 14 : 0));
         carry = vm ? c0 + (int)__builtin_ctzll(vm) : carry;
       }
     }
     __syncthreads();
   }
-  auto tile_state = [&](int kt) __attribute__((always_inline)) -> uint32_t {
-    if constexpr (MASK == MASK_BOOL) {
-      return (uint32_t)s_tstate[kt];
-    } else {
-      return TILE_MIXED;
-    }
-  };
   // (the states are read from LDS, which the compiler takes for per-lane values: the
   // result, the same in every lane, is read from the first lane to keep it scalar)
+  // (bool masks: the tile index and its state in bits 14-15; a tile at or past kt_end is
+  // returned as it is, with state 0)
   auto next_tile = [&](int kt) __attribute__((always_inline)) -> int {
     if constexpr (MASK == MASK_BOOL) {
       if (kt < kt_end) kt = __builtin_amdgcn_readfirstlane((int)s_next[kt]);
     }
     return kt;
   };
+  // index and state parts of next_tile's result (other masks: the index alone, any size)
+  auto tile_idx = [](int v) __attribute__((always_inline)) -> int { return MASK == MASK_BOOL ? v & 0x3fff : v; };
+  auto tile_st = [](int v) __attribute__((always_inline)) -> uint32_t { return MASK == MASK_BOOL ? (uint32_t)v >> 14 : 0u; };
 
   // ---- global -> register staging of one KV tile ------------------------------------------
   uint4 kx[KCPT];
@@ -655,12 +654,13 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   };
 
   // exclusions of one tile: sequence tail, causal diagonal, masks
-  auto fixup = [&](int kt, f32x16* sacc, const char* sM) __attribute__((always_inline)) {
+  // (bool masks: st = the tile's state, carried with its index from the lookup)
+  auto fixup = [&](int kt, uint32_t st_in, f32x16* sacc, const char* sM) __attribute__((always_inline)) {
     const int kv0 = kt * BN;
     const bool tail = kv0 + BN > S;
     const bool diag = CAUSAL && (kv0 + BN - 1 > q0);
     uint32_t st = TILE_ALL_TRUE;
-    if constexpr (MASK == MASK_BOOL) st = tile_state(kt);
+    if constexpr (MASK == MASK_BOOL) st = st_in;
     if constexpr (MASK == MASK_ADD || MASK == MASK_ADD_TILE) {
       if constexpr (kMaskTileLds) {
         // row 32 wave + r of the tile, keys 32kb + 16c + 8hh .. +7 = logical chunk 4kb + 2c + hh,
@@ -827,8 +827,13 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   f32x16 sacc[2][NKB];
   float mx = 0.f;     // row max of the current tile's scores (valid where need was computed)
   bool need = false;  // the current tile raises some row max by more than 2^8
-  int kt = next_tile(t0);
-  int kt1 = kt < kt_end ? next_tile(kt + 1) : kt_end;
+  const int ktp = next_tile(t0);
+  int kt = tile_idx(ktp);
+  const int kt1p = kt < kt_end ? next_tile(kt + 1) : kt_end;
+  int kt1 = tile_idx(kt1p);
+  uint32_t st_t1 = tile_st(kt1p);  // bool masks: state of t_{i+1}
+  // bool masks: the lookup of the tile after t_{i+1}, one step ahead
+  int kt2p = kt1 < kt_end ? next_tile(kt1 + 1) : kt_end;
   float ks0 = 0.f, ks_t1 = 0.f;  // int8: K scales of tiles t_0 and t_{i+1}
   if (kt < kt_end) {
     load_k(kt);
@@ -846,7 +851,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
   wait_vmem_and_sync();
   if (kt < kt_end) {
     qk(sk0, sacc[0], ks0);
-    fixup(kt, sacc[0], sm0);
+    fixup(kt, tile_st(ktp), sacc[0], sm0);
     need = check(sacc[0], mx);
   }
   __syncthreads();  // sk0 and sm0 are refilled in the first iteration
@@ -862,7 +867,15 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     char* sMw = st ? sm1 : sm0;        // mask tile of t_{i+2}
     if (need) rescale(s_cur, mx);
     const bool has1 = kt1 < kt_end;
-    const int kt2 = has1 ? next_tile(kt1 + 1) : kt_end;
+    int kt2 = has1 ? next_tile(kt1 + 1) : kt_end;
+    uint32_t st_t2 = 0u;
+    int kt3_raw = 0;  // bool masks: lookup of the tile after t_{i+2}, made scalar after the barrier
+    if constexpr (MASK == MASK_BOOL) {
+      const int pk = has1 ? kt2p : kt_end;
+      kt2 = tile_idx(pk);
+      st_t2 = tile_st(pk);
+      kt3_raw = kt2 + 1 < kt_end ? (int)s_next[min(kt2 + 1, kMaxStateTiles - 1)] : kt_end;
+    }
     // issued whether or not t_{i+1} and t_{i+2} exist (tile kt_end then: in range or read
     // as zeros, into buffers that are not read again), so the counts of loads in flight are
     // the same on every path and the wait for K(t_{i+2}) leaves the V loads in flight; the
@@ -901,7 +914,7 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     // hoisted into phase A, where their registers would add to its peak)
     if constexpr (kMaskTileLds) asm volatile("" ::: "memory");
     // phase B
-    if (has1) fixup(kt1, s_nxt, sMr);
+    if (has1) fixup(kt1, st_t1, s_nxt, sMr);
     pv(sVr, pt);
     // (stale registers when there is no t_{i+2}: the buffer is not read)
     const float ks_t2 = store_tile(sKw, kt2);
@@ -911,6 +924,10 @@ __global__ __launch_bounds__(FwdCfg<T>::NT, 1) void fwd_kernel(FwdParams p) {
     kt = kt1;
     kt1 = kt2;
     ks_t1 = ks_t2;
+    if constexpr (MASK == MASK_BOOL) {
+      st_t1 = st_t2;
+      kt2p = __builtin_amdgcn_readfirstlane(kt3_raw);
+    }
   };
   while (kt < kt_end) {
     body(std::integral_constant<int, 0>{});
