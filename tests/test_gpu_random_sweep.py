@@ -231,3 +231,90 @@ def test_random_split_forward(case):
     check_out("O", to64(o), O_ref, c["dtype"])
     if c["lse"]:
         check_lse(to64(lse), L_ref, c["dtype"])
+
+
+# ---- bool masks with whole excluded tiles ---------------------------------------------------
+# Element-wise random masks almost never leave a 64 x 64 tile all-false, so the skipping of
+# all-false key tiles (and the next-tile table built for it) is reached here: runs of
+# excluded keys (key padding, [B, 1, 1, S] or [B, H, 1, S]) or excluded key and query ranges
+# ([B, 1, S, S]: whole rows excluded give O = 0 and LSE = -inf), of random positions and
+# lengths, at lengths up to 2600 (the longer ones take the split schedule).
+
+N_RUN_CASES = 32 * _SCALE
+
+
+def _runs(r, S, n_max, len_max, min_keep=0):
+    """Bool [S]: True except for 1..n_max runs of random start and length 1..len_max, drawn
+    again until at least min_keep positions stay True."""
+    while True:
+        keep = np.ones(S, dtype=bool)
+        for _ in range(int(r.integers(1, n_max + 1))):
+            a = int(r.integers(0, S))
+            keep[a:a + int(r.integers(1, len_max + 1))] = False
+        if keep.sum() >= min_keep:
+            return keep
+
+
+def _run_cases():
+    r = np.random.default_rng(20261206)
+    out = []
+    for i in range(N_RUN_CASES):
+        B = int(r.choice([1, 2]))
+        H = int(r.choice([1, 2, 3, 4]))
+        Hkv = int(r.choice([d for d in range(1, H + 1) if H % d == 0]))
+        S = int(r.integers(64, 2601))
+        out.append(dict(i=i, B=B, H=H, Hkv=Hkv, S=S, D=int(r.choice([64, 128])),
+                        dtype=str(r.choice(["bf16", "f16", "f32"])),
+                        form=str(r.choice(["keys", "keys_per_head", "keys_and_queries"])),
+                        scale=None if r.random() < 0.6 else float(r.uniform(0.05, 0.3)),
+                        grad=bool(r.random() < 0.7) and S <= 1200))
+    return out
+
+
+RUN_CASES = _run_cases()
+
+
+def _run_mask(c):
+    """The case's bool mask (True = attend), drawn from its own seed.  Key masks keep at least
+    S/8 keys (and 2): with a single key left in every row the exact gradients of Q and K
+    vanish, and a relative error bound then measures only rounding noise against zero."""
+    r = np.random.default_rng(30000 + c["i"])
+    B, H, S = c["B"], c["H"], c["S"]
+    nk = max(2, S // 8)
+    if c["form"] == "keys":
+        m = np.stack([_runs(r, S, 4, 400, nk) for _ in range(B)])[:, None, None, :]
+    elif c["form"] == "keys_per_head":
+        m = np.stack([np.stack([_runs(r, S, 4, 400, nk) for _ in range(H)]) for _ in range(B)])[:, :, None, :]
+    else:
+        m = np.stack([_runs(r, S, 3, 300)[:, None] & _runs(r, S, 4, 400, nk)[None, :] for _ in range(B)])[:, None]
+    return torch.from_numpy(np.ascontiguousarray(m))
+
+
+@pytest.mark.parametrize("case", RUN_CASES, ids=lambda c: f"r{c['i']}_b{c['B']}h{c['H']}kv{c['Hkv']}s{c['S']}"
+                         f"d{c['D']}_{c['dtype']}_{c['form']}{'_g' if c['grad'] else ''}")
+def test_random_bool_runs(case):
+    c = case
+    mask = _run_mask(c)
+    w = syn.random_small(c["B"], c["H"], c["S"], c["D"], c["dtype"], seed=3900 + c["i"], with_grad=c["grad"],
+                         kv_heads=c["Hkv"] if c["Hkv"] < c["H"] else None)
+    d = dev()
+    q, k, v = (t.to(d) for t in (w.q, w.k, w.v))
+    okw = dict(mask=mask, mask_kind="bool", scale=c["scale"], workers=8)
+    O_ref, L_ref = rope_sdpa_forward(w.q, w.k, w.v, w.cos, w.sin, **okw)
+    if c["grad"]:
+        q, k, v = (t.detach().requires_grad_() for t in (q, k, v))
+        o = rfa.rope_scaled_dot_product_attention(q, k, v, w.cos.to(d), w.sin.to(d), attn_mask=mask.to(d),
+                                                  scale=c["scale"])
+        o.backward(w.do.to(d))
+        torch.cuda.synchronize()
+        check_out("O", to64(o), O_ref, c["dtype"])
+        grads = rope_sdpa_backward(w.q, w.k, w.v, w.cos, w.sin, w.do, **okw)
+        for name, g, ref in zip(("dQ", "dK", "dV"), (q.grad, k.grad, v.grad), grads):
+            check_grad(name, to64(g), ref, c["dtype"])
+    else:
+        with torch.no_grad():
+            o, lse = rfa.rope_sdpa_fwd_with_lse(q, k, v, w.cos.to(d), w.sin.to(d), attn_mask=mask.to(d),
+                                                scale=c["scale"])
+        torch.cuda.synchronize()
+        check_out("O", to64(o), O_ref, c["dtype"])
+        check_lse(to64(lse), L_ref, c["dtype"])
