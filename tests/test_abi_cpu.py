@@ -154,6 +154,17 @@ def test_mask_validation():
     assert c3.fwd() == ERR["RS_ERR_INVALID"]
 
 
+def test_bool_mask_length_limit():
+    """Bool masks gather their key-tile states into LDS: S <= 262144, longer is RS_ERR_SHAPE
+    (before any device work); other mask kinds have no such limit."""
+    for S, want in [(262144, "RS_ERR_NO_DEVICE"), (262145, "RS_ERR_SHAPE")]:
+        c = Call(B=1, H=1, S=S, D=64)
+        _bool_mask(c, (1, 1, 1, S), (0, 0, 0, 1))
+        assert c.fwd() == ERR[want], S
+        c.mask, c.kind = None, RS_MASK_NONE
+        assert c.fwd() == ERR["RS_ERR_NO_DEVICE"], S
+
+
 def test_int8_flag_limits():
     c = Call(dt=RS_F32, es=4)
     c.flags = RS_FLAG_QUANT_INT8_QK

@@ -273,6 +273,20 @@ def test_long_sequence_two_full_heads():
     _compare(w, pairs=[(0, 0), (0, 47)])
 
 
+def test_bool_mask_at_the_length_limit():
+    """S = 262144, the longest sequence a bool mask is accepted for (its 4096 key-tile states
+    and next-tile table in LDS): B = H = 1, D = 64, bf16, a key mask with excluded runs
+    (whole all-false tiles among all-true and mixed ones).  Sampled rows of O and LSE, each
+    against all keys, compared with the oracle."""
+    S = 262144
+    w = syn.random_small(1, 1, S, 64, dtype="bf16", seed=140)
+    keep = torch.ones(S, dtype=torch.bool)
+    for a, n in [(100, 5000), (70000, 64 * 40 + 7), (131000, 300), (200003, 9000), (S - 777, 777)]:
+        keep[a:a + n] = False
+    w.mask, w.mask_kind = keep.view(1, 1, 1, S), "bool"
+    _compare(w, rows=[0, 1, 4999, 65535, 131072, 200100, 262000, S - 1])
+
+
 # ---- additive masks in the input dtype, S a multiple of 8 -----------------------------------
 # Such masks go from memory straight into LDS with the K/V tiles.  S = 328: two query tiles
 # of the 16-bit kernel and a ragged last key tile of 8 keys.
